@@ -1,0 +1,175 @@
+"""fp64 CPU oracle for RMSNorm / LayerNorm forward and backward (ctypes wrapper of oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` import this package.  The GPU library never
+imports, links or calls it, and it never imports the GPU library.
+
+Arrays passed in are host numpy arrays of raw element bits: ``uint16`` for bfloat16
+and ``float32`` for fp32 (as produced by :mod:`gen`).  Results are float64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+F32 = 0
+BF16 = 1
+
+
+def build(src: str = SRC_PATH, out: str = LIB_PATH, verbose: bool = False) -> str:
+    """Compile the oracle (gcc, -O2, OpenMP, strict IEEE double: no -ffast-math)."""
+    cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", "-ffp-contract=off",
+           "-I", _HERE, src, "-o", out, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+_INT = ctypes.c_int
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _dtype_of(a: np.ndarray) -> int:
+    if a.dtype == np.uint16:
+        return BF16
+    if a.dtype == np.float32:
+        return F32
+    raise TypeError(f"oracle inputs are uint16 (bf16 bits) or float32, got {a.dtype}")
+
+
+class Oracle:
+    """Handle on one compiled oracle library (the real one, or a test mutant)."""
+
+    def __init__(self, path: str = LIB_PATH):
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+        lib = ctypes.CDLL(path)
+        lib.oracle_rms_fwd.argtypes = [_P, _P, _INT, _I64, _D, _P, _I64, _P, _P]
+        lib.oracle_ln_fwd.argtypes = [_P, _P, _P, _INT, _I64, _D, _P, _I64, _P, _P, _P]
+        lib.oracle_rms_bwd_dx.argtypes = [_P, _P, _P, _INT, _I64, _D, _P, _I64, _P]
+        lib.oracle_ln_bwd_dx.argtypes = [_P, _P, _P, _INT, _I64, _D, _P, _I64, _P]
+        lib.oracle_rms_bwd_dgamma.argtypes = [_P, _P, _INT, _I64, _I64, _D, _P, _P]
+        lib.oracle_ln_bwd_dgamma_dbeta.argtypes = [_P, _P, _INT, _I64, _I64, _D, _P, _P, _P, _P]
+        for name in ("oracle_rms_fwd", "oracle_ln_fwd", "oracle_rms_bwd_dx", "oracle_ln_bwd_dx",
+                     "oracle_rms_bwd_dgamma", "oracle_ln_bwd_dgamma_dbeta"):
+            getattr(lib, name).restype = None
+        lib.oracle_num_threads.restype = _INT
+        lib.oracle_num_threads.argtypes = []
+        self.lib = lib
+        self.path = path
+
+    # ----------------------------------------------------------------- helpers
+    @staticmethod
+    def _prep(x, *others):
+        x = np.ascontiguousarray(x)
+        if x.ndim != 2:
+            raise ValueError("x must be 2-D [M, N]")
+        dt = _dtype_of(x)
+        outs = []
+        for o in others:
+            if o is None:
+                outs.append(None)
+                continue
+            o = np.ascontiguousarray(o)
+            if _dtype_of(o) != dt:
+                raise TypeError("all inputs must share x's dtype")
+            outs.append(o)
+        return x, dt, outs
+
+    @staticmethod
+    def _rows(rows, M):
+        if rows is None:
+            return None, M
+        r = np.ascontiguousarray(rows, dtype=np.int64)
+        if r.size and (r.min() < 0 or r.max() >= M):
+            raise IndexError("row index out of range")
+        return r, r.size
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    # ----------------------------------------------------------------- forward
+    def rms_fwd(self, x, gamma, eps, rows=None):
+        """-> (y [k, N] float64, rstd [k] float64) for the selected rows."""
+        x, dt, (gamma,) = self._prep(x, gamma)
+        M, N = x.shape
+        r, k = self._rows(rows, M)
+        y = np.empty((k, N), np.float64)
+        rstd = np.empty(k, np.float64)
+        self.lib.oracle_rms_fwd(_ptr(x), _ptr(gamma), dt, N, float(eps), _ptr(r), k,
+                                _ptr(y), _ptr(rstd))
+        return y, rstd
+
+    def ln_fwd(self, x, gamma, beta, eps, rows=None):
+        """-> (y, mean, rstd) float64 for the selected rows."""
+        x, dt, (gamma, beta) = self._prep(x, gamma, beta)
+        M, N = x.shape
+        r, k = self._rows(rows, M)
+        y = np.empty((k, N), np.float64)
+        mean = np.empty(k, np.float64)
+        rstd = np.empty(k, np.float64)
+        self.lib.oracle_ln_fwd(_ptr(x), _ptr(gamma), _ptr(beta), dt, N, float(eps), _ptr(r), k,
+                               _ptr(y), _ptr(mean), _ptr(rstd))
+        return y, mean, rstd
+
+    # ---------------------------------------------------------------- backward
+    def rms_bwd_dx(self, dy, x, gamma, eps, rows=None):
+        x, dt, (dy, gamma) = self._prep(x, dy, gamma)
+        M, N = x.shape
+        r, k = self._rows(rows, M)
+        dx = np.empty((k, N), np.float64)
+        self.lib.oracle_rms_bwd_dx(_ptr(dy), _ptr(x), _ptr(gamma), dt, N, float(eps), _ptr(r), k,
+                                   _ptr(dx))
+        return dx
+
+    def ln_bwd_dx(self, dy, x, gamma, eps, rows=None):
+        x, dt, (dy, gamma) = self._prep(x, dy, gamma)
+        M, N = x.shape
+        r, k = self._rows(rows, M)
+        dx = np.empty((k, N), np.float64)
+        self.lib.oracle_ln_bwd_dx(_ptr(dy), _ptr(x), _ptr(gamma), dt, N, float(eps), _ptr(r), k,
+                                  _ptr(dx))
+        return dx
+
+    def rms_dgamma(self, dy, x, eps):
+        """-> (dgamma [N], scale [N]) float64."""
+        x, dt, (dy,) = self._prep(x, dy)
+        M, N = x.shape
+        dg = np.empty(N, np.float64)
+        sc = np.empty(N, np.float64)
+        self.lib.oracle_rms_bwd_dgamma(_ptr(dy), _ptr(x), dt, M, N, float(eps), _ptr(dg), _ptr(sc))
+        return dg, sc
+
+    def ln_dgamma_dbeta(self, dy, x, eps):
+        """-> (dgamma, dbeta, dgamma_scale, dbeta_scale), each [N] float64."""
+        x, dt, (dy,) = self._prep(x, dy)
+        M, N = x.shape
+        dg, db, sg, sb = (np.empty(N, np.float64) for _ in range(4))
+        self.lib.oracle_ln_bwd_dgamma_dbeta(_ptr(dy), _ptr(x), dt, M, N, float(eps), _ptr(dg),
+                                            _ptr(db), _ptr(sg), _ptr(sb))
+        return dg, db, sg, sb
+
+
+_default = None
+
+
+def get() -> Oracle:
+    """The oracle built next to this file."""
+    global _default
+    if _default is None:
+        _default = Oracle(LIB_PATH)
+    return _default

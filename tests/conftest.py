@@ -1,0 +1,28 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
+    # The CPU helper libraries are built on demand (gcc) when they are missing.
+    import gen
+    import oracle
+    if not os.path.exists(gen._LIB_PATH):
+        gen.build()
+    if not os.path.exists(oracle.LIB_PATH):
+        oracle.build()
+
+
+@pytest.fixture(scope="session")
+def orc():
+    import oracle
+    return oracle.get()
