@@ -1,0 +1,197 @@
+/*
+ * rownorm.h -- fused row normalization (RMSNorm and LayerNorm, forward and backward)
+ * for AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes, no C++ types,
+ * no exceptions across the boundary.
+ *
+ * What is computed (row i of a row-major [M, N] matrix, j = column):
+ *
+ *   RMSNorm forward -- "Fused RMSNorm" (aryanashta.me), section "What it is": the row
+ *   is divided by its root-mean-square and scaled by gamma, the steps being square,
+ *   mean, add eps, reciprocal square root, multiply, multiply:
+ *       rstd_i = 1 / sqrt(mean_j(x_ij^2) + eps),   y_ij = x_ij * rstd_i * gamma_j
+ *
+ *   LayerNorm forward -- "SOTA normalization performance with torch.compile"
+ *   (theaicatchup.com), section "How Did Torch.compile Catch Quack?": subtract the row
+ *   mean, divide by the standard deviation, scale by gamma, shift by beta; the
+ *   statistics are stored when the backward needs them:
+ *       mean_i = mean_j(x_ij),  var_i = mean_j((x_ij - mean_i)^2) (biased),
+ *       rstd_i = 1 / sqrt(var_i + eps),  y_ij = (x_ij - mean_i) * rstd_i * gamma_j + beta_j
+ *
+ *   Backward -- same page, section "Why Is Peak Vectorization Your New Best Friend?":
+ *   the outputs are dX, dW (gamma) and, for LayerNorm, dB, with reductions over the
+ *   rows of dY.  With xhat = (x - mean) * rstd (RMSNorm: x * rstd) and g = dy * gamma:
+ *       c1_i = mean_j(g_ij * xhat_ij),  c2_i = mean_j(g_ij)   (LayerNorm only)
+ *       dx_ij = rstd_i * (g_ij - c2_i - xhat_ij * c1_i)       (RMSNorm: no c2 term)
+ *       dgamma_j = sum_i dy_ij * xhat_ij,  dbeta_j = sum_i dy_ij
+ *   dgamma/dbeta are reduced in two stages without atomics (per-workgroup partial
+ *   rows in a workspace, then a column-reduce kernel), the scheme "Fused RMSNorm",
+ *   section "What didn't work", credits for the backward's speed.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller allocates and frees every buffer.  The library allocates
+ *     no device memory and keeps no pointer after it returns.
+ *   - Asynchrony: work is enqueued on `stream` (0 = the null stream); results are
+ *     valid once the stream has synchronised.  The workspace must stay alive until
+ *     the backward has completed on that stream.  Calls on one stream are ordered;
+ *     concurrent calls on different streams must not share a workspace.
+ *   - Errors: every argument check runs on the host before any HIP call; on an
+ *     invalid argument the call returns its status and enqueues nothing.  A failed
+ *     launch returns NORM_ERR_HIP.  No C++ exception crosses the boundary.
+ *   - Layout: x, y, dy, dx are contiguous row-major [M, N] with row stride N; gamma
+ *     and beta are [N]; mean and rstd are float [M]; dgamma and dbeta are float [N].
+ *     x, gamma, beta, y, dy, dx share `dtype`.  Element pointers must be aligned to
+ *     their element size and float pointers to 4 bytes.  The fast kernels need 16-byte
+ *     aligned pointers and N * sizeof(element) a multiple of 16; other inputs run
+ *     on a correct, slower scalar path.
+ *   - Shapes: M >= 0, 1 <= N <= 2^31 - 1.  M = 0 is a no-op for the forward; the
+ *     backward then writes zeros to dgamma/dbeta (a sum over no rows).
+ *   - eps must be finite and >= 0 (eps = 0 is allowed; a constant or zero row then
+ *     gives inf/NaN, as the definition does).
+ *   - Outputs must not overlap inputs.  dgamma/dbeta are overwritten, not accumulated.
+ *   - NaN/Inf inputs propagate: a non-finite element makes its row's outputs (and
+ *     the dgamma/dbeta columns it touches) non-finite.
+ */
+#ifndef ROWNORM_H
+#define ROWNORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum norm_dtype { NORM_DTYPE_F32 = 0, NORM_DTYPE_BF16 = 1 } norm_dtype_t;
+
+typedef enum norm_status {
+  NORM_OK = 0,
+  NORM_ERR_NULL_PTR = 1,             /* a required pointer is NULL */
+  NORM_ERR_BAD_SHAPE = 2,            /* M < 0, N < 1, N > 2^31-1 or M*N overflows */
+  NORM_ERR_BAD_DTYPE = 3,            /* dtype is not a norm_dtype_t value */
+  NORM_ERR_BAD_EPS = 4,              /* eps is negative, NaN or infinite */
+  NORM_ERR_WORKSPACE_TOO_SMALL = 5,  /* workspace_bytes < the size the call needs */
+  NORM_ERR_HIP = 6,                  /* a HIP runtime call or launch failed */
+  NORM_ERR_MISALIGNED = 7,           /* a pointer is not aligned to its element size */
+  NORM_ERR_BAD_OPTION = 8            /* a norm_options_t field is out of range */
+} norm_status_t;
+
+/* ------------------------------------------------------------------ forward */
+
+/* RMSNorm forward.  x, gamma, y: `dtype`; rstd: float [M], or NULL to not save it. */
+norm_status_t norm_rms_fwd(const void* x, const void* gamma, void* y, float* rstd,
+                           int64_t M, int64_t N, float eps, norm_dtype_t dtype,
+                           hipStream_t stream);
+
+/* LayerNorm forward.  mean and rstd: float [M]; each may be NULL to not save it. */
+norm_status_t norm_ln_fwd(const void* x, const void* gamma, const void* beta, void* y,
+                          float* mean, float* rstd, int64_t M, int64_t N, float eps,
+                          norm_dtype_t dtype, hipStream_t stream);
+
+/* ----------------------------------------------------------------- backward */
+
+/* Bytes of workspace the backward needs for this shape (0 means none).  A pure
+ * function of its arguments: it makes no HIP call and is valid on any gfx950 device. */
+size_t norm_bwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype);
+
+/* RMSNorm backward.  dy, x, gamma, dx: `dtype`; rstd: the forward's saved float [M];
+ * dgamma: float [N], overwritten.  workspace: device memory of at least
+ * norm_bwd_workspace_size(M, N, 0, dtype) bytes, 16-byte aligned (may be NULL when
+ * that size is 0).  Its contents on entry do not matter. */
+norm_status_t norm_rms_bwd(const void* dy, const void* x, const void* gamma, const float* rstd,
+                           void* dx, float* dgamma, int64_t M, int64_t N, norm_dtype_t dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* LayerNorm backward.  mean, rstd: the forward's saved float [M]; dgamma, dbeta:
+ * float [N], overwritten.  Workspace as above with is_layernorm = 1. */
+norm_status_t norm_ln_bwd(const void* dy, const void* x, const void* gamma, const float* mean,
+                          const float* rstd, void* dx, float* dgamma, float* dbeta, int64_t M,
+                          int64_t N, norm_dtype_t dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* norm_status_string(norm_status_t status);
+
+/* ------------------------------------------------ options, plans, measurement */
+
+/* How dgamma/dbeta are reduced over rows.  TWO_STAGE is the library's scheme.  The two
+ * atomic modes exist to measure the alternative the "Fused RMSNorm" page describes in
+ * its sections "How it works" and "What didn't work" (every block adding its partial
+ * into one shared vector with atomics): ATOMIC_ROW adds every row's contribution
+ * (M*N atomic adds), ATOMIC_WG adds one partial per workgroup (grid*N atomic adds).
+ * Atomic results depend on the order of the adds and are not bitwise reproducible. */
+typedef enum norm_dgamma_mode {
+  NORM_DGAMMA_TWO_STAGE = 0,
+  NORM_DGAMMA_ATOMIC_ROW = 1,
+  NORM_DGAMMA_ATOMIC_WG = 2
+} norm_dgamma_mode_t;
+
+/* Kernel families. */
+typedef enum norm_path {
+  NORM_PATH_AUTO = 0,      /* the planner's choice */
+  NORM_PATH_ROWS = 1,      /* register-resident rows: lanes_per_row lanes hold one row */
+  NORM_PATH_SPLIT = 2,     /* backward for rows too long to keep per-column partials in
+                              registers: a per-row reduction pass, then a
+                              column-sliced pass for dx and the partials */
+  NORM_PATH_GENERIC = 3    /* scalar loads, any N and alignment */
+} norm_path_t;
+
+/* Options for the *_ex entry points; zero-initialise for defaults.  Used by tests and
+ * benchmarks to force every mapping on the same inputs. */
+typedef struct norm_options {
+  int path;            /* norm_path_t */
+  int lanes_per_row;   /* ROWS path: 8, 16, 32 or 64 (lanes of one wavefront) or 128,
+                          256, 512, 1024 (one workgroup per row); 0 = planner */
+  int vecs_per_lane;   /* ROWS path: 16-byte vectors each lane holds per row; 0 = planner */
+  int dgamma_mode;     /* norm_dgamma_mode_t (backward only) */
+  int grid;            /* persistent workgroups; 0 = planner.  For the backward it must
+                          not exceed the planner's partial-row count for the shape */
+  hipEvent_t ev_start; /* if non-NULL, recorded on `stream` just before the main kernel */
+  hipEvent_t ev_stop;  /* if non-NULL, recorded on `stream` just after the main kernel */
+} norm_options_t;
+
+/* What the planner chose for a call (filled by norm_plan). */
+typedef struct norm_plan_info {
+  int path;              /* norm_path_t actually used */
+  int lanes_per_row;
+  int vecs_per_lane;
+  int block;             /* threads per workgroup of the main kernel */
+  int grid;              /* workgroups of the main kernel */
+  int partial_rows;      /* rows of dgamma/dbeta partials the backward writes */
+  size_t workspace_bytes;
+} norm_plan_info_t;
+
+/* Fill *info for a forward (is_backward = 0) or backward call with these arguments.
+ * Pure host function; `aligned16` states whether every element pointer of the call
+ * is 16-byte aligned. */
+norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
+                        norm_dtype_t dtype, int aligned16, const norm_options_t* opt,
+                        norm_plan_info_t* info);
+
+/* Workspace size for a backward call made with these options (NULL = defaults). */
+size_t norm_bwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
+                                  const norm_options_t* opt);
+
+/* The entry points above with options (opt may be NULL). */
+norm_status_t norm_rms_fwd_ex(const void* x, const void* gamma, void* y, float* rstd,
+                              int64_t M, int64_t N, float eps, norm_dtype_t dtype,
+                              hipStream_t stream, const norm_options_t* opt);
+norm_status_t norm_ln_fwd_ex(const void* x, const void* gamma, const void* beta, void* y,
+                             float* mean, float* rstd, int64_t M, int64_t N, float eps,
+                             norm_dtype_t dtype, hipStream_t stream, const norm_options_t* opt);
+norm_status_t norm_rms_bwd_ex(const void* dy, const void* x, const void* gamma,
+                              const float* rstd, void* dx, float* dgamma, int64_t M, int64_t N,
+                              norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const norm_options_t* opt);
+norm_status_t norm_ln_bwd_ex(const void* dy, const void* x, const void* gamma,
+                             const float* mean, const float* rstd, void* dx, float* dgamma,
+                             float* dbeta, int64_t M, int64_t N, norm_dtype_t dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             const norm_options_t* opt);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ROWNORM_H */

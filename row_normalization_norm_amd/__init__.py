@@ -1,0 +1,264 @@
+"""Python binding of librownorm.so: fused RMSNorm / LayerNorm forward and backward on
+MI355X (gfx950).
+
+The functions carry the C entry points' names (include/rownorm.h) and only marshal
+arguments: they read shapes, dtypes and device pointers off torch tensors, pass the
+current HIP stream, and raise :class:`NormError` on a non-OK status.  Every step of the
+computation runs in the library's HIP kernels; there is no fallback.  torch is used for
+device memory and streams only.
+
+Raw ctypes access to the library is available through :func:`lib`.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librownorm.so")
+
+# norm_dtype_t
+NORM_DTYPE_F32 = 0
+NORM_DTYPE_BF16 = 1
+# norm_status_t
+NORM_OK = 0
+NORM_ERR_NULL_PTR = 1
+NORM_ERR_BAD_SHAPE = 2
+NORM_ERR_BAD_DTYPE = 3
+NORM_ERR_BAD_EPS = 4
+NORM_ERR_WORKSPACE_TOO_SMALL = 5
+NORM_ERR_HIP = 6
+NORM_ERR_MISALIGNED = 7
+NORM_ERR_BAD_OPTION = 8
+# norm_dgamma_mode_t
+NORM_DGAMMA_TWO_STAGE = 0
+NORM_DGAMMA_ATOMIC_ROW = 1
+NORM_DGAMMA_ATOMIC_WG = 2
+# norm_path_t
+NORM_PATH_AUTO = 0
+NORM_PATH_ROWS = 1
+NORM_PATH_SPLIT = 2
+NORM_PATH_GENERIC = 3
+
+
+class NormError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class Options(ctypes.Structure):
+    """norm_options_t."""
+    _fields_ = [("path", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
+                ("vecs_per_lane", ctypes.c_int), ("dgamma_mode", ctypes.c_int),
+                ("grid", ctypes.c_int), ("ev_start", ctypes.c_void_p),
+                ("ev_stop", ctypes.c_void_p)]
+
+
+class PlanInfo(ctypes.Structure):
+    """norm_plan_info_t."""
+    _fields_ = [("path", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
+                ("vecs_per_lane", ctypes.c_int), ("block", ctypes.c_int),
+                ("grid", ctypes.c_int), ("partial_rows", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_INT = ctypes.c_int
+_F = ctypes.c_float
+_SZ = ctypes.c_size_t
+_OPT = ctypes.POINTER(Options)
+
+SIGNATURES = {
+    "norm_rms_fwd": (_INT, [_P, _P, _P, _P, _I64, _I64, _F, _INT, _P]),
+    "norm_ln_fwd": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P]),
+    "norm_bwd_workspace_size": (_SZ, [_I64, _I64, _INT, _INT]),
+    "norm_rms_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P]),
+    "norm_ln_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P]),
+    "norm_status_string": (ctypes.c_char_p, [_INT]),
+    "norm_plan": (_INT, [_INT, _INT, _I64, _I64, _INT, _INT, _OPT, ctypes.POINTER(PlanInfo)]),
+    "norm_bwd_workspace_size_ex": (_SZ, [_I64, _I64, _INT, _INT, _OPT]),
+    "norm_rms_fwd_ex": (_INT, [_P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _OPT]),
+    "norm_ln_fwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _OPT]),
+    "norm_rms_bwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P, _OPT]),
+    "norm_ln_bwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P,
+                              _OPT]),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librownorm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                f"g.build()'` (hipcc, gfx950)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().norm_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != NORM_OK:
+        raise NormError(status, where)
+
+
+# ------------------------------------------------------------------- marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return NORM_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return NORM_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, name, numel, dtype, device):
+    if t is None:
+        return
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def _shape(x):
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, N] (reshape leading dimensions into M)")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def _stream(device, stream):
+    torch = _torch()
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _opt(options):
+    return None if options is None else ctypes.byref(options)
+
+
+# ------------------------------------------------------------------- entry points
+def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, stream=None, options=None):
+    """y = x * rstd * gamma with rstd = 1/sqrt(mean(x^2) + eps) per row; rstd saved if given."""
+    torch = _torch()
+    M, N = _shape(x)
+    _need(x, "x", M * N, x.dtype, x.device)
+    for t, n, k in ((gamma, "gamma", N), (y, "y", M * N)):
+        _need(t, n, k, x.dtype, x.device)
+    _need(rstd, "rstd", M, torch.float32, x.device)
+    args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), _dtype_code(x),
+            _stream(x.device, stream))
+    if options is None:
+        _check(lib().norm_rms_fwd(*args), "norm_rms_fwd")
+    else:
+        _check(lib().norm_rms_fwd_ex(*args, _opt(options)), "norm_rms_fwd_ex")
+    return y
+
+
+def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, stream=None,
+                options=None):
+    """y = (x - mean) * rstd * gamma + beta per row; mean and rstd saved if given."""
+    torch = _torch()
+    M, N = _shape(x)
+    _need(x, "x", M * N, x.dtype, x.device)
+    for t, n, k in ((gamma, "gamma", N), (beta, "beta", N), (y, "y", M * N)):
+        _need(t, n, k, x.dtype, x.device)
+    _need(mean, "mean", M, torch.float32, x.device)
+    _need(rstd, "rstd", M, torch.float32, x.device)
+    args = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, float(eps),
+            _dtype_code(x), _stream(x.device, stream))
+    if options is None:
+        _check(lib().norm_ln_fwd(*args), "norm_ln_fwd")
+    else:
+        _check(lib().norm_ln_fwd_ex(*args, _opt(options)), "norm_ln_fwd_ex")
+    return y
+
+
+def norm_bwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, options=None) -> int:
+    if options is None:
+        return int(lib().norm_bwd_workspace_size(M, N, int(bool(is_layernorm)), dtype))
+    return int(lib().norm_bwd_workspace_size_ex(M, N, int(bool(is_layernorm)), dtype,
+                                                _opt(options)))
+
+
+def _workspace(M, N, ln, dtype, device, workspace, options):
+    torch = _torch()
+    need = norm_bwd_workspace_size(M, N, ln, dtype, options)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def norm_rms_bwd(dy, x, gamma, rstd, dx, dgamma, workspace=None, stream=None, options=None):
+    """dx and dgamma (overwritten) of RMSNorm from the forward's saved rstd."""
+    torch = _torch()
+    M, N = _shape(x)
+    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (gamma, "gamma", N), (dx, "dx", M * N)):
+        _need(t, n, k, x.dtype, x.device)
+    _need(rstd, "rstd", M, torch.float32, x.device)
+    _need(dgamma, "dgamma", N, torch.float32, x.device)
+    dt = _dtype_code(x)
+    ws, ws_bytes = _workspace(M, N, False, dt, x.device, workspace, options)
+    args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N, dt,
+            _ptr(ws), ws_bytes, _stream(x.device, stream))
+    if options is None:
+        _check(lib().norm_rms_bwd(*args), "norm_rms_bwd")
+    else:
+        _check(lib().norm_rms_bwd_ex(*args, _opt(options)), "norm_rms_bwd_ex")
+    return dx, dgamma
+
+
+def norm_ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace=None, stream=None,
+                options=None):
+    """dx, dgamma and dbeta (overwritten) of LayerNorm from the saved mean and rstd."""
+    torch = _torch()
+    M, N = _shape(x)
+    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (gamma, "gamma", N), (dx, "dx", M * N)):
+        _need(t, n, k, x.dtype, x.device)
+    for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
+                    (dbeta, "dbeta", N)):
+        _need(t, n, k, torch.float32, x.device)
+    dt = _dtype_code(x)
+    ws, ws_bytes = _workspace(M, N, True, dt, x.device, workspace, options)
+    args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
+            _ptr(dbeta), M, N, dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
+    if options is None:
+        _check(lib().norm_ln_bwd(*args), "norm_ln_bwd")
+    else:
+        _check(lib().norm_ln_bwd_ex(*args, _opt(options)), "norm_ln_bwd_ex")
+    return dx, dgamma, dbeta
+
+
+def norm_plan(is_backward: bool, is_layernorm: bool, M: int, N: int, dtype: int,
+              aligned16: bool = True, options=None) -> PlanInfo:
+    info = PlanInfo()
+    _check(lib().norm_plan(int(bool(is_backward)), int(bool(is_layernorm)), M, N, dtype,
+                           int(bool(aligned16)), _opt(options), ctypes.byref(info)), "norm_plan")
+    return info

@@ -1,0 +1,327 @@
+// C ABI of the row-normalization library (declared in include/rownorm.h).
+//
+// Every argument is checked on the host before any HIP call, so an invalid call
+// returns its status with nothing enqueued.  Valid calls plan the mapping (plan.cpp)
+// and enqueue the kernels on the caller's stream; nothing here synchronises,
+// allocates device memory, or keeps a pointer past the call.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/rownorm.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace rownorm {
+
+// Per-(kind, dtype) launchers, one translation unit each.
+hipError_t launch_fwd_rows_k0_d0(int, int, const FwdArgs&, int, hipStream_t);
+hipError_t launch_fwd_rows_k0_d1(int, int, const FwdArgs&, int, hipStream_t);
+hipError_t launch_fwd_rows_k1_d0(int, int, const FwdArgs&, int, hipStream_t);
+hipError_t launch_fwd_rows_k1_d1(int, int, const FwdArgs&, int, hipStream_t);
+hipError_t launch_bwd_rows_k0_d0(int, int, const BwdArgs&, int, hipStream_t);
+hipError_t launch_bwd_rows_k0_d1(int, int, const BwdArgs&, int, hipStream_t);
+hipError_t launch_bwd_rows_k1_d0(int, int, const BwdArgs&, int, hipStream_t);
+hipError_t launch_bwd_rows_k1_d1(int, int, const BwdArgs&, int, hipStream_t);
+
+hipError_t launch_fwd_rows(int kind, int dtype, int lpr, int vpl, const FwdArgs& a, int grid,
+                           hipStream_t s) {
+  if (kind == 0) {
+    return dtype ? launch_fwd_rows_k0_d1(lpr, vpl, a, grid, s)
+                 : launch_fwd_rows_k0_d0(lpr, vpl, a, grid, s);
+  }
+  return dtype ? launch_fwd_rows_k1_d1(lpr, vpl, a, grid, s)
+               : launch_fwd_rows_k1_d0(lpr, vpl, a, grid, s);
+}
+
+hipError_t launch_bwd_rows(int kind, int dtype, int lpr, int vpl, const BwdArgs& a, int grid,
+                           hipStream_t s) {
+  if (kind == 0) {
+    return dtype ? launch_bwd_rows_k0_d1(lpr, vpl, a, grid, s)
+                 : launch_bwd_rows_k0_d0(lpr, vpl, a, grid, s);
+  }
+  return dtype ? launch_bwd_rows_k1_d1(lpr, vpl, a, grid, s)
+               : launch_bwd_rows_k1_d0(lpr, vpl, a, grid, s);
+}
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+norm_status_t check_shape_dtype(int64_t M, int64_t N, norm_dtype_t dtype) {
+  if (dtype != NORM_DTYPE_F32 && dtype != NORM_DTYPE_BF16) return NORM_ERR_BAD_DTYPE;
+  if (M < 0 || N < 1 || N > INT32_MAX) return NORM_ERR_BAD_SHAPE;
+  // Keep M*N*16 (the largest byte offset any kernel forms) within int64.
+  if (M > 0 && M > (INT64_MAX / 16) / N) return NORM_ERR_BAD_SHAPE;
+  return NORM_OK;
+}
+
+norm_status_t hip_status(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_ERR_HIP; }
+
+struct EventScope {
+  const norm_options_t* opt;
+  hipStream_t stream;
+  hipError_t start() const {
+    return (opt && opt->ev_start) ? hipEventRecord(opt->ev_start, stream) : hipSuccess;
+  }
+  hipError_t stop() const {
+    return (opt && opt->ev_stop) ? hipEventRecord(opt->ev_stop, stream) : hipSuccess;
+  }
+};
+
+norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* beta, void* y,
+                       float* mean, float* rstd, int64_t M, int64_t N, float eps,
+                       norm_dtype_t dtype, hipStream_t stream, const norm_options_t* opt) {
+  norm_status_t st = check_shape_dtype(M, N, dtype);
+  if (st != NORM_OK) return st;
+  if (!gamma || (ln && !beta)) return NORM_ERR_NULL_PTR;
+  if (M > 0 && (!x || !y)) return NORM_ERR_NULL_PTR;
+  if (!std::isfinite(eps) || eps < 0.0f) return NORM_ERR_BAD_EPS;
+  const uintptr_t es = dtype == NORM_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, es) || !aligned(beta, es) ||
+      !aligned(mean, 4) || !aligned(rstd, 4))
+    return NORM_ERR_MISALIGNED;
+  const bool a16 = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16);
+
+  Plan p;
+  st = make_plan(false, ln, M, N, dtype, a16, opt, &p);
+  if (st != NORM_OK) return st;
+  if (M == 0) return NORM_OK;
+
+  FwdArgs a;
+  a.x = x;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.y = y;
+  a.mean = mean;
+  a.rstd = rstd;
+  a.M = M;
+  a.N = int32_t(N);
+  a.nvec = p.nvec;
+  a.eps = eps;
+  a.inv_n = 1.0f / float(N);
+  a.groups = p.groups;
+
+  const int kind = ln ? 1 : 0;
+  const int dt = dtype == NORM_DTYPE_BF16 ? 1 : 0;
+  EventScope ev{opt, stream};
+  if (ev.start() != hipSuccess) return NORM_ERR_HIP;
+  hipError_t e = p.path == NORM_PATH_ROWS
+                     ? launch_fwd_rows(kind, dt, p.lpr, p.vpl, a, p.grid, stream)
+                     : launch_fwd_generic(kind, dt, a, p.grid, stream);
+  if (e != hipSuccess) return NORM_ERR_HIP;
+  return hip_status(ev.stop());
+}
+
+norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma,
+                       const float* mean, const float* rstd, void* dx, float* dgamma,
+                       float* dbeta, int64_t M, int64_t N, norm_dtype_t dtype, void* workspace,
+                       size_t workspace_bytes_given, hipStream_t stream,
+                       const norm_options_t* opt) {
+  norm_status_t st = check_shape_dtype(M, N, dtype);
+  if (st != NORM_OK) return st;
+  if (!gamma || !dgamma || (ln && !dbeta)) return NORM_ERR_NULL_PTR;
+  if (M > 0 && (!dy || !x || !rstd || !dx || (ln && !mean))) return NORM_ERR_NULL_PTR;
+  const uintptr_t es = dtype == NORM_DTYPE_BF16 ? 2 : 4;
+  if (!aligned(dy, es) || !aligned(x, es) || !aligned(gamma, es) || !aligned(dx, es) ||
+      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4))
+    return NORM_ERR_MISALIGNED;
+  const bool a16 = aligned(dy, 16) && aligned(x, 16) && aligned(gamma, 16) && aligned(dx, 16);
+
+  Plan p;
+  st = make_plan(true, ln, M, N, dtype, a16, opt, &p);
+  if (st != NORM_OK) return st;
+  if (p.ws_bytes > 0) {
+    if (!workspace) return NORM_ERR_NULL_PTR;
+    if (!aligned(workspace, 16)) return NORM_ERR_MISALIGNED;
+    if (workspace_bytes_given < p.ws_bytes) return NORM_ERR_WORKSPACE_TOO_SMALL;
+  }
+
+  const int kind = ln ? 1 : 0;
+  const int dt = dtype == NORM_DTYPE_BF16 ? 1 : 0;
+  const int mode = opt ? opt->dgamma_mode : NORM_DGAMMA_TWO_STAGE;
+  float* const db = ln ? dbeta : nullptr;
+
+  if (M == 0) {  // a sum over no rows
+    return hip_status(launch_zero(dgamma, db, int32_t(N), stream));
+  }
+
+  char* ws = static_cast<char*>(workspace);
+  BwdArgs a;
+  a.dy = dy;
+  a.x = x;
+  a.gamma = gamma;
+  a.mean = mean;
+  a.rstd = rstd;
+  a.dx = dx;
+  a.part_g = p.ws_bytes ? reinterpret_cast<float*>(ws + p.off_part_g) : nullptr;
+  a.part_b = (p.ws_bytes && ln) ? reinterpret_cast<float*>(ws + p.off_part_b) : nullptr;
+  a.dgamma = dgamma;
+  a.dbeta = db;
+  a.rowc = (p.ws_bytes && p.path != NORM_PATH_ROWS) ? reinterpret_cast<float*>(ws + p.off_rowc)
+                                                     : nullptr;
+  a.M = M;
+  a.N = int32_t(N);
+  a.nvec = p.nvec;
+  a.inv_n = 1.0f / float(N);
+  a.mode = mode;
+  a.groups = p.groups;
+  a.rows_per_block = p.rows_per_block;
+
+  EventScope ev{opt, stream};
+  hipError_t e = hipSuccess;
+  if (mode != NORM_DGAMMA_TWO_STAGE) {
+    e = launch_zero(dgamma, db, int32_t(N), stream);
+    if (e != hipSuccess) return NORM_ERR_HIP;
+  }
+  if (ev.start() != hipSuccess) return NORM_ERR_HIP;
+  if (p.path == NORM_PATH_ROWS) {
+    e = launch_bwd_rows(kind, dt, p.lpr, p.vpl, a, p.grid, stream);
+  } else {
+    const bool vec = p.path == NORM_PATH_SPLIT;
+    e = launch_bwd_rowdot(kind, dt, vec, a, p.grid, stream);
+    if (e == hipSuccess)
+      e = launch_bwd_colslice(kind, dt, vec, a, p.slices, int(p.partial_rows), stream);
+  }
+  if (e != hipSuccess) return NORM_ERR_HIP;
+  if (ev.stop() != hipSuccess) return NORM_ERR_HIP;
+  if (mode == NORM_DGAMMA_TWO_STAGE) {
+    e = launch_colreduce(a.part_g, a.part_b, p.partial_rows, int32_t(N), dgamma, db, stream);
+  }
+  return hip_status(e);
+}
+
+template <typename F>
+norm_status_t guarded(F&& f) {
+  try {
+    return f();
+  } catch (...) {
+    return NORM_ERR_HIP;
+  }
+}
+
+}  // namespace
+}  // namespace rownorm
+
+using rownorm::bwd_impl;
+using rownorm::fwd_impl;
+using rownorm::guarded;
+
+extern "C" {
+
+norm_status_t norm_rms_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M,
+                           int64_t N, float eps, norm_dtype_t dtype, hipStream_t stream) {
+  return guarded([&] {
+    return fwd_impl(false, x, gamma, nullptr, y, nullptr, rstd, M, N, eps, dtype, stream, nullptr);
+  });
+}
+
+norm_status_t norm_ln_fwd(const void* x, const void* gamma, const void* beta, void* y,
+                          float* mean, float* rstd, int64_t M, int64_t N, float eps,
+                          norm_dtype_t dtype, hipStream_t stream) {
+  return guarded([&] {
+    return fwd_impl(true, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream, nullptr);
+  });
+}
+
+norm_status_t norm_rms_fwd_ex(const void* x, const void* gamma, void* y, float* rstd, int64_t M,
+                              int64_t N, float eps, norm_dtype_t dtype, hipStream_t stream,
+                              const norm_options_t* opt) {
+  return guarded([&] {
+    return fwd_impl(false, x, gamma, nullptr, y, nullptr, rstd, M, N, eps, dtype, stream, opt);
+  });
+}
+
+norm_status_t norm_ln_fwd_ex(const void* x, const void* gamma, const void* beta, void* y,
+                             float* mean, float* rstd, int64_t M, int64_t N, float eps,
+                             norm_dtype_t dtype, hipStream_t stream, const norm_options_t* opt) {
+  return guarded([&] {
+    return fwd_impl(true, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream, opt);
+  });
+}
+
+size_t norm_bwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype) {
+  return norm_bwd_workspace_size_ex(M, N, is_layernorm, dtype, nullptr);
+}
+
+size_t norm_bwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
+                                  const norm_options_t* opt) {
+  if (rownorm::check_shape_dtype(M, N, dtype) != NORM_OK) return 0;
+  return rownorm::workspace_bytes(M, N, is_layernorm != 0, dtype, opt);
+}
+
+norm_status_t norm_rms_bwd(const void* dy, const void* x, const void* gamma, const float* rstd,
+                           void* dx, float* dgamma, int64_t M, int64_t N, norm_dtype_t dtype,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return guarded([&] {
+    return bwd_impl(false, dy, x, gamma, nullptr, rstd, dx, dgamma, nullptr, M, N, dtype,
+                    workspace, workspace_bytes, stream, nullptr);
+  });
+}
+
+norm_status_t norm_ln_bwd(const void* dy, const void* x, const void* gamma, const float* mean,
+                          const float* rstd, void* dx, float* dgamma, float* dbeta, int64_t M,
+                          int64_t N, norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  return guarded([&] {
+    return bwd_impl(true, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, M, N, dtype, workspace,
+                    workspace_bytes, stream, nullptr);
+  });
+}
+
+norm_status_t norm_rms_bwd_ex(const void* dy, const void* x, const void* gamma,
+                              const float* rstd, void* dx, float* dgamma, int64_t M, int64_t N,
+                              norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const norm_options_t* opt) {
+  return guarded([&] {
+    return bwd_impl(false, dy, x, gamma, nullptr, rstd, dx, dgamma, nullptr, M, N, dtype,
+                    workspace, workspace_bytes, stream, opt);
+  });
+}
+
+norm_status_t norm_ln_bwd_ex(const void* dy, const void* x, const void* gamma,
+                             const float* mean, const float* rstd, void* dx, float* dgamma,
+                             float* dbeta, int64_t M, int64_t N, norm_dtype_t dtype,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             const norm_options_t* opt) {
+  return guarded([&] {
+    return bwd_impl(true, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, M, N, dtype, workspace,
+                    workspace_bytes, stream, opt);
+  });
+}
+
+norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
+                        norm_dtype_t dtype, int aligned16, const norm_options_t* opt,
+                        norm_plan_info_t* info) {
+  if (!info) return NORM_ERR_NULL_PTR;
+  norm_status_t st = rownorm::check_shape_dtype(M, N, dtype);
+  if (st != NORM_OK) return st;
+  rownorm::Plan p;
+  st = rownorm::make_plan(is_backward != 0, is_layernorm != 0, M, N, dtype, aligned16 != 0, opt, &p);
+  if (st != NORM_OK) return st;
+  info->path = p.path;
+  info->lanes_per_row = p.lpr;
+  info->vecs_per_lane = p.vpl;
+  info->block = p.block;
+  info->grid = (p.path == NORM_PATH_ROWS || !is_backward) ? p.grid
+                                                            : int(p.slices * p.partial_rows);
+  info->partial_rows = int(p.partial_rows);
+  info->workspace_bytes = p.ws_bytes;
+  return NORM_OK;
+}
+
+const char* norm_status_string(norm_status_t s) {
+  switch (s) {
+    case NORM_OK: return "ok";
+    case NORM_ERR_NULL_PTR: return "a required pointer is NULL";
+    case NORM_ERR_BAD_SHAPE: return "bad shape (need M >= 0, 1 <= N <= 2^31-1)";
+    case NORM_ERR_BAD_DTYPE: return "bad dtype";
+    case NORM_ERR_BAD_EPS: return "eps must be finite and >= 0";
+    case NORM_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case NORM_ERR_HIP: return "HIP runtime error";
+    case NORM_ERR_MISALIGNED: return "pointer not aligned to its element size";
+    case NORM_ERR_BAD_OPTION: return "bad option";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

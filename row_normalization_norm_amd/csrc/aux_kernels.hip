@@ -1,0 +1,382 @@
+// The kernels outside the register-resident row mapping:
+//
+//  * rowdot   -- per-row reduction pass of the SPLIT and GENERIC backward:
+//                c1 = mean(g * xhat), c2 = mean(g) with g = dy * gamma, written to a
+//                [M, 2] table.  One workgroup per row, looping over the row.
+//  * colslice -- column-sliced pass of the SPLIT and GENERIC backward: a workgroup owns
+//                a slice of columns and a block of rows, writes dx = rstd*(g - c2 -
+//                xhat*c1) from the table, keeps per-column dgamma/dbeta sums in
+//                registers and writes them as one partial row.  It never needs a row
+//                reduction, so a row of any length is handled without cross-workgroup
+//                communication (the price is a second read of x and dy).
+//  * colreduce -- stage 2 of the two-stage dgamma/dbeta reduction: out[j] = sum over p of
+//                part[p, j], in a fixed order (deterministic, no atomics; "Fused RMSNorm",
+//                aryanashta.me, "What didn't work" and "Next").
+//  * zero     -- clears dgamma/dbeta before the atomic comparison variants add into them.
+//  * fwd_generic -- scalar forward for any N and alignment: a workgroup per row, one pass
+//                for the sums and a second (cache-resident) pass to normalize.
+//
+// Formulas as in the forward and backward row kernels ("Fused RMSNorm", "What it is";
+// "SOTA normalization performance with torch.compile", "How Did Torch.compile Catch
+// Quack?" and "Why Is Peak Vectorization Your New Best Friend?").
+#include <type_traits>
+
+#include "launch.h"
+#include "rownorm_dev.h"
+
+namespace rownorm {
+namespace {
+
+constexpr int kRowWaves = kRowBlock / 64;
+
+// Sum of two values over a kRowBlock-thread workgroup, identical in every thread.
+// `red` holds 2 * kRowWaves * 2 floats, double-buffered by `parity`.
+__device__ inline void block_sum2(float& a, float& b, float* red, int& parity) {
+  a = group_sum<64>(a);
+  b = group_sum<64>(b);
+  const int wave = threadIdx.x >> 6;
+  float* buf = red + parity * kRowWaves * 2;
+  if ((threadIdx.x & 63) == 0) {
+    buf[2 * wave] = a;
+    buf[2 * wave + 1] = b;
+  }
+  __syncthreads();
+  a = 0.0f;
+  b = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    a += buf[2 * w];
+    b += buf[2 * w + 1];
+  }
+  parity ^= 1;
+}
+
+// ----------------------------------------------------------------------- rowdot
+template <bool LN, typename D, bool VEC>
+__global__ __launch_bounds__(kRowBlock) void rowdot_kernel(const BwdArgs a) {
+  constexpr int EPV = D::kPerVec;
+  __shared__ float red[2 * kRowWaves * 2];
+  int parity = 0;
+  const int tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
+    const float r = a.rstd[row];
+    const float mu = LN ? a.mean[row] : 0.0f;
+    float s1 = 0.0f, s2 = 0.0f;
+    if constexpr (VEC) {
+      const int64_t vbase = row * a.nvec;
+#pragma unroll 4
+      for (int vi = tid; vi < a.nvec; vi += kRowBlock) {
+        const u32x4 xv = ld16(a.x, vbase + vi);
+        const u32x4 dv = ld16(a.dy, vbase + vi);
+        const u32x4 gv = ld16(a.gamma, vi);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float xh = (D::get(xv, e) - mu) * r;
+          const float g = D::get(dv, e) * D::get(gv, e);
+          s1 = fmaf(g, xh, s1);
+          if constexpr (LN) s2 += g;
+        }
+      }
+    } else {
+      const int64_t base = row * a.N;
+#pragma unroll 4
+      for (int j = tid; j < a.N; j += kRowBlock) {
+        const float xh = (D::scalar(a.x, base + j) - mu) * r;
+        const float g = D::scalar(a.dy, base + j) * D::scalar(a.gamma, j);
+        s1 = fmaf(g, xh, s1);
+        if constexpr (LN) s2 += g;
+      }
+    }
+    block_sum2(s1, s2, red, parity);
+    if (tid == 0) {
+      a.rowc[2 * row] = s1 * a.inv_n;
+      a.rowc[2 * row + 1] = LN ? s2 * a.inv_n : 0.0f;
+    }
+  }
+}
+
+// --------------------------------------------------------------------- colslice
+template <bool LN, typename D, bool VEC>
+__global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) {
+  constexpr int EPV = VEC ? D::kPerVec : 1;
+  constexpr int V = VEC ? kSliceVecs : 1;
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.y * a.rows_per_block;
+  const int64_t r1 = r0 + a.rows_per_block < a.M ? r0 + a.rows_per_block : a.M;
+
+  // Vector (or column) indices this lane owns.
+  int idx[V];
+  bool own[V];
+  const int limit = VEC ? a.nvec : a.N;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    idx[v] = (blockIdx.x * V + v) * kSliceBlock + tid;
+    own[v] = idx[v] < limit;
+  }
+
+  float gam[V][EPV];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    if constexpr (VEC) {
+      const u32x4 gv = own[v] ? ld16(a.gamma, idx[v]) : zero16();
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) gam[v][e] = D::get(gv, e);
+    } else {
+      gam[v][0] = own[v] ? D::scalar(a.gamma, idx[v]) : 0.0f;
+    }
+  }
+
+  float accg[V][EPV], accb[LN ? V : 1][EPV];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      accg[v][e] = 0.0f;
+      if constexpr (LN) accb[v][e] = 0.0f;
+    }
+  }
+
+#pragma unroll 2
+  for (int64_t row = r0; row < r1; ++row) {
+    const float r = a.rstd[row];
+    const float mu = LN ? a.mean[row] : 0.0f;
+    const float c1 = a.rowc[2 * row];
+    const float c2 = a.rowc[2 * row + 1];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      if (!own[v]) continue;
+      float xs[EPV], ds[EPV];
+      if constexpr (VEC) {
+        const int64_t vi = row * a.nvec + idx[v];
+        const u32x4 xv = ld16(a.x, vi);
+        const u32x4 dv = ld16(a.dy, vi);
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          xs[e] = D::get(xv, e);
+          ds[e] = D::get(dv, e);
+        }
+      } else {
+        const int64_t i = row * a.N + idx[v];
+        xs[0] = D::scalar(a.x, i);
+        ds[0] = D::scalar(a.dy, i);
+      }
+      float o[VEC ? D::kPerVec : 1];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float xh = (xs[e] - mu) * r;
+        const float g = ds[e] * gam[v][e];
+        o[e] = r * fmaf(-xh, c1, g - c2);
+        accg[v][e] = fmaf(ds[e], xh, accg[v][e]);
+        if constexpr (LN) accb[v][e] += ds[e];
+      }
+      if constexpr (VEC) {
+        st16(a.dx, row * a.nvec + idx[v], D::pack(o));
+      } else {
+        D::put_scalar(a.dx, row * a.N + idx[v], o[0]);
+      }
+    }
+  }
+
+  float* const out_g = a.part_g + (int64_t)blockIdx.y * a.N;
+  float* const out_b = a.part_b + (int64_t)blockIdx.y * a.N;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    if (!own[v]) continue;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const int64_t col = (int64_t)idx[v] * EPV + e;
+      out_g[col] = accg[v][e];
+      if constexpr (LN) out_b[col] = accb[v][e];
+    }
+  }
+}
+
+// -------------------------------------------------------------------- colreduce
+template <bool VEC4>
+__global__ __launch_bounds__(kColRedLanes * kColRedSplits) void colreduce_kernel(
+    const float* __restrict__ part_g, const float* __restrict__ part_b, int64_t P, int32_t N,
+    float* __restrict__ dgamma, float* __restrict__ dbeta) {
+  const float* src = blockIdx.y ? part_b : part_g;
+  float* dst = blockIdx.y ? dbeta : dgamma;
+  const int tx = threadIdx.x % kColRedLanes;
+  const int ty = threadIdx.x / kColRedLanes;
+  constexpr int W = VEC4 ? 4 : 1;
+  const int64_t col = ((int64_t)blockIdx.x * kColRedLanes + tx) * W;
+  float s[W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) s[k] = 0.0f;
+  if (col < N) {
+#pragma unroll 4
+    for (int64_t p = ty; p < P; p += kColRedSplits) {
+      if constexpr (VEC4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + p * N + col);
+        s[0] += v.x;
+        s[1] += v.y;
+        s[2] += v.z;
+        s[3] += v.w;
+      } else {
+        s[0] += src[p * N + col];
+      }
+    }
+  }
+  __shared__ float buf[kColRedSplits][kColRedLanes * W];
+#pragma unroll
+  for (int k = 0; k < W; ++k) buf[ty][tx * W + k] = s[k];
+  __syncthreads();
+  if (ty == 0 && col < N) {
+#pragma unroll
+    for (int k = 0; k < W; ++k) {
+      float t = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kColRedSplits; ++q) t += buf[q][tx * W + k];
+      dst[col + k] = t;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(float* a, float* b, int32_t N) {
+  for (int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x; j < N; j += (int64_t)gridDim.x * 256) {
+    a[j] = 0.0f;
+    if (b) b[j] = 0.0f;
+  }
+}
+
+// ------------------------------------------------------------------ fwd_generic
+template <bool LN, typename D>
+__global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a) {
+  __shared__ float red[2 * kRowWaves * 2];
+  int parity = 0;
+  const int tid = threadIdx.x;
+  for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
+    const int64_t base = row * a.N;
+    // RMSNorm: mean of squares.  LayerNorm: mean, then mean squared deviation (a second,
+    // cache-resident pass), as the register-resident kernel does.
+    float mu = 0.0f, var;
+    if constexpr (LN) {
+      float s = 0.0f, unused = 0.0f;
+#pragma unroll 4
+      for (int j = tid; j < a.N; j += kRowBlock) s += D::scalar(a.x, base + j);
+      block_sum2(s, unused, red, parity);
+      mu = s * a.inv_n;
+      float ss = 0.0f;
+#pragma unroll 4
+      for (int j = tid; j < a.N; j += kRowBlock) {
+        const float d = D::scalar(a.x, base + j) - mu;
+        ss = fmaf(d, d, ss);
+      }
+      block_sum2(ss, unused, red, parity);
+      var = ss * a.inv_n;
+    } else {
+      float ss = 0.0f, unused = 0.0f;
+#pragma unroll 4
+      for (int j = tid; j < a.N; j += kRowBlock) {
+        const float f = D::scalar(a.x, base + j);
+        ss = fmaf(f, f, ss);
+      }
+      block_sum2(ss, unused, red, parity);
+      var = ss * a.inv_n;
+    }
+    const float r = rsqrtf(var + a.eps);
+    if (tid == 0) {
+      if (a.rstd) a.rstd[row] = r;
+      if constexpr (LN) {
+        if (a.mean) a.mean[row] = mu;
+      }
+    }
+#pragma unroll 4
+    for (int j = tid; j < a.N; j += kRowBlock) {
+      const float f = D::scalar(a.x, base + j);
+      const float gm = D::scalar(a.gamma, j);
+      float o;
+      if constexpr (LN) {
+        o = fmaf((f - mu) * r, gm, D::scalar(a.beta, j));
+      } else {
+        o = f * r * gm;
+      }
+      D::put_scalar(a.y, base + j, o);
+    }
+  }
+}
+
+}  // namespace
+
+// --------------------------------------------------------------------- launchers
+#define RN_DISPATCH_KD(kind, dtype, CALL)     \
+  do {                                        \
+    if (kind == 0 && dtype == 0) CALL(false, F32); \
+    if (kind == 0 && dtype == 1) CALL(false, BF16); \
+    if (kind == 1 && dtype == 0) CALL(true, F32);  \
+    if (kind == 1 && dtype == 1) CALL(true, BF16); \
+  } while (0)
+
+hipError_t launch_bwd_rowdot(int kind, int dtype, bool vec, const BwdArgs& a, int grid,
+                             hipStream_t s) {
+#define RN_CALL(LN, D)                                                                    \
+  {                                                                                      \
+    if (vec) {                                                                           \
+      hipLaunchKernelGGL((rowdot_kernel<LN, D, true>), dim3(grid), dim3(kRowBlock), 0, s, a); \
+    } else {                                                                             \
+      hipLaunchKernelGGL((rowdot_kernel<LN, D, false>), dim3(grid), dim3(kRowBlock), 0, s, a); \
+    }                                                                                    \
+    return hipGetLastError();                                                            \
+  }
+  RN_DISPATCH_KD(kind, dtype, RN_CALL);
+#undef RN_CALL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_colslice(int kind, int dtype, bool vec, const BwdArgs& a, int slices,
+                               int row_blocks, hipStream_t s) {
+  const dim3 grid(slices, row_blocks);
+#define RN_CALL(LN, D)                                                                       \
+  {                                                                                         \
+    if (vec) {                                                                              \
+      hipLaunchKernelGGL((colslice_kernel<LN, D, true>), grid, dim3(kSliceBlock), 0, s, a);  \
+    } else {                                                                                \
+      hipLaunchKernelGGL((colslice_kernel<LN, D, false>), grid, dim3(kSliceBlock), 0, s, a); \
+    }                                                                                       \
+    return hipGetLastError();                                                               \
+  }
+  RN_DISPATCH_KD(kind, dtype, RN_CALL);
+#undef RN_CALL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_generic(int kind, int dtype, const FwdArgs& a, int grid, hipStream_t s) {
+#define RN_CALL(LN, D)                                                                    \
+  {                                                                                      \
+    hipLaunchKernelGGL((fwd_generic_kernel<LN, D>), dim3(grid), dim3(kRowBlock), 0, s, a); \
+    return hipGetLastError();                                                            \
+  }
+  RN_DISPATCH_KD(kind, dtype, RN_CALL);
+#undef RN_CALL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P, int32_t N,
+                            float* dgamma, float* dbeta, hipStream_t s) {
+  const bool vec4 = (N % 4 == 0) && ((reinterpret_cast<uintptr_t>(part_g) & 15) == 0) &&
+                    (part_b == nullptr || (reinterpret_cast<uintptr_t>(part_b) & 15) == 0) &&
+                    ((reinterpret_cast<uintptr_t>(dgamma) & 15) == 0) &&
+                    (dbeta == nullptr || (reinterpret_cast<uintptr_t>(dbeta) & 15) == 0);
+  const int per_block = kColRedLanes * (vec4 ? 4 : 1);
+  const dim3 grid((N + per_block - 1) / per_block, part_b ? 2 : 1);
+  if (vec4) {
+    hipLaunchKernelGGL((colreduce_kernel<true>), grid, dim3(kColRedLanes * kColRedSplits), 0, s,
+                       part_g, part_b, P, N, dgamma, dbeta);
+  } else {
+    hipLaunchKernelGGL((colreduce_kernel<false>), grid, dim3(kColRedLanes * kColRedSplits), 0, s,
+                       part_g, part_b, P, N, dgamma, dbeta);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* a, float* b, int32_t N, hipStream_t s) {
+  int grid = (N + 255) / 256;
+  if (grid > 1024) grid = 1024;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, a, b, N);
+  return hipGetLastError();
+}
+
+}  // namespace rownorm

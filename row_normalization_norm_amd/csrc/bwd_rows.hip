@@ -1,0 +1,226 @@
+// Backward kernel, register-resident rows (ROWS path), stage 1 of the two-stage
+// dgamma/dbeta reduction.
+//
+// The backward's outputs are dx, dgamma and, for LayerNorm, dbeta, with reductions
+// over dy ("SOTA normalization performance with torch.compile", theaicatchup.com,
+// "Why Is Peak Vectorization Your New Best Friend?").  Per row, with the forward's
+// saved statistics, xhat = (x - mean) * rstd (RMSNorm: x * rstd) and g = dy * gamma:
+//     c1 = mean(g * xhat), c2 = mean(g) (LayerNorm only)
+//     dx = rstd * (g - c2 - xhat * c1)
+// and per column dgamma += dy * xhat, dbeta += dy.
+//
+// dx is computed the way the forward computes y: the rows of x and dy are loaded once
+// into registers (16-byte loads), the two row sums are reduced across the row's lanes,
+// and dx is written once.  The column sums stay in fp32 registers for every row the
+// workgroup handles; at the end the workgroup's row slots are combined through LDS in
+// a fixed order and written as ONE partial row of a [P, N] workspace.  A separate
+// column-reduce kernel then adds the P partial rows.  That is the atomic-free two-stage
+// scheme the "Fused RMSNorm" page (aryanashta.me, "What didn't work") contrasts with
+// atomically adding every block's partial into one shared vector; the atomic variants
+// (per row, per workgroup) are kept for measurement only.
+//
+// Built once per (kind, dtype) from RN_KIND / RN_DTYPE on the command line.
+#include <type_traits>
+
+#include "launch.h"
+#include "rownorm_dev.h"
+
+#ifndef RN_KIND
+#error "RN_KIND must be defined"
+#endif
+#ifndef RN_DTYPE
+#error "RN_DTYPE must be defined"
+#endif
+
+namespace rownorm {
+namespace {
+
+template <bool LN, typename D, int LPR, int VPL>
+__global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs a) {
+  constexpr int BLOCK = bwd_block(LPR);
+  constexpr int EPV = D::kPerVec;
+  constexpr int ROWS = BLOCK / LPR;
+  constexpr int WPR = LPR > 64 ? LPR / 64 : 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % LPR;
+  const int slot = tid / LPR;
+  const int nvec = a.nvec;
+  const int mode = a.mode;
+
+  float accg[VPL][EPV];
+  float accb[LN ? VPL : 1][EPV];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      accg[v][e] = 0.0f;
+      if constexpr (LN) accb[v][e] = 0.0f;
+    }
+  }
+
+  __shared__ float red[WPR > 1 ? 2 * ROWS * WPR * 2 : 1];
+  int parity = 0;
+
+  for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
+    const int64_t row = grp * ROWS + slot;
+    const bool row_ok = row < a.M;
+    const int64_t vbase = row * nvec;
+
+    u32x4 xv[VPL], dv[VPL], gv[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      const bool ok = row_ok && vi < nvec;
+      xv[v] = ok ? ld16(a.x, vbase + vi) : zero16();
+      dv[v] = ok ? ld16(a.dy, vbase + vi) : zero16();
+      gv[v] = ok ? ld16(a.gamma, vi) : zero16();
+    }
+    const float r = row_ok ? a.rstd[row] : 0.0f;
+    const float mu = (LN && row_ok) ? a.mean[row] : 0.0f;
+
+    // Row sums, and the per-column contributions (which do not need the row sums).
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float xh = (D::get(xv[v], e) - mu) * r;
+        const float d = D::get(dv[v], e);
+        const float g = d * D::get(gv[v], e);
+        s1 = fmaf(g, xh, s1);
+        if constexpr (LN) s2 += g;
+        accg[v][e] = fmaf(d, xh, accg[v][e]);
+        if constexpr (LN) accb[v][e] += d;
+      }
+    }
+
+    constexpr int W = LPR < 64 ? LPR : 64;
+    s1 = group_sum<W>(s1);
+    if constexpr (LN) s2 = group_sum<W>(s2);
+    if constexpr (WPR > 1) {
+      const int wave = (tid >> 6) % WPR;
+      float* buf = red + (parity * ROWS + slot) * WPR * 2;
+      if ((tid & 63) == 0) {
+        buf[2 * wave] = s1;
+        buf[2 * wave + 1] = s2;
+      }
+      __syncthreads();
+      s1 = 0.0f;
+      s2 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) {
+        s1 += buf[2 * w];
+        if constexpr (LN) s2 += buf[2 * w + 1];
+      }
+      parity ^= 1;
+    }
+    const float c1 = s1 * a.inv_n;
+    const float c2 = LN ? s2 * a.inv_n : 0.0f;
+
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      if (row_ok && vi < nvec) {
+        float o[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float xh = (D::get(xv[v], e) - mu) * r;
+          const float g = D::get(dv[v], e) * D::get(gv[v], e);
+          o[e] = r * fmaf(-xh, c1, g - c2);
+        }
+        st16(a.dx, vbase + vi, D::pack(o));
+        if (mode == kAtomicRow) {
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const int col = vi * EPV + e;
+            const float d = D::get(dv[v], e);
+            unsafeAtomicAdd(a.dgamma + col, d * ((D::get(xv[v], e) - mu) * r));
+            if constexpr (LN) unsafeAtomicAdd(a.dbeta + col, d);
+          }
+        }
+      }
+    }
+  }
+
+  if (mode == kAtomicRow) return;
+
+  // Combine the workgroup's row slots and emit one partial row (or, in the per-workgroup
+  // atomic mode, add it into dgamma/dbeta).
+  float* const out_g = mode == kTwoStage ? a.part_g + (int64_t)blockIdx.x * a.N : a.dgamma;
+  float* const out_b = mode == kTwoStage ? a.part_b + (int64_t)blockIdx.x * a.N : a.dbeta;
+  if constexpr (ROWS == 1) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      if (vi < nvec) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const int col = vi * EPV + e;
+          if (mode == kTwoStage) {
+            out_g[col] = accg[v][e];
+            if constexpr (LN) out_b[col] = accb[v][e];
+          } else {
+            unsafeAtomicAdd(out_g + col, accg[v][e]);
+            if constexpr (LN) unsafeAtomicAdd(out_b + col, accb[v][e]);
+          }
+        }
+      }
+    }
+  } else {
+    // cbuf[slot][lane*EPV + e] holds one vector column block of every slot.
+    constexpr int SPAN = LPR * EPV;
+    __shared__ float cbuf[ROWS * SPAN];
+#pragma unroll
+    for (int pass = 0; pass < (LN ? 2 : 1); ++pass) {
+      float* const out = pass == 0 ? out_g : out_b;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          cbuf[slot * SPAN + lane * EPV + e] = pass == 0 ? accg[v][e] : accb[LN ? v : 0][e];
+        }
+        __syncthreads();
+        for (int c = tid; c < SPAN; c += BLOCK) {
+          float sum = 0.0f;
+#pragma unroll 4
+          for (int k = 0; k < ROWS; ++k) sum += cbuf[k * SPAN + c];
+          const int col = v * SPAN + c;
+          if (col < a.N) {
+            if (mode == kTwoStage) {
+              out[col] = sum;
+            } else {
+              unsafeAtomicAdd(out + col, sum);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool LN, typename D, int LPR, int VPL>
+hipError_t launch_one(const BwdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((bwd_rows_kernel<LN, D, LPR, VPL>), dim3(grid), dim3(bwd_block(LPR)), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define RN_CAT_(a, b, c, d) a##b##c##d
+#define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
+#define RN_LAUNCHER RN_CAT(launch_bwd_rows_k, RN_KIND, _d, RN_DTYPE)
+
+hipError_t RN_LAUNCHER(int lpr, int vpl, const BwdArgs& a, int grid, hipStream_t s) {
+  constexpr bool kLN = RN_KIND == 1;
+  using D = typename std::conditional<RN_DTYPE == 1, BF16, F32>::type;
+#define RN_CASE(L, V) \
+  if (lpr == L && vpl == V) return launch_one<kLN, D, L, V>(a, grid, s);
+  RN_BWD_MAPPINGS(RN_CASE)
+#undef RN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rownorm

@@ -1,0 +1,192 @@
+// Forward kernel, register-resident rows (ROWS path).
+//
+// RMSNorm: rstd = 1/sqrt(mean(x^2) + eps), y = x * rstd * gamma ("Fused RMSNorm",
+// aryanashta.me, "What it is").  LayerNorm: mean and biased variance of the row,
+// y = (x - mean) * rstd * gamma + beta ("SOTA normalization performance with
+// torch.compile", theaicatchup.com, "How Did Torch.compile Catch Quack?").
+//
+// One pass over HBM: the row is read once into registers with 16-byte loads, its sum
+// and sum of squares are accumulated in fp32 (the "Fused RMSNorm" page, "How it works",
+// on why low-precision accumulation drifts), reduced across the row's lanes (DPP inside
+// a wavefront, LDS across wavefronts), then normalized from the registers and written
+// once with 16-byte stores.
+//
+// Mapping: LPR lanes hold one row, VPL 16-byte vectors each.  Lane l of the row holds
+// vectors v*LPR + l (v < VPL), so consecutive lanes touch consecutive 16 bytes and each
+// wavefront-wide load instruction covers a contiguous 64*16-byte span of the row.
+// LPR <= 64 packs 64/LPR rows into a wavefront (a row is one aligned lane group);
+// LPR > 64 spreads a row over LPR/64 wavefronts.  The grid is persistent: workgroup b
+// takes row groups b, b + gridDim.x, ...  gamma (and beta) are loaded once per
+// workgroup and kept in registers when they fit.
+//
+// Built once per (kind, dtype): RN_KIND (0 RMSNorm, 1 LayerNorm) and RN_DTYPE
+// (0 fp32, 1 bf16) come from the compiler command line.
+#include <type_traits>
+
+#include "launch.h"
+#include "rownorm_dev.h"
+
+#ifndef RN_KIND
+#error "RN_KIND must be defined"
+#endif
+#ifndef RN_DTYPE
+#error "RN_DTYPE must be defined"
+#endif
+
+namespace rownorm {
+namespace {
+
+template <bool LN, typename D, int LPR, int VPL>
+__global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs a) {
+  constexpr int BLOCK = fwd_block(LPR);
+  constexpr int EPV = D::kPerVec;
+  constexpr int ROWS = BLOCK / LPR;              // rows per workgroup per iteration
+  constexpr int WPR = LPR > 64 ? LPR / 64 : 1;   // wavefronts per row
+  constexpr bool GREG = LN ? (VPL <= 4) : (VPL <= 8);  // gamma/beta kept in registers
+
+  const int tid = threadIdx.x;
+  const int lane = tid % LPR;
+  const int slot = tid / LPR;
+  const int nvec = a.nvec;
+
+  u32x4 g[GREG ? VPL : 1];
+  u32x4 b[(GREG && LN) ? VPL : 1];
+  if constexpr (GREG) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      g[v] = vi < nvec ? ld16(a.gamma, vi) : zero16();
+      if constexpr (LN) b[v] = vi < nvec ? ld16(a.beta, vi) : zero16();
+    }
+  }
+
+  // Cross-wavefront partial sums.  Each reduction has its own pair of buffers, used by
+  // alternate rows, so one barrier per reduction suffices: a wavefront cannot reuse a
+  // buffer until every wavefront has passed the barrier of the following reduction,
+  // i.e. has finished reading it.
+  __shared__ float red[WPR > 1 ? 2 * 2 * ROWS * WPR : 1];
+  int parity = 0;
+  auto row_sum = [&](float v, int which) {
+    constexpr int W = LPR < 64 ? LPR : 64;
+    v = group_sum<W>(v);
+    if constexpr (WPR > 1) {
+      float* buf = red + ((which * 2 + parity) * ROWS + slot) * WPR;
+      if ((tid & 63) == 0) buf[(tid >> 6) % WPR] = v;
+      __syncthreads();
+      v = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) v += buf[w];
+    }
+    return v;
+  };
+
+  for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
+    const int64_t row = grp * ROWS + slot;
+    const bool row_ok = row < a.M;
+    const int64_t vbase = row * nvec;
+
+    u32x4 xv[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      xv[v] = (row_ok && vi < nvec) ? ld16(a.x, vbase + vi) : zero16();
+    }
+
+    // RMSNorm: mean of squares.  LayerNorm: the mean, then the mean squared deviation
+    // from it, both reduced from the registers (the row is read from memory once).
+    // Deviations about the mean keep the variance exact for constant rows and free of
+    // the cancellation of mean(x^2) - mean^2 when |mean| >> deviation.
+    float mu = 0.0f, var;
+    if constexpr (LN) {
+      float s = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) s += D::get(xv[v], e);
+      }
+      mu = row_sum(s, 0) * a.inv_n;
+      float ss = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const bool in_row = v * LPR + lane < nvec;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float d = in_row ? D::get(xv[v], e) - mu : 0.0f;
+          ss = fmaf(d, d, ss);
+        }
+      }
+      var = row_sum(ss, 1) * a.inv_n;
+    } else {
+      float ss = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float f = D::get(xv[v], e);
+          ss = fmaf(f, f, ss);
+        }
+      }
+      var = row_sum(ss, 0) * a.inv_n;
+    }
+    if constexpr (WPR > 1) parity ^= 1;
+
+    const float r = rsqrtf(var + a.eps);
+    if (row_ok && lane == 0) {
+      if (a.rstd) a.rstd[row] = r;
+      if constexpr (LN) {
+        if (a.mean) a.mean[row] = mu;
+      }
+    }
+
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      if (row_ok && vi < nvec) {
+        u32x4 gv, bv;
+        if constexpr (GREG) {
+          gv = g[v];
+          if constexpr (LN) bv = b[v];
+        } else {
+          gv = ld16(a.gamma, vi);
+          if constexpr (LN) bv = ld16(a.beta, vi);
+        }
+        float o[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float f = D::get(xv[v], e);
+          if constexpr (LN) {
+            o[e] = fmaf((f - mu) * r, D::get(gv, e), D::get(bv, e));
+          } else {
+            o[e] = f * r * D::get(gv, e);
+          }
+        }
+        st16(a.y, vbase + vi, D::pack(o));
+      }
+    }
+  }
+}
+
+template <bool LN, typename D, int LPR, int VPL>
+hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t s) {
+  hipLaunchKernelGGL((fwd_rows_kernel<LN, D, LPR, VPL>), dim3(grid), dim3(fwd_block(LPR)), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+#define RN_CAT_(a, b, c, d) a##b##c##d
+#define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
+#define RN_LAUNCHER RN_CAT(launch_fwd_rows_k, RN_KIND, _d, RN_DTYPE)
+
+hipError_t RN_LAUNCHER(int lpr, int vpl, const FwdArgs& a, int grid, hipStream_t s) {
+  constexpr bool kLN = RN_KIND == 1;
+  using D = typename std::conditional<RN_DTYPE == 1, BF16, F32>::type;
+#define RN_CASE(L, V) \
+  if (lpr == L && vpl == V) return launch_one<kLN, D, L, V>(a, grid, s);
+  RN_FWD_MAPPINGS(RN_CASE)
+#undef RN_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace rownorm

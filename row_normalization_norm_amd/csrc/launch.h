@@ -1,0 +1,110 @@
+// Kernel argument blocks, the list of compiled row mappings, and the launcher
+// entry points shared by the host API (api.cpp) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rownorm {
+
+// ------------------------------------------------------------ compiled mappings
+// (lanes per row, 16-byte vectors per lane).  8..64 lanes: several rows per
+// wavefront (a row is one aligned lane group); 128..1024 lanes: one row spans
+// several wavefronts of a workgroup and is reduced through LDS.
+#define RN_FWD_MAPPINGS(X)                                                             \
+  X(8, 1) X(8, 2) X(8, 3) X(8, 4) X(8, 6) X(8, 8)                                      \
+  X(16, 1) X(16, 2) X(16, 3) X(16, 4) X(16, 6) X(16, 8)                                \
+  X(32, 1) X(32, 2) X(32, 3) X(32, 4) X(32, 6) X(32, 8)                                \
+  X(64, 1) X(64, 2) X(64, 3) X(64, 4) X(64, 6) X(64, 8) X(64, 12) X(64, 16)            \
+  X(128, 2) X(128, 3) X(128, 4) X(128, 6) X(128, 8) X(128, 12) X(128, 16)              \
+  X(256, 2) X(256, 3) X(256, 4) X(256, 6) X(256, 8) X(256, 12) X(256, 16)              \
+  X(512, 2) X(512, 3) X(512, 4) X(512, 6) X(512, 8) X(512, 12) X(512, 16)              \
+  X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 6) X(1024, 8) X(1024, 12) X(1024, 16)
+
+// The backward keeps x, dy and per-column fp32 partials of dgamma (and dbeta) in
+// registers; beyond 4 vectors per lane (1 at 1024 lanes, where a lane may use at
+// most 128 VGPRs) the kernel spills, so those mappings are not built.
+#define RN_BWD_MAPPINGS(X)                                                             \
+  X(8, 1) X(8, 2) X(8, 3) X(8, 4)                                                      \
+  X(16, 1) X(16, 2) X(16, 3) X(16, 4)                                                  \
+  X(32, 1) X(32, 2) X(32, 3) X(32, 4)                                                  \
+  X(64, 1) X(64, 2) X(64, 3) X(64, 4)                                                  \
+  X(128, 1) X(128, 2) X(128, 3) X(128, 4)                                              \
+  X(256, 1) X(256, 2) X(256, 3) X(256, 4)                                              \
+  X(512, 1) X(512, 2) X(512, 3) X(512, 4)                                              \
+  X(1024, 1)
+
+// Threads per workgroup for a row mapping.
+constexpr int fwd_block(int lpr) { return lpr >= 256 ? lpr : 256; }
+constexpr int bwd_block(int lpr) { return lpr >= 512 ? lpr : 512; }
+
+// Column-sliced backward pass (SPLIT path): threads and vectors per lane.
+constexpr int kSliceBlock = 256;
+constexpr int kSliceVecs = 2;
+// Row-reduction pass (SPLIT and GENERIC backward) and the scalar forward.
+constexpr int kRowBlock = 256;
+// Column reduce of the partial rows.
+constexpr int kColRedLanes = 64;
+constexpr int kColRedSplits = 16;
+
+enum DgammaMode { kTwoStage = 0, kAtomicRow = 1, kAtomicWg = 2 };
+
+// ------------------------------------------------------------------ arguments
+struct FwdArgs {
+  const void* x;
+  const void* gamma;
+  const void* beta;
+  void* y;
+  float* mean;
+  float* rstd;
+  int64_t M;
+  int32_t N;
+  int32_t nvec;    // N / elements per 16-byte vector (ROWS path)
+  float eps;
+  float inv_n;
+  int64_t groups;  // row groups = ceil(M / rows per workgroup iteration)
+};
+
+struct BwdArgs {
+  const void* dy;
+  const void* x;
+  const void* gamma;
+  const float* mean;
+  const float* rstd;
+  void* dx;
+  float* part_g;   // [P, N] dgamma partial rows (TWO_STAGE)
+  float* part_b;   // [P, N] dbeta partial rows (LayerNorm, TWO_STAGE)
+  float* dgamma;   // final outputs (atomic modes add into them)
+  float* dbeta;
+  float* rowc;     // SPLIT / GENERIC: [M, 2] per-row (c1, c2)
+  int64_t M;
+  int32_t N;
+  int32_t nvec;
+  float inv_n;
+  int32_t mode;    // DgammaMode
+  int64_t groups;
+  int64_t rows_per_block;  // SPLIT / GENERIC column pass: rows per row block
+};
+
+// ------------------------------------------------------------------ launchers
+// kind: 0 = RMSNorm, 1 = LayerNorm.  dtype: 0 = fp32, 1 = bf16.  Each returns
+// hipErrorInvalidValue when the (lpr, vpl) mapping is not compiled.
+hipError_t launch_fwd_rows(int kind, int dtype, int lpr, int vpl, const FwdArgs& a, int grid,
+                           hipStream_t s);
+hipError_t launch_bwd_rows(int kind, int dtype, int lpr, int vpl, const BwdArgs& a, int grid,
+                           hipStream_t s);
+// SPLIT path (16-byte vectors): per-row reduction, then the column-sliced pass on a
+// (slices, row_blocks) grid.
+hipError_t launch_bwd_rowdot(int kind, int dtype, bool vec, const BwdArgs& a, int grid,
+                             hipStream_t s);
+hipError_t launch_bwd_colslice(int kind, int dtype, bool vec, const BwdArgs& a, int slices,
+                               int row_blocks, hipStream_t s);
+// GENERIC forward (scalar loads).
+hipError_t launch_fwd_generic(int kind, int dtype, const FwdArgs& a, int grid, hipStream_t s);
+// Column reduce: out[j] = sum_p part[p*N + j] for dgamma (and dbeta if part_b).
+hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P, int32_t N,
+                            float* dgamma, float* dbeta, hipStream_t s);
+// dgamma (and dbeta) <- 0, for the atomic modes.
+hipError_t launch_zero(float* a, float* b, int32_t N, hipStream_t s);
+
+}  // namespace rownorm

@@ -1,0 +1,108 @@
+// Device primitives for the row-normalization kernels (gfx950, wave64).
+//
+//  * 16-byte vector loads and stores (one global_load/store_dwordx4 per lane);
+//  * bf16 <-> fp32: widening is exact (bf16 bits are the top half of an fp32);
+//    narrowing uses v_cvt_pk_bf16_f32 (round to nearest even, NaN stays NaN);
+//  * sums over aligned groups of 2..64 lanes with DPP (quad_perm, row_half_mirror,
+//    row_mirror) inside a 16-lane row and lane shuffles across rows.  Every lane of a
+//    group ends with the same bits, because each step adds the same two operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rownorm {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- element types
+struct F32 {
+  static constexpr int kBytes = 4;
+  static constexpr int kPerVec = 4;  // elements per 16-byte vector
+  __device__ static inline float get(const u32x4& v, int e) { return __uint_as_float(v[e]); }
+  __device__ static inline float scalar(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ static inline void put_scalar(void* p, int64_t i, float f) {
+    static_cast<float*>(p)[i] = f;
+  }
+  __device__ static inline u32x4 pack(const float (&f)[4]) {
+    u32x4 r;
+    r[0] = __float_as_uint(f[0]);
+    r[1] = __float_as_uint(f[1]);
+    r[2] = __float_as_uint(f[2]);
+    r[3] = __float_as_uint(f[3]);
+    return r;
+  }
+};
+
+struct BF16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  // Element e of the vector lives in 32-bit word e/2: low half for even e.
+  __device__ static inline float get(const u32x4& v, int e) {
+    const uint32_t w = v[e >> 1];
+    return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  __device__ static inline float scalar(const void* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+  }
+  __device__ static inline void put_scalar(void* p, int64_t i, float f) {
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack2(f, 0.0f) & 0xFFFFu);
+  }
+  __device__ static inline u32x4 pack(const float (&f)[8]) {
+    u32x4 r;
+    r[0] = pack2(f[0], f[1]);
+    r[1] = pack2(f[2], f[3]);
+    r[2] = pack2(f[4], f[5]);
+    r[3] = pack2(f[6], f[7]);
+    return r;
+  }
+};
+
+// ------------------------------------------------------------------ vector memory
+__device__ inline u32x4 ld16(const void* base, int64_t vec_index) {
+  return static_cast<const u32x4*>(base)[vec_index];
+}
+__device__ inline void st16(void* base, int64_t vec_index, const u32x4& v) {
+  static_cast<u32x4*>(base)[vec_index] = v;
+}
+__device__ inline u32x4 zero16() {
+  u32x4 z = {0u, 0u, 0u, 0u};
+  return z;
+}
+
+// ------------------------------------------------------------------- reductions
+// DPP control codes (GFX9): quad_perm selectors, and the row mirrors.
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm:[1,0,3,2]  (lane ^ 1)
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm:[2,3,0,1]  (lane ^ 2)
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within each 8 lanes
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within each 16 lanes
+
+template <int kCtrl>
+__device__ inline float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                            0, __builtin_bit_cast(int, v), kCtrl, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of W consecutive lanes (W a power of two, 1..64); the result
+// is in every lane of the group.  Needs every lane of the wavefront to execute it.
+template <int W>
+__device__ inline float group_sum(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "group width");
+  if constexpr (W >= 2) v = dpp_add<kDppQuadSwap1>(v);
+  if constexpr (W >= 4) v = dpp_add<kDppQuadSwap2>(v);
+  if constexpr (W >= 8) v = dpp_add<kDppRowHalfMirror>(v);
+  if constexpr (W >= 16) v = dpp_add<kDppRowMirror>(v);
+  if constexpr (W >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (W >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+}  // namespace rownorm

@@ -26,3 +26,14 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.get()
+
+
+@pytest.fixture(scope="session")
+def device():
+    """cuda:0 with the HIP library loaded; GPU tests are skipped only on a host with no GPU."""
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU on this host")
+    import row_normalization_norm_amd as rn
+    rn.lib()  # raises when librownorm.so is missing: never fall back
+    return torch.device("cuda:0")

@@ -1,0 +1,219 @@
+"""GPU-vs-oracle parity helpers shared by the GPU tests and the smoke check.
+
+Tolerances (the GPU result against the fp64 oracle, per element):
+  * bf16 y / dx:   |gpu - ref| <= 2^-7 * max(1, |ref|)
+  * fp32 y:        |gpu - ref| <= 1e-5 * max(1, |ref|)
+  * fp32 dx:       |gpu - ref| <= 1e-5 * max(1, |ref|, rstd*(|g| + |c2| + |xhat*c1|)):
+                   dx is a difference and can cancel (for N = 1, RMSNorm's dx is
+                   rstd*g*eps/(x^2+eps)); the rounding of the fp32 statistics alone is then
+                   amplified, so the bound is relative to the size of the terms the
+                   difference is formed from.  (This scale is a tolerance only; the
+                   expected values are the oracle's.)
+  * rstd:          |gpu - ref| <= 1e-5 * |ref|
+  * mean:          |gpu - ref| <= 1e-5 * RMS(x row)   (the mean of a centred row is ~0,
+                   so a purely relative bound would be meaningless there)
+  * dgamma/dbeta:  |gpu - ref| <= 1e-4 * max(|ref|, sqrt(sum_i t_ij^2)), t the summed
+                   terms (dy*xhat, dy): the natural size of a sum of random-sign terms.
+The GPU backward consumes the GPU forward's saved fp32 statistics (the pipeline as it
+runs); the oracle always uses its own fp64 statistics.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import gen
+import oracle
+import row_normalization_norm_amd as rn
+
+TOL_BF16 = 2.0 ** -7
+TOL_F32 = 1e-5
+TOL_STAT = 1e-5
+TOL_DGAMMA = 1e-4
+
+
+# ------------------------------------------------------------------ host <-> device
+def to_device(a: np.ndarray, dtype: str, device):
+    import torch
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(device)
+
+
+def to_host64(t) -> np.ndarray:
+    import torch
+    if t.dtype == torch.bfloat16:
+        bits = t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+        return gen.bf16_to_f32(bits).astype(np.float64)
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def rows_to_host64(t, rows) -> np.ndarray:
+    import torch
+    idx = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=t.device)
+    return to_host64(t.index_select(0, idx))
+
+
+def sample_rows(M: int, k: int = 48, seed: int = 0) -> np.ndarray:
+    """First, last and a spread of rows (deterministic)."""
+    if M <= k:
+        return np.arange(M, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    picks = set([0, 1, M - 2, M - 1]) | set(rng.choice(M, size=k - 4, replace=False).tolist())
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+# ------------------------------------------------------------------------ running
+class GpuRun:
+    """Device tensors for one workload and the library's outputs for them."""
+
+    def __init__(self, w: gen.Workload, inputs: dict, device, x_offset: int = 0):
+        import torch
+        self.w = w
+        self.device = device
+        self.torch_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        M, N = int(inputs["x"].shape[0]), w.N
+        self.M, self.N = M, N
+        if x_offset:
+            # Place x and dy at an element offset inside a larger buffer (misaligned).
+            def shifted(a):
+                flat = to_device(a.reshape(-1), w.dtype, device)
+                buf = torch.empty(flat.numel() + x_offset, dtype=flat.dtype, device=device)
+                view = buf[x_offset:]
+                view.copy_(flat)
+                return view.view(M, N)
+            self.x = shifted(inputs["x"])
+            self.dy = shifted(inputs["dy"])
+        else:
+            self.x = to_device(inputs["x"], w.dtype, device)
+            self.dy = to_device(inputs["dy"], w.dtype, device)
+        self.gamma = to_device(inputs["gamma"], w.dtype, device)
+        self.beta = to_device(inputs["beta"], w.dtype, device) if w.kind == "ln" else None
+        self.y = torch.empty_like(self.x)
+        self.dx = torch.empty_like(self.x)
+        self.mean = torch.empty(M, dtype=torch.float32, device=device) if w.kind == "ln" else None
+        self.rstd = torch.empty(M, dtype=torch.float32, device=device)
+        self.dgamma = torch.empty(N, dtype=torch.float32, device=device)
+        self.dbeta = torch.empty(N, dtype=torch.float32, device=device) if w.kind == "ln" else None
+
+    def forward(self, options=None):
+        w = self.w
+        if w.kind == "rms":
+            rn.norm_rms_fwd(self.x, self.gamma, self.y, self.rstd, eps=w.eps, options=options)
+        else:
+            rn.norm_ln_fwd(self.x, self.gamma, self.beta, self.y, self.mean, self.rstd, eps=w.eps,
+                           options=options)
+
+    def backward(self, options=None, workspace=None, mean=None, rstd=None):
+        mean = self.mean if mean is None else mean
+        rstd = self.rstd if rstd is None else rstd
+        if self.w.kind == "rms":
+            rn.norm_rms_bwd(self.dy, self.x, self.gamma, rstd, self.dx, self.dgamma,
+                            workspace=workspace, options=options)
+        else:
+            rn.norm_ln_bwd(self.dy, self.x, self.gamma, mean, rstd, self.dx, self.dgamma,
+                           self.dbeta, workspace=workspace, options=options)
+
+    def sync(self):
+        import torch
+        torch.cuda.synchronize(self.device)
+
+
+# --------------------------------------------------------------------- comparing
+def _check(name, got, ref, tol, floor=1.0, scale=None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, f"{name}: shape {got.shape} vs {ref.shape}"
+    if got.size == 0:
+        return 0.0
+    bound = tol * (np.maximum(floor, np.abs(ref)) if scale is None else scale)
+    err = np.abs(got - ref)
+    bad = ~(err <= bound)  # NaN counts as bad
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        raise AssertionError(
+            f"{name}: {bad.sum()} of {bad.size} elements out of tolerance; first at flat index "
+            f"{i}: gpu {got.ravel()[i]!r} ref {ref.ravel()[i]!r} bound {np.ravel(bound)[i]!r}")
+    return float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def out_tol(dtype: str) -> float:
+    return TOL_BF16 if dtype == "bf16" else TOL_F32
+
+
+def check_forward(run: GpuRun, inputs: dict, rows, orc=None):
+    orc = orc or oracle.get()
+    w = run.w
+    rows = np.asarray(rows, dtype=np.int64)
+    y = rows_to_host64(run.y, rows)
+    rstd = run.rstd.cpu().numpy().astype(np.float64)[rows]
+    if w.kind == "rms":
+        y_ref, rstd_ref = orc.rms_fwd(inputs["x"], inputs["gamma"], w.eps, rows=rows)
+    else:
+        y_ref, mean_ref, rstd_ref = orc.ln_fwd(inputs["x"], inputs["gamma"], inputs["beta"], w.eps,
+                                              rows=rows)
+        mean = run.mean.cpu().numpy().astype(np.float64)[rows]
+        xr = inputs["x"][rows]
+        xr = gen.bf16_to_f32(xr) if w.dtype == "bf16" else xr
+        row_rms = np.sqrt(np.mean(xr.astype(np.float64) ** 2, axis=1))
+        _check("mean", mean, mean_ref, TOL_STAT, scale=np.maximum(row_rms, 1e-30))
+    _check("rstd", rstd, rstd_ref, TOL_STAT, scale=np.abs(rstd_ref))
+    _check("y", y, y_ref, out_tol(w.dtype))
+
+
+def dx_term_scale(w, inputs, rows, dx_ref, orc):
+    """max(1, |dx|, rstd*(|g| + |c2| + |xhat*c1|)) per element, from the oracle's statistics."""
+    x = inputs["x"][rows].astype(np.float64)
+    dy = inputs["dy"][rows].astype(np.float64)
+    gam = inputs["gamma"].astype(np.float64)
+    if w.kind == "rms":
+        _, r = orc.rms_fwd(inputs["x"], inputs["gamma"], w.eps, rows=rows)
+        mu = np.zeros_like(r)
+    else:
+        _, mu, r = orc.ln_fwd(inputs["x"], inputs["gamma"], inputs["beta"], w.eps, rows=rows)
+    xh = (x - mu[:, None]) * r[:, None]
+    g = dy * gam[None, :]
+    c1 = np.mean(g * xh, axis=1, keepdims=True)
+    c2 = np.mean(g, axis=1, keepdims=True) if w.kind == "ln" else 0.0
+    terms = r[:, None] * (np.abs(g) + np.abs(c2) + np.abs(xh * c1))
+    return np.maximum(1.0, np.maximum(np.abs(dx_ref), terms))
+
+
+def check_backward(run: GpuRun, inputs: dict, rows, orc=None, check_dgamma=True):
+    orc = orc or oracle.get()
+    w = run.w
+    rows = np.asarray(rows, dtype=np.int64)
+    dx = rows_to_host64(run.dx, rows)
+    if w.kind == "rms":
+        dx_ref = orc.rms_bwd_dx(inputs["dy"], inputs["x"], inputs["gamma"], w.eps, rows=rows)
+    else:
+        dx_ref = orc.ln_bwd_dx(inputs["dy"], inputs["x"], inputs["gamma"], w.eps, rows=rows)
+    if w.dtype == "f32":
+        _check("dx", dx, dx_ref, TOL_F32, scale=dx_term_scale(w, inputs, rows, dx_ref, orc))
+    else:
+        _check("dx", dx, dx_ref, out_tol(w.dtype))
+    if not check_dgamma:
+        return
+    dg = run.dgamma.cpu().numpy().astype(np.float64)
+    if w.kind == "rms":
+        dg_ref, sg = orc.rms_dgamma(inputs["dy"], inputs["x"], w.eps)
+    else:
+        dg_ref, db_ref, sg, sb = orc.ln_dgamma_dbeta(inputs["dy"], inputs["x"], w.eps)
+        db = run.dbeta.cpu().numpy().astype(np.float64)
+        _check("dbeta", db, db_ref, TOL_DGAMMA, scale=np.maximum(np.abs(db_ref), sb))
+    _check("dgamma", dg, dg_ref, TOL_DGAMMA, scale=np.maximum(np.abs(dg_ref), sg))
+
+
+def full_check(w: gen.Workload, device, rows=None, fwd_options=None, bwd_options=None,
+               inputs=None, x_offset=0):
+    """Generate, run forward + backward on the GPU, compare with the oracle."""
+    inputs = inputs or gen.make_inputs(w)
+    run = GpuRun(w, inputs, device, x_offset=x_offset)
+    run.forward(fwd_options)
+    run.backward(bwd_options)
+    run.sync()
+    rows = sample_rows(run.M) if rows is None else rows
+    check_forward(run, inputs, rows)
+    check_backward(run, inputs, rows)
+    return run, inputs

@@ -1,0 +1,180 @@
+"""The C ABI on a host without a GPU: the library loads, exports what include/rownorm.h
+declares, rejects every invalid argument before any HIP call, and plans/sizes
+workspaces as a pure function.  Every call below fails validation (or is a pure query),
+so no kernel is ever launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_normalization_norm_amd as rn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rownorm.h")
+
+BF16, F32 = rn.NORM_DTYPE_BF16, rn.NORM_DTYPE_F32
+A = 0x10000  # a 16-byte-aligned fake address: only ever passed to calls that fail validation
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_][a-z0-9_]*\s*\*?\s*(norm_[a-z0-9_]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) == 12, names
+    lib = rn.lib()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in rownorm.h but not exported"
+    assert set(names) == set(rn.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_status_strings():
+    for s in range(0, 9):
+        assert rn.status_string(s)
+    assert rn.status_string(0) == "ok"
+    assert rn.status_string(99) == "unknown status"
+
+
+def rms_fwd(**kw):
+    a = dict(x=A, gamma=A, y=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16, stream=None)
+    a.update(kw)
+    return rn.lib().norm_rms_fwd(a["x"], a["gamma"], a["y"], a["rstd"], a["M"], a["N"], a["eps"],
+                                 a["dtype"], a["stream"])
+
+
+def ln_fwd(**kw):
+    a = dict(x=A, gamma=A, beta=A, y=A, mean=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16)
+    a.update(kw)
+    return rn.lib().norm_ln_fwd(a["x"], a["gamma"], a["beta"], a["y"], a["mean"], a["rstd"],
+                                a["M"], a["N"], a["eps"], a["dtype"], None)
+
+
+def rms_bwd(**kw):
+    a = dict(dy=A, x=A, gamma=A, rstd=A, dx=A, dgamma=A, M=4, N=64, dtype=BF16, ws=A,
+             ws_bytes=1 << 30)
+    a.update(kw)
+    return rn.lib().norm_rms_bwd(a["dy"], a["x"], a["gamma"], a["rstd"], a["dx"], a["dgamma"],
+                                 a["M"], a["N"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+
+def ln_bwd(**kw):
+    a = dict(dy=A, x=A, gamma=A, mean=A, rstd=A, dx=A, dgamma=A, dbeta=A, M=4, N=64, dtype=BF16,
+             ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return rn.lib().norm_ln_bwd(a["dy"], a["x"], a["gamma"], a["mean"], a["rstd"], a["dx"],
+                                a["dgamma"], a["dbeta"], a["M"], a["N"], a["dtype"], a["ws"],
+                                a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("call,kw,status", [
+    (rms_fwd, dict(x=None), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(gamma=None), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(y=None), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(M=-1), rn.NORM_ERR_BAD_SHAPE),
+    (rms_fwd, dict(N=0), rn.NORM_ERR_BAD_SHAPE),
+    (rms_fwd, dict(N=1 << 31), rn.NORM_ERR_BAD_SHAPE),
+    (rms_fwd, dict(M=1 << 60, N=1 << 20), rn.NORM_ERR_BAD_SHAPE),
+    (rms_fwd, dict(dtype=7), rn.NORM_ERR_BAD_DTYPE),
+    (rms_fwd, dict(eps=-1e-6), rn.NORM_ERR_BAD_EPS),
+    (rms_fwd, dict(eps=float("nan")), rn.NORM_ERR_BAD_EPS),
+    (rms_fwd, dict(eps=float("inf")), rn.NORM_ERR_BAD_EPS),
+    (rms_fwd, dict(x=A + 1), rn.NORM_ERR_MISALIGNED),
+    (rms_fwd, dict(rstd=A + 2), rn.NORM_ERR_MISALIGNED),
+    (rms_fwd, dict(dtype=F32, y=A + 2), rn.NORM_ERR_MISALIGNED),
+    (ln_fwd, dict(beta=None), rn.NORM_ERR_NULL_PTR),
+    (ln_fwd, dict(mean=A + 1), rn.NORM_ERR_MISALIGNED),
+    (rms_bwd, dict(dy=None), rn.NORM_ERR_NULL_PTR),
+    (rms_bwd, dict(rstd=None), rn.NORM_ERR_NULL_PTR),
+    (rms_bwd, dict(dgamma=None), rn.NORM_ERR_NULL_PTR),
+    (rms_bwd, dict(ws=None), rn.NORM_ERR_NULL_PTR),
+    (rms_bwd, dict(ws_bytes=16), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
+    (rms_bwd, dict(ws=A + 4), rn.NORM_ERR_MISALIGNED),
+    (rms_bwd, dict(N=-5), rn.NORM_ERR_BAD_SHAPE),
+    (rms_bwd, dict(dtype=-1), rn.NORM_ERR_BAD_DTYPE),
+    (ln_bwd, dict(mean=None), rn.NORM_ERR_NULL_PTR),
+    (ln_bwd, dict(dbeta=None), rn.NORM_ERR_NULL_PTR),
+    (ln_bwd, dict(dbeta=A + 1), rn.NORM_ERR_MISALIGNED),
+    (ln_bwd, dict(ws_bytes=0), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_validation_rejects(call, kw, status):
+    assert call(**kw) == status
+
+
+def test_bad_options_rejected():
+    lib = rn.lib()
+    bad = [rn.Options(path=9), rn.Options(lanes_per_row=-1),
+           rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=48, vecs_per_lane=1),
+           rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=8, vecs_per_lane=1),  # cannot cover N
+           rn.Options(path=rn.NORM_PATH_SPLIT),  # forward has no SPLIT path
+           rn.Options(dgamma_mode=5)]
+    for o in bad:
+        st = lib.norm_rms_fwd_ex(A, A, A, A, 4, 4096, 1e-6, BF16, None, ctypes.byref(o))
+        assert st == rn.NORM_ERR_BAD_OPTION, (o.path, o.lanes_per_row, o.vecs_per_lane)
+    # atomic dgamma is only offered on the ROWS path
+    o = rn.Options(path=rn.NORM_PATH_SPLIT, dgamma_mode=rn.NORM_DGAMMA_ATOMIC_ROW)
+    st = lib.norm_rms_bwd_ex(A, A, A, A, A, A, 4, 4096, BF16, A, 1 << 30, None, ctypes.byref(o))
+    assert st == rn.NORM_ERR_BAD_OPTION
+    # a backward grid above the planner's partial-row count would overflow the workspace
+    o = rn.Options(grid=100000)
+    st = lib.norm_rms_bwd_ex(A, A, A, A, A, A, 1 << 20, 1024, BF16, A, 1 << 40, None,
+                             ctypes.byref(o))
+    assert st == rn.NORM_ERR_BAD_OPTION
+
+
+def test_plan_shape_classes():
+    # non-power-of-2 N = 384 (bf16): 48 vectors = 16 lanes x 3, several rows per wavefront
+    p = rn.norm_plan(False, False, 262144, 384, BF16)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 16, 3)
+    p = rn.norm_plan(True, False, 262144, 384, BF16)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 16, 3)
+    # very long rows: forward keeps the row in one workgroup's registers ...
+    p = rn.norm_plan(False, False, 2048, 131072, BF16)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 1024, 16)
+    # ... the backward switches to the column-sliced path
+    p = rn.norm_plan(True, False, 2048, 131072, BF16)
+    assert p.path == rn.NORM_PATH_SPLIT and p.partial_rows >= 1
+    # misaligned pointers or N not a multiple of the vector fall back to the scalar path
+    assert rn.norm_plan(False, True, 100, 4096, BF16, aligned16=False).path == rn.NORM_PATH_GENERIC
+    assert rn.norm_plan(False, True, 100, 4095, BF16).path == rn.NORM_PATH_GENERIC
+    assert rn.norm_plan(True, True, 100, 7, F32).path == rn.NORM_PATH_GENERIC
+    # every plan's lanes x vectors covers the row with less than one vector slot of padding
+    for N in (256, 384, 512, 768, 1024, 2048, 4096, 8192, 16384, 65536):
+        for dt, epv in ((BF16, 8), (F32, 4)):
+            for bwd in (False, True):
+                p = rn.norm_plan(bwd, True, (1 << 27) // N, N, dt)
+                if p.path == rn.NORM_PATH_ROWS:
+                    cover = p.lanes_per_row * p.vecs_per_lane
+                    assert N // epv <= cover < N // epv + p.lanes_per_row
+
+
+def test_workspace_size():
+    ws = rn.norm_bwd_workspace_size
+    for ln in (False, True):
+        for dt in (BF16, F32):
+            prev = 0
+            for M in (0, 1, 7, 100, 4096, 65536, 1 << 20):
+                s = ws(M, 4096, ln, dt)
+                assert s >= prev, "workspace size must not shrink as M grows"
+                prev = s
+            prev = 0
+            for N in (1, 8, 384, 1000, 4096, 32768, 131072):
+                s = ws(4096, N, ln, dt)
+                assert s >= prev, "workspace size must not shrink as N grows"
+                prev = s
+    # LayerNorm needs room for dbeta partials too
+    assert ws(4096, 1024, True, BF16) > ws(4096, 1024, False, BF16)
+    # the query is enough for the aligned plan and for the scalar plan
+    for (M, N) in ((4096, 1024), (65536, 4096), (2048, 131072), (333, 7)):
+        need = ws(M, N, True, BF16)
+        for al in (True, False):
+            assert rn.norm_plan(True, True, M, N, BF16, aligned16=al).workspace_bytes <= need
+    # atomic comparison modes need no workspace
+    o = rn.Options(dgamma_mode=rn.NORM_DGAMMA_ATOMIC_ROW)
+    assert ws(4096, 1024, True, BF16, o) == 0
+    # an invalid shape sizes to 0
+    assert ws(-1, 1024, True, BF16) == 0

@@ -1,0 +1,264 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element.
+
+Small cases compare every row; the full-size workloads compare sampled rows of y and dx
+(the oracle evaluates them one by one) and the complete dgamma/dbeta vectors (the
+oracle sums all rows).  Tolerances are in parity.py.  All calls go through the C ABI.
+"""
+import numpy as np
+import pytest
+
+import gen
+import row_normalization_norm_amd as rn
+from parity import GpuRun, check_backward, check_forward, full_check, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+SMALL_N = (1, 7, 64, 100, 256, 384, 512, 768, 1000, 1024, 2048, 4095, 4096, 8192, 16384, 32768,
+           65536, 131072)
+
+
+def small_workload(kind, dtype, N, M=None, eps=1e-6, x_mean=0.0, x_std=1.0):
+    if M is None:
+        # several row groups plus a ragged tail, within a few million elements
+        M = max(3, min(1531, 3_000_000 // N))
+    return gen.Workload(f"{kind}_{dtype}_{M}x{N}", kind, dtype, M, N, eps, x_mean=x_mean,
+                        x_std=x_std, config=9)
+
+
+@pytest.mark.parametrize("N", SMALL_N)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_small_shapes(device, kind, dtype, N):
+    w = small_workload(kind, dtype, N, x_mean=0.25 if kind == "ln" else 0.0, x_std=1.5)
+    full_check(w, device, rows=np.arange(w.M))
+
+
+@pytest.mark.parametrize("name", ["rms1", "ln2", "rms3", "rms4"])
+def test_workloads_full_size(device, name):
+    """The named workloads at full size, in the launch configuration the benchmark times."""
+    full_check(gen.WORKLOADS[name], device, rows=sample_rows(gen.WORKLOADS[name].M, 64))
+
+
+@pytest.mark.parametrize("N", gen.SWEEP_N)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_sweep_full_size(device, kind, dtype, N):
+    w = gen.sweep_workload(kind, dtype, N)
+    full_check(w, device, rows=sample_rows(w.M, 24))
+
+
+def _mapping_cases():
+    cases = []
+    import re
+    src = open(rn.__file__.replace("__init__.py", "csrc/launch.h")).read()
+    for direction, macro in (("fwd", "RN_FWD_MAPPINGS"), ("bwd", "RN_BWD_MAPPINGS")):
+        body = src[src.index(f"#define {macro}"):]
+        body = body[:body.index("\n\n")]
+        for lpr, vpl in re.findall(r"X\((\d+), (\d+)\)", body):
+            cases.append((direction, int(lpr), int(vpl)))
+    return cases
+
+
+MAPPINGS = _mapping_cases()
+
+
+@pytest.mark.parametrize("direction,lpr,vpl", MAPPINGS,
+                         ids=[f"{d}-{l}x{v}" for d, l, v in MAPPINGS])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_every_mapping(device, kind, dtype, direction, lpr, vpl):
+    """Force each compiled (lanes per row, vectors per lane) mapping on a row that leaves
+    the last vector slot partly empty, with a ragged final row group."""
+    epv = 8 if dtype == "bf16" else 4
+    nvec = lpr * vpl - max(1, lpr // 3) if lpr * vpl > 1 else 1
+    N = nvec * epv
+    M = max(5, min(301, 400_000 // N))
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.1)
+    opt = rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=lpr, vecs_per_lane=vpl)
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    if direction == "fwd":
+        run.forward(opt)
+        run.sync()
+        check_forward(run, inputs, np.arange(M))
+    else:
+        run.forward()
+        run.backward(opt)
+        run.sync()
+        check_backward(run, inputs, np.arange(M))
+
+
+@pytest.mark.parametrize("path", [rn.NORM_PATH_SPLIT, rn.NORM_PATH_GENERIC])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+@pytest.mark.parametrize("N", [256, 384, 4096, 12288])
+def test_forced_paths(device, kind, dtype, N, path):
+    w = small_workload(kind, dtype, N, M=517)
+    fwd_opt = rn.Options(path=rn.NORM_PATH_GENERIC) if path == rn.NORM_PATH_GENERIC else None
+    full_check(w, device, rows=np.arange(w.M), fwd_options=fwd_opt,
+               bwd_options=rn.Options(path=path))
+
+
+@pytest.mark.parametrize("grid", [1, 3, 64])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_grid_override(device, kind, grid):
+    w = small_workload(kind, "bf16", 1024, M=1000)
+    full_check(w, device, rows=np.arange(w.M), fwd_options=rn.Options(grid=grid),
+               bwd_options=rn.Options(grid=grid))
+
+
+@pytest.mark.parametrize("mode", [rn.NORM_DGAMMA_ATOMIC_ROW, rn.NORM_DGAMMA_ATOMIC_WG])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_atomic_dgamma_variants(device, kind, mode):
+    """The atomic comparison variants agree with the oracle (not bitwise with each other)."""
+    w = small_workload(kind, "bf16", 4096, M=2000)
+    full_check(w, device, rows=sample_rows(w.M), bwd_options=rn.Options(dgamma_mode=mode))
+
+
+@pytest.mark.parametrize("name", ["ln2", "rms3", "rms4"])
+def test_two_stage_is_deterministic(device, name):
+    """Two-stage backward: bitwise identical dx, dgamma, dbeta across runs."""
+    import torch
+    w = gen.WORKLOADS[name].scaled(min(gen.WORKLOADS[name].M, 4096))
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    run.forward()
+    outs = []
+    for _ in range(3):
+        run.backward()
+        run.sync()
+        outs.append([t.clone() for t in (run.dx, run.dgamma, run.dbeta) if t is not None])
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_backward_with_oracle_stats(device, kind):
+    """Feed the backward the oracle's statistics rounded to fp32: isolates the backward."""
+    import oracle
+    import torch
+    w = small_workload(kind, "bf16", 2048, M=700)
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    orc = oracle.get()
+    if kind == "rms":
+        _, rstd = orc.rms_fwd(inputs["x"], inputs["gamma"], w.eps)
+        mean = None
+    else:
+        _, mean, rstd = orc.ln_fwd(inputs["x"], inputs["gamma"], inputs["beta"], w.eps)
+        mean = torch.tensor(mean.astype(np.float32), device=device)
+    rstd = torch.tensor(rstd.astype(np.float32), device=device)
+    run.backward(mean=mean, rstd=rstd)
+    run.sync()
+    check_backward(run, inputs, np.arange(w.M))
+
+
+@pytest.mark.parametrize("offset", [1, 3])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_misaligned_inputs(device, kind, offset):
+    w = small_workload(kind, "bf16", 1024, M=300)
+    full_check(w, device, rows=np.arange(w.M), x_offset=offset)
+
+
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_empty_batch(device, kind):
+    import torch
+    N = 1024
+    x = torch.empty(0, N, dtype=torch.bfloat16, device=device)
+    g = torch.ones(N, dtype=torch.bfloat16, device=device)
+    b = torch.zeros(N, dtype=torch.bfloat16, device=device)
+    y = torch.empty_like(x)
+    rstd = torch.empty(0, dtype=torch.float32, device=device)
+    mean = torch.empty(0, dtype=torch.float32, device=device)
+    dg = torch.full((N,), 7.0, device=device)
+    db = torch.full((N,), 7.0, device=device)
+    if kind == "rms":
+        rn.norm_rms_fwd(x, g, y, rstd)
+        rn.norm_rms_bwd(x, x, g, rstd, torch.empty_like(x), dg)
+    else:
+        rn.norm_ln_fwd(x, g, b, y, mean, rstd)
+        rn.norm_ln_bwd(x, x, g, mean, rstd, torch.empty_like(x), dg, db)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(db).item() == 0
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dg).item() == 0, "a sum over no rows is zero"
+
+
+def test_degenerate_rows(device):
+    """RMSNorm of a zero row is 0 (rstd = 1/sqrt(eps)); LayerNorm of a constant row is beta."""
+    import torch
+    N, eps = 512, 1e-5
+    x = torch.zeros(3, N, dtype=torch.bfloat16, device=device)
+    x[1] = 2.5
+    x[2, ::2] = 1.0
+    g = torch.full((N,), 1.5, dtype=torch.bfloat16, device=device)
+    b = (torch.arange(N, device=device) % 7 * 0.125).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    rstd = torch.empty(3, device=device)
+    mean = torch.empty(3, device=device)
+    rn.norm_rms_fwd(x, g, y, rstd, eps=eps)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y[0]).item() == 0
+    assert abs(rstd[0].item() - eps ** -0.5) <= 1e-5 * eps ** -0.5
+    rn.norm_ln_fwd(x, g, b, y, mean, rstd, eps=eps)
+    torch.cuda.synchronize()
+    assert torch.equal(y[1].float(), b.float()), "constant row must give beta"
+    assert torch.equal(y[0].float(), b.float())
+
+
+def test_nan_propagates_to_its_row_only(device):
+    import torch
+    w = small_workload("rms", "bf16", 1024, M=64)
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    run.x[5, 17] = float("nan")
+    run.forward()
+    run.sync()
+    assert torch.isnan(run.y[5].float()).all()
+    assert not torch.isnan(run.y[torch.arange(64, device=device) != 5].float()).any()
+
+
+def test_invariants_on_gpu_outputs(device):
+    """gamma = 1: RMS of each y row is 1; LayerNorm rows have mean 0, variance 1 (bf16)."""
+    import torch
+    M, N = 256, 4096
+    x = gen.fill(M * N, "bf16", 77, 0.5, 2.0).reshape(M, N)
+    from parity import to_device
+    xd = to_device(x, "bf16", device)
+    g = torch.ones(N, dtype=torch.bfloat16, device=device)
+    b = torch.zeros(N, dtype=torch.bfloat16, device=device)
+    y = torch.empty_like(xd)
+    rstd = torch.empty(M, device=device)
+    mean = torch.empty(M, device=device)
+    rn.norm_rms_fwd(xd, g, y, rstd, eps=0.0)
+    torch.cuda.synchronize()
+    ms = y.double().pow(2).mean(dim=1)
+    assert (ms - 1).abs().max().item() < 2 ** -7
+    rn.norm_ln_fwd(xd, g, b, y, mean, rstd, eps=0.0)
+    torch.cuda.synchronize()
+    assert y.double().mean(dim=1).abs().max().item() < 2 ** -7
+    assert (y.double().var(dim=1, unbiased=False) - 1).abs().max().item() < 2 ** -6
+
+
+def test_events_and_streams(device):
+    """Options' events bracket the main kernel; calls run on a side stream."""
+    import torch
+    w = small_workload("ln", "bf16", 4096, M=4096)
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    s = torch.cuda.Stream(device)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(s):
+        e0.record(s)
+        e1.record(s)  # materialise the handles
+        s.synchronize()
+        opt = rn.Options(ev_start=e0.cuda_event, ev_stop=e1.cuda_event)
+        run.forward(opt)
+        run.backward(opt)
+    s.synchronize()
+    assert e0.elapsed_time(e1) > 0
+    check_forward(run, inputs, sample_rows(w.M))
+    check_backward(run, inputs, sample_rows(w.M))
