@@ -104,18 +104,21 @@ class Bench:
         dt = rn.NORM_DTYPE_BF16 if w.dtype == "bf16" else rn.NORM_DTYPE_F32
         ws = rn.norm_bwd_workspace_size(w.M, w.N, w.kind == "ln", dt)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        fws = rn.norm_fwd_workspace_size(w.M, w.N, w.kind == "ln", dt)
+        self.fws = torch.empty(fws, dtype=torch.uint8, device=device) if fws else None
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
 
     def step(self, k, fwd_opt=None, bwd_opt=None):
         rn, w, b = self.rn, self.w, self.bufs[k % self.sets]
         if w.kind == "rms":
-            rn.norm_rms_fwd(b["x"], self.gamma, b["y"], b["rstd"], eps=w.eps, options=fwd_opt)
+            rn.norm_rms_fwd(b["x"], self.gamma, b["y"], b["rstd"], eps=w.eps, workspace=self.fws,
+                            options=fwd_opt)
             rn.norm_rms_bwd(b["dy"], b["x"], self.gamma, b["rstd"], b["dx"], self.dgamma,
                             workspace=self.ws, options=bwd_opt)
         else:
             rn.norm_ln_fwd(b["x"], self.gamma, self.beta, b["y"], b["mean"], b["rstd"], eps=w.eps,
-                           options=fwd_opt)
+                           workspace=self.fws, options=fwd_opt)
             rn.norm_ln_bwd(b["dy"], b["x"], self.gamma, b["mean"], b["rstd"], b["dx"], self.dgamma,
                            self.dbeta, workspace=self.ws, options=bwd_opt)
 
@@ -131,6 +134,11 @@ def make_events(n):
 
 
 def run_gpu(w, steps, warmup, device):
+    """Two timed passes of `steps` steps each, after `warmup` untimed steps:
+    pass A records events only before and after the K steps (the step time); pass B also
+    records HIP events around every launch of the forward kernel and of the backward's
+    main kernel on the stream they run on (per-kernel average durations).  Per-launch
+    events add a few microseconds of gap each, which is why the step time comes from A."""
     import torch
     import row_normalization_norm_amd as rn
     b = Bench(w, device)
@@ -138,28 +146,53 @@ def run_gpu(w, steps, warmup, device):
         b.step(k)
     torch.cuda.synchronize()
 
-    # Per-launch events around the forward kernel and the backward's main kernel.
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        b.step(warmup + k)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+
     fev = make_events(2 * steps)
     bev = make_events(2 * steps)
     fopts = [rn.Options(ev_start=fev[2 * i].cuda_event, ev_stop=fev[2 * i + 1].cuda_event)
              for i in range(steps)]
     bopts = [rn.Options(ev_start=bev[2 * i].cuda_event, ev_stop=bev[2 * i + 1].cuda_event)
              for i in range(steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record()
     for k in range(steps):
-        b.step(warmup + k, fopts[k], bopts[k])
-    stop.record()
+        b.step(warmup + steps + k, fopts[k], bopts[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = start.elapsed_time(stop)
     fwd_ms = sum(fev[2 * i].elapsed_time(fev[2 * i + 1]) for i in range(steps)) / steps
     bwd_ms = sum(bev[2 * i].elapsed_time(bev[2 * i + 1]) for i in range(steps)) / steps
     return dict(ms_per_step=total_ms / steps, fwd_kernel_ms=fwd_ms, bwd_main_kernel_ms=bwd_ms,
                 wall_s=wall, sets=b.sets, setup_s=b.setup_s)
+
+
+def copy_probe(nbytes, steps, device):
+    """Time a plain device copy of nbytes (torch's copy kernel): the achievable
+    read+write bandwidth next to the nominal peak, and the kernel whose rocprofv3
+    FETCH_SIZE / WRITE_SIZE readings scale the counters to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "ms": round(ms, 5),
+            "GBs_read_plus_write": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -213,6 +246,8 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--all", metavar="JSON", help="also time every workload, write a table")
+    ap.add_argument("--copy-probe", type=int, metavar="BYTES",
+                    help="only time a plain device copy of BYTES and print it")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -229,6 +264,9 @@ def main():
     import row_normalization_norm_amd as rn
     rn.lib()
     device = torch.device("cuda:0")
+    if args.copy_probe:
+        print(json.dumps(copy_probe(args.copy_probe, args.steps, device)), flush=True)
+        return
 
     w = gen.WORKLOADS[args.workload]
     s = 2 if w.dtype == "bf16" else 4
@@ -269,6 +307,8 @@ def main():
             "traffic": load_counters(w),
             "avg_launch_ms": round(r["bwd_main_kernel_ms"], 5),
             "algorithmic_bytes_per_launch": main_bytes,
+            "timing": "HIP events around every launch of the kernel in a second timed "
+                      "pass of the same steps",
         },
         "rotating_buffer_sets": r["sets"],
     }
@@ -276,12 +316,17 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w)
     if args.all:
         table = []
-        for name, wl in list(gen.WORKLOADS.items()):
+        sweep = [gen.sweep_workload(k, d, n) for k in ("rms", "ln") for d in ("bf16", "f32")
+                 for n in gen.SWEEP_N]
+        for wl in list(gen.WORKLOADS.values()) + sweep:
+            name = wl.name
             rr = run_gpu(wl, max(5, args.steps // 2), 3, device)
             ss = 2 if wl.dtype == "bf16" else 4
             fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, ss)
-            table.append({"workload": name, "desc": describe(wl), **{k: round(v, 5) for k, v in rr.items()},
+            table.append({"workload": name, "desc": describe(wl),
+                          **{k: round(v, 5) for k, v in rr.items()},
                           "fwd_GBs": fb / (rr["fwd_kernel_ms"] * 1e-3) / 1e9,
+                          "bwd_GBs": bb / ((rr["ms_per_step"] - rr["fwd_kernel_ms"]) * 1e-3) / 1e9,
                           "step_GBs": (fb + bb) / (rr["ms_per_step"] * 1e-3) / 1e9})
             print(f"# {name}: {table[-1]['step_GBs']:.0f} GB/s", file=sys.stderr, flush=True)
         with open(args.all, "w") as f:

@@ -79,15 +79,25 @@ typedef enum norm_status {
 
 /* ------------------------------------------------------------------ forward */
 
-/* RMSNorm forward.  x, gamma, y: `dtype`; rstd: float [M], or NULL to not save it. */
+/* Bytes of workspace the forward needs for this shape: 0 except for rows long enough to
+ * be split over several workgroups, where it holds their per-row partial sums (a few
+ * KiB).  A pure function of its arguments: no HIP call; valid on any gfx950 device. */
+size_t norm_fwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype);
+
+/* RMSNorm forward.  x, gamma, y: `dtype`; rstd: float [M], or NULL to not save it.
+ * workspace: device memory of at least norm_fwd_workspace_size(M, N, 0, dtype) bytes,
+ * 16-byte aligned (may be NULL when that size is 0); its contents on entry do not
+ * matter and it must stay alive until the call has completed on `stream`. */
 norm_status_t norm_rms_fwd(const void* x, const void* gamma, void* y, float* rstd,
                            int64_t M, int64_t N, float eps, norm_dtype_t dtype,
-                           hipStream_t stream);
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* LayerNorm forward.  mean and rstd: float [M]; each may be NULL to not save it. */
+/* LayerNorm forward.  mean and rstd: float [M]; each may be NULL to not save it.
+ * Workspace as above with is_layernorm = 1. */
 norm_status_t norm_ln_fwd(const void* x, const void* gamma, const void* beta, void* y,
                           float* mean, float* rstd, int64_t M, int64_t N, float eps,
-                          norm_dtype_t dtype, hipStream_t stream);
+                          norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* ----------------------------------------------------------------- backward */
 
@@ -134,7 +144,10 @@ typedef enum norm_path {
   NORM_PATH_SPLIT = 2,     /* backward for rows too long to keep per-column partials in
                               registers: a per-row reduction pass, then a
                               column-sliced pass for dx and the partials */
-  NORM_PATH_GENERIC = 3    /* scalar loads, any N and alignment */
+  NORM_PATH_GENERIC = 3,   /* scalar loads, any N and alignment */
+  NORM_PATH_CLUSTER = 4    /* long rows split over a cluster of co-resident workgroups
+                              (cooperative launch), each owning a column slice and
+                              exchanging per-row partial sums through the workspace */
 } norm_path_t;
 
 /* Options for the *_ex entry points; zero-initialise for defaults.  Used by tests and
@@ -145,8 +158,12 @@ typedef struct norm_options {
                           256, 512, 1024 (one workgroup per row); 0 = planner */
   int vecs_per_lane;   /* ROWS path: 16-byte vectors each lane holds per row; 0 = planner */
   int dgamma_mode;     /* norm_dgamma_mode_t (backward only) */
-  int grid;            /* persistent workgroups; 0 = planner.  For the backward it must
-                          not exceed the planner's partial-row count for the shape */
+  int grid;            /* persistent workgroups; 0 = planner.  For the backward this is
+                          also the number of dgamma/dbeta partial rows, so size the
+                          workspace with norm_bwd_workspace_size_ex and the same options.
+                          CLUSTER path: total workgroups (clusters x cluster_size) */
+  int cluster_size;    /* CLUSTER path: workgroups per row (2, 4, 8, 16 or 32); 0 = planner */
+  int cluster_rows;    /* CLUSTER path: rows per exchange step (1 or 2); 0 = planner */
   hipEvent_t ev_start; /* if non-NULL, recorded on `stream` just before the main kernel */
   hipEvent_t ev_stop;  /* if non-NULL, recorded on `stream` just after the main kernel */
 } norm_options_t;
@@ -159,6 +176,8 @@ typedef struct norm_plan_info {
   int block;             /* threads per workgroup of the main kernel */
   int grid;              /* workgroups of the main kernel */
   int partial_rows;      /* rows of dgamma/dbeta partials the backward writes */
+  int cluster_size;      /* CLUSTER path: workgroups per row (else 0) */
+  int cluster_rows;      /* CLUSTER path: rows per exchange step (else 0) */
   size_t workspace_bytes;
 } norm_plan_info_t;
 
@@ -169,17 +188,29 @@ norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
                         norm_dtype_t dtype, int aligned16, const norm_options_t* opt,
                         norm_plan_info_t* info);
 
-/* Workspace size for a backward call made with these options (NULL = defaults). */
+/* Workspace sizes for calls made with these options (NULL = defaults). */
+size_t norm_fwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
+                                  const norm_options_t* opt);
 size_t norm_bwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
                                   const norm_options_t* opt);
+
+/* Whether a call with these arguments would run on the CLUSTER path on the current
+ * device: 1 yes, 0 no (another path is planned, or the device cannot hold even one
+ * cluster and the call falls back to the SPLIT / GENERIC path), -1 on invalid
+ * arguments.  When the device holds fewer workgroups than planned, the call runs fewer
+ * clusters.  Assumes 16-byte-aligned pointers.  Makes HIP queries (current device). */
+int norm_cluster_resident(int is_backward, int is_layernorm, int64_t M, int64_t N,
+                          norm_dtype_t dtype, const norm_options_t* opt);
 
 /* The entry points above with options (opt may be NULL). */
 norm_status_t norm_rms_fwd_ex(const void* x, const void* gamma, void* y, float* rstd,
                               int64_t M, int64_t N, float eps, norm_dtype_t dtype,
-                              hipStream_t stream, const norm_options_t* opt);
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              const norm_options_t* opt);
 norm_status_t norm_ln_fwd_ex(const void* x, const void* gamma, const void* beta, void* y,
                              float* mean, float* rstd, int64_t M, int64_t N, float eps,
-                             norm_dtype_t dtype, hipStream_t stream, const norm_options_t* opt);
+                             norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, const norm_options_t* opt);
 norm_status_t norm_rms_bwd_ex(const void* dy, const void* x, const void* gamma,
                               const float* rstd, void* dx, float* dgamma, int64_t M, int64_t N,
                               norm_dtype_t dtype, void* workspace, size_t workspace_bytes,

@@ -39,6 +39,7 @@ NORM_PATH_AUTO = 0
 NORM_PATH_ROWS = 1
 NORM_PATH_SPLIT = 2
 NORM_PATH_GENERIC = 3
+NORM_PATH_CLUSTER = 4
 
 
 class NormError(RuntimeError):
@@ -51,7 +52,8 @@ class Options(ctypes.Structure):
     """norm_options_t."""
     _fields_ = [("path", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
                 ("vecs_per_lane", ctypes.c_int), ("dgamma_mode", ctypes.c_int),
-                ("grid", ctypes.c_int), ("ev_start", ctypes.c_void_p),
+                ("grid", ctypes.c_int), ("cluster_size", ctypes.c_int),
+                ("cluster_rows", ctypes.c_int), ("ev_start", ctypes.c_void_p),
                 ("ev_stop", ctypes.c_void_p)]
 
 
@@ -60,6 +62,7 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("lanes_per_row", ctypes.c_int),
                 ("vecs_per_lane", ctypes.c_int), ("block", ctypes.c_int),
                 ("grid", ctypes.c_int), ("partial_rows", ctypes.c_int),
+                ("cluster_size", ctypes.c_int), ("cluster_rows", ctypes.c_int),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
@@ -71,16 +74,19 @@ _SZ = ctypes.c_size_t
 _OPT = ctypes.POINTER(Options)
 
 SIGNATURES = {
-    "norm_rms_fwd": (_INT, [_P, _P, _P, _P, _I64, _I64, _F, _INT, _P]),
-    "norm_ln_fwd": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P]),
+    "norm_fwd_workspace_size": (_SZ, [_I64, _I64, _INT, _INT]),
+    "norm_rms_fwd": (_INT, [_P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _SZ, _P]),
+    "norm_ln_fwd": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _SZ, _P]),
     "norm_bwd_workspace_size": (_SZ, [_I64, _I64, _INT, _INT]),
     "norm_rms_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P]),
     "norm_ln_bwd": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P]),
     "norm_status_string": (ctypes.c_char_p, [_INT]),
     "norm_plan": (_INT, [_INT, _INT, _I64, _I64, _INT, _INT, _OPT, ctypes.POINTER(PlanInfo)]),
+    "norm_cluster_resident": (_INT, [_INT, _INT, _I64, _I64, _INT, _OPT]),
+    "norm_fwd_workspace_size_ex": (_SZ, [_I64, _I64, _INT, _INT, _OPT]),
     "norm_bwd_workspace_size_ex": (_SZ, [_I64, _I64, _INT, _INT, _OPT]),
-    "norm_rms_fwd_ex": (_INT, [_P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _OPT]),
-    "norm_ln_fwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _OPT]),
+    "norm_rms_fwd_ex": (_INT, [_P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _SZ, _P, _OPT]),
+    "norm_ln_fwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _SZ, _P, _OPT]),
     "norm_rms_bwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P, _OPT]),
     "norm_ln_bwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P,
                               _OPT]),
@@ -165,7 +171,25 @@ def _opt(options):
 
 
 # ------------------------------------------------------------------- entry points
-def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, stream=None, options=None):
+def norm_fwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, options=None) -> int:
+    if options is None:
+        return int(lib().norm_fwd_workspace_size(M, N, int(bool(is_layernorm)), dtype))
+    return int(lib().norm_fwd_workspace_size_ex(M, N, int(bool(is_layernorm)), dtype,
+                                                _opt(options)))
+
+
+def _fwd_workspace(M, N, ln, dtype, device, workspace, options):
+    torch = _torch()
+    need = norm_fwd_workspace_size(M, N, ln, dtype, options)
+    if workspace is None:
+        if need == 0:
+            return None, 0
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stream=None,
+                 options=None):
     """y = x * rstd * gamma with rstd = 1/sqrt(mean(x^2) + eps) per row; rstd saved if given."""
     torch = _torch()
     M, N = _shape(x)
@@ -173,7 +197,9 @@ def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, stream=None, options
     for t, n, k in ((gamma, "gamma", N), (y, "y", M * N)):
         _need(t, n, k, x.dtype, x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
-    args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), _dtype_code(x),
+    dt = _dtype_code(x)
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options)
+    args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
             _stream(x.device, stream))
     if options is None:
         _check(lib().norm_rms_fwd(*args), "norm_rms_fwd")
@@ -182,8 +208,8 @@ def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, stream=None, options
     return y
 
 
-def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, stream=None,
-                options=None):
+def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, workspace=None,
+                stream=None, options=None):
     """y = (x - mean) * rstd * gamma + beta per row; mean and rstd saved if given."""
     torch = _torch()
     M, N = _shape(x)
@@ -192,8 +218,10 @@ def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, stre
         _need(t, n, k, x.dtype, x.device)
     _need(mean, "mean", M, torch.float32, x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
+    dt = _dtype_code(x)
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options)
     args = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, float(eps),
-            _dtype_code(x), _stream(x.device, stream))
+            dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
     if options is None:
         _check(lib().norm_ln_fwd(*args), "norm_ln_fwd")
     else:
@@ -262,3 +290,10 @@ def norm_plan(is_backward: bool, is_layernorm: bool, M: int, N: int, dtype: int,
     _check(lib().norm_plan(int(bool(is_backward)), int(bool(is_layernorm)), M, N, dtype,
                            int(bool(aligned16)), _opt(options), ctypes.byref(info)), "norm_plan")
     return info
+
+
+def norm_cluster_resident(is_backward: bool, is_layernorm: bool, M: int, N: int, dtype: int,
+                          options=None) -> int:
+    """1 if the call would run on the CLUSTER path on the current device, else 0."""
+    return int(lib().norm_cluster_resident(int(bool(is_backward)), int(bool(is_layernorm)), M, N,
+                                           dtype, _opt(options)))

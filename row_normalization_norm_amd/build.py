@@ -27,7 +27,7 @@ def _units():
     units = []
     for k in (0, 1):
         for d in (0, 1):
-            for name in ("fwd_rows", "bwd_rows"):
+            for name in ("fwd_rows", "bwd_rows", "cluster"):
                 units.append((os.path.join(CSRC, f"{name}.hip"),
                               os.path.join(BUILD_DIR, f"{name}_k{k}_d{d}.o"),
                               [f"-DRN_KIND={k}", f"-DRN_DTYPE={d}"]))

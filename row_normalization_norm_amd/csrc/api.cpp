@@ -4,8 +4,10 @@
 // returns its status with nothing enqueued.  Valid calls plan the mapping (plan.cpp)
 // and enqueue the kernels on the caller's stream; nothing here synchronises,
 // allocates device memory, or keeps a pointer past the call.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/rownorm.h"
 #include "launch.h"
@@ -43,6 +45,53 @@ hipError_t launch_bwd_rows(int kind, int dtype, int lpr, int vpl, const BwdArgs&
                : launch_bwd_rows_k1_d0(lpr, vpl, a, grid, s);
 }
 
+hipError_t launch_fwd_cluster_k0_d0(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
+hipError_t launch_fwd_cluster_k0_d1(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
+hipError_t launch_fwd_cluster_k1_d0(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
+hipError_t launch_fwd_cluster_k1_d1(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
+hipError_t launch_bwd_cluster_k0_d0(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
+hipError_t launch_bwd_cluster_k0_d1(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
+hipError_t launch_bwd_cluster_k1_d0(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
+hipError_t launch_bwd_cluster_k1_d1(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
+int occupancy_fwd_cluster_k0_d0(int, int, int);
+int occupancy_fwd_cluster_k0_d1(int, int, int);
+int occupancy_fwd_cluster_k1_d0(int, int, int);
+int occupancy_fwd_cluster_k1_d1(int, int, int);
+int occupancy_bwd_cluster_k0_d0(int, int, int);
+int occupancy_bwd_cluster_k0_d1(int, int, int);
+int occupancy_bwd_cluster_k1_d0(int, int, int);
+int occupancy_bwd_cluster_k1_d1(int, int, int);
+
+hipError_t launch_fwd_cluster(int kind, int dtype, int t, int vpl, int rows, const FwdArgs& a,
+                              const ClusterArgs& c, int grid, hipStream_t s) {
+  if (kind == 0) {
+    return dtype ? launch_fwd_cluster_k0_d1(t, vpl, rows, a, c, grid, s)
+                 : launch_fwd_cluster_k0_d0(t, vpl, rows, a, c, grid, s);
+  }
+  return dtype ? launch_fwd_cluster_k1_d1(t, vpl, rows, a, c, grid, s)
+               : launch_fwd_cluster_k1_d0(t, vpl, rows, a, c, grid, s);
+}
+
+hipError_t launch_bwd_cluster(int kind, int dtype, int t, int vpl, int rows, const BwdArgs& a,
+                              const ClusterArgs& c, int grid, hipStream_t s) {
+  if (kind == 0) {
+    return dtype ? launch_bwd_cluster_k0_d1(t, vpl, rows, a, c, grid, s)
+                 : launch_bwd_cluster_k0_d0(t, vpl, rows, a, c, grid, s);
+  }
+  return dtype ? launch_bwd_cluster_k1_d1(t, vpl, rows, a, c, grid, s)
+               : launch_bwd_cluster_k1_d0(t, vpl, rows, a, c, grid, s);
+}
+
+int occupancy_fwd_cluster(int kind, int dtype, int t, int vpl, int rows) {
+  if (kind == 0) return dtype ? occupancy_fwd_cluster_k0_d1(t, vpl, rows) : occupancy_fwd_cluster_k0_d0(t, vpl, rows);
+  return dtype ? occupancy_fwd_cluster_k1_d1(t, vpl, rows) : occupancy_fwd_cluster_k1_d0(t, vpl, rows);
+}
+
+int occupancy_bwd_cluster(int kind, int dtype, int t, int vpl, int rows) {
+  if (kind == 0) return dtype ? occupancy_bwd_cluster_k0_d1(t, vpl, rows) : occupancy_bwd_cluster_k0_d0(t, vpl, rows);
+  return dtype ? occupancy_bwd_cluster_k1_d1(t, vpl, rows) : occupancy_bwd_cluster_k1_d0(t, vpl, rows);
+}
+
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -68,9 +117,90 @@ struct EventScope {
   }
 };
 
+}  // namespace
+
+// Workgroups of a cluster kernel the current device can hold at once (0 if unknown).
+// Cached per (device, direction, kind, dtype, threads, vectors, rows per step).
+int cluster_capacity(bool backward, int kind, int dtype, int t, int vpl, int rows) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  static std::atomic<int> cus[64];
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  // occupancy depends only on the kernel and the device's per-CU limits
+  static std::mutex mu;
+  // [dev][bwd][kind][dtype][t: 256/512/1024][vpl: 1/2/4][rows per step: 1/2]
+  static int cache[64][2][2][2][3][3][2];
+  const int ti = t == 256 ? 0 : t == 512 ? 1 : 2;
+  const int vi = vpl == 1 ? 0 : vpl == 2 ? 1 : 2;
+  int occ;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    const int ri = rows == 1 ? 0 : 1;
+    occ = cache[dev][backward][kind][dtype][ti][vi][ri];
+    if (occ == 0) {
+      occ = backward ? occupancy_bwd_cluster(kind, dtype, t, vpl, rows)
+                     : occupancy_fwd_cluster(kind, dtype, t, vpl, rows);
+      cache[dev][backward][kind][dtype][ti][vi][ri] = occ > 0 ? occ : -1;
+    }
+  }
+  return occ > 0 ? occ * n : 0;
+}
+
+// Fit a CLUSTER plan to the device: clamp the number of clusters to what can be
+// co-resident (fewer clusters also means fewer dgamma/dbeta partial rows, so the
+// workspace the plan sized still suffices).  Returns false when not even one cluster
+// fits; the caller then takes the fallback plan.
+bool fit_cluster(bool backward, int kind, int dtype, Plan& p) {
+  const int cap = cluster_capacity(backward, kind, dtype, p.lpr, p.vpl, p.rows_per_step);
+  if (cap < p.cluster) return false;
+  if (p.grid > cap) {
+    int ncl = cap / p.cluster;
+    if (ncl >= 8) ncl -= ncl % 8;
+    p.nclusters = ncl;
+    p.grid = ncl * p.cluster;
+    if (backward) p.partial_rows = ncl;
+  }
+  return true;
+}
+
+namespace {
+
+ClusterArgs cluster_args(const Plan& p, char* ws) {
+  ClusterArgs c;
+  c.C = p.cluster;
+  c.nclusters = p.nclusters;
+  c.slice_vecs = p.slice_vecs;
+  c.rows_per_step = p.rows_per_step;
+  c.spin_limit = kSpinLimit;
+  c.xchg = reinterpret_cast<unsigned long long*>(ws + p.off_xchg);
+  c.status = reinterpret_cast<unsigned*>(ws + p.off_status);
+  return c;
+}
+
+// Zero the exchange slots and the status word before a cluster launch.  A fill kernel
+// rather than a memset, so the call stays safe to capture in a graph.
+hipError_t clear_exchange(const Plan& p, char* ws, hipStream_t s) {
+  return launch_zero(reinterpret_cast<float*>(ws + p.off_xchg), nullptr,
+                     int32_t((p.off_status + 256 - p.off_xchg) / 4), s);
+}
+
+norm_status_t check_workspace(const Plan& p, void* workspace, size_t given) {
+  if (p.ws_need == 0) return NORM_OK;
+  if (!workspace) return NORM_ERR_NULL_PTR;
+  if (!aligned(workspace, 16)) return NORM_ERR_MISALIGNED;
+  if (given < p.ws_need) return NORM_ERR_WORKSPACE_TOO_SMALL;
+  return NORM_OK;
+}
+
 norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* beta, void* y,
                        float* mean, float* rstd, int64_t M, int64_t N, float eps,
-                       norm_dtype_t dtype, hipStream_t stream, const norm_options_t* opt) {
+                       norm_dtype_t dtype, void* workspace, size_t workspace_bytes_given,
+                       hipStream_t stream, const norm_options_t* opt) {
   norm_status_t st = check_shape_dtype(M, N, dtype);
   if (st != NORM_OK) return st;
   if (!gamma || (ln && !beta)) return NORM_ERR_NULL_PTR;
@@ -84,6 +214,8 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
 
   Plan p;
   st = make_plan(false, ln, M, N, dtype, a16, opt, &p);
+  if (st != NORM_OK) return st;
+  st = check_workspace(p, workspace, workspace_bytes_given);
   if (st != NORM_OK) return st;
   if (M == 0) return NORM_OK;
 
@@ -104,10 +236,26 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   const int kind = ln ? 1 : 0;
   const int dt = dtype == NORM_DTYPE_BF16 ? 1 : 0;
   EventScope ev{opt, stream};
+  char* ws = static_cast<char*>(workspace);
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(false, kind, dt, p)) {
+    make_fallback_plan(false, ln, M, N, dtype, &p);
+  }
+  hipError_t e = hipSuccess;
+  if (p.path == NORM_PATH_CLUSTER) {
+    e = clear_exchange(p, ws, stream);
+    if (e != hipSuccess) return NORM_ERR_HIP;
+  }
   if (ev.start() != hipSuccess) return NORM_ERR_HIP;
-  hipError_t e = p.path == NORM_PATH_ROWS
-                     ? launch_fwd_rows(kind, dt, p.lpr, p.vpl, a, p.grid, stream)
-                     : launch_fwd_generic(kind, dt, a, p.grid, stream);
+  switch (p.path) {
+    case NORM_PATH_ROWS:
+      e = launch_fwd_rows(kind, dt, p.lpr, p.vpl, a, p.grid, stream);
+      break;
+    case NORM_PATH_CLUSTER:
+      e = launch_fwd_cluster(kind, dt, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws), p.grid, stream);
+      break;
+    default:
+      e = launch_fwd_generic(kind, dt, a, p.grid, stream);
+  }
   if (e != hipSuccess) return NORM_ERR_HIP;
   return hip_status(ev.stop());
 }
@@ -130,11 +278,8 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   Plan p;
   st = make_plan(true, ln, M, N, dtype, a16, opt, &p);
   if (st != NORM_OK) return st;
-  if (p.ws_bytes > 0) {
-    if (!workspace) return NORM_ERR_NULL_PTR;
-    if (!aligned(workspace, 16)) return NORM_ERR_MISALIGNED;
-    if (workspace_bytes_given < p.ws_bytes) return NORM_ERR_WORKSPACE_TOO_SMALL;
-  }
+  st = check_workspace(p, workspace, workspace_bytes_given);
+  if (st != NORM_OK) return st;
 
   const int kind = ln ? 1 : 0;
   const int dt = dtype == NORM_DTYPE_BF16 ? 1 : 0;
@@ -146,6 +291,9 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   }
 
   char* ws = static_cast<char*>(workspace);
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(true, kind, dt, p)) {
+    make_fallback_plan(true, ln, M, N, dtype, &p);
+  }
   BwdArgs a;
   a.dy = dy;
   a.x = x;
@@ -157,8 +305,8 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   a.part_b = (p.ws_bytes && ln) ? reinterpret_cast<float*>(ws + p.off_part_b) : nullptr;
   a.dgamma = dgamma;
   a.dbeta = db;
-  a.rowc = (p.ws_bytes && p.path != NORM_PATH_ROWS) ? reinterpret_cast<float*>(ws + p.off_rowc)
-                                                     : nullptr;
+  const bool two_pass = p.path == NORM_PATH_SPLIT || p.path == NORM_PATH_GENERIC;
+  a.rowc = two_pass ? reinterpret_cast<float*>(ws + p.off_rowc) : nullptr;
   a.M = M;
   a.N = int32_t(N);
   a.nvec = p.nvec;
@@ -173,9 +321,15 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
     e = launch_zero(dgamma, db, int32_t(N), stream);
     if (e != hipSuccess) return NORM_ERR_HIP;
   }
+  if (p.path == NORM_PATH_CLUSTER) {
+    e = clear_exchange(p, ws, stream);
+    if (e != hipSuccess) return NORM_ERR_HIP;
+  }
   if (ev.start() != hipSuccess) return NORM_ERR_HIP;
   if (p.path == NORM_PATH_ROWS) {
     e = launch_bwd_rows(kind, dt, p.lpr, p.vpl, a, p.grid, stream);
+  } else if (p.path == NORM_PATH_CLUSTER) {
+    e = launch_bwd_cluster(kind, dt, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws), p.grid, stream);
   } else {
     const bool vec = p.path == NORM_PATH_SPLIT;
     e = launch_bwd_rowdot(kind, dt, vec, a, p.grid, stream);
@@ -209,34 +363,52 @@ using rownorm::guarded;
 extern "C" {
 
 norm_status_t norm_rms_fwd(const void* x, const void* gamma, void* y, float* rstd, int64_t M,
-                           int64_t N, float eps, norm_dtype_t dtype, hipStream_t stream) {
+                           int64_t N, float eps, norm_dtype_t dtype, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   return guarded([&] {
-    return fwd_impl(false, x, gamma, nullptr, y, nullptr, rstd, M, N, eps, dtype, stream, nullptr);
+    return fwd_impl(false, x, gamma, nullptr, y, nullptr, rstd, M, N, eps, dtype, workspace,
+                    workspace_bytes, stream, nullptr);
   });
 }
 
 norm_status_t norm_ln_fwd(const void* x, const void* gamma, const void* beta, void* y,
                           float* mean, float* rstd, int64_t M, int64_t N, float eps,
-                          norm_dtype_t dtype, hipStream_t stream) {
+                          norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   return guarded([&] {
-    return fwd_impl(true, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream, nullptr);
+    return fwd_impl(true, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, workspace,
+                    workspace_bytes, stream, nullptr);
   });
 }
 
 norm_status_t norm_rms_fwd_ex(const void* x, const void* gamma, void* y, float* rstd, int64_t M,
-                              int64_t N, float eps, norm_dtype_t dtype, hipStream_t stream,
+                              int64_t N, float eps, norm_dtype_t dtype, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream,
                               const norm_options_t* opt) {
   return guarded([&] {
-    return fwd_impl(false, x, gamma, nullptr, y, nullptr, rstd, M, N, eps, dtype, stream, opt);
+    return fwd_impl(false, x, gamma, nullptr, y, nullptr, rstd, M, N, eps, dtype, workspace,
+                    workspace_bytes, stream, opt);
   });
 }
 
 norm_status_t norm_ln_fwd_ex(const void* x, const void* gamma, const void* beta, void* y,
                              float* mean, float* rstd, int64_t M, int64_t N, float eps,
-                             norm_dtype_t dtype, hipStream_t stream, const norm_options_t* opt) {
+                             norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream, const norm_options_t* opt) {
   return guarded([&] {
-    return fwd_impl(true, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, stream, opt);
+    return fwd_impl(true, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, workspace,
+                    workspace_bytes, stream, opt);
   });
+}
+
+size_t norm_fwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype) {
+  return norm_fwd_workspace_size_ex(M, N, is_layernorm, dtype, nullptr);
+}
+
+size_t norm_fwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
+                                  const norm_options_t* opt) {
+  if (rownorm::check_shape_dtype(M, N, dtype) != NORM_OK) return 0;
+  return rownorm::workspace_bytes(false, M, N, is_layernorm != 0, dtype, opt);
 }
 
 size_t norm_bwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype) {
@@ -246,7 +418,7 @@ size_t norm_bwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtyp
 size_t norm_bwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
                                   const norm_options_t* opt) {
   if (rownorm::check_shape_dtype(M, N, dtype) != NORM_OK) return 0;
-  return rownorm::workspace_bytes(M, N, is_layernorm != 0, dtype, opt);
+  return rownorm::workspace_bytes(true, M, N, is_layernorm != 0, dtype, opt);
 }
 
 norm_status_t norm_rms_bwd(const void* dy, const void* x, const void* gamma, const float* rstd,
@@ -302,11 +474,27 @@ norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
   info->lanes_per_row = p.lpr;
   info->vecs_per_lane = p.vpl;
   info->block = p.block;
-  info->grid = (p.path == NORM_PATH_ROWS || !is_backward) ? p.grid
-                                                            : int(p.slices * p.partial_rows);
+  info->grid = (p.path == NORM_PATH_ROWS || p.path == NORM_PATH_CLUSTER || !is_backward)
+                   ? p.grid
+                   : int(p.slices * p.partial_rows);
   info->partial_rows = int(p.partial_rows);
-  info->workspace_bytes = p.ws_bytes;
+  info->cluster_size = p.cluster;
+  info->cluster_rows = p.rows_per_step;
+  info->workspace_bytes = p.ws_need;
   return NORM_OK;
+}
+
+int norm_cluster_resident(int is_backward, int is_layernorm, int64_t M, int64_t N,
+                          norm_dtype_t dtype, const norm_options_t* opt) {
+  if (rownorm::check_shape_dtype(M, N, dtype) != NORM_OK) return -1;
+  rownorm::Plan p;
+  if (rownorm::make_plan(is_backward != 0, is_layernorm != 0, M, N, dtype, true, opt, &p) != NORM_OK)
+    return -1;
+  if (p.path != NORM_PATH_CLUSTER) return 0;
+  return rownorm::fit_cluster(is_backward != 0, is_layernorm ? 1 : 0,
+                              dtype == NORM_DTYPE_BF16 ? 1 : 0, p)
+             ? 1
+             : 0;
 }
 
 const char* norm_status_string(norm_status_t s) {

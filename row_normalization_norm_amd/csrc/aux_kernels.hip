@@ -148,8 +148,8 @@ __global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) 
       float xs[EPV], ds[EPV];
       if constexpr (VEC) {
         const int64_t vi = row * a.nvec + idx[v];
-        const u32x4 xv = ld16(a.x, vi);
-        const u32x4 dv = ld16(a.dy, vi);
+        const u32x4 xv = ld16_stream(a.x, vi);
+        const u32x4 dv = ld16_stream(a.dy, vi);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           xs[e] = D::get(xv, e);
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) 
         if constexpr (LN) accb[v][e] += ds[e];
       }
       if constexpr (VEC) {
-        st16(a.dx, row * a.nvec + idx[v], D::pack(o));
+        st16_stream(a.dx, row * a.nvec + idx[v], D::pack(o));
       } else {
         D::put_scalar(a.dx, row * a.N + idx[v], o[0]);
       }

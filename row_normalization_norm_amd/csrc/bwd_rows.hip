@@ -72,8 +72,8 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
       const bool ok = row_ok && vi < nvec;
-      xv[v] = ok ? ld16(a.x, vbase + vi) : zero16();
-      dv[v] = ok ? ld16(a.dy, vbase + vi) : zero16();
+      xv[v] = ok ? ld16_stream(a.x, vbase + vi) : zero16();
+      dv[v] = ok ? ld16_stream(a.dy, vbase + vi) : zero16();
       gv[v] = ok ? ld16(a.gamma, vi) : zero16();
     }
     const float r = row_ok ? a.rstd[row] : 0.0f;
@@ -125,17 +125,17 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float xh = (D::get(xv[v], e) - mu) * r;
-          const float g = D::get(dv[v], e) * D::get(gv[v], e);
+          const float xh = (D::get_fresh(xv[v], e) - mu) * r;
+          const float g = D::get_fresh(dv[v], e) * D::get_fresh(gv[v], e);
           o[e] = r * fmaf(-xh, c1, g - c2);
         }
-        st16(a.dx, vbase + vi, D::pack(o));
+        st16_stream(a.dx, vbase + vi, D::pack(o));
         if (mode == kAtomicRow) {
 #pragma unroll
           for (int e = 0; e < EPV; ++e) {
             const int col = vi * EPV + e;
-            const float d = D::get(dv[v], e);
-            unsafeAtomicAdd(a.dgamma + col, d * ((D::get(xv[v], e) - mu) * r));
+            const float d = D::get_fresh(dv[v], e);
+            unsafeAtomicAdd(a.dgamma + col, d * ((D::get_fresh(xv[v], e) - mu) * r));
             if constexpr (LN) unsafeAtomicAdd(a.dbeta + col, d);
           }
         }

@@ -1,0 +1,500 @@
+// Split-row ("cluster") kernels for rows too long for one workgroup's registers.
+//
+// The pages note that very long rows cost Triton on H100 because it cannot reduce a
+// row across cooperating SMs ("SOTA normalization performance with torch.compile",
+// theaicatchup.com, "How Did Torch.compile Catch Quack?").  Here C co-resident
+// workgroups share each row: workgroup k of a cluster owns the k-th column slice of every
+// row the cluster handles, keeps its slice of gamma (and beta) in registers for all of
+// them, and, in the backward, its slice's dgamma/dbeta column sums as well.  Per row, each
+// member reduces its slice inside the workgroup (DPP + LDS), publishes the partial sums,
+// waits for the other members' partials of the same row and combines all C of them in
+// member order (identical, deterministic bits in every member).  HBM sees every element
+// once, as in the register-resident kernels.
+//
+// Exchange: every row has its own slots, one per member, of 64-bit words each holding a
+// 32-bit tag (derived from the row index, never 0) and a 32-bit float.  A member writes
+// its words with relaxed agent-scope atomic stores and readers spin on agent-scope
+// atomic loads until the tag matches, so every word validates itself and no ordering
+// between different words is needed.  The slots are zeroed by a fill kernel before each
+// launch and each is written once per launch.
+// Co-residency of all workgroups is guaranteed by a cooperative launch; every wait is
+// bounded, and a timed-out wait yields NaN (and sets a status word) instead of hanging.
+//
+// LayerNorm statistics merge per-slice (sum, sum of squared deviations about the slice
+// mean) with the pairwise-update formula of Chan, Golub and LeVeque, so the variance is
+// exact for constant rows and free of mean(x^2) - mean^2 cancellation.
+//
+// Built once per (kind, dtype) from RN_KIND / RN_DTYPE on the command line.
+#include <type_traits>
+
+#include "launch.h"
+#include "rownorm_dev.h"
+
+#ifndef RN_KIND
+#error "RN_KIND must be defined"
+#endif
+#ifndef RN_DTYPE
+#error "RN_DTYPE must be defined"
+#endif
+
+namespace rownorm {
+namespace {
+
+__device__ inline uint32_t row_tag(int64_t row) {
+  return static_cast<uint32_t>((row + 1) & 0x7FFFFFFF) | 0x80000000u;
+}
+
+__device__ inline void publish(unsigned long long* slot, uint32_t tag, float v) {
+  const unsigned long long w = (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Spin until the slot carries `tag`.  Gives up after `limit` polls, or as soon as any
+// wait of the launch has given up (the status word is sticky), so a failed exchange
+// costs one time-out per launch, not one per row; the result is then NaN.
+__device__ inline float wait_for(unsigned long long* slot, uint32_t tag, uint32_t limit,
+                                 unsigned* status) {
+  for (uint32_t n = 0;; ++n) {
+    const unsigned long long w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (static_cast<uint32_t>(w >> 32) == tag) return __uint_as_float(static_cast<uint32_t>(w));
+    if (n >= limit) {
+      atomicOr(status, 1u);
+      return __builtin_nanf("");
+    }
+    if ((n & 63) == 63 &&
+        __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+      return __builtin_nanf("");
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Sum of K values over the workgroup at once (one barrier), identical in every thread.
+// red: 2 * NW * K floats, alternated by `parity`.
+template <int NW, int K>
+__device__ inline void block_sum_n(float (&v)[K], float* red, int& parity) {
+#pragma unroll
+  for (int k = 0; k < K; ++k) v[k] = group_sum<64>(v[k]);
+  if constexpr (NW > 1) {
+    float* buf = red + parity * NW * K;
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+      for (int k = 0; k < K; ++k) buf[(threadIdx.x >> 6) * K + k] = v[k];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      float t = 0.0f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += buf[w * K + k];
+      v[k] = t;
+    }
+    parity ^= 1;
+  }
+}
+
+// A cluster works in steps of R consecutive rows: step t covers rows t*R .. t*R+R-1, and
+// cluster cl takes steps cl, cl + nclusters, ...  One reduction and one exchange serve
+// all R rows of a step.  Every step has its own exchange slots: [member][K] 64-bit words.
+template <int K>
+__device__ inline void publish_step(const ClusterArgs& c, int member, int64_t step,
+                                    const float (&mine)[K]) {
+  if (threadIdx.x == 0) {
+    unsigned long long* base = c.xchg + step * c.C * K;
+#pragma unroll
+    for (int j = 0; j < K; ++j) publish(base + member * K + j, row_tag(step), mine[j]);
+  }
+}
+
+// Gather every member's K partials of `step` into xin[member * K + j]; visible to the whole
+// workgroup after the barrier.  The caller alternates between two xin buffers, so values
+// are never overwritten before every thread has read them.
+template <int K>
+__device__ inline void gather_step(const ClusterArgs& c, int64_t step, float* xin) {
+  if (threadIdx.x < c.C) {
+    unsigned long long* base = c.xchg + step * c.C * K;
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      xin[threadIdx.x * K + j] =
+          wait_for(base + threadIdx.x * K + j, row_tag(step), c.spin_limit, c.status);
+  }
+  __syncthreads();
+}
+
+// Each workgroup keeps three steps in registers: it publishes step t+1's partial sums and
+// issues step t+2's loads before it waits for the other members' partials of step t, so
+// the exchange round trip overlaps a step of work instead of stalling every step.
+
+// --------------------------------------------------------------------------- forward
+template <bool LN, typename D, int T, int VPL, int R>
+__global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const ClusterArgs c) {
+  constexpr int EPV = D::kPerVec;
+  constexpr int NW = T / 64;
+  constexpr int K = (LN ? 2 : 1) * R;  // exchanged values per member and step
+  const int tid = threadIdx.x;
+  const int cl = blockIdx.x % c.nclusters;
+  const int member = blockIdx.x / c.nclusters;
+  const int64_t vofs = static_cast<int64_t>(member) * c.slice_vecs;
+  const float slice_n = static_cast<float>(c.slice_vecs) * EPV;
+  const int64_t nsteps = (a.M + R - 1) / R;
+
+  bool own[VPL];
+  u32x4 g[VPL], b[LN ? VPL : 1];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    own[v] = v * T + tid < c.slice_vecs;
+    g[v] = own[v] ? ld16(a.gamma, vofs + v * T + tid) : zero16();
+    if constexpr (LN) b[v] = own[v] ? ld16(a.beta, vofs + v * T + tid) : zero16();
+  }
+
+  __shared__ float red[2 * NW * R];
+  __shared__ float xin[2][kMaxCluster * K];
+  int parity = 0, xp = 0;
+
+  auto load = [&](int64_t st, u32x4 (&buf)[R][VPL]) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = st * R + i;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+        buf[i][v] = (own[v] && row < a.M) ? ld16_stream(a.x, row * a.nvec + vofs + v * T + tid)
+                                          : zero16();
+    }
+  };
+  // This member's partial sums of a step's rows: RMSNorm sums of squares; LayerNorm slice
+  // sums and sums of squared deviations about the slice means.
+  auto partial = [&](const u32x4 (&buf)[R][VPL], float (&out)[K]) {
+    if constexpr (LN) {
+      float s[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        s[i] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) s[i] += D::get_fresh(buf[i][v], e);
+      }
+      block_sum_n<NW, R>(s, red, parity);
+      float m2[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float m_k = s[i] / slice_n;
+        m2[i] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const float d = own[v] ? D::get_fresh(buf[i][v], e) - m_k : 0.0f;
+            m2[i] = fmaf(d, d, m2[i]);
+          }
+      }
+      block_sum_n<NW, R>(m2, red, parity);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        out[2 * i] = s[i];
+        out[2 * i + 1] = m2[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        out[i] = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v)
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const float f = D::get_fresh(buf[i][v], e);
+            out[i] = fmaf(f, f, out[i]);
+          }
+      }
+      block_sum_n<NW, K>(out, red, parity);
+    }
+  };
+
+  u32x4 b0[R][VPL], b1[R][VPL], b2[R][VPL];
+  int64_t st = cl;
+  if (st >= nsteps) return;
+  load(st, b0);
+  if (st + c.nclusters < nsteps) load(st + c.nclusters, b1);
+  {
+    float mine[K];
+    partial(b0, mine);
+    publish_step<K>(c, member, st, mine);
+  }
+  for (; st < nsteps; st += c.nclusters) {
+    const int64_t s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
+    if (s1 < nsteps) {
+      float mine[K];
+      partial(b1, mine);
+      publish_step<K>(c, member, s1, mine);
+    }
+    if (s2 < nsteps) load(s2, b2);
+
+    float* xs = xin[xp];
+    xp ^= 1;
+    gather_step<K>(c, st, xs);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = st * R + i;
+      if (row >= a.M) break;
+      float mu = 0.0f, var;
+      if constexpr (LN) {
+        float tot = 0.0f;
+        for (int j = 0; j < c.C; ++j) tot += xs[j * K + 2 * i];
+        mu = tot * a.inv_n;
+        float m2t = 0.0f;
+        for (int j = 0; j < c.C; ++j) {
+          const float dm = xs[j * K + 2 * i] / slice_n - mu;
+          m2t += xs[j * K + 2 * i + 1] + slice_n * dm * dm;
+        }
+        var = m2t * a.inv_n;
+      } else {
+        float tot = 0.0f;
+        for (int j = 0; j < c.C; ++j) tot += xs[j * K + i];
+        var = tot * a.inv_n;
+      }
+      const float r = rsqrtf(var + a.eps);
+      if (member == 0 && tid == 0) {
+        if (a.rstd) a.rstd[row] = r;
+        if constexpr (LN) {
+          if (a.mean) a.mean[row] = mu;
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        if (!own[v]) continue;
+        float o[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float f = D::get_fresh(b0[i][v], e);
+          if constexpr (LN) {
+            o[e] = fmaf((f - mu) * r, D::get_fresh(g[v], e), D::get_fresh(b[v], e));
+          } else {
+            o[e] = f * r * D::get_fresh(g[v], e);
+          }
+        }
+        st16_stream(a.y, row * a.nvec + vofs + v * T + tid, D::pack(o));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        b0[i][v] = b1[i][v];
+        b1[i][v] = b2[i][v];
+      }
+  }
+}
+
+// -------------------------------------------------------------------------- backward
+template <bool LN, typename D, int T, int VPL, int R>
+__global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const ClusterArgs c) {
+  constexpr int EPV = D::kPerVec;
+  constexpr int NW = T / 64;
+  constexpr int K = 2 * R;  // exchanged values per member and step: (sum g*xhat, sum g) x R
+  const int tid = threadIdx.x;
+  const int cl = blockIdx.x % c.nclusters;
+  const int member = blockIdx.x / c.nclusters;
+  const int64_t vofs = static_cast<int64_t>(member) * c.slice_vecs;
+  const int64_t nsteps = (a.M + R - 1) / R;
+
+  bool own[VPL];
+  u32x4 g[VPL];
+  float accg[VPL][EPV], accb[LN ? VPL : 1][EPV];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    own[v] = v * T + tid < c.slice_vecs;
+    g[v] = own[v] ? ld16(a.gamma, vofs + v * T + tid) : zero16();
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      accg[v][e] = 0.0f;
+      if constexpr (LN) accb[v][e] = 0.0f;
+    }
+  }
+
+  __shared__ float red[2 * NW * K];
+  __shared__ float xin[2][kMaxCluster * K];
+  int parity = 0, xp = 0;
+
+  auto load = [&](int64_t st, u32x4 (&xb)[R][VPL], u32x4 (&db)[R][VPL]) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = st * R + i;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const bool ok = own[v] && row < a.M;
+        const int64_t idx = row * a.nvec + vofs + v * T + tid;
+        xb[i][v] = ok ? ld16_stream(a.x, idx) : zero16();
+        db[i][v] = ok ? ld16_stream(a.dy, idx) : zero16();
+      }
+    }
+  };
+  // Partial row sums of g*xhat and g over this member's slice, for each row of the step,
+  // and the slice's column contributions to dgamma/dbeta (which need no row sums).
+  // Rows past M have zero x and dy, so they add nothing.
+  auto partial = [&](int64_t st, const u32x4 (&xb)[R][VPL], const u32x4 (&db)[R][VPL],
+                     float (&out)[K]) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = st * R + i;
+      const float r = row < a.M ? a.rstd[row] : 0.0f;
+      const float mu = (LN && row < a.M) ? a.mean[row] : 0.0f;
+      float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float xh = (D::get_fresh(xb[i][v], e) - mu) * r;
+          const float d = D::get_fresh(db[i][v], e);
+          const float gg = d * D::get_fresh(g[v], e);
+          s1 = fmaf(gg, xh, s1);
+          if constexpr (LN) s2 += gg;
+          accg[v][e] = fmaf(d, xh, accg[v][e]);
+          if constexpr (LN) accb[v][e] += d;
+        }
+      }
+      out[2 * i] = s1;
+      out[2 * i + 1] = s2;
+    }
+    block_sum_n<NW, K>(out, red, parity);
+  };
+
+  u32x4 x0[R][VPL], d0[R][VPL], x1[R][VPL], d1[R][VPL], x2[R][VPL], d2[R][VPL];
+  int64_t st = cl;
+  if (st < nsteps) {
+    load(st, x0, d0);
+    if (st + c.nclusters < nsteps) load(st + c.nclusters, x1, d1);
+    float mine[K];
+    partial(st, x0, d0, mine);
+    publish_step<K>(c, member, st, mine);
+  }
+  for (; st < nsteps; st += c.nclusters) {
+    const int64_t s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
+    if (s1 < nsteps) {
+      float mine[K];
+      partial(s1, x1, d1, mine);
+      publish_step<K>(c, member, s1, mine);
+    }
+    if (s2 < nsteps) load(s2, x2, d2);
+
+    float* xs = xin[xp];
+    xp ^= 1;
+    gather_step<K>(c, st, xs);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = st * R + i;
+      if (row >= a.M) break;
+      float t1 = 0.0f, t2 = 0.0f;
+      for (int j = 0; j < c.C; ++j) {
+        t1 += xs[j * K + 2 * i];
+        t2 += xs[j * K + 2 * i + 1];
+      }
+      const float c1 = t1 * a.inv_n;
+      const float c2 = LN ? t2 * a.inv_n : 0.0f;
+      const float r = a.rstd[row];
+      const float mu = LN ? a.mean[row] : 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        if (!own[v]) continue;
+        float o[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float xh = (D::get_fresh(x0[i][v], e) - mu) * r;
+          const float gg = D::get_fresh(d0[i][v], e) * D::get_fresh(g[v], e);
+          o[e] = r * fmaf(-xh, c1, gg - c2);
+        }
+        st16_stream(a.dx, row * a.nvec + vofs + v * T + tid, D::pack(o));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        x0[i][v] = x1[i][v];
+        d0[i][v] = d1[i][v];
+        x1[i][v] = x2[i][v];
+        d1[i][v] = d2[i][v];
+      }
+  }
+
+  // This member's slice of the cluster's partial row.
+  float* const out_g = a.part_g + static_cast<int64_t>(cl) * a.N;
+  float* const out_b = LN ? a.part_b + static_cast<int64_t>(cl) * a.N : nullptr;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    if (!own[v]) continue;
+    const int64_t col0 = (vofs + v * T + tid) * EPV;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      out_g[col0 + e] = accg[v][e];
+      if constexpr (LN) out_b[col0 + e] = accb[v][e];
+    }
+  }
+}
+
+template <typename K, typename A>
+hipError_t launch_coop(K kernel, int grid, int block, const A& a, const ClusterArgs& c,
+                       hipStream_t s) {
+  A a_copy = a;
+  ClusterArgs c_copy = c;
+  void* args[] = {&a_copy, &c_copy};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block),
+                                    args, 0, s);
+}
+
+template <typename K>
+int occupancy(K kernel, int block) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(kernel), block,
+                                                   0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+}  // namespace
+
+#define RN_CAT_(a, b, c, d) a##b##c##d
+#define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
+#define RN_FWD_LAUNCHER RN_CAT(launch_fwd_cluster_k, RN_KIND, _d, RN_DTYPE)
+#define RN_BWD_LAUNCHER RN_CAT(launch_bwd_cluster_k, RN_KIND, _d, RN_DTYPE)
+#define RN_FWD_OCC RN_CAT(occupancy_fwd_cluster_k, RN_KIND, _d, RN_DTYPE)
+#define RN_BWD_OCC RN_CAT(occupancy_bwd_cluster_k, RN_KIND, _d, RN_DTYPE)
+
+using DT = std::conditional<RN_DTYPE == 1, BF16, F32>::type;
+constexpr bool kLN = RN_KIND == 1;
+
+hipError_t RN_FWD_LAUNCHER(int t, int vpl, int rows, const FwdArgs& a, const ClusterArgs& c, int grid,
+                           hipStream_t s) {
+#define RN_CASE(T_, V_, R_)                                                              \
+  if (t == T_ && vpl == V_ && rows == R_)                                                \
+    return launch_coop(fwd_cluster_kernel<kLN, DT, T_, V_, R_>, grid, T_, a, c, s);
+  RN_CLUSTER_FWD_MAPPINGS(RN_CASE)
+#undef RN_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t RN_BWD_LAUNCHER(int t, int vpl, int rows, const BwdArgs& a, const ClusterArgs& c, int grid,
+                           hipStream_t s) {
+#define RN_CASE(T_, V_, R_)                                                              \
+  if (t == T_ && vpl == V_ && rows == R_)                                                \
+    return launch_coop(bwd_cluster_kernel<kLN, DT, T_, V_, R_>, grid, T_, a, c, s);
+  RN_CLUSTER_BWD_MAPPINGS(RN_CASE)
+#undef RN_CASE
+  return hipErrorInvalidValue;
+}
+
+int RN_FWD_OCC(int t, int vpl, int rows) {
+#define RN_CASE(T_, V_, R_) \
+  if (t == T_ && vpl == V_ && rows == R_) return occupancy(fwd_cluster_kernel<kLN, DT, T_, V_, R_>, T_);
+  RN_CLUSTER_FWD_MAPPINGS(RN_CASE)
+#undef RN_CASE
+  return 0;
+}
+
+int RN_BWD_OCC(int t, int vpl, int rows) {
+#define RN_CASE(T_, V_, R_) \
+  if (t == T_ && vpl == V_ && rows == R_) return occupancy(bwd_cluster_kernel<kLN, DT, T_, V_, R_>, T_);
+  RN_CLUSTER_BWD_MAPPINGS(RN_CASE)
+#undef RN_CASE
+  return 0;
+}
+
+}  // namespace rownorm

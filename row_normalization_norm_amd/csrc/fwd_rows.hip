@@ -89,7 +89,7 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
-      xv[v] = (row_ok && vi < nvec) ? ld16(a.x, vbase + vi) : zero16();
+      xv[v] = (row_ok && vi < nvec) ? ld16_stream(a.x, vbase + vi) : zero16();
     }
 
     // RMSNorm: mean of squares.  LayerNorm: the mean, then the mean squared deviation
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
         const bool in_row = v * LPR + lane < nvec;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float d = in_row ? D::get(xv[v], e) - mu : 0.0f;
+          const float d = in_row ? D::get_fresh(xv[v], e) - mu : 0.0f;
           ss = fmaf(d, d, ss);
         }
       }
@@ -153,14 +153,16 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float f = D::get(xv[v], e);
+          // Second use of the packed row: unpack afresh so that only the packed words
+          // stay live across the reductions.
+          const float f = D::get_fresh(xv[v], e);
           if constexpr (LN) {
-            o[e] = fmaf((f - mu) * r, D::get(gv, e), D::get(bv, e));
+            o[e] = fmaf((f - mu) * r, D::get_fresh(gv, e), D::get_fresh(bv, e));
           } else {
-            o[e] = f * r * D::get(gv, e);
+            o[e] = f * r * D::get_fresh(gv, e);
           }
         }
-        st16(a.y, vbase + vi, D::pack(o));
+        st16_stream(a.y, vbase + vi, D::pack(o));
       }
     }
   }

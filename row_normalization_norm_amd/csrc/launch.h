@@ -34,6 +34,18 @@ namespace rownorm {
   X(512, 1) X(512, 2) X(512, 3) X(512, 4)                                              \
   X(1024, 1)
 
+// Split-row (cluster) kernels: (threads per member workgroup, vectors per lane, rows
+// per step).
+#define RN_CLUSTER_FWD_MAPPINGS(X)                                                       \
+  X(256, 1, 1) X(256, 2, 1) X(256, 4, 1) X(512, 1, 1) X(512, 2, 1) X(512, 4, 1)           \
+  X(1024, 1, 1) X(1024, 2, 1) X(1024, 4, 1)                                              \
+  X(256, 1, 2) X(256, 2, 2) X(512, 1, 2) X(512, 2, 2) X(1024, 1, 2) X(1024, 2, 2)
+#define RN_CLUSTER_BWD_MAPPINGS(X)                                                       \
+  X(256, 1, 1) X(256, 2, 1) X(512, 1, 1) X(512, 2, 1) X(1024, 1, 1) X(1024, 2, 1)         \
+  X(256, 1, 2) X(512, 1, 2) X(1024, 1, 2) X(256, 2, 2) X(512, 2, 2)
+constexpr int kMaxCluster = 32;            // workgroups sharing one row, at most
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls before a cluster wait gives up
+
 // Threads per workgroup for a row mapping.
 constexpr int fwd_block(int lpr) { return lpr >= 256 ? lpr : 256; }
 constexpr int bwd_block(int lpr) { return lpr >= 512 ? lpr : 512; }
@@ -86,6 +98,17 @@ struct BwdArgs {
   int64_t rows_per_block;  // SPLIT / GENERIC column pass: rows per row block
 };
 
+struct ClusterArgs {
+  int32_t C;                 // workgroups per row
+  int32_t nclusters;         // clusters; workgroup b is member b / nclusters of cluster
+                             // b % nclusters
+  int32_t slice_vecs;        // 16-byte vectors of a row each member owns (nvec / C)
+  int32_t rows_per_step;     // R: rows one reduction and one exchange serve
+  uint32_t spin_limit;
+  unsigned long long* xchg;  // [steps][C][2R] tagged partial sums, zeroed before each launch
+  unsigned* status;          // set to nonzero when a wait gave up
+};
+
 // ------------------------------------------------------------------ launchers
 // kind: 0 = RMSNorm, 1 = LayerNorm.  dtype: 0 = fp32, 1 = bf16.  Each returns
 // hipErrorInvalidValue when the (lpr, vpl) mapping is not compiled.
@@ -99,6 +122,13 @@ hipError_t launch_bwd_rowdot(int kind, int dtype, bool vec, const BwdArgs& a, in
                              hipStream_t s);
 hipError_t launch_bwd_colslice(int kind, int dtype, bool vec, const BwdArgs& a, int slices,
                                int row_blocks, hipStream_t s);
+// Split-row kernels (cooperative launch) and their occupancy (workgroups per CU).
+hipError_t launch_fwd_cluster(int kind, int dtype, int t, int vpl, int rows, const FwdArgs& a,
+                              const ClusterArgs& c, int grid, hipStream_t s);
+hipError_t launch_bwd_cluster(int kind, int dtype, int t, int vpl, int rows, const BwdArgs& a,
+                              const ClusterArgs& c, int grid, hipStream_t s);
+int occupancy_fwd_cluster(int kind, int dtype, int t, int vpl, int rows);
+int occupancy_bwd_cluster(int kind, int dtype, int t, int vpl, int rows);
 // GENERIC forward (scalar loads).
 hipError_t launch_fwd_generic(int kind, int dtype, const FwdArgs& a, int grid, hipStream_t s);
 // Column reduce: out[j] = sum_p part[p*N + j] for dgamma (and dbeta if part_b).

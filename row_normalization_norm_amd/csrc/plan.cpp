@@ -9,8 +9,10 @@
 //     (N=384 bf16 is 48 vectors = 16 lanes x 3, one DPP row of a wavefront, no padding);
 //   * among exact covers, VPL closest to a per-direction target (enough bytes in flight
 //     per lane without starving occupancy), then the fewest lanes (cheaper reduction);
-//   * the backward keeps per-column partial sums in registers, so it only takes mappings
-//     that fit its register budget; longer rows go to the SPLIT path.
+//   * rows longer than one workgroup's register budget are split over a cluster of
+//     co-resident workgroups (CLUSTER), each owning a column slice;
+//   * without 16-byte alignment, or when N is not a whole number of vectors, a scalar
+//     path handles any shape.
 #include "plan.h"
 
 #include "launch.h"
@@ -27,10 +29,39 @@ constexpr Mapping kFwdMappings[] = {RN_FWD_MAPPINGS(RN_ENTRY)};
 constexpr Mapping kBwdMappings[] = {RN_BWD_MAPPINGS(RN_ENTRY)};
 #undef RN_ENTRY
 
-constexpr int kFwdTargetVpl = 4;
-constexpr int kBwdTargetVpl = 2;
-constexpr int kFwdBlocksPerCu = 8;      // 256-thread workgroups resident per CU (target)
-constexpr int kBwdPartialsCap = 512;    // dgamma/dbeta partial rows of the ROWS backward
+struct ClusterMapping {
+  int t, vpl, rows;
+};
+#define RN_ENTRY(T, V, R) {T, V, R},
+constexpr ClusterMapping kClusterFwdMappings[] = {RN_CLUSTER_FWD_MAPPINGS(RN_ENTRY)};
+constexpr ClusterMapping kClusterBwdMappings[] = {RN_CLUSTER_BWD_MAPPINGS(RN_ENTRY)};
+#undef RN_ENTRY
+
+// Vectors per lane the mapping choice aims at, and the persistent grids (measured on
+// MI355X across the row lengths 256..32768): the forward wants ~4 vectors (2 for rows of
+// 1024+ vectors) and 512 workgroups; the backward, which also keeps per-column partial
+// sums in registers, wants 2 vectors for short rows, 1 around 256 vectors and 4 beyond,
+// with one workgroup per CU (two for the light 1-vector mappings).
+constexpr int kFwdGrid = 512;
+constexpr int kBwdGrid = 256;
+int fwd_target_vpl(int64_t nvec) { return nvec < 1024 ? 4 : 2; }
+int bwd_target_vpl(int64_t nvec) { return nvec <= 128 ? 2 : nvec <= 256 ? 1 : 4; }
+// Longest row (in 16-byte vectors) the forward keeps in one workgroup before splitting it
+// over a cluster; fp32 RMSNorm (no beta, 4 elements per vector) stays resident longer.
+constexpr int64_t kFwdRowsMaxVecs = 8192;
+constexpr int64_t kFwdRowsMaxVecsF32Rms = 16384;
+constexpr int64_t kBwdRowsMaxVecs = 2048;  // same for the backward
+// Vectors per lane of the cluster kernels: beyond these the kernels need more than the
+// 128 VGPRs a 1024-thread workgroup may use (the backward also holds the per-column
+// partial sums and a prefetched row of x and dy).
+constexpr int kClusterFwdMaxVpl = 4;
+constexpr int kClusterBwdMaxVpl = 2;
+// Rows per cluster step: one reduction and one exchange serve this many rows.  The bf16
+// backward moves half the bytes per element, so it batches two rows to amortise the
+// per-step synchronisation over as many bytes as fp32 moves in one.
+constexpr int kClusterFwdRows = 1;
+constexpr int kClusterBwdRowsBf16 = 2;
+constexpr int kClusterBwdRowsF32 = 1;
 constexpr int kSplitTargetBlocks = 2048;
 constexpr int kSplitMaxRowBlocks = 256;
 constexpr int kRowPassMaxGrid = 2048;
@@ -38,16 +69,13 @@ constexpr int kRowPassMaxGrid = 2048;
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Best (lanes, vectors) covering `units` 16-byte vectors: least padding, then vectors per
+// lane closest to `target`, then the fewest lanes (with `distance_first`, closeness to the
+// target ranks before padding).  Mappings whose last vector slot would be empty in every
+// lane are not considered.
 template <size_t K>
-bool compiled(const Mapping (&list)[K], int lpr, int vpl) {
-  for (const Mapping& m : list)
-    if (m.lpr == lpr && m.vpl == vpl) return true;
-  return false;
-}
-
-template <size_t K>
-bool choose_mapping(const Mapping (&list)[K], int64_t nvec, int target, int req_lpr, int req_vpl,
-                    Mapping* out) {
+bool choose_mapping(const Mapping (&list)[K], int64_t units, int target, int max_vpl, int req_lpr,
+                    int req_vpl, bool distance_first, Mapping* out) {
   bool found = false;
   Mapping best{0, 0};
   int64_t best_waste = 0;
@@ -55,15 +83,19 @@ bool choose_mapping(const Mapping (&list)[K], int64_t nvec, int target, int req_
   for (const Mapping& m : list) {
     if (req_lpr && m.lpr != req_lpr) continue;
     if (req_vpl && m.vpl != req_vpl) continue;
+    if (!req_vpl && m.vpl > max_vpl) continue;
     const int64_t cover = int64_t(m.lpr) * m.vpl;
-    if (cover < nvec) continue;
-    // Reject mappings where whole vector slots of every lane would be empty.
-    if (cover - nvec >= m.lpr) continue;
-    const int64_t waste = cover - nvec;
+    if (cover < units || cover - units >= m.lpr) continue;
+    const int64_t waste = cover - units;
     const int dist = m.vpl > target ? m.vpl - target : target - m.vpl;
-    const bool better = !found || waste < best_waste ||
-                        (waste == best_waste && dist < best_dist) ||
-                        (waste == best_waste && dist == best_dist && m.lpr < best.lpr);
+    const bool fewer = m.lpr < best.lpr;
+    const bool better =
+        !found ||
+        (distance_first
+             ? (dist < best_dist || (dist == best_dist && waste < best_waste) ||
+                (dist == best_dist && waste == best_waste && fewer))
+             : (waste < best_waste || (waste == best_waste && dist < best_dist) ||
+                (waste == best_waste && dist == best_dist && fewer)));
     if (better) {
       found = true;
       best = m;
@@ -75,101 +107,138 @@ bool choose_mapping(const Mapping (&list)[K], int64_t nvec, int target, int req_
   return found;
 }
 
-}  // namespace
+// choose_mapping over a runtime list, preferring more lanes (fewer registers per lane).
+bool choose_mapping_n(const Mapping* list, int n, int64_t units, int target, int max_vpl,
+                      int req_lpr, int req_vpl, Mapping* out) {
+  bool found = false;
+  Mapping best{0, 0};
+  int64_t best_waste = 0;
+  int best_dist = 0;
+  for (int k = 0; k < n; ++k) {
+    const Mapping& m = list[k];
+    if (req_lpr && m.lpr != req_lpr) continue;
+    if (req_vpl && m.vpl != req_vpl) continue;
+    if (!req_vpl && m.vpl > max_vpl) continue;
+    const int64_t cover = int64_t(m.lpr) * m.vpl;
+    if (cover < units || cover - units >= m.lpr) continue;
+    const int64_t waste = cover - units;
+    const int dist = m.vpl > target ? m.vpl - target : target - m.vpl;
+    const bool better = !found || waste < best_waste || (waste == best_waste && dist < best_dist) ||
+                        (waste == best_waste && dist == best_dist && m.lpr > best.lpr);
+    if (better) {
+      found = true;
+      best = m;
+      best_waste = waste;
+      best_dist = dist;
+    }
+  }
+  if (found) *out = best;
+  return found;
+}
 
-norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
-                        bool aligned16, const norm_options_t* opt, Plan* out) {
-  norm_options_t defaults = {};
-  const norm_options_t& o = opt ? *opt : defaults;
-  if (o.path < NORM_PATH_AUTO || o.path > NORM_PATH_GENERIC || o.lanes_per_row < 0 ||
-      o.vecs_per_lane < 0 || o.grid < 0 || o.dgamma_mode < NORM_DGAMMA_TWO_STAGE ||
-      o.dgamma_mode > NORM_DGAMMA_ATOMIC_WG)
-    return NORM_ERR_BAD_OPTION;
-  const bool atomic = backward && o.dgamma_mode != NORM_DGAMMA_TWO_STAGE;
-
-  Plan p;
-  const int epv = dtype == NORM_DTYPE_BF16 ? 8 : 4;
-  const bool vec_ok = aligned16 && (N % epv == 0);
-  const int64_t nvec = vec_ok ? N / epv : 0;
-  p.nvec = int(nvec);
-
-  int path = o.path;
+bool plan_rows(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec,
+               const norm_options_t& o, bool atomic, Plan& p) {
   Mapping m{0, 0};
-  if (path == NORM_PATH_AUTO) {
-    if (!vec_ok) {
-      path = NORM_PATH_GENERIC;
-    } else if (!backward) {
-      path = choose_mapping(kFwdMappings, nvec, kFwdTargetVpl, o.lanes_per_row, o.vecs_per_lane, &m)
-                 ? NORM_PATH_ROWS
-                 : NORM_PATH_GENERIC;
-    } else {
-      path = choose_mapping(kBwdMappings, nvec, kBwdTargetVpl, o.lanes_per_row, o.vecs_per_lane, &m)
-                 ? NORM_PATH_ROWS
-                 : NORM_PATH_SPLIT;
+  const bool ok = backward ? choose_mapping(kBwdMappings, nvec, bwd_target_vpl(nvec), 1 << 30,
+                                            o.lanes_per_row, o.vecs_per_lane, true, &m)
+                           : choose_mapping(kFwdMappings, nvec, fwd_target_vpl(nvec), 1 << 30,
+                                            o.lanes_per_row, o.vecs_per_lane, false, &m);
+  if (!ok) return false;
+  p.path = NORM_PATH_ROWS;
+  p.lpr = m.lpr;
+  p.vpl = m.vpl;
+  if (!backward) {
+    p.block = fwd_block(m.lpr);
+    p.groups = ceil_div(M, p.block / m.lpr);
+    int64_t grid = p.groups < kFwdGrid ? p.groups : kFwdGrid;
+    if (o.grid) grid = o.grid;
+    p.grid = int(grid);
+  } else {
+    p.block = bwd_block(m.lpr);
+    p.groups = ceil_div(M, p.block / m.lpr);
+    const int64_t cap = (m.vpl == 1 && m.lpr >= 128) ? 2 * kBwdGrid : kBwdGrid;
+    int64_t grid = p.groups < cap ? p.groups : cap;
+    // An explicit grid sets the number of partial rows; the workspace size follows it
+    // (norm_bwd_workspace_size_ex with the same options).
+    if (o.grid) grid = o.grid < p.groups ? o.grid : p.groups;
+    if (grid < 1) grid = 1;
+    p.grid = int(grid);
+    if (!atomic) {
+      p.partial_rows = grid;
+      p.off_part_g = 0;
+      p.off_part_b = align256(size_t(grid) * size_t(N) * 4);
+      p.ws_bytes = layernorm ? 2 * p.off_part_b : p.off_part_b;
     }
-  } else if (path == NORM_PATH_ROWS) {
-    if (!vec_ok) return NORM_ERR_BAD_OPTION;
-    const bool ok = backward ? choose_mapping(kBwdMappings, nvec, kBwdTargetVpl, o.lanes_per_row,
-                                              o.vecs_per_lane, &m)
-                             : choose_mapping(kFwdMappings, nvec, kFwdTargetVpl, o.lanes_per_row,
-                                              o.vecs_per_lane, &m);
-    if (!ok) return NORM_ERR_BAD_OPTION;
-  } else if (path == NORM_PATH_SPLIT) {
-    if (!vec_ok || !backward) return NORM_ERR_BAD_OPTION;
   }
-  if (path != NORM_PATH_ROWS && (o.lanes_per_row || o.vecs_per_lane)) return NORM_ERR_BAD_OPTION;
-  if (atomic && path != NORM_PATH_ROWS) return NORM_ERR_BAD_OPTION;
-  p.path = path;
+  return true;
+}
 
-  if (path == NORM_PATH_ROWS) {
-    p.lpr = m.lpr;
-    p.vpl = m.vpl;
-    if (!backward) {
-      p.block = fwd_block(m.lpr);
-      p.groups = ceil_div(M, p.block / m.lpr);
-      const int64_t cap = int64_t(kGfx950Cus) * (kFwdBlocksPerCu * 256 / p.block > 0
-                                                     ? kFwdBlocksPerCu * 256 / p.block
-                                                     : 1);
-      int64_t grid = p.groups < cap ? p.groups : cap;
-      if (o.grid) grid = o.grid;
-      p.grid = int(grid);
-    } else {
-      p.block = bwd_block(m.lpr);
-      p.groups = ceil_div(M, p.block / m.lpr);
-      int64_t grid = p.groups < kBwdPartialsCap ? p.groups : kBwdPartialsCap;
-      if (o.grid) {
-        if (o.grid > grid && !atomic) return NORM_ERR_BAD_OPTION;
-        grid = o.grid;
-      }
-      p.grid = int(grid);
-      if (!atomic) {
-        p.partial_rows = grid;
-        p.off_part_g = 0;
-        p.off_part_b = align256(size_t(grid) * size_t(N) * 4);
-        p.ws_bytes = layernorm ? 2 * p.off_part_b : p.off_part_b;
-      }
+bool plan_cluster(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec, int dtype,
+                  const norm_options_t& o, Plan& p) {
+  const int max_vpl = backward ? kClusterBwdMaxVpl : kClusterFwdMaxVpl;
+  const int rows = o.cluster_rows ? o.cluster_rows
+                   : !backward               ? kClusterFwdRows
+                   : dtype == NORM_DTYPE_BF16 ? kClusterBwdRowsBf16
+                                              : kClusterBwdRowsF32;
+  // The compiled (threads, vectors) pairs for this rows-per-step.
+  Mapping list[32];
+  int n = 0;
+  const ClusterMapping* all = backward ? kClusterBwdMappings : kClusterFwdMappings;
+  const int count = backward ? int(sizeof(kClusterBwdMappings) / sizeof(ClusterMapping))
+                             : int(sizeof(kClusterFwdMappings) / sizeof(ClusterMapping));
+  for (int k = 0; k < count; ++k) {
+    if (all[k].rows == rows && n < 32) list[n++] = Mapping{all[k].t, all[k].vpl};
+  }
+  Mapping m{0, 0};
+  int C = 0;
+  for (int c = 2; c <= kMaxCluster && n > 0; c *= 2) {
+    if (o.cluster_size && c != o.cluster_size) continue;
+    if (nvec % c) continue;
+    const int64_t sv = nvec / c;
+    if (choose_mapping_n(list, n, sv, max_vpl, max_vpl, o.lanes_per_row, o.vecs_per_lane, &m)) {
+      C = c;
+      break;
     }
-    if (M == 0) p.grid = 0;
-    *out = p;
-    return NORM_OK;
   }
-
-  if (!backward) {  // GENERIC forward
-    p.block = kRowBlock;
-    p.grid = int(M < kRowPassMaxGrid ? M : kRowPassMaxGrid);
-    if (o.grid) p.grid = o.grid;
-    if (M == 0) p.grid = 0;
-    *out = p;
-    return NORM_OK;
+  if (!C) return false;
+  p.rows_per_step = rows;
+  p.path = NORM_PATH_CLUSTER;
+  p.lpr = m.lpr;
+  p.vpl = m.vpl;
+  p.block = m.lpr;
+  p.cluster = C;
+  p.slice_vecs = int(nvec / C);
+  const int per_cu = 1024 / m.lpr;  // workgroups per CU the grid assumes resident
+  int64_t ncl = int64_t(kGfx950Cus) * per_cu / C;
+  if (ncl >= 8) ncl -= ncl % 8;     // members of a cluster land on one XCD
+  if (o.grid) ncl = o.grid / C;
+  if (ncl > M) ncl = M;
+  if (ncl < 1) ncl = 1;
+  p.nclusters = int(ncl);
+  p.grid = int(ncl * C);
+  p.off_xchg = 0;
+  // every step of rows has its own exchange slots: 2 values per row and member
+  p.xchg_bytes = size_t(M + rows) * C * 2 * 8;
+  p.off_status = align256(p.xchg_bytes);
+  size_t end = p.off_status + 256;
+  if (backward) {
+    p.partial_rows = ncl;
+    const size_t part = align256(size_t(ncl) * size_t(N) * 4);
+    p.off_part_g = end;
+    p.off_part_b = end + part;
+    end += layernorm ? 2 * part : part;
   }
+  p.ws_bytes = end;
+  return true;
+}
 
-  // SPLIT / GENERIC backward: row pass, column pass, column reduce.
+void plan_split(bool layernorm, int64_t M, int64_t N, int64_t nvec, bool vec,
+                const norm_options_t& o, Plan& p) {
+  p.path = vec ? NORM_PATH_SPLIT : NORM_PATH_GENERIC;
   p.block = kSliceBlock;
   p.grid = int(M < kRowPassMaxGrid ? M : kRowPassMaxGrid);
-  const int64_t slice_width = path == NORM_PATH_SPLIT ? int64_t(kSliceBlock) * kSliceVecs
-                                                      : int64_t(kSliceBlock);
-  const int64_t units = path == NORM_PATH_SPLIT ? nvec : N;
-  p.slices = int(ceil_div(units, slice_width));
+  const int64_t slice_width = vec ? int64_t(kSliceBlock) * kSliceVecs : int64_t(kSliceBlock);
+  p.slices = int(ceil_div(vec ? nvec : N, slice_width));
   int64_t row_blocks = ceil_div(kSplitTargetBlocks, p.slices);
   if (row_blocks > kSplitMaxRowBlocks) row_blocks = kSplitMaxRowBlocks;
   if (o.grid) row_blocks = o.grid;
@@ -182,18 +251,117 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
   const size_t part = align256(size_t(p.partial_rows) * size_t(N) * 4);
   p.off_part_b = p.off_part_g + part;
   p.ws_bytes = layernorm ? p.off_part_b + part : p.off_part_b;
+}
+
+void plan_generic_fwd(int64_t M, const norm_options_t& o, Plan& p) {
+  p.path = NORM_PATH_GENERIC;
+  p.block = kRowBlock;
+  p.grid = int(M < kRowPassMaxGrid ? M : kRowPassMaxGrid);
+  if (o.grid) p.grid = o.grid;
+}
+
+}  // namespace
+
+norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
+                        bool aligned16, const norm_options_t* opt, Plan* out) {
+  norm_options_t defaults = {};
+  const norm_options_t& o = opt ? *opt : defaults;
+  if (o.path < NORM_PATH_AUTO || o.path > NORM_PATH_CLUSTER || o.lanes_per_row < 0 ||
+      o.vecs_per_lane < 0 || o.grid < 0 || o.cluster_size < 0 || o.cluster_size > kMaxCluster ||
+      o.cluster_rows < 0 || o.cluster_rows > 2 ||
+      o.dgamma_mode < NORM_DGAMMA_TWO_STAGE || o.dgamma_mode > NORM_DGAMMA_ATOMIC_WG)
+    return NORM_ERR_BAD_OPTION;
+  const bool atomic = backward && o.dgamma_mode != NORM_DGAMMA_TWO_STAGE;
+
+  Plan p;
+  const int epv = dtype == NORM_DTYPE_BF16 ? 8 : 4;
+  const bool vec_ok = aligned16 && (N % epv == 0);
+  const int64_t nvec = vec_ok ? N / epv : 0;
+  p.nvec = int(nvec);
+
+  bool ok = true;
+  switch (o.path) {
+    case NORM_PATH_AUTO:
+      if (!vec_ok) {
+        if (backward) {
+          plan_split(layernorm, M, N, nvec, false, o, p);
+        } else {
+          plan_generic_fwd(M, o, p);
+        }
+      } else if (atomic ||
+                 nvec <= (backward                                    ? kBwdRowsMaxVecs
+                          : (dtype == NORM_DTYPE_F32 && !layernorm) ? kFwdRowsMaxVecsF32Rms
+                                                                    : kFwdRowsMaxVecs)) {
+        ok = plan_rows(backward, layernorm, M, N, nvec, o, atomic, p);
+      } else if (!plan_cluster(backward, layernorm, M, N, nvec, dtype, o, p)) {
+        if (backward) {
+          plan_split(layernorm, M, N, nvec, true, o, p);
+        } else if (!plan_rows(false, layernorm, M, N, nvec, o, false, p)) {
+          plan_generic_fwd(M, o, p);
+        }
+      }
+      break;
+    case NORM_PATH_ROWS:
+      ok = vec_ok && plan_rows(backward, layernorm, M, N, nvec, o, atomic, p);
+      break;
+    case NORM_PATH_CLUSTER:
+      ok = vec_ok && !atomic && plan_cluster(backward, layernorm, M, N, nvec, dtype, o, p);
+      break;
+    case NORM_PATH_SPLIT:
+      ok = vec_ok && backward;
+      if (ok) plan_split(layernorm, M, N, nvec, true, o, p);
+      break;
+    case NORM_PATH_GENERIC:
+      if (backward) {
+        plan_split(layernorm, M, N, nvec, false, o, p);
+      } else {
+        plan_generic_fwd(M, o, p);
+      }
+      break;
+  }
+  if (!ok) return NORM_ERR_BAD_OPTION;
+  if (p.path != NORM_PATH_ROWS && p.path != NORM_PATH_CLUSTER &&
+      (o.lanes_per_row || o.vecs_per_lane))
+    return NORM_ERR_BAD_OPTION;
+  if (p.path != NORM_PATH_CLUSTER && (o.cluster_size || o.cluster_rows)) return NORM_ERR_BAD_OPTION;
+  if (atomic && p.path != NORM_PATH_ROWS) return NORM_ERR_BAD_OPTION;
+
+  p.ws_need = p.ws_bytes;
+  if (p.path == NORM_PATH_CLUSTER) {
+    Plan f;
+    make_fallback_plan(backward, layernorm, M, N, dtype, &f);
+    if (f.ws_bytes > p.ws_need) p.ws_need = f.ws_bytes;
+  }
   if (M == 0) p.grid = 0;
   *out = p;
   return NORM_OK;
 }
 
-size_t workspace_bytes(int64_t M, int64_t N, bool layernorm, int dtype, const norm_options_t* opt) {
+norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
+                                 Plan* out) {
+  norm_options_t o = {};
+  Plan p;
+  const int epv = dtype == NORM_DTYPE_BF16 ? 8 : 4;
+  p.nvec = int(N / epv);
+  if (backward) {
+    plan_split(layernorm, M, N, p.nvec, true, o, p);
+  } else {
+    plan_generic_fwd(M, o, p);
+  }
+  if (M == 0) p.grid = 0;
+  p.ws_need = p.ws_bytes;
+  *out = p;
+  return NORM_OK;
+}
+
+size_t workspace_bytes(bool backward, int64_t M, int64_t N, bool layernorm, int dtype,
+                       const norm_options_t* opt) {
   size_t best = 0;
   for (int aligned = 0; aligned < 2; ++aligned) {
     Plan p;
-    if (make_plan(true, layernorm, M, N, dtype, aligned != 0, opt, &p) == NORM_OK &&
-        p.ws_bytes > best)
-      best = p.ws_bytes;
+    if (make_plan(backward, layernorm, M, N, dtype, aligned != 0, opt, &p) == NORM_OK &&
+        p.ws_need > best)
+      best = p.ws_need;
   }
   return best;
 }

@@ -1,7 +1,7 @@
 // Row-mapping planner: picks the kernel family, the lanes-per-row / vectors-per-lane
-// mapping, the persistent grid and the workspace layout for one call.  Pure host code
-// (no HIP calls), so the same answer is available to norm_plan(), to the workspace-size
-// query and to the launch itself.
+// mapping, the grid and the workspace layout for one call.  Pure host code (no HIP
+// calls), so the same answer is available to norm_plan(), to the workspace-size queries
+// and to the launch itself.
 #pragma once
 
 #include <stddef.h>
@@ -11,31 +11,43 @@
 
 namespace rownorm {
 
-// Compute units of a gfx950 part (MI350X / MI355X).  Used only to size persistent grids
-// and the number of dgamma/dbeta partial rows; a device with fewer CUs runs the same
-// grid with fewer workgroups resident at a time.
+// Compute units of a gfx950 part (MI350X / MI355X).  Sizes persistent grids and the
+// number of dgamma/dbeta partial rows; a device with fewer CUs runs the same grid with
+// fewer workgroups resident at a time (the cluster path then falls back, see api.cpp).
 constexpr int kGfx950Cus = 256;
 
 struct Plan {
   int path = NORM_PATH_GENERIC;
-  int lpr = 0, vpl = 0;       // ROWS mapping
+  int lpr = 0, vpl = 0;       // ROWS: lanes per row / vectors per lane.
+                              // CLUSTER: threads per member workgroup / vectors per lane.
   int block = 0;              // threads per workgroup of the main kernel
   int64_t groups = 0;         // ROWS: row groups
-  int grid = 0;               // ROWS: persistent grid; SPLIT/GENERIC bwd: rowdot grid
+  int grid = 0;               // ROWS / CLUSTER: main grid; SPLIT/GENERIC bwd: row-pass grid
   int64_t partial_rows = 0;   // P: rows of dgamma/dbeta partials (two-stage backward)
   int slices = 0;             // SPLIT/GENERIC bwd: column slices of the column pass
   int64_t rows_per_block = 0; // SPLIT/GENERIC bwd: rows per row block of the column pass
   int nvec = 0;               // N / elements per 16-byte vector (vector paths)
-  size_t ws_bytes = 0;
+  int cluster = 0;            // CLUSTER: workgroups per row
+  int nclusters = 0;          // CLUSTER: clusters
+  int slice_vecs = 0;         // CLUSTER: vectors per member slice
+  int rows_per_step = 0;      // CLUSTER: rows one reduction and one exchange serve
+  size_t ws_bytes = 0;        // bytes this plan uses
+  size_t ws_need = 0;         // bytes the call requires (covers the fallback plan too)
   size_t off_part_g = 0, off_part_b = 0, off_rowc = 0;  // byte offsets into the workspace
+  size_t off_xchg = 0, off_status = 0, xchg_bytes = 0;
 };
 
 // Returns NORM_OK or NORM_ERR_BAD_OPTION.  Shapes and dtype must already be valid.
 norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
                         bool aligned16, const norm_options_t* opt, Plan* out);
 
-// Workspace bytes a backward call needs with these options, for either pointer
-// alignment (the maximum over the aligned and the scalar plan).
-size_t workspace_bytes(int64_t M, int64_t N, bool layernorm, int dtype, const norm_options_t* opt);
+// The SPLIT (bwd) or GENERIC (fwd) plan a CLUSTER plan falls back to when the device
+// cannot hold the cooperative grid.
+norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
+                                 Plan* out);
+
+// Workspace bytes a call needs with these options, for either pointer alignment.
+size_t workspace_bytes(bool backward, int64_t M, int64_t N, bool layernorm, int dtype,
+                       const norm_options_t* opt);
 
 }  // namespace rownorm

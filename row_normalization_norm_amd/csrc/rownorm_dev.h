@@ -22,6 +22,7 @@ struct F32 {
   static constexpr int kBytes = 4;
   static constexpr int kPerVec = 4;  // elements per 16-byte vector
   __device__ static inline float get(const u32x4& v, int e) { return __uint_as_float(v[e]); }
+  __device__ static inline float get_fresh(const u32x4& v, int e) { return __uint_as_float(v[e]); }
   __device__ static inline float scalar(const void* p, int64_t i) {
     return static_cast<const float*>(p)[i];
   }
@@ -45,6 +46,19 @@ struct BF16 {
   __device__ static inline float get(const u32x4& v, int e) {
     const uint32_t w = v[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  // Same value as get(), through an opaque instruction: the compiler can neither merge
+  // it with an earlier unpack nor hoist it out of a loop, so only the packed words have
+  // to stay live in registers between two uses of a row.
+  __device__ static inline float get_fresh(const u32x4& v, int e) {
+    const uint32_t w = v[e >> 1];
+    uint32_t r;
+    if (e & 1) {
+      asm volatile("v_and_b32 %0, 0xffff0000, %1" : "=v"(r) : "v"(w));
+    } else {
+      asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(w));
+    }
+    return __uint_as_float(r);
   }
   __device__ static inline float scalar(const void* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
@@ -72,6 +86,14 @@ __device__ inline u32x4 ld16(const void* base, int64_t vec_index) {
 }
 __device__ inline void st16(void* base, int64_t vec_index, const u32x4& v) {
   static_cast<u32x4*>(base)[vec_index] = v;
+}
+// Streaming variants for data touched once (x, dy, y, dx): non-temporal hint, so the
+// stream does not evict gamma/beta and the partial rows from the caches.
+__device__ inline u32x4 ld16_stream(const void* base, int64_t vec_index) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + vec_index);
+}
+__device__ inline void st16_stream(void* base, int64_t vec_index, const u32x4& v) {
+  __builtin_nontemporal_store(v, static_cast<u32x4*>(base) + vec_index);
 }
 __device__ inline u32x4 zero16() {
   u32x4 z = {0u, 0u, 0u, 0u};

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 15, names
     lib = rn.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in rownorm.h but not exported"
@@ -41,17 +41,18 @@ def test_status_strings():
 
 
 def rms_fwd(**kw):
-    a = dict(x=A, gamma=A, y=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16, stream=None)
+    a = dict(x=A, gamma=A, y=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16, ws=None, ws_bytes=0)
     a.update(kw)
     return rn.lib().norm_rms_fwd(a["x"], a["gamma"], a["y"], a["rstd"], a["M"], a["N"], a["eps"],
-                                 a["dtype"], a["stream"])
+                                 a["dtype"], a["ws"], a["ws_bytes"], None)
 
 
 def ln_fwd(**kw):
-    a = dict(x=A, gamma=A, beta=A, y=A, mean=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16)
+    a = dict(x=A, gamma=A, beta=A, y=A, mean=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16, ws=None,
+             ws_bytes=0)
     a.update(kw)
     return rn.lib().norm_ln_fwd(a["x"], a["gamma"], a["beta"], a["y"], a["mean"], a["rstd"],
-                                a["M"], a["N"], a["eps"], a["dtype"], None)
+                                a["M"], a["N"], a["eps"], a["dtype"], a["ws"], a["ws_bytes"], None)
 
 
 def rms_bwd(**kw):
@@ -88,6 +89,10 @@ def ln_bwd(**kw):
     (rms_fwd, dict(dtype=F32, y=A + 2), rn.NORM_ERR_MISALIGNED),
     (ln_fwd, dict(beta=None), rn.NORM_ERR_NULL_PTR),
     (ln_fwd, dict(mean=A + 1), rn.NORM_ERR_MISALIGNED),
+    # rows long enough to be split over a cluster of workgroups need a forward workspace
+    (rms_fwd, dict(M=2048, N=131072), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(M=2048, N=131072, ws=A, ws_bytes=64), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
+    (ln_fwd, dict(M=2048, N=131072, ws=A + 8, ws_bytes=1 << 20), rn.NORM_ERR_MISALIGNED),
     (rms_bwd, dict(dy=None), rn.NORM_ERR_NULL_PTR),
     (rms_bwd, dict(rstd=None), rn.NORM_ERR_NULL_PTR),
     (rms_bwd, dict(dgamma=None), rn.NORM_ERR_NULL_PTR),
@@ -111,32 +116,41 @@ def test_bad_options_rejected():
            rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=48, vecs_per_lane=1),
            rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=8, vecs_per_lane=1),  # cannot cover N
            rn.Options(path=rn.NORM_PATH_SPLIT),  # forward has no SPLIT path
-           rn.Options(dgamma_mode=5)]
+           rn.Options(dgamma_mode=5),
+           rn.Options(cluster_size=64),  # above the largest cluster
+           rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=3)]  # not a power of two
     for o in bad:
-        st = lib.norm_rms_fwd_ex(A, A, A, A, 4, 4096, 1e-6, BF16, None, ctypes.byref(o))
+        st = lib.norm_rms_fwd_ex(A, A, A, A, 4, 4096, 1e-6, BF16, None, 0, None, ctypes.byref(o))
         assert st == rn.NORM_ERR_BAD_OPTION, (o.path, o.lanes_per_row, o.vecs_per_lane)
     # atomic dgamma is only offered on the ROWS path
     o = rn.Options(path=rn.NORM_PATH_SPLIT, dgamma_mode=rn.NORM_DGAMMA_ATOMIC_ROW)
     st = lib.norm_rms_bwd_ex(A, A, A, A, A, A, 4, 4096, BF16, A, 1 << 30, None, ctypes.byref(o))
     assert st == rn.NORM_ERR_BAD_OPTION
-    # a backward grid above the planner's partial-row count would overflow the workspace
-    o = rn.Options(grid=100000)
-    st = lib.norm_rms_bwd_ex(A, A, A, A, A, A, 1 << 20, 1024, BF16, A, 1 << 40, None,
+    # a larger backward grid means more partial rows: the default-sized workspace is then
+    # rejected instead of overflowed
+    o = rn.Options(grid=4096)
+    need_default = rn.norm_bwd_workspace_size(1 << 20, 1024, False, BF16)
+    need = rn.norm_bwd_workspace_size(1 << 20, 1024, False, BF16, o)
+    assert need > need_default
+    st = lib.norm_rms_bwd_ex(A, A, A, A, A, A, 1 << 20, 1024, BF16, A, need_default, None,
                              ctypes.byref(o))
-    assert st == rn.NORM_ERR_BAD_OPTION
+    assert st == rn.NORM_ERR_WORKSPACE_TOO_SMALL
 
 
 def test_plan_shape_classes():
     # non-power-of-2 N = 384 (bf16): 48 vectors = 16 lanes x 3, several rows per wavefront
     p = rn.norm_plan(False, False, 262144, 384, BF16)
     assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 16, 3)
+    # the backward (which also holds per-column partial sums) measured faster with 2 vectors
+    # per lane and 16 of 64 vector slots padded
     p = rn.norm_plan(True, False, 262144, 384, BF16)
-    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 16, 3)
-    # very long rows: forward keeps the row in one workgroup's registers ...
-    p = rn.norm_plan(False, False, 2048, 131072, BF16)
-    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 1024, 16)
-    # ... the backward switches to the column-sliced path
-    p = rn.norm_plan(True, False, 2048, 131072, BF16)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 32, 2)
+    # very long rows are split over a cluster of workgroups, forward and backward
+    for bwd in (False, True):
+        p = rn.norm_plan(bwd, False, 2048, 131072, BF16)
+        assert p.path == rn.NORM_PATH_CLUSTER and p.cluster_size >= 2 and p.cluster_rows >= 1
+    # the two-pass column-sliced backward remains available
+    p = rn.norm_plan(True, False, 2048, 131072, BF16, options=rn.Options(path=rn.NORM_PATH_SPLIT))
     assert p.path == rn.NORM_PATH_SPLIT and p.partial_rows >= 1
     # misaligned pointers or N not a multiple of the vector fall back to the scalar path
     assert rn.norm_plan(False, True, 100, 4096, BF16, aligned16=False).path == rn.NORM_PATH_GENERIC
@@ -178,3 +192,26 @@ def test_workspace_size():
     assert ws(4096, 1024, True, BF16, o) == 0
     # an invalid shape sizes to 0
     assert ws(-1, 1024, True, BF16) == 0
+
+
+def test_cluster_plans():
+    """Rows longer than one workgroup's registers are split over a cluster of workgroups,
+    each owning a column slice; forward and backward both, bf16 and fp32."""
+    cases = [(False, BF16, 131072), (False, F32, 65536), (True, BF16, 131072), (True, BF16, 65536),
+             (True, BF16, 32768), (True, F32, 65536), (True, F32, 32768), (True, F32, 16384)]
+    for bwd, dt, N in cases:
+            M = (1 << 27) // N
+            p = rn.norm_plan(bwd, True, M, N, dt)
+            assert p.path == rn.NORM_PATH_CLUSTER, (bwd, dt, N, p.path)
+            epv = 8 if dt == BF16 else 4
+            slice_vecs = N // epv // p.cluster_size
+            assert slice_vecs <= p.lanes_per_row * p.vecs_per_lane < slice_vecs + p.lanes_per_row
+            assert p.grid % p.cluster_size == 0
+            if bwd:
+                assert p.partial_rows == p.grid // p.cluster_size
+            ws = (rn.norm_bwd_workspace_size if bwd else rn.norm_fwd_workspace_size)(M, N, True, dt)
+            assert ws >= p.workspace_bytes > 0
+    # shorter rows stay in one workgroup's registers (no forward workspace)
+    assert rn.norm_plan(False, True, 2048, 65536, BF16).path == rn.NORM_PATH_ROWS
+    assert rn.norm_plan(True, True, 8192, 16384, BF16).path == rn.NORM_PATH_ROWS
+    assert rn.norm_fwd_workspace_size(65536, 4096, True, BF16) == 0

@@ -99,6 +99,44 @@ def test_forced_paths(device, kind, dtype, N, path):
                bwd_options=rn.Options(path=path))
 
 
+CLUSTER_CASES = [(N, C) for N in (2048, 8192, 65536) for C in (2, 4, 8, 16, 32)
+                 if (N // 8) % C == 0 and (N // 8) // C <= 4096]
+
+
+@pytest.mark.parametrize("R", [1, 2])
+@pytest.mark.parametrize("N,C", CLUSTER_CASES, ids=[f"N{n}-C{c}" for n, c in CLUSTER_CASES])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_cluster_path(device, kind, dtype, N, C, R):
+    """Rows split over C co-resident workgroups (cooperative launch), forward and backward,
+    with a row count that leaves the clusters unevenly loaded."""
+    epv = 8 if dtype == "bf16" else 4
+    if (N // epv) % C:
+        pytest.skip("row does not split evenly")
+    M = max(3, min(997, 2_000_000 // N))
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.3, x_std=1.2)
+    opt = rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=C, cluster_rows=R)
+    code = rn.NORM_DTYPE_BF16 if dtype == "bf16" else rn.NORM_DTYPE_F32
+    try:
+        rn.norm_plan(False, kind == "ln", M, N, code, options=opt)
+        rn.norm_plan(True, kind == "ln", M, N, code, options=opt)
+    except rn.NormError:
+        pytest.skip("no compiled cluster mapping covers this slice")
+    for bwd in (False, True):
+        assert rn.norm_cluster_resident(bwd, kind == "ln", M, N, code, opt) == 1, \
+            "the cooperative grid must fit (otherwise the call silently takes another path)"
+    full_check(w, device, rows=np.arange(M), fwd_options=opt, bwd_options=opt)
+
+
+@pytest.mark.parametrize("name", ["rms4"])
+def test_long_rows_run_on_cluster_path(device, name):
+    w = gen.WORKLOADS[name]
+    code = rn.NORM_DTYPE_BF16 if w.dtype == "bf16" else rn.NORM_DTYPE_F32
+    for bwd in (False, True):
+        assert rn.norm_plan(bwd, w.kind == "ln", w.M, w.N, code).path == rn.NORM_PATH_CLUSTER
+        assert rn.norm_cluster_resident(bwd, w.kind == "ln", w.M, w.N, code) == 1
+
+
 @pytest.mark.parametrize("grid", [1, 3, 64])
 @pytest.mark.parametrize("kind", ["rms", "ln"])
 def test_grid_override(device, kind, grid):
@@ -115,11 +153,12 @@ def test_atomic_dgamma_variants(device, kind, mode):
     full_check(w, device, rows=sample_rows(w.M), bwd_options=rn.Options(dgamma_mode=mode))
 
 
-@pytest.mark.parametrize("name", ["ln2", "rms3", "rms4"])
+@pytest.mark.parametrize("name", ["ln2", "rms3", "rms4", "sweep_ln_f32_65536"])
 def test_two_stage_is_deterministic(device, name):
     """Two-stage backward: bitwise identical dx, dgamma, dbeta across runs."""
     import torch
-    w = gen.WORKLOADS[name].scaled(min(gen.WORKLOADS[name].M, 4096))
+    base = gen.WORKLOADS[name] if name in gen.WORKLOADS else gen.sweep_workload("ln", "f32", 65536)
+    w = base.scaled(min(base.M, 4096))
     inputs = gen.make_inputs(w)
     run = GpuRun(w, inputs, device)
     run.forward()
