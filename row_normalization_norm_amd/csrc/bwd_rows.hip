@@ -62,6 +62,21 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
   __shared__ float red[WPR > 1 ? 2 * ROWS * WPR * 2 : 1];
   int parity = 0;
 
+  // The next row group's x and dy loads are issued before the current one is reduced,
+  // so HBM reads stay in flight through the reduction and the dx stores.
+  auto load = [&](int64_t grp, u32x4 (&xb)[VPL], u32x4 (&db)[VPL]) {
+    const int64_t row = grp * ROWS + slot;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      const bool ok = row < a.M && vi < nvec;
+      xb[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
+      db[v] = ok ? ld16_stream(a.dy, row * nvec + vi) : zero16();
+    }
+  };
+  u32x4 nx[VPL], nd[VPL];
+  if (blockIdx.x < a.groups) load(blockIdx.x, nx, nd);
+
   for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
     const int64_t row = grp * ROWS + slot;
     const bool row_ok = row < a.M;
@@ -71,11 +86,11 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
-      const bool ok = row_ok && vi < nvec;
-      xv[v] = ok ? ld16_stream(a.x, vbase + vi) : zero16();
-      dv[v] = ok ? ld16_stream(a.dy, vbase + vi) : zero16();
-      gv[v] = ok ? ld16(a.gamma, vi) : zero16();
+      xv[v] = nx[v];
+      dv[v] = nd[v];
+      gv[v] = (row_ok && vi < nvec) ? ld16(a.gamma, vi) : zero16();
     }
+    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd);
     const float r = row_ok ? a.rstd[row] : 0.0f;
     const float mu = (LN && row_ok) ? a.mean[row] : 0.0f;
 

@@ -80,6 +80,19 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
     return v;
   };
 
+  // The next row group's loads are issued before the current one is reduced, so HBM
+  // reads stay in flight through the reduction and the stores.
+  auto load = [&](int64_t grp, u32x4 (&buf)[VPL]) {
+    const int64_t row = grp * ROWS + slot;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      buf[v] = (row < a.M && vi < nvec) ? ld16_stream(a.x, row * nvec + vi) : zero16();
+    }
+  };
+  u32x4 nx[VPL];
+  if (blockIdx.x < a.groups) load(blockIdx.x, nx);
+
   for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
     const int64_t row = grp * ROWS + slot;
     const bool row_ok = row < a.M;
@@ -87,10 +100,8 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
 
     u32x4 xv[VPL];
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int vi = v * LPR + lane;
-      xv[v] = (row_ok && vi < nvec) ? ld16_stream(a.x, vbase + vi) : zero16();
-    }
+    for (int v = 0; v < VPL; ++v) xv[v] = nx[v];
+    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx);
 
     // RMSNorm: mean of squares.  LayerNorm: the mean, then the mean squared deviation
     // from it, both reduced from the registers (the row is read from memory once).

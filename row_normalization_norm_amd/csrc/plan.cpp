@@ -16,6 +16,7 @@
 #include "plan.h"
 
 #include "launch.h"
+#include "tuned.h"
 
 namespace rownorm {
 namespace {
@@ -260,6 +261,15 @@ void plan_generic_fwd(int64_t M, const norm_options_t& o, Plan& p) {
   if (o.grid) p.grid = o.grid;
 }
 
+const TunedPlan* find_tuned(bool backward, bool layernorm, int dtype, int64_t nvec) {
+  for (const TunedPlan& t : kTunedPlans) {
+    if (t.backward == int(backward) && t.layernorm == int(layernorm) &&
+        t.bf16 == int(dtype == NORM_DTYPE_BF16) && t.nvec == nvec)
+      return &t;
+  }
+  return nullptr;
+}
+
 }  // namespace
 
 norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
@@ -282,6 +292,26 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
   bool ok = true;
   switch (o.path) {
     case NORM_PATH_AUTO:
+      if (const TunedPlan* t = (vec_ok && !atomic && !o.lanes_per_row && !o.vecs_per_lane &&
+                                !o.cluster_size && !o.cluster_rows)
+                                   ? find_tuned(backward, layernorm, dtype, nvec)
+                                   : nullptr) {
+        norm_options_t ot = o;
+        ot.lanes_per_row = t->lanes;
+        ot.vecs_per_lane = t->vecs;
+        if (!ot.grid) ot.grid = t->grid;
+        if (t->path == NORM_PATH_CLUSTER) {
+          ot.cluster_size = t->cluster;
+          ot.cluster_rows = t->rows;
+          ok = plan_cluster(backward, layernorm, M, N, nvec, dtype, ot, p);
+        } else {
+          ok = plan_rows(backward, layernorm, M, N, nvec, ot, false, p);
+        }
+        if (ok) break;
+        ok = true;  // the entry does not fit this call: fall through to the rules
+        p = Plan();
+        p.nvec = int(nvec);
+      }
       if (!vec_ok) {
         if (backward) {
           plan_split(layernorm, M, N, nvec, false, o, p);
