@@ -197,15 +197,14 @@ def copy_probe(nbytes, steps, device):
 
 def cpu_baseline(w, target_s=12.0):
     """The oracle (as it stands) on the first rows of the same workload: forward (y, stats),
-    dx, and dgamma/dbeta over the sampled rows.  Reported in the metric's unit."""
+    dx, and dgamma/dbeta over the sampled rows.  Reported in the metric's unit.  The sample
+    grows until one pass takes about a quarter of target_s; when the whole workload is
+    faster than that, whole passes repeat until that much time has gone by."""
     import gen
     import oracle
     orc = oracle.get()
-    rows = 64
-    while True:
-        sub = w.scaled(rows)
-        inp = gen.make_inputs(sub)
-        t0 = time.perf_counter()
+
+    def one_pass(inp):
         if w.kind == "rms":
             orc.rms_fwd(inp["x"], inp["gamma"], w.eps)
             orc.rms_bwd_dx(inp["dy"], inp["x"], inp["gamma"], w.eps)
@@ -214,16 +213,174 @@ def cpu_baseline(w, target_s=12.0):
             orc.ln_fwd(inp["x"], inp["gamma"], inp["beta"], w.eps)
             orc.ln_bwd_dx(inp["dy"], inp["x"], inp["gamma"], w.eps)
             orc.ln_dgamma_dbeta(inp["dy"], inp["x"], w.eps)
+
+    rows = 64
+    while True:
+        inp = gen.make_inputs(w.scaled(rows))
+        t0 = time.perf_counter()
+        one_pass(inp)
         dt = time.perf_counter() - t0
         if dt >= target_s / 4 or rows >= w.M:
             break
         rows = min(w.M, int(rows * max(2.0, target_s / max(dt, 1e-3))))
+    passes = 1
+    while dt * passes < target_s / 4:
+        t0 = time.perf_counter()
+        one_pass(inp)
+        dt = (dt * passes + time.perf_counter() - t0) / (passes + 1)
+        passes += 1
     s = 2 if w.dtype == "bf16" else 4
     f, bwd = ideal_bytes(w.kind, rows, w.N, s)
     return {"value": round((f + bwd) / dt / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle",
             "sample": f"first {rows} of {w.M} rows of the same workload (fp64 C oracle, "
-                      f"forward + dx + dgamma/dbeta), {dt:.1f} s"}
+                      f"forward + dx + dgamma/dbeta), {passes} pass(es) of {dt:.2f} s"}
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name):
+    name = name.replace("rownorm::(anonymous namespace)::", "").replace("rownorm::", "")
+    return name[5:] if name.startswith("void ") else name
+
+
+def summarize(d, workload, warmup, steps, copy_bytes):
+    """Turn the rocprofv3 outputs of one profiling session into the text summaries kept
+    under profiles/ and the counter file the benchmark reads.  Layout of d (each a
+    rocprofv3 -d directory): trace/<w>_kernel_trace.csv (--kernel-trace),
+    FETCH_SIZE/<w>_counter_collection.csv and WRITE_SIZE/... (--pmc on this benchmark),
+    FETCH_SIZE_copy/copy_counter_collection.csv and WRITE_SIZE_copy/... (--pmc on
+    --copy-probe copy_bytes), LDS/<w>_counter_collection.csv (LDS counters), and the
+    benchmark's own stdout for the FETCH_SIZE run in FETCH_SIZE.log (source hash)."""
+    import statistics
+    w = workload
+    out_dir = os.path.join(ROOT, "profiles")
+    lines = []
+    # kernel trace
+    tr = _read_csv(os.path.join(d, "trace", f"{w}_kernel_trace.csv"))
+    per = {}
+    for r in sorted(tr, key=lambda r: int(r["Start_Timestamp"])):
+        per.setdefault(_short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines.append("| kernel | calls | avg us (all) | warm-up avg | pass A avg (back to back) | "
+                 "pass B avg (per-launch events) | min us | max us |")
+    lines.append("|---|---|---|---|---|---|---|---|")
+    trace_avg = {}
+    for k, v in per.items():
+        if len(v) == warmup + 2 * steps:
+            ph = [v[:warmup], v[warmup:warmup + steps], v[warmup + steps:]]
+            phs = " | ".join(f"{statistics.fmean(p):.1f}" for p in ph)
+            trace_avg[k] = statistics.fmean(ph[2])
+        else:
+            phs = "- | - | -"
+        lines.append(f"| `{k}` | {len(v)} | {statistics.fmean(v):.1f} | {phs} | "
+                     f"{min(v):.1f} | {max(v):.1f} |")
+    trace_table = "\n".join(lines)
+
+    def counter(sub, fname, name):
+        vals = {}
+        for r in _read_csv(os.path.join(d, sub, fname)):
+            if r["Counter_Name"] == name:
+                vals.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    fetch = counter("FETCH_SIZE", f"{w}_counter_collection.csv", "FETCH_SIZE")
+    write = counter("WRITE_SIZE", f"{w}_counter_collection.csv", "WRITE_SIZE")
+    cf = max(counter("FETCH_SIZE_copy", "copy_counter_collection.csv", "FETCH_SIZE").values())
+    cw = max(counter("WRITE_SIZE_copy", "copy_counter_collection.csv", "WRITE_SIZE").values())
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    lds = {}
+    lds_path = os.path.join(d, "LDS", f"{w}_counter_collection.csv")
+    if os.path.exists(lds_path):
+        for name in ("SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT"):
+            for k, v in counter("LDS", f"{w}_counter_collection.csv", name).items():
+                lds.setdefault(k, {})[name] = v
+    import gen
+    wl = gen.WORKLOADS[w]
+    s = 2 if wl.dtype == "bf16" else 4
+    fwd_b, bwd_b = ideal_bytes(wl.kind, wl.M, wl.N, s)
+    main_b = main_bwd_kernel_bytes(wl.kind, wl.M, wl.N, s)
+    algo = {"fwd_rows_kernel": fwd_b, "bwd_rows_kernel": main_b,
+            "colreduce_kernel": bwd_b - main_b}
+    clines = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes read | bytes written | "
+              "traffic | algorithmic | traffic / algorithmic | LDS instr | LDS bank conflicts |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    bwd_traffic = None
+    for k in fetch:
+        if "rocclr" in k or k not in write:
+            continue
+        rb, wb = fetch[k] * 1024 * f_scale, write[k] * 1024 * w_scale
+        a = next((v for n, v in algo.items() if k.startswith(n)), None)
+        if k.startswith("bwd_rows_kernel"):
+            bwd_traffic = rb + wb
+        li = lds.get(k, {})
+        clines.append(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {rb:.4g} | {wb:.4g} | "
+                      f"{rb + wb:.4g} | {a if a else '-'} | "
+                      f"{(rb + wb) / a if a else float('nan'):.4f} | "
+                      f"{li.get('SQ_INSTS_LDS', float('nan')):.0f} | "
+                      f"{li.get('SQ_LDS_BANK_CONFLICT', float('nan')):.0f} |")
+    src_hash = None
+    log = os.path.join(d, "FETCH_SIZE.log")
+    if os.path.exists(log):
+        for line in open(log):
+            if line.startswith("{"):
+                src_hash = json.loads(line).get("kernel_source_hash")
+    return trace_table, trace_avg, "\n".join(clines), f_scale, w_scale, bwd_traffic, src_hash
+
+
+PROFILE_STEPS = (
+    "cd /tmp && export TMPDIR=/tmp; R=/root/repo; D=$R/gpurun_out/prof",
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $D/trace -o {w} -- "
+    "python3 $R/bench.py --workload {w} --steps 10 --warmup 3 --no-cpu",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE -o {w} -- "
+    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu > $D/FETCH_SIZE.log",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $D/WRITE_SIZE -o {w} -- "
+    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE_copy -o copy -- "
+    "python3 $R/bench.py --copy-probe {c} --steps 3",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $D/WRITE_SIZE_copy -o copy -- "
+    "python3 $R/bench.py --copy-probe {c} --steps 3",
+    "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS --output-format csv -d $D/LDS -o {w} -- "
+    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu",
+    "python3 $R/bench.py --summarize $D --workload {w}",
+)
+
+
+def write_summaries(d, w, warmup=3, steps=10, copy_bytes=1 << 30):
+    """--summarize: write profiles/<w>_kernel_trace.md, profiles/<w>_hbm_counters.md and
+    (for the benchmark's own workload) the counter file bench.py reports traffic from."""
+    tt, tavg, ct, fs, ws_, bwd_traffic, src_hash = summarize(d, w, warmup, steps, copy_bytes)
+    cmds = "\n".join(c.format(w=w, c=copy_bytes) for c in PROFILE_STEPS)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{w}_kernel_trace.md"), "w") as f:
+        f.write(f"# Kernel durations, workload {w} (rocprofv3 --kernel-trace --stats)\n\n"
+                f"Commands (the whole profiling session; this file comes from the first):\n\n"
+                f"```\n{cmds}\n```\n\n{tt}\n\n"
+                f"Kernel source hash: `{src_hash}`. The profiled run makes {warmup} warm-up "
+                f"steps, then pass A ({steps} steps launched back to back: the step time) "
+                f"and pass B ({steps} steps with HIP events recorded around each launch: "
+                f"the per-kernel time bench.py reports as avg_launch_ms).\n")
+    with open(os.path.join(ROOT, "profiles", f"{w}_hbm_counters.md"), "w") as f:
+        f.write(f"# HBM traffic and LDS counters, workload {w} (rocprofv3 --pmc)\n\n"
+                f"Commands:\n\n```\n{cmds}\n```\n\n"
+                f"Counter scale from a {copy_bytes} B device copy: FETCH_SIZE x{fs:.4f}, "
+                f"WRITE_SIZE x{ws_:.4f} (bytes = KiB x 1024 x scale). Values are the median "
+                f"over the run's dispatches of each kernel.\n\n{ct}\n\n"
+                f"Kernel source hash: `{src_hash}`.\n")
+    if w == DEFAULT_WORKLOAD and bwd_traffic:
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump({"workload": w, "kernel": "bwd_rows_kernel",
+                       "kernel_source_hash": src_hash,
+                       "traffic_bytes_per_launch": round(bwd_traffic),
+                       "fetch_scale": round(fs, 4), "write_scale": round(ws_, 4),
+                       "trace_avg_us_pass_b": {k: round(v, 2) for k, v in tavg.items()}},
+                      f, indent=1)
+            f.write("\n")
 
 
 def load_counters(w):
@@ -248,7 +405,12 @@ def main():
     ap.add_argument("--all", metavar="JSON", help="also time every workload, write a table")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only time a plain device copy of BYTES and print it")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="only write the profiles/ summaries from a profiling session in DIR")
     args = ap.parse_args()
+    if args.summarize:
+        write_summaries(args.summarize, args.workload)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -311,6 +473,7 @@ def main():
                       "pass of the same steps",
         },
         "rotating_buffer_sets": r["sets"],
+        "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w)
