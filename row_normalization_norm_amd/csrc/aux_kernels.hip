@@ -193,21 +193,25 @@ __global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) 
 
 // -------------------------------------------------------------------- colreduce
 template <bool VEC4>
-__global__ __launch_bounds__(kColRedLanes * kColRedSplits) void colreduce_kernel(
+__global__ __launch_bounds__(kColRedThreads) void colreduce_kernel(
     const float* __restrict__ part_g, const float* __restrict__ part_b, int64_t P, int32_t N,
     float* __restrict__ dgamma, float* __restrict__ dbeta) {
+  constexpr int L = colred_lanes(VEC4);
+  constexpr int S = kColRedThreads / L;
+  constexpr int W = VEC4 ? 4 : 1;
   const float* src = blockIdx.y ? part_b : part_g;
   float* dst = blockIdx.y ? dbeta : dgamma;
-  const int tx = threadIdx.x % kColRedLanes;
-  const int ty = threadIdx.x / kColRedLanes;
-  constexpr int W = VEC4 ? 4 : 1;
-  const int64_t col = ((int64_t)blockIdx.x * kColRedLanes + tx) * W;
+  const int tx = threadIdx.x % L;
+  const int ty = threadIdx.x / L;
+  const int64_t col = ((int64_t)blockIdx.x * L + tx) * W;
+  // Split ty adds rows ty, ty + S, ty + 2S, ... in order; the S split sums are then added
+  // in split order: a fixed order for a given P, so the result is reproducible bit for bit.
   float s[W];
 #pragma unroll
   for (int k = 0; k < W; ++k) s[k] = 0.0f;
   if (col < N) {
 #pragma unroll 4
-    for (int64_t p = ty; p < P; p += kColRedSplits) {
+    for (int64_t p = ty; p < P; p += S) {
       if constexpr (VEC4) {
         const float4 v = *reinterpret_cast<const float4*>(src + p * N + col);
         s[0] += v.x;
@@ -219,18 +223,17 @@ __global__ __launch_bounds__(kColRedLanes * kColRedSplits) void colreduce_kernel
       }
     }
   }
-  __shared__ float buf[kColRedSplits][kColRedLanes * W];
+  __shared__ float buf[S][L * W];
 #pragma unroll
   for (int k = 0; k < W; ++k) buf[ty][tx * W + k] = s[k];
   __syncthreads();
-  if (ty == 0 && col < N) {
+  if (threadIdx.x < L * W) {
+    const int c = threadIdx.x;
+    const int64_t out = (int64_t)blockIdx.x * L * W + c;
+    float t = 0.0f;
 #pragma unroll
-    for (int k = 0; k < W; ++k) {
-      float t = 0.0f;
-#pragma unroll
-      for (int q = 0; q < kColRedSplits; ++q) t += buf[q][tx * W + k];
-      dst[col + k] = t;
-    }
+    for (int q = 0; q < S; ++q) t += buf[q][c];
+    if (out < N) dst[out] = t;
   }
 }
 
@@ -359,14 +362,14 @@ hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P,
                     (part_b == nullptr || (reinterpret_cast<uintptr_t>(part_b) & 15) == 0) &&
                     ((reinterpret_cast<uintptr_t>(dgamma) & 15) == 0) &&
                     (dbeta == nullptr || (reinterpret_cast<uintptr_t>(dbeta) & 15) == 0);
-  const int per_block = kColRedLanes * (vec4 ? 4 : 1);
+  const int per_block = colred_lanes(vec4) * (vec4 ? 4 : 1);
   const dim3 grid((N + per_block - 1) / per_block, part_b ? 2 : 1);
   if (vec4) {
-    hipLaunchKernelGGL((colreduce_kernel<true>), grid, dim3(kColRedLanes * kColRedSplits), 0, s,
-                       part_g, part_b, P, N, dgamma, dbeta);
+    hipLaunchKernelGGL((colreduce_kernel<true>), grid, dim3(kColRedThreads), 0, s, part_g, part_b,
+                       P, N, dgamma, dbeta);
   } else {
-    hipLaunchKernelGGL((colreduce_kernel<false>), grid, dim3(kColRedLanes * kColRedSplits), 0, s,
-                       part_g, part_b, P, N, dgamma, dbeta);
+    hipLaunchKernelGGL((colreduce_kernel<false>), grid, dim3(kColRedThreads), 0, s, part_g, part_b,
+                       P, N, dgamma, dbeta);
   }
   return hipGetLastError();
 }

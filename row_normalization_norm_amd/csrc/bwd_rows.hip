@@ -62,20 +62,43 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
   __shared__ float red[WPR > 1 ? 2 * ROWS * WPR * 2 : 1];
   int parity = 0;
 
-  // The next row group's x and dy loads are issued before the current one is reduced,
-  // so HBM reads stay in flight through the reduction and the dx stores.
-  auto load = [&](int64_t grp, u32x4 (&xb)[VPL], u32x4 (&db)[VPL]) {
-    const int64_t row = grp * ROWS + slot;
+  // gamma stays in registers across the workgroup's rows when the row is short enough,
+  // for the shortest rows also unpacked to fp32.
+  constexpr bool GREG = VPL <= 2;
+  constexpr bool GUNP = GREG && VPL * EPV <= 16;
+  constexpr bool kBf16 = std::is_same<D, BF16>::value;
+  u32x4 greg[GREG ? VPL : 1];
+  float gunp[GUNP ? VPL : 1][EPV];
+  if constexpr (GREG) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
-      const bool ok = row < a.M && vi < nvec;
+      greg[v] = vi < nvec ? ld16(a.gamma, vi) : zero16();
+      if constexpr (GUNP) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) gunp[v][e] = D::get(greg[v], e);
+      }
+    }
+  }
+
+  // The next row group's x, dy and saved statistics are loaded before the current one is
+  // reduced, so HBM reads stay in flight through the reduction and the dx stores.
+  auto load = [&](int64_t grp, u32x4 (&xb)[VPL], u32x4 (&db)[VPL], float& rb, float& mb) {
+    const int64_t row = grp * ROWS + slot;
+    const bool rok = row < a.M;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      const bool ok = rok && vi < nvec;
       xb[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
       db[v] = ok ? ld16_stream(a.dy, row * nvec + vi) : zero16();
     }
+    rb = rok ? a.rstd[row] : 0.0f;
+    mb = (LN && rok) ? a.mean[row] : 0.0f;
   };
   u32x4 nx[VPL], nd[VPL];
-  if (blockIdx.x < a.groups) load(blockIdx.x, nx, nd);
+  float nr = 0.0f, nmu = 0.0f;
+  if (blockIdx.x < a.groups) load(blockIdx.x, nx, nd, nr, nmu);
 
   for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
     const int64_t row = grp * ROWS + slot;
@@ -88,25 +111,39 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
       const int vi = v * LPR + lane;
       xv[v] = nx[v];
       dv[v] = nd[v];
-      gv[v] = (row_ok && vi < nvec) ? ld16(a.gamma, vi) : zero16();
+      if constexpr (GREG) {
+        gv[v] = greg[v];
+      } else {
+        gv[v] = (row_ok && vi < nvec) ? ld16(a.gamma, vi) : zero16();
+      }
     }
-    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd);
-    const float r = row_ok ? a.rstd[row] : 0.0f;
-    const float mu = (LN && row_ok) ? a.mean[row] : 0.0f;
+    const float r = nr;
+    const float mu = nmu;
+    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd, nr, nmu);
 
     // Row sums, and the per-column contributions (which do not need the row sums).
+    // Short rows keep xhat and g in registers for the dx pass; longer ones unpack the
+    // packed words again there, so that only those stay live across the reduction.
+    constexpr bool KEEP = VPL * EPV <= 16;
+    float kxh[KEEP ? VPL : 1][EPV], kg[KEEP ? VPL : 1][EPV];
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
+      // LayerNorm's sum of g = dy * gamma: for bf16 straight from the packed words.
+      if constexpr (LN && kBf16) s2 = D::dot(dv[v], gv[v], s2);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
         const float xh = (D::get(xv[v], e) - mu) * r;
         const float d = D::get(dv[v], e);
-        const float g = d * D::get(gv[v], e);
+        const float g = d * (GUNP ? gunp[GUNP ? v : 0][e] : D::get(gv[v], e));
         s1 = fmaf(g, xh, s1);
-        if constexpr (LN) s2 += g;
+        if constexpr (LN && !kBf16) s2 += g;
         accg[v][e] = fmaf(d, xh, accg[v][e]);
         if constexpr (LN) accb[v][e] += d;
+        if constexpr (KEEP) {
+          kxh[v][e] = xh;
+          kg[v][e] = g;
+        }
       }
     }
 
@@ -130,8 +167,9 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
       }
       parity ^= 1;
     }
-    const float c1 = s1 * a.inv_n;
-    const float c2 = LN ? s2 * a.inv_n : 0.0f;
+    // dx = r * (g - c2 - xhat * c1) = g * r + (xhat * (-r * c1) + (-r * c2)).
+    const float nrc1 = -r * (s1 * a.inv_n);
+    const float nrc2 = LN ? -r * (s2 * a.inv_n) : 0.0f;
 
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
@@ -140,9 +178,15 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float xh = (D::get_fresh(xv[v], e) - mu) * r;
-          const float g = D::get_fresh(dv[v], e) * D::get_fresh(gv[v], e);
-          o[e] = r * fmaf(-xh, c1, g - c2);
+          float xh, g;
+          if constexpr (KEEP) {
+            xh = kxh[v][e];
+            g = kg[v][e];
+          } else {
+            xh = (D::get_fresh(xv[v], e) - mu) * r;
+            g = D::get_fresh(dv[v], e) * D::get_fresh(gv[v], e);
+          }
+          o[e] = fmaf(g, r, fmaf(xh, nrc1, nrc2));
         }
         st16_stream(a.dx, vbase + vi, D::pack(o));
         if (mode == kAtomicRow) {

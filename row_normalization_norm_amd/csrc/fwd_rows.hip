@@ -107,14 +107,14 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
     // from it, both reduced from the registers (the row is read from memory once).
     // Deviations about the mean keep the variance exact for constant rows and free of
     // the cancellation of mean(x^2) - mean^2 when |mean| >> deviation.
+    // Short rows keep the deviations from the mean for the output pass.
+    constexpr bool KEEP = LN && VPL * EPV <= 32;
+    float dev[KEEP ? VPL : 1][EPV];
     float mu = 0.0f, var;
     if constexpr (LN) {
       float s = 0.0f;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) s += D::get(xv[v], e);
-      }
+      for (int v = 0; v < VPL; ++v) s = D::sum(xv[v], s);
       mu = row_sum(s, 0) * a.inv_n;
       float ss = 0.0f;
 #pragma unroll
@@ -122,21 +122,16 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
         const bool in_row = v * LPR + lane < nvec;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float d = in_row ? D::get_fresh(xv[v], e) - mu : 0.0f;
+          const float d = in_row ? D::get(xv[v], e) - mu : 0.0f;
           ss = fmaf(d, d, ss);
+          if constexpr (KEEP) dev[v][e] = d;
         }
       }
       var = row_sum(ss, 1) * a.inv_n;
     } else {
       float ss = 0.0f;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float f = D::get(xv[v], e);
-          ss = fmaf(f, f, ss);
-        }
-      }
+      for (int v = 0; v < VPL; ++v) ss = D::sumsq(xv[v], ss);
       var = row_sum(ss, 0) * a.inv_n;
     }
     if constexpr (WPR > 1) parity ^= 1;
@@ -164,13 +159,13 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          // Second use of the packed row: unpack afresh so that only the packed words
-          // stay live across the reductions.
-          const float f = D::get_fresh(xv[v], e);
+          // Unpack the packed row afresh (or reuse the kept deviations), so that only
+          // the packed words stay live across the reductions.
           if constexpr (LN) {
-            o[e] = fmaf((f - mu) * r, D::get_fresh(gv, e), D::get_fresh(bv, e));
+            const float d = KEEP ? dev[KEEP ? v : 0][e] : D::get_fresh(xv[v], e) - mu;
+            o[e] = fmaf(d * r, D::get_fresh(gv, e), D::get_fresh(bv, e));
           } else {
-            o[e] = f * r * D::get_fresh(gv, e);
+            o[e] = D::get_fresh(xv[v], e) * r * D::get_fresh(gv, e);
           }
         }
         st16_stream(a.y, vbase + vi, D::pack(o));

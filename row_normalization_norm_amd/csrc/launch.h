@@ -55,9 +55,11 @@ constexpr int kSliceBlock = 256;
 constexpr int kSliceVecs = 2;
 // Row-reduction pass (SPLIT and GENERIC backward) and the scalar forward.
 constexpr int kRowBlock = 256;
-// Column reduce of the partial rows.
-constexpr int kColRedLanes = 64;
-constexpr int kColRedSplits = 16;
+// Column reduce of the partial rows: 256 threads = lanes along N x splits of the P rows.
+// The 16-byte path gives each workgroup 8 lanes x 4 columns (128-byte row segments), so
+// a 4096-column LayerNorm spreads over 256 workgroups; the scalar path 32 lanes x 1.
+constexpr int kColRedThreads = 256;
+constexpr int colred_lanes(bool vec4) { return vec4 ? 8 : 32; }
 
 enum DgammaMode { kTwoStage = 0, kAtomicRow = 1, kAtomicWg = 2 };
 

@@ -29,6 +29,15 @@ struct F32 {
   __device__ static inline void put_scalar(void* p, int64_t i, float f) {
     static_cast<float*>(p)[i] = f;
   }
+  // Sum and sum of squares of the vector's elements added to acc.
+  __device__ static inline float sum(const u32x4& v, float acc) {
+    return acc + ((get(v, 0) + get(v, 1)) + (get(v, 2) + get(v, 3)));
+  }
+  __device__ static inline float sumsq(const u32x4& v, float acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(get(v, e), get(v, e), acc);
+    return acc;
+  }
   __device__ static inline u32x4 pack(const float (&f)[4]) {
     u32x4 r;
     r[0] = __float_as_uint(f[0]);
@@ -62,6 +71,37 @@ struct BF16 {
   }
   __device__ static inline float scalar(const void* p, int64_t i) {
     return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+  // Sum and sum of squares straight from the packed words with the bf16 dot product
+  // (v_dot2_f32_bf16: two exact bf16 products added to an fp32 accumulator), so the
+  // reductions need no unpacking.  The word goes through a local copy: a direct bit
+  // cast of the extracted vector element to bf16x2 has been seen to make hipcc read
+  // the same word four times.
+  __device__ static inline bf16x2 word(const u32x4& v, int w) {
+    const uint32_t u = v[w];
+    bf16x2 h;
+    __builtin_memcpy(&h, &u, sizeof(h));
+    return h;
+  }
+  __device__ static inline float sum(const u32x4& v, float acc) {
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = __builtin_amdgcn_fdot2_f32_bf16(word(v, w), one, acc, false);
+    return acc;
+  }
+  __device__ static inline float sumsq(const u32x4& v, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const bf16x2 h = word(v, w);
+      acc = __builtin_amdgcn_fdot2_f32_bf16(h, h, acc, false);
+    }
+    return acc;
+  }
+  // acc + sum_e a_e * b_e.
+  __device__ static inline float dot(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = __builtin_amdgcn_fdot2_f32_bf16(word(a, w), word(b, w), acc, false);
+    return acc;
   }
   __device__ static inline uint32_t pack2(float lo, float hi) {
     f32x2 f = {lo, hi};
