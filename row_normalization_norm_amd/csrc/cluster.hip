@@ -105,24 +105,44 @@ __device__ inline void publish_step(const ClusterArgs& c, int member, int64_t st
   }
 }
 
-// Gather every member's K partials of `step` into xin[member * K + j]; visible to the whole
-// workgroup after the barrier.  The caller alternates between two xin buffers, so values
-// are never overwritten before every thread has read them.
+// Thread m < C reads member m's K words of `step` ahead of the gather, so the round trip
+// of the first poll overlaps other work instead of stalling the whole workgroup.
 template <int K>
-__device__ inline void gather_step(const ClusterArgs& c, int64_t step, float* xin) {
+__device__ inline void prefetch_step(const ClusterArgs& c, int64_t step,
+                                     unsigned long long (&pre)[K]) {
   if (threadIdx.x < c.C) {
     unsigned long long* base = c.xchg + step * c.C * K;
 #pragma unroll
     for (int j = 0; j < K; ++j)
+      pre[j] = __hip_atomic_load(base + threadIdx.x * K + j, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Gather every member's K partials of `step` into xin[member * K + j]; visible to the whole
+// workgroup after the barrier.  A prefetched word that already carries the step's tag is
+// used as is; otherwise the thread polls.  The caller alternates between two xin buffers,
+// so values are never overwritten before every thread has read them.
+template <int K>
+__device__ inline void gather_step(const ClusterArgs& c, int64_t step,
+                                   const unsigned long long (&pre)[K], float* xin) {
+  if (threadIdx.x < c.C) {
+    unsigned long long* base = c.xchg + step * c.C * K;
+    const uint32_t tag = row_tag(step);
+#pragma unroll
+    for (int j = 0; j < K; ++j)
       xin[threadIdx.x * K + j] =
-          wait_for(base + threadIdx.x * K + j, row_tag(step), c.spin_limit, c.status);
+          static_cast<uint32_t>(pre[j] >> 32) == tag
+              ? __uint_as_float(static_cast<uint32_t>(pre[j]))
+              : wait_for(base + threadIdx.x * K + j, tag, c.spin_limit, c.status);
   }
   __syncthreads();
 }
 
-// Each workgroup keeps three steps in registers: it publishes step t+1's partial sums and
-// issues step t+2's loads before it waits for the other members' partials of step t, so
-// the exchange round trip overlaps a step of work instead of stalling every step.
+// Each workgroup keeps several steps in registers: the forward publishes step t+1's partial
+// sums and issues step t+2's loads before it waits for the other members' partials of step
+// t, so the exchange round trip overlaps a step of work instead of stalling every step; the
+// backward runs up to two steps ahead when its registers allow.
 
 // --------------------------------------------------------------------------- forward
 template <bool LN, typename D, int T, int VPL, int R>
@@ -169,9 +189,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
       for (int i = 0; i < R; ++i) {
         s[i] = 0.0f;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) s[i] += D::get_fresh(buf[i][v], e);
+        for (int v = 0; v < VPL; ++v) s[i] = D::sum(buf[i][v], s[i]);
       }
       block_sum_n<NW, R>(s, red, parity);
       float m2[R];
@@ -198,12 +216,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
       for (int i = 0; i < R; ++i) {
         out[i] = 0.0f;
 #pragma unroll
-        for (int v = 0; v < VPL; ++v)
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            const float f = D::get_fresh(buf[i][v], e);
-            out[i] = fmaf(f, f, out[i]);
-          }
+        for (int v = 0; v < VPL; ++v) out[i] = D::sumsq(buf[i][v], out[i]);
       }
       block_sum_n<NW, K>(out, red, parity);
     }
@@ -221,6 +234,8 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
   }
   for (; st < nsteps; st += c.nclusters) {
     const int64_t s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
+    unsigned long long pre[K];
+    prefetch_step<K>(c, st, pre);
     if (s1 < nsteps) {
       float mine[K];
       partial(b1, mine);
@@ -230,7 +245,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
 
     float* xs = xin[xp];
     xp ^= 1;
-    gather_step<K>(c, st, xs);
+    gather_step<K>(c, st, pre, xs);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = st * R + i;
@@ -290,6 +305,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   constexpr int EPV = D::kPerVec;
   constexpr int NW = T / 64;
   constexpr int K = 2 * R;  // exchanged values per member and step: (sum g*xhat, sum g) x R
+  constexpr bool kBf16 = std::is_same<D, BF16>::value;
   const int tid = threadIdx.x;
   const int cl = blockIdx.x % c.nclusters;
   const int member = blockIdx.x / c.nclusters;
@@ -298,6 +314,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
 
   bool own[VPL];
   u32x4 g[VPL];
+  float gf[VPL][EPV];  // gamma unpacked once: the slice is the same for every row
   float accg[VPL][EPV], accb[LN ? VPL : 1][EPV];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
@@ -305,6 +322,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     g[v] = own[v] ? ld16(a.gamma, vofs + v * T + tid) : zero16();
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
+      gf[v][e] = D::get(g[v], e);
       accg[v][e] = 0.0f;
       if constexpr (LN) accb[v][e] = 0.0f;
     }
@@ -314,7 +332,12 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   __shared__ float xin[2][kMaxCluster * K];
   int parity = 0, xp = 0;
 
-  auto load = [&](int64_t st, u32x4 (&xb)[R][VPL], u32x4 (&db)[R][VPL]) {
+  // A step's x and dy slices and its rows' saved statistics, loaded together.
+  struct Stage {
+    u32x4 x[R][VPL], d[R][VPL];
+    float r[R], mu[R];
+  };
+  auto load = [&](int64_t st, Stage& sb) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = st * R + i;
@@ -322,31 +345,32 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
       for (int v = 0; v < VPL; ++v) {
         const bool ok = own[v] && row < a.M;
         const int64_t idx = row * a.nvec + vofs + v * T + tid;
-        xb[i][v] = ok ? ld16_stream(a.x, idx) : zero16();
-        db[i][v] = ok ? ld16_stream(a.dy, idx) : zero16();
+        sb.x[i][v] = ok ? ld16_stream(a.x, idx) : zero16();
+        sb.d[i][v] = ok ? ld16_stream(a.dy, idx) : zero16();
       }
+      sb.r[i] = row < a.M ? a.rstd[row] : 0.0f;
+      sb.mu[i] = (LN && row < a.M) ? a.mean[row] : 0.0f;
     }
   };
   // Partial row sums of g*xhat and g over this member's slice, for each row of the step,
   // and the slice's column contributions to dgamma/dbeta (which need no row sums).
   // Rows past M have zero x and dy, so they add nothing.
-  auto partial = [&](int64_t st, const u32x4 (&xb)[R][VPL], const u32x4 (&db)[R][VPL],
-                     float (&out)[K]) {
+  auto partial = [&](const Stage& sb, float (&out)[K]) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int64_t row = st * R + i;
-      const float r = row < a.M ? a.rstd[row] : 0.0f;
-      const float mu = (LN && row < a.M) ? a.mean[row] : 0.0f;
+      const float r = sb.r[i];
+      const float mu = sb.mu[i];
       float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
+        if constexpr (LN && kBf16) s2 = D::dot(sb.d[i][v], g[v], s2);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float xh = (D::get_fresh(xb[i][v], e) - mu) * r;
-          const float d = D::get_fresh(db[i][v], e);
-          const float gg = d * D::get_fresh(g[v], e);
+          const float xh = (D::get_fresh(sb.x[i][v], e) - mu) * r;
+          const float d = D::get_fresh(sb.d[i][v], e);
+          const float gg = d * gf[v][e];
           s1 = fmaf(gg, xh, s1);
-          if constexpr (LN) s2 += gg;
+          if constexpr (LN && !kBf16) s2 += gg;
           accg[v][e] = fmaf(d, xh, accg[v][e]);
           if constexpr (LN) accb[v][e] += d;
         }
@@ -357,27 +381,42 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     block_sum_n<NW, K>(out, red, parity);
   };
 
-  u32x4 x0[R][VPL], d0[R][VPL], x1[R][VPL], d1[R][VPL], x2[R][VPL], d2[R][VPL];
+  // S steps live in registers: b[0] waits for the exchange, b[1 .. S-3] are published,
+  // b[S-2] is reduced and published this iteration and b[S-1] is being loaded, so the
+  // exchange round trip of a step overlaps S-2 steps of work.
+  constexpr int S = (T <= 512 && VPL * R <= 2) ? 4 : 3;
+  Stage b[S];
   int64_t st = cl;
   if (st < nsteps) {
-    load(st, x0, d0);
-    if (st + c.nclusters < nsteps) load(st + c.nclusters, x1, d1);
-    float mine[K];
-    partial(st, x0, d0, mine);
-    publish_step<K>(c, member, st, mine);
+#pragma unroll
+    for (int k = 0; k < S - 1; ++k) {
+      const int64_t sk = st + k * c.nclusters;
+      if (sk < nsteps) load(sk, b[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < S - 2; ++k) {
+      const int64_t sk = st + k * c.nclusters;
+      if (sk < nsteps) {
+        float mine[K];
+        partial(b[k], mine);
+        publish_step<K>(c, member, sk, mine);
+      }
+    }
   }
   for (; st < nsteps; st += c.nclusters) {
-    const int64_t s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
-    if (s1 < nsteps) {
+    const int64_t sp = st + (S - 2) * c.nclusters, sl = st + (S - 1) * c.nclusters;
+    unsigned long long pre[K];
+    prefetch_step<K>(c, st, pre);
+    if (sp < nsteps) {
       float mine[K];
-      partial(s1, x1, d1, mine);
-      publish_step<K>(c, member, s1, mine);
+      partial(b[S - 2], mine);
+      publish_step<K>(c, member, sp, mine);
     }
-    if (s2 < nsteps) load(s2, x2, d2);
+    if (sl < nsteps) load(sl, b[S - 1]);
 
     float* xs = xin[xp];
     xp ^= 1;
-    gather_step<K>(c, st, xs);
+    gather_step<K>(c, st, pre, xs);
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = st * R + i;
@@ -387,32 +426,26 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
         t1 += xs[j * K + 2 * i];
         t2 += xs[j * K + 2 * i + 1];
       }
-      const float c1 = t1 * a.inv_n;
-      const float c2 = LN ? t2 * a.inv_n : 0.0f;
-      const float r = a.rstd[row];
-      const float mu = LN ? a.mean[row] : 0.0f;
+      const float r = b[0].r[i];
+      const float mu = b[0].mu[i];
+      // dx = r * (g - c2 - xhat * c1) = g * r + (xhat * (-r * c1) + (-r * c2)).
+      const float nrc1 = -r * (t1 * a.inv_n);
+      const float nrc2 = LN ? -r * (t2 * a.inv_n) : 0.0f;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         if (!own[v]) continue;
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float xh = (D::get_fresh(x0[i][v], e) - mu) * r;
-          const float gg = D::get_fresh(d0[i][v], e) * D::get_fresh(g[v], e);
-          o[e] = r * fmaf(-xh, c1, gg - c2);
+          const float xh = (D::get_fresh(b[0].x[i][v], e) - mu) * r;
+          const float gg = D::get_fresh(b[0].d[i][v], e) * gf[v][e];
+          o[e] = fmaf(gg, r, fmaf(xh, nrc1, nrc2));
         }
         st16_stream(a.dx, row * a.nvec + vofs + v * T + tid, D::pack(o));
       }
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        x0[i][v] = x1[i][v];
-        d0[i][v] = d1[i][v];
-        x1[i][v] = x2[i][v];
-        d1[i][v] = d2[i][v];
-      }
+    for (int k = 0; k < S - 1; ++k) b[k] = b[k + 1];
   }
 
   // This member's slice of the cluster's partial row.

@@ -38,6 +38,11 @@ struct F32 {
     for (int e = 0; e < 4; ++e) acc = fmaf(get(v, e), get(v, e), acc);
     return acc;
   }
+  __device__ static inline float dot(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(get(a, e), get(b, e), acc);
+    return acc;
+  }
   __device__ static inline u32x4 pack(const float (&f)[4]) {
     u32x4 r;
     r[0] = __float_as_uint(f[0]);

@@ -138,11 +138,13 @@ def test_bad_options_rejected():
 
 
 def test_plan_shape_classes():
-    # non-power-of-2 N = 384 (bf16): 48 vectors covered exactly, several rows per wavefront
+    # non-power-of-2 N = 384 (bf16): 48 vectors, several rows per wavefront, less than one
+    # vector of padding per lane
     for bwd in (False, True):
         p = rn.norm_plan(bwd, False, 262144, 384, BF16)
-        assert p.path == rn.NORM_PATH_ROWS and p.lanes_per_row * p.vecs_per_lane == 48
-        assert p.lanes_per_row <= 16
+        cover = p.lanes_per_row * p.vecs_per_lane
+        assert p.path == rn.NORM_PATH_ROWS and 48 <= cover < 48 + p.lanes_per_row
+        assert p.lanes_per_row <= 32
     # very long rows are split over a cluster of workgroups, forward and backward
     for bwd in (False, True):
         p = rn.norm_plan(bwd, False, 2048, 131072, BF16)
@@ -193,8 +195,7 @@ def test_workspace_size():
 def test_cluster_plans():
     """Rows longer than one workgroup's registers are split over a cluster of workgroups,
     each owning a column slice; forward and backward both, bf16 and fp32."""
-    cases = [(False, BF16, 131072), (False, BF16, 65536), (False, F32, 65536), (True, BF16, 131072),
-             (True, BF16, 65536),
+    cases = [(False, BF16, 131072), (False, F32, 65536), (True, BF16, 131072), (True, BF16, 65536),
              (True, BF16, 32768), (True, F32, 65536), (True, F32, 32768), (True, F32, 16384)]
     for bwd, dt, N in cases:
             M = (1 << 27) // N
