@@ -143,7 +143,7 @@ def _ptr(t):
 def _need(t, name, numel, dtype, device):
     if t is None:
         return
-    if not t.is_cuda or t.device != device:
+    if t.device != device:
         raise ValueError(f"{name} must be on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -156,12 +156,17 @@ def _need(t, name, numel, dtype, device):
 def _shape(x):
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, N] (reshape leading dimensions into M)")
+    if not x.is_cuda:
+        raise ValueError("x must be a GPU tensor")
     return int(x.shape[0]), int(x.shape[1])
 
 
 def _stream(device, stream):
     torch = _torch()
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(device.index if device.index is not None else torch.cuda.current_device())
         return torch.cuda.current_stream(device).cuda_stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -178,14 +183,24 @@ def norm_fwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
                                                 _opt(options)))
 
 
+_FWD_WS = {}
+
+
 def _fwd_workspace(M, N, ln, dtype, device, workspace, options):
-    torch = _torch()
-    need = norm_fwd_workspace_size(M, N, ln, dtype, options)
-    if workspace is None:
-        if need == 0:
-            return None, 0
-        workspace = torch.empty(need, dtype=torch.uint8, device=device)
-    return workspace, workspace.numel() * workspace.element_size()
+    """The caller's workspace (the library checks its size), or a new one of the size the
+    call needs (None when it needs none)."""
+    if workspace is not None:
+        return workspace, workspace.numel() * workspace.element_size()
+    if options is None:
+        key = (M, N, ln, dtype)
+        need = _FWD_WS.get(key)
+        if need is None:
+            need = _FWD_WS.setdefault(key, norm_fwd_workspace_size(M, N, ln, dtype))
+    else:
+        need = norm_fwd_workspace_size(M, N, ln, dtype, options)
+    if need == 0:
+        return None, 0
+    return _torch().empty(need, dtype=_torch().uint8, device=device), need
 
 
 def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stream=None,
@@ -237,9 +252,11 @@ def norm_bwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
 
 
 def _workspace(M, N, ln, dtype, device, workspace, options):
-    torch = _torch()
-    need = norm_bwd_workspace_size(M, N, ln, dtype, options)
+    """The caller's workspace (the library checks its size), or a new one of the size the
+    call needs."""
     if workspace is None:
+        torch = _torch()
+        need = norm_bwd_workspace_size(M, N, ln, dtype, options)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     return workspace, workspace.numel() * workspace.element_size()
 

@@ -227,9 +227,12 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
       }
     }
   } else {
-    // cbuf[slot][lane*EPV + e] holds one vector column block of every slot.
+    // cbuf holds one vector column block of every slot: element e of lane l of a slot at
+    // l*(EPV+1) + e.  The pad word keeps the lanes' stores, EPV words apart otherwise, on
+    // distinct LDS banks.
     constexpr int SPAN = LPR * EPV;
-    __shared__ float cbuf[ROWS * SPAN];
+    constexpr int PSPAN = LPR * (EPV + 1);
+    __shared__ float cbuf[ROWS * PSPAN];
 #pragma unroll
     for (int pass = 0; pass < (LN ? 2 : 1); ++pass) {
       float* const out = pass == 0 ? out_g : out_b;
@@ -238,13 +241,13 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
         __syncthreads();
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          cbuf[slot * SPAN + lane * EPV + e] = pass == 0 ? accg[v][e] : accb[LN ? v : 0][e];
+          cbuf[slot * PSPAN + lane * (EPV + 1) + e] = pass == 0 ? accg[v][e] : accb[LN ? v : 0][e];
         }
         __syncthreads();
         for (int c = tid; c < SPAN; c += BLOCK) {
           float sum = 0.0f;
 #pragma unroll 4
-          for (int k = 0; k < ROWS; ++k) sum += cbuf[k * SPAN + c];
+          for (int k = 0; k < ROWS; ++k) sum += cbuf[k * PSPAN + (c / EPV) * (EPV + 1) + c % EPV];
           const int col = v * SPAN + c;
           if (col < a.N) {
             if (mode == kTwoStage) {
