@@ -34,7 +34,11 @@ _LIB_PATH = os.path.join(_HERE, "libgen.so")
 
 F32 = 0
 BF16 = 1
-_DTYPES = {"f32": F32, "fp32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF16}
+F16 = 2
+_DTYPES = {"f32": F32, "fp32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF16,
+           "f16": F16, "fp16": F16, "float16": F16}
+# host array dtype of each element type: bf16 as raw uint16 bits, fp16 as numpy float16
+_NP = {F32: np.float32, BF16: np.uint16, F16: np.float16}
 
 TENSOR_IDS = {"x": 0, "gamma": 1, "beta": 2, "dy": 3}
 SEED_BASE = 0x5EED0000
@@ -62,8 +66,9 @@ def _load():
         lib.gen_fill.restype = ctypes.c_int
         lib.gen_fill.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double]
-        lib.gen_round_bf16.restype = None
-        lib.gen_round_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
+        for name in ("gen_round_bf16", "gen_round_f16"):
+            getattr(lib, name).restype = None
+            getattr(lib, name).argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64]
         _lib = lib
     return _lib
 
@@ -77,9 +82,9 @@ def dtype_code(dtype: str) -> int:
 
 def fill(n: int, dtype: str, seed: int, mean: float = 0.0, std: float = 1.0,
          outlier_p: float = 0.0, outlier_scale: float = 1.0) -> np.ndarray:
-    """n draws of mean + std*N(0,1); float32 array, or uint16 bfloat16 bits for bf16."""
+    """n draws of mean + std*N(0,1): float32, uint16 bfloat16 bits (bf16) or float16."""
     code = dtype_code(dtype)
-    out = np.empty(n, dtype=np.uint16 if code == BF16 else np.float32)
+    out = np.empty(n, dtype=_NP[code])
     rc = _load().gen_fill(out.ctypes.data, code, n, seed & (2**64 - 1), mean, std,
                           outlier_p, outlier_scale)
     if rc != 0:
@@ -95,6 +100,24 @@ def round_bf16(values) -> np.ndarray:
     return out.reshape(np.shape(values))
 
 
+def round_f16(values) -> np.ndarray:
+    """float values -> float16 (binary16 bits), round-to-nearest-even."""
+    a = np.ascontiguousarray(values, dtype=np.float32).ravel()
+    out = np.empty(a.size, dtype=np.uint16)
+    _load().gen_round_f16(a.ctypes.data, out.ctypes.data, a.size)
+    return out.view(np.float16).reshape(np.shape(values))
+
+
+def round_to(values, dtype: str) -> np.ndarray:
+    """float values as host arrays of `dtype` (the form make_inputs returns)."""
+    code = dtype_code(dtype)
+    if code == BF16:
+        return round_bf16(values)
+    if code == F16:
+        return round_f16(values)
+    return np.ascontiguousarray(values, dtype=np.float32)
+
+
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
     """Exact widening of uint16 bfloat16 bits to float32."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
@@ -104,7 +127,7 @@ def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
 class Workload:
     name: str
     kind: str            # "rms" or "ln"
-    dtype: str           # "bf16" or "f32"
+    dtype: str           # activations: "bf16", "f16" or "f32"
     M: int
     N: int
     eps: float
@@ -114,6 +137,11 @@ class Workload:
     outlier_scale: float = 1.0
     config: int = 0      # seed namespace
     extra: dict = field(default_factory=dict, compare=False)
+    pdtype: str | None = None  # gamma/beta type when it differs from the activations
+
+    @property
+    def param_dtype(self) -> str:
+        return self.pdtype or self.dtype
 
     def seed(self, tensor: str) -> int:
         return SEED_BASE + 16 * self.config + TENSOR_IDS[tensor]
@@ -121,7 +149,8 @@ class Workload:
     def scaled(self, M: int, name: str | None = None) -> "Workload":
         """Same distributions and seeds with a different row count."""
         return Workload(name or f"{self.name}_M{M}", self.kind, self.dtype, M, self.N, self.eps,
-                        self.x_mean, self.x_std, self.outlier_p, self.outlier_scale, self.config)
+                        self.x_mean, self.x_std, self.outlier_p, self.outlier_scale, self.config,
+                        pdtype=self.pdtype)
 
 
 SWEEP_N = (256, 384, 512, 768, 1024, 2048, 4096, 8192, 16384, 32768, 65536)
@@ -151,9 +180,9 @@ def make_inputs(w: Workload, rows: int | None = None) -> dict:
     out = {
         "x": fill(n, w.dtype, w.seed("x"), w.x_mean, w.x_std, w.outlier_p, w.outlier_scale
                   ).reshape(M, w.N),
-        "gamma": fill(w.N, w.dtype, w.seed("gamma"), 1.0, 0.1),
+        "gamma": fill(w.N, w.param_dtype, w.seed("gamma"), 1.0, 0.1),
         "dy": fill(n, w.dtype, w.seed("dy"), 0.0, 1.0).reshape(M, w.N),
     }
     if w.kind == "ln":
-        out["beta"] = fill(w.N, w.dtype, w.seed("beta"), 0.0, 0.1)
+        out["beta"] = fill(w.N, w.param_dtype, w.seed("beta"), 0.0, 0.1)
     return out

@@ -13,8 +13,9 @@
  * (Box and Muller, 1958): draw k yields the pair (z0, z1) used for elements
  * 2k and 2k+1.
  *
- * Values are formed in double, rounded once to float, and, for bf16 output,
- * rounded again to bfloat16 with round-to-nearest-even (NaN stays NaN).
+ * Values are formed in double, rounded once to float, and, for bf16 or fp16
+ * output, rounded again with round-to-nearest-even (NaN stays NaN; fp16 values
+ * beyond its range become infinities).
  */
 #include <math.h>
 #include <stdint.h>
@@ -22,6 +23,7 @@
 
 #define GEN_F32 0
 #define GEN_BF16 1
+#define GEN_F16 2
 
 static const uint64_t kGolden = 0x9E3779B97F4A7C15ULL;
 
@@ -55,6 +57,27 @@ static inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+/* IEEE binary16 bits of a float, round-to-nearest-even. */
+static inline uint16_t f32_to_f16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  const uint16_t sign = (uint16_t)((u >> 16) & 0x8000u);
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x7F800000u) return (uint16_t)(sign | (a > 0x7F800000u ? 0x7E00u : 0x7C00u));
+  if (a >= 0x477FF000u) return (uint16_t)(sign | 0x7C00u); /* >= 65520 rounds to inf */
+  if (a < 0x38800000u) {                                     /* below 2^-14: subnormal */
+    float m;
+    memcpy(&m, &a, 4);
+    /* m * 2^24 is exact; rounding it to an integer (ties to even) gives the subnormal
+     * significand, and 1024 is the smallest normal, encoded the same way. */
+    return (uint16_t)(sign | (uint16_t)lrintf(m * 16777216.0f));
+  }
+  uint32_t h = ((a >> 23) - 112u) << 10 | ((a >> 13) & 0x3FFu); /* rebias 127 -> 15 */
+  const uint32_t rem = a & 0x1FFFu;
+  if (rem > 0x1000u || (rem == 0x1000u && (h & 1u))) h += 1u; /* may carry into the exponent */
+  return (uint16_t)(sign | h);
+}
+
 /* Stream identifiers derived from the user seed, kept apart by a fixed odd
  * offset so that the normal stream and the outlier-mask stream never share
  * draws. */
@@ -74,12 +97,15 @@ static inline double normal_at(uint64_t stream, int64_t i) {
  * Fill out[0..n) with mean + std * z_i, where z_i ~ N(0,1).  When
  * outlier_p > 0, an independent Bernoulli(outlier_p) mask multiplies the
  * selected entries by outlier_scale (in float, before any bf16 rounding).
- * dtype: GEN_F32 writes float, GEN_BF16 writes uint16 bfloat16 bits.
+ * dtype: GEN_F32 writes float, GEN_BF16 / GEN_F16 write uint16 bfloat16 / binary16
+ * bits.
  * Returns 0 on success, -1 on a bad argument.
  */
 int gen_fill(void* out, int dtype, int64_t n, uint64_t seed, double mean, double std,
              double outlier_p, double outlier_scale) {
-  if (n < 0 || (n > 0 && out == NULL) || (dtype != GEN_F32 && dtype != GEN_BF16)) return -1;
+  if (n < 0 || (n > 0 && out == NULL) ||
+      (dtype != GEN_F32 && dtype != GEN_BF16 && dtype != GEN_F16))
+    return -1;
   const uint64_t ns = normal_stream(seed);
   const uint64_t ms = mask_stream(seed);
 #pragma omp parallel for schedule(static)
@@ -88,8 +114,10 @@ int gen_fill(void* out, int dtype, int64_t n, uint64_t seed, double mean, double
     if (outlier_p > 0.0 && unit_53(draw(ms, (uint64_t)i)) < outlier_p) v = v * (float)outlier_scale;
     if (dtype == GEN_F32) {
       ((float*)out)[i] = v;
-    } else {
+    } else if (dtype == GEN_BF16) {
       ((uint16_t*)out)[i] = f32_to_bf16_rne(v);
+    } else {
+      ((uint16_t*)out)[i] = f32_to_f16_rne(v);
     }
   }
   return 0;
@@ -100,4 +128,10 @@ int gen_fill(void* out, int dtype, int64_t n, uint64_t seed, double mean, double
 void gen_round_bf16(const float* in, uint16_t* out, int64_t n) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16_rne(in[i]);
+}
+
+/* Round float values to binary16 bits (RNE). */
+void gen_round_f16(const float* in, uint16_t* out, int64_t n) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = f32_to_f16_rne(in[i]);
 }

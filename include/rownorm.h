@@ -39,10 +39,12 @@
  *     launch returns NORM_ERR_HIP.  No C++ exception crosses the boundary.
  *   - Layout: x, y, dy, dx are contiguous row-major [M, N] with row stride N; gamma
  *     and beta are [N]; mean and rstd are float [M]; dgamma and dbeta are float [N].
- *     x, gamma, beta, y, dy, dx share `dtype`.  Element pointers must be aligned to
+ *     x, y, dy, dx have the activation type of `dtype`, gamma and beta its parameter
+ *     type (the same unless NORM_DTYPE_MIXED).  Element pointers must be aligned to
  *     their element size and float pointers to 4 bytes.  The fast kernels need 16-byte
- *     aligned pointers and N * sizeof(element) a multiple of 16; other inputs run
- *     on a correct, slower scalar path.
+ *     aligned pointers and N * sizeof(activation) a multiple of 16; other inputs run
+ *     on a correct, slower scalar path.  fp16 results that exceed the fp16 range
+ *     become +-inf, as a conversion of the fp32 result would.
  *   - Shapes: M >= 0, 1 <= N <= 2^31 - 1.  M = 0 is a no-op for the forward; the
  *     backward then writes zeros to dgamma/dbeta (a sum over no rows).
  *   - eps must be finite and >= 0 (eps = 0 is allowed; a constant or zero row then
@@ -63,7 +65,15 @@
 extern "C" {
 #endif
 
-typedef enum norm_dtype { NORM_DTYPE_F32 = 0, NORM_DTYPE_BF16 = 1 } norm_dtype_t;
+/* Element types.  The `dtype` argument of every entry point names the type of the
+ * activations (x, y, dy, dx) and, by default, of gamma and beta too.  To give gamma and
+ * beta a different type, pass NORM_DTYPE_MIXED(activations, parameters); supported
+ * pairs: fp32/fp32, bf16/bf16, fp16/fp16, bf16 with fp32 parameters, fp16 with fp32
+ * parameters (the "Fused RMSNorm" page, "How it works", loads rows in fp16 or bf16 and
+ * accumulates in fp32).  Any other code or pair is NORM_ERR_BAD_DTYPE.  mean, rstd,
+ * dgamma and dbeta are fp32 whatever the types. */
+typedef enum norm_dtype { NORM_DTYPE_F32 = 0, NORM_DTYPE_BF16 = 1, NORM_DTYPE_F16 = 2 } norm_dtype_t;
+#define NORM_DTYPE_MIXED(act, param) ((norm_dtype_t)((int)(act) | (((int)(param) + 1) << 8)))
 
 typedef enum norm_status {
   NORM_OK = 0,

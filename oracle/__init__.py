@@ -4,8 +4,10 @@ TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` import this package.  The GPU library never
 imports, links or calls it, and it never imports the GPU library.
 
-Arrays passed in are host numpy arrays of raw element bits: ``uint16`` for bfloat16
-and ``float32`` for fp32 (as produced by :mod:`gen`).  Results are float64.
+Arrays passed in are host numpy arrays of raw element bits: ``uint16`` for bfloat16,
+``float16`` for IEEE binary16 and ``float32`` for fp32 (as produced by :mod:`gen`).
+x and dy share a type; gamma and beta share a type, which may differ from x's.
+Results are float64.
 """
 from __future__ import annotations
 
@@ -21,6 +23,7 @@ SRC_PATH = os.path.join(_HERE, "oracle.c")
 
 F32 = 0
 BF16 = 1
+F16 = 2
 
 
 def build(src: str = SRC_PATH, out: str = LIB_PATH, verbose: bool = False) -> str:
@@ -46,9 +49,11 @@ def _ptr(a):
 def _dtype_of(a: np.ndarray) -> int:
     if a.dtype == np.uint16:
         return BF16
+    if a.dtype == np.float16:
+        return F16
     if a.dtype == np.float32:
         return F32
-    raise TypeError(f"oracle inputs are uint16 (bf16 bits) or float32, got {a.dtype}")
+    raise TypeError(f"oracle inputs are uint16 (bf16 bits), float16 or float32, got {a.dtype}")
 
 
 class Oracle:
@@ -58,10 +63,10 @@ class Oracle:
         if not os.path.exists(path):
             raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
         lib = ctypes.CDLL(path)
-        lib.oracle_rms_fwd.argtypes = [_P, _P, _INT, _I64, _D, _P, _I64, _P, _P]
-        lib.oracle_ln_fwd.argtypes = [_P, _P, _P, _INT, _I64, _D, _P, _I64, _P, _P, _P]
-        lib.oracle_rms_bwd_dx.argtypes = [_P, _P, _P, _INT, _I64, _D, _P, _I64, _P]
-        lib.oracle_ln_bwd_dx.argtypes = [_P, _P, _P, _INT, _I64, _D, _P, _I64, _P]
+        lib.oracle_rms_fwd.argtypes = [_P, _P, _INT, _INT, _I64, _D, _P, _I64, _P, _P]
+        lib.oracle_ln_fwd.argtypes = [_P, _P, _P, _INT, _INT, _I64, _D, _P, _I64, _P, _P, _P]
+        lib.oracle_rms_bwd_dx.argtypes = [_P, _P, _P, _INT, _INT, _I64, _D, _P, _I64, _P]
+        lib.oracle_ln_bwd_dx.argtypes = [_P, _P, _P, _INT, _INT, _I64, _D, _P, _I64, _P]
         lib.oracle_rms_bwd_dgamma.argtypes = [_P, _P, _INT, _I64, _I64, _D, _P, _P]
         lib.oracle_ln_bwd_dgamma_dbeta.argtypes = [_P, _P, _INT, _I64, _I64, _D, _P, _P, _P, _P]
         for name in ("oracle_rms_fwd", "oracle_ln_fwd", "oracle_rms_bwd_dx", "oracle_ln_bwd_dx",
@@ -75,6 +80,7 @@ class Oracle:
     # ----------------------------------------------------------------- helpers
     @staticmethod
     def _prep(x, *others):
+        """x and the arrays of x's type (dy)."""
         x = np.ascontiguousarray(x)
         if x.ndim != 2:
             raise ValueError("x must be 2-D [M, N]")
@@ -86,9 +92,20 @@ class Oracle:
                 continue
             o = np.ascontiguousarray(o)
             if _dtype_of(o) != dt:
-                raise TypeError("all inputs must share x's dtype")
+                raise TypeError("dy must share x's dtype")
             outs.append(o)
         return x, dt, outs
+
+    @staticmethod
+    def _params(gamma, beta=None):
+        """gamma (and beta) and their shared type."""
+        gamma = np.ascontiguousarray(gamma)
+        gdt = _dtype_of(gamma)
+        if beta is not None:
+            beta = np.ascontiguousarray(beta)
+            if _dtype_of(beta) != gdt:
+                raise TypeError("beta must share gamma's dtype")
+        return gamma, beta, gdt
 
     @staticmethod
     def _rows(rows, M):
@@ -105,44 +122,48 @@ class Oracle:
     # ----------------------------------------------------------------- forward
     def rms_fwd(self, x, gamma, eps, rows=None):
         """-> (y [k, N] float64, rstd [k] float64) for the selected rows."""
-        x, dt, (gamma,) = self._prep(x, gamma)
+        x, dt, _ = self._prep(x)
+        gamma, _, gdt = self._params(gamma)
         M, N = x.shape
         r, k = self._rows(rows, M)
         y = np.empty((k, N), np.float64)
         rstd = np.empty(k, np.float64)
-        self.lib.oracle_rms_fwd(_ptr(x), _ptr(gamma), dt, N, float(eps), _ptr(r), k,
+        self.lib.oracle_rms_fwd(_ptr(x), _ptr(gamma), dt, gdt, N, float(eps), _ptr(r), k,
                                 _ptr(y), _ptr(rstd))
         return y, rstd
 
     def ln_fwd(self, x, gamma, beta, eps, rows=None):
         """-> (y, mean, rstd) float64 for the selected rows."""
-        x, dt, (gamma, beta) = self._prep(x, gamma, beta)
+        x, dt, _ = self._prep(x)
+        gamma, beta, gdt = self._params(gamma, beta)
         M, N = x.shape
         r, k = self._rows(rows, M)
         y = np.empty((k, N), np.float64)
         mean = np.empty(k, np.float64)
         rstd = np.empty(k, np.float64)
-        self.lib.oracle_ln_fwd(_ptr(x), _ptr(gamma), _ptr(beta), dt, N, float(eps), _ptr(r), k,
-                               _ptr(y), _ptr(mean), _ptr(rstd))
+        self.lib.oracle_ln_fwd(_ptr(x), _ptr(gamma), _ptr(beta), dt, gdt, N, float(eps), _ptr(r),
+                               k, _ptr(y), _ptr(mean), _ptr(rstd))
         return y, mean, rstd
 
     # ---------------------------------------------------------------- backward
     def rms_bwd_dx(self, dy, x, gamma, eps, rows=None):
-        x, dt, (dy, gamma) = self._prep(x, dy, gamma)
+        x, dt, (dy,) = self._prep(x, dy)
+        gamma, _, gdt = self._params(gamma)
         M, N = x.shape
         r, k = self._rows(rows, M)
         dx = np.empty((k, N), np.float64)
-        self.lib.oracle_rms_bwd_dx(_ptr(dy), _ptr(x), _ptr(gamma), dt, N, float(eps), _ptr(r), k,
-                                   _ptr(dx))
+        self.lib.oracle_rms_bwd_dx(_ptr(dy), _ptr(x), _ptr(gamma), dt, gdt, N, float(eps), _ptr(r),
+                                   k, _ptr(dx))
         return dx
 
     def ln_bwd_dx(self, dy, x, gamma, eps, rows=None):
-        x, dt, (dy, gamma) = self._prep(x, dy, gamma)
+        x, dt, (dy,) = self._prep(x, dy)
+        gamma, _, gdt = self._params(gamma)
         M, N = x.shape
         r, k = self._rows(rows, M)
         dx = np.empty((k, N), np.float64)
-        self.lib.oracle_ln_bwd_dx(_ptr(dy), _ptr(x), _ptr(gamma), dt, N, float(eps), _ptr(r), k,
-                                  _ptr(dx))
+        self.lib.oracle_ln_bwd_dx(_ptr(dy), _ptr(x), _ptr(gamma), dt, gdt, N, float(eps), _ptr(r),
+                                  k, _ptr(dx))
         return dx
 
     def rms_dgamma(self, dy, x, eps):

@@ -19,13 +19,29 @@
 #include <omp.h>
 #endif
 
-/* Exact decode of one stored element to double. */
+/* Exact decode of one stored element to double.  bfloat16 is the top half of a
+ * binary32; binary16 has 1 sign, 5 exponent (bias 15) and 10 fraction bits, exponent 0
+ * meaning subnormal (fraction * 2^-24) and 31 infinity or NaN. */
 static double elem(const void* p, int dtype, int64_t i) {
   if (dtype == ORACLE_BF16) {
     uint32_t u = (uint32_t)((const uint16_t*)p)[i] << 16;
     float f;
     memcpy(&f, &u, sizeof f);
     return (double)f;
+  }
+  if (dtype == ORACLE_F16) {
+    const uint16_t h = ((const uint16_t*)p)[i];
+    const int e = (h >> 10) & 0x1F;
+    const int frac = h & 0x3FF;
+    double v;
+    if (e == 0) {
+      v = ldexp((double)frac, -24);
+    } else if (e == 31) {
+      v = frac ? NAN : INFINITY;
+    } else {
+      v = ldexp((double)(frac + 1024), e - 25);
+    }
+    return (h & 0x8000) ? -v : v;
   }
   return (double)((const float*)p)[i];
 }
@@ -65,8 +81,8 @@ static void ln_stats_of_row(const void* x, int dtype, int64_t N, double eps, int
 
 /* ------------------------------------------------------------------ forward */
 
-void oracle_rms_fwd(const void* x, const void* gamma, int dtype, int64_t N, double eps,
-                    const int64_t* rows, int64_t nrows, double* y, double* rstd) {
+void oracle_rms_fwd(const void* x, const void* gamma, int dtype, int gdtype, int64_t N,
+                    double eps, const int64_t* rows, int64_t nrows, double* y, double* rstd) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < nrows; ++k) {
     const int64_t row = pick_row(rows, k);
@@ -74,15 +90,15 @@ void oracle_rms_fwd(const void* x, const void* gamma, int dtype, int64_t N, doub
     if (rstd) rstd[k] = r;
     if (y) {
       for (int64_t j = 0; j < N; ++j) {
-        y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, dtype, j);
+        y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, gdtype, j);
       }
     }
   }
 }
 
-void oracle_ln_fwd(const void* x, const void* gamma, const void* beta, int dtype, int64_t N,
-                   double eps, const int64_t* rows, int64_t nrows, double* y, double* mean,
-                   double* rstd) {
+void oracle_ln_fwd(const void* x, const void* gamma, const void* beta, int dtype, int gdtype,
+                   int64_t N, double eps, const int64_t* rows, int64_t nrows, double* y,
+                   double* mean, double* rstd) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < nrows; ++k) {
     const int64_t row = pick_row(rows, k);
@@ -93,7 +109,7 @@ void oracle_ln_fwd(const void* x, const void* gamma, const void* beta, int dtype
     if (y) {
       for (int64_t j = 0; j < N; ++j) {
         double xhat = (elem(x, dtype, row * N + j) - mu) * r;
-        y[k * N + j] = xhat * elem(gamma, dtype, j) + elem(beta, dtype, j);
+        y[k * N + j] = xhat * elem(gamma, gdtype, j) + elem(beta, gdtype, j);
       }
     }
   }
@@ -107,8 +123,8 @@ void oracle_ln_fwd(const void* x, const void* gamma, const void* beta, int dtype
  * With g_j = dy_j * gamma_j:
  *   dx_k = sum_j g_j d xhat_j / d x_k = r (g_k - xhat_k * c1),  c1 = (1/N) sum_j g_j xhat_j.
  */
-void oracle_rms_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int64_t N,
-                       double eps, const int64_t* rows, int64_t nrows, double* dx) {
+void oracle_rms_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int gdtype,
+                       int64_t N, double eps, const int64_t* rows, int64_t nrows, double* dx) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < nrows; ++k) {
     const int64_t row = pick_row(rows, k);
@@ -116,13 +132,13 @@ void oracle_rms_bwd_dx(const void* dy, const void* x, const void* gamma, int dty
     const double r = rms_rstd_of_row(x, dtype, N, eps, row);
     double sum_g_xhat = 0.0;
     for (int64_t j = 0; j < N; ++j) {
-      double g = elem(dy, dtype, base + j) * elem(gamma, dtype, j);
+      double g = elem(dy, dtype, base + j) * elem(gamma, gdtype, j);
       double xhat = elem(x, dtype, base + j) * r;
       sum_g_xhat += g * xhat;
     }
     const double c1 = sum_g_xhat / (double)N;
     for (int64_t j = 0; j < N; ++j) {
-      double g = elem(dy, dtype, base + j) * elem(gamma, dtype, j);
+      double g = elem(dy, dtype, base + j) * elem(gamma, gdtype, j);
       double xhat = elem(x, dtype, base + j) * r;
       dx[k * N + j] = r * (g - xhat * c1);
     }
@@ -134,8 +150,8 @@ void oracle_rms_bwd_dx(const void* dy, const void* x, const void* gamma, int dty
  * d xhat_j / d x_k = r (delta_jk - 1/N - xhat_j xhat_k / N), so with g_j = dy_j gamma_j:
  *   dx_k = r (g_k - c2 - xhat_k c1),  c1 = (1/N) sum_j g_j xhat_j,  c2 = (1/N) sum_j g_j.
  */
-void oracle_ln_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int64_t N,
-                      double eps, const int64_t* rows, int64_t nrows, double* dx) {
+void oracle_ln_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int gdtype,
+                      int64_t N, double eps, const int64_t* rows, int64_t nrows, double* dx) {
 #pragma omp parallel for schedule(static)
   for (int64_t k = 0; k < nrows; ++k) {
     const int64_t row = pick_row(rows, k);
@@ -144,7 +160,7 @@ void oracle_ln_bwd_dx(const void* dy, const void* x, const void* gamma, int dtyp
     ln_stats_of_row(x, dtype, N, eps, row, &mu, &r);
     double sum_g_xhat = 0.0, sum_g = 0.0;
     for (int64_t j = 0; j < N; ++j) {
-      double g = elem(dy, dtype, base + j) * elem(gamma, dtype, j);
+      double g = elem(dy, dtype, base + j) * elem(gamma, gdtype, j);
       double xhat = (elem(x, dtype, base + j) - mu) * r;
       sum_g_xhat += g * xhat;
       sum_g += g;
@@ -152,7 +168,7 @@ void oracle_ln_bwd_dx(const void* dy, const void* x, const void* gamma, int dtyp
     const double c1 = sum_g_xhat / (double)N;
     const double c2 = sum_g / (double)N;
     for (int64_t j = 0; j < N; ++j) {
-      double g = elem(dy, dtype, base + j) * elem(gamma, dtype, j);
+      double g = elem(dy, dtype, base + j) * elem(gamma, gdtype, j);
       double xhat = (elem(x, dtype, base + j) - mu) * r;
       dx[k * N + j] = r * (g - c2 - xhat * c1);
     }

@@ -16,8 +16,10 @@
  *    section "Why Is Peak Vectorization Your New Best Friend?").  The pages give no
  *    formulas; the ones used here are the exact derivatives of the forward.
  *
- * Inputs are raw element bits (ORACLE_F32: float, ORACLE_BF16: uint16 bfloat16),
- * decoded exactly to double.  All arithmetic is in double.  Statistics are always
+ * Inputs are raw element bits (ORACLE_F32: float, ORACLE_BF16: uint16 bfloat16,
+ * ORACLE_F16: uint16 IEEE binary16), decoded exactly to double.  `dtype` is the type of
+ * x and dy, `gdtype` that of gamma and beta (the "Fused RMSNorm" page, "How it works",
+ * loads the row in fp16 or bf16; the parameters may be kept in fp32).  All arithmetic is in double.  Statistics are always
  * computed by the oracle from x; it never takes statistics from elsewhere.
  *
  * Row selection: `rows` lists the row indices to evaluate (into a matrix with row
@@ -33,22 +35,22 @@
 extern "C" {
 #endif
 
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
 
 /* y[k,:] (may be NULL), rstd[k] (may be NULL) */
-void oracle_rms_fwd(const void* x, const void* gamma, int dtype, int64_t N, double eps,
-                    const int64_t* rows, int64_t nrows, double* y, double* rstd);
+void oracle_rms_fwd(const void* x, const void* gamma, int dtype, int gdtype, int64_t N,
+                    double eps, const int64_t* rows, int64_t nrows, double* y, double* rstd);
 
 /* y, mean, rstd each may be NULL */
-void oracle_ln_fwd(const void* x, const void* gamma, const void* beta, int dtype, int64_t N,
-                   double eps, const int64_t* rows, int64_t nrows, double* y, double* mean,
-                   double* rstd);
+void oracle_ln_fwd(const void* x, const void* gamma, const void* beta, int dtype, int gdtype,
+                   int64_t N, double eps, const int64_t* rows, int64_t nrows, double* y,
+                   double* mean, double* rstd);
 
-void oracle_rms_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int64_t N,
-                       double eps, const int64_t* rows, int64_t nrows, double* dx);
+void oracle_rms_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int gdtype,
+                       int64_t N, double eps, const int64_t* rows, int64_t nrows, double* dx);
 
-void oracle_ln_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int64_t N,
-                      double eps, const int64_t* rows, int64_t nrows, double* dx);
+void oracle_ln_bwd_dx(const void* dy, const void* x, const void* gamma, int dtype, int gdtype,
+                      int64_t N, double eps, const int64_t* rows, int64_t nrows, double* dx);
 
 /* Column sums over all M rows.  dgamma[j] = sum_i dy[i,j] * xhat[i,j]; for LayerNorm
  * also dbeta[j] = sum_i dy[i,j].  The *_scale outputs (may be NULL) hold

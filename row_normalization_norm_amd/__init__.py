@@ -20,6 +20,12 @@ LIB_PATH = os.path.join(_HERE, "librownorm.so")
 # norm_dtype_t
 NORM_DTYPE_F32 = 0
 NORM_DTYPE_BF16 = 1
+NORM_DTYPE_F16 = 2
+
+
+def dtype_mixed(act: int, param: int) -> int:
+    """NORM_DTYPE_MIXED: activations of type `act` with gamma/beta of type `param`."""
+    return act | ((param + 1) << 8)
 # norm_status_t
 NORM_OK = 0
 NORM_ERR_NULL_PTR = 1
@@ -133,7 +139,25 @@ def _dtype_code(t) -> int:
         return NORM_DTYPE_BF16
     if t.dtype == torch.float32:
         return NORM_DTYPE_F32
-    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+    if t.dtype == torch.float16:
+        return NORM_DTYPE_F16
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float16 or float32)")
+
+
+def _pdtype(x, gamma):
+    return x.dtype if gamma is None else gamma.dtype
+
+
+def _types(x, gamma):
+    """The library's dtype code for activations like x and parameters like gamma."""
+    act = _dtype_code(x)
+    par = act if gamma is None else _dtype_code(gamma)
+    if par == act:
+        return act
+    if par == NORM_DTYPE_F32 and act in (NORM_DTYPE_BF16, NORM_DTYPE_F16):
+        return dtype_mixed(act, par)
+    raise TypeError(f"gamma/beta of {gamma.dtype} with activations of {x.dtype}: use the "
+                    f"activations' type or float32")
 
 
 def _ptr(t):
@@ -209,10 +233,10 @@ def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stre
     torch = _torch()
     M, N = _shape(x)
     _need(x, "x", M * N, x.dtype, x.device)
-    for t, n, k in ((gamma, "gamma", N), (y, "y", M * N)):
-        _need(t, n, k, x.dtype, x.device)
+    _need(y, "y", M * N, x.dtype, x.device)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
-    dt = _dtype_code(x)
+    dt = _types(x, gamma)
     ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options)
     args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
             _stream(x.device, stream))
@@ -229,11 +253,12 @@ def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, work
     torch = _torch()
     M, N = _shape(x)
     _need(x, "x", M * N, x.dtype, x.device)
-    for t, n, k in ((gamma, "gamma", N), (beta, "beta", N), (y, "y", M * N)):
-        _need(t, n, k, x.dtype, x.device)
+    _need(y, "y", M * N, x.dtype, x.device)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
+    _need(beta, "beta", N, _pdtype(x, gamma), x.device)
     _need(mean, "mean", M, torch.float32, x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
-    dt = _dtype_code(x)
+    dt = _types(x, gamma)
     ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options)
     args = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, float(eps),
             dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
@@ -265,11 +290,12 @@ def norm_rms_bwd(dy, x, gamma, rstd, dx, dgamma, workspace=None, stream=None, op
     """dx and dgamma (overwritten) of RMSNorm from the forward's saved rstd."""
     torch = _torch()
     M, N = _shape(x)
-    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (gamma, "gamma", N), (dx, "dx", M * N)):
+    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
         _need(t, n, k, x.dtype, x.device)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     _need(dgamma, "dgamma", N, torch.float32, x.device)
-    dt = _dtype_code(x)
+    dt = _types(x, gamma)
     ws, ws_bytes = _workspace(M, N, False, dt, x.device, workspace, options)
     args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N, dt,
             _ptr(ws), ws_bytes, _stream(x.device, stream))
@@ -285,12 +311,13 @@ def norm_ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace=None, str
     """dx, dgamma and dbeta (overwritten) of LayerNorm from the saved mean and rstd."""
     torch = _torch()
     M, N = _shape(x)
-    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (gamma, "gamma", N), (dx, "dx", M * N)):
+    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
         _need(t, n, k, x.dtype, x.device)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
     for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
                     (dbeta, "dbeta", N)):
         _need(t, n, k, torch.float32, x.device)
-    dt = _dtype_code(x)
+    dt = _types(x, gamma)
     ws, ws_bytes = _workspace(M, N, True, dt, x.device, workspace, options)
     args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
             _ptr(dbeta), M, N, dt, _ptr(ws), ws_bytes, _stream(x.device, stream))

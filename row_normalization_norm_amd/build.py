@@ -25,12 +25,13 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 def _units():
     units = []
+    # kind (0 RMSNorm, 1 LayerNorm) x type pair (TypeCombo in csrc/launch.h)
     for k in (0, 1):
-        for d in (0, 1):
+        for tc in range(5):
             for name in ("fwd_rows", "bwd_rows", "cluster"):
                 units.append((os.path.join(CSRC, f"{name}.hip"),
-                              os.path.join(BUILD_DIR, f"{name}_k{k}_d{d}.o"),
-                              [f"-DRN_KIND={k}", f"-DRN_DTYPE={d}"]))
+                              os.path.join(BUILD_DIR, f"{name}_k{k}_t{tc}.o"),
+                              [f"-DRN_KIND={k}", f"-DRN_TC={tc}"]))
     units.append((os.path.join(CSRC, "aux_kernels.hip"), os.path.join(BUILD_DIR, "aux.o"), []))
     units.append((os.path.join(CSRC, "plan.cpp"), os.path.join(BUILD_DIR, "plan.o"), ["-x", "hip"]))
     units.append((os.path.join(CSRC, "api.cpp"), os.path.join(BUILD_DIR, "api.o"), ["-x", "hip"]))

@@ -15,89 +15,106 @@
 
 namespace rownorm {
 
-// Per-(kind, dtype) launchers, one translation unit each.
-hipError_t launch_fwd_rows_k0_d0(int, int, const FwdArgs&, int, hipStream_t);
-hipError_t launch_fwd_rows_k0_d1(int, int, const FwdArgs&, int, hipStream_t);
-hipError_t launch_fwd_rows_k1_d0(int, int, const FwdArgs&, int, hipStream_t);
-hipError_t launch_fwd_rows_k1_d1(int, int, const FwdArgs&, int, hipStream_t);
-hipError_t launch_bwd_rows_k0_d0(int, int, const BwdArgs&, int, hipStream_t);
-hipError_t launch_bwd_rows_k0_d1(int, int, const BwdArgs&, int, hipStream_t);
-hipError_t launch_bwd_rows_k1_d0(int, int, const BwdArgs&, int, hipStream_t);
-hipError_t launch_bwd_rows_k1_d1(int, int, const BwdArgs&, int, hipStream_t);
+// Per-(kind, type pair) launchers, one translation unit each (TypeCombo in launch.h).
+#define RN_DECL_TU(K, T)                                                                  \
+  hipError_t launch_fwd_rows_k##K##_t##T(int, int, const FwdArgs&, int, hipStream_t);      \
+  hipError_t launch_bwd_rows_k##K##_t##T(int, int, const BwdArgs&, int, hipStream_t);      \
+  hipError_t launch_fwd_cluster_k##K##_t##T(int, int, int, const FwdArgs&, const ClusterArgs&, \
+                                            int, hipStream_t);                             \
+  hipError_t launch_bwd_cluster_k##K##_t##T(int, int, int, const BwdArgs&, const ClusterArgs&, \
+                                            int, hipStream_t);                             \
+  int occupancy_fwd_cluster_k##K##_t##T(int, int, int);                                    \
+  int occupancy_bwd_cluster_k##K##_t##T(int, int, int);
+RN_DECL_TU(0, 0) RN_DECL_TU(0, 1) RN_DECL_TU(0, 2) RN_DECL_TU(0, 3) RN_DECL_TU(0, 4)
+RN_DECL_TU(1, 0) RN_DECL_TU(1, 1) RN_DECL_TU(1, 2) RN_DECL_TU(1, 3) RN_DECL_TU(1, 4)
+#undef RN_DECL_TU
 
-hipError_t launch_fwd_rows(int kind, int dtype, int lpr, int vpl, const FwdArgs& a, int grid,
+#define RN_TABLE(PFX)                                                      \
+  {                                                                        \
+    {PFX##_k0_t0, PFX##_k0_t1, PFX##_k0_t2, PFX##_k0_t3, PFX##_k0_t4}, {   \
+      PFX##_k1_t0, PFX##_k1_t1, PFX##_k1_t2, PFX##_k1_t3, PFX##_k1_t4      \
+    }                                                                      \
+  }
+
+namespace {
+using FwdRowsFn = hipError_t (*)(int, int, const FwdArgs&, int, hipStream_t);
+using BwdRowsFn = hipError_t (*)(int, int, const BwdArgs&, int, hipStream_t);
+using FwdClusterFn = hipError_t (*)(int, int, int, const FwdArgs&, const ClusterArgs&, int,
+                                    hipStream_t);
+using BwdClusterFn = hipError_t (*)(int, int, int, const BwdArgs&, const ClusterArgs&, int,
+                                    hipStream_t);
+using OccFn = int (*)(int, int, int);
+const FwdRowsFn kFwdRows[2][kNumTypeCombos] = RN_TABLE(launch_fwd_rows);
+const BwdRowsFn kBwdRows[2][kNumTypeCombos] = RN_TABLE(launch_bwd_rows);
+const FwdClusterFn kFwdCluster[2][kNumTypeCombos] = RN_TABLE(launch_fwd_cluster);
+const BwdClusterFn kBwdCluster[2][kNumTypeCombos] = RN_TABLE(launch_bwd_cluster);
+const OccFn kFwdOcc[2][kNumTypeCombos] = RN_TABLE(occupancy_fwd_cluster);
+const OccFn kBwdOcc[2][kNumTypeCombos] = RN_TABLE(occupancy_bwd_cluster);
+}  // namespace
+#undef RN_TABLE
+
+hipError_t launch_fwd_rows(int kind, int tc, int lpr, int vpl, const FwdArgs& a, int grid,
                            hipStream_t s) {
-  if (kind == 0) {
-    return dtype ? launch_fwd_rows_k0_d1(lpr, vpl, a, grid, s)
-                 : launch_fwd_rows_k0_d0(lpr, vpl, a, grid, s);
-  }
-  return dtype ? launch_fwd_rows_k1_d1(lpr, vpl, a, grid, s)
-               : launch_fwd_rows_k1_d0(lpr, vpl, a, grid, s);
+  return kFwdRows[kind][tc](lpr, vpl, a, grid, s);
 }
-
-hipError_t launch_bwd_rows(int kind, int dtype, int lpr, int vpl, const BwdArgs& a, int grid,
+hipError_t launch_bwd_rows(int kind, int tc, int lpr, int vpl, const BwdArgs& a, int grid,
                            hipStream_t s) {
-  if (kind == 0) {
-    return dtype ? launch_bwd_rows_k0_d1(lpr, vpl, a, grid, s)
-                 : launch_bwd_rows_k0_d0(lpr, vpl, a, grid, s);
-  }
-  return dtype ? launch_bwd_rows_k1_d1(lpr, vpl, a, grid, s)
-               : launch_bwd_rows_k1_d0(lpr, vpl, a, grid, s);
+  return kBwdRows[kind][tc](lpr, vpl, a, grid, s);
 }
-
-hipError_t launch_fwd_cluster_k0_d0(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
-hipError_t launch_fwd_cluster_k0_d1(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
-hipError_t launch_fwd_cluster_k1_d0(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
-hipError_t launch_fwd_cluster_k1_d1(int, int, int, const FwdArgs&, const ClusterArgs&, int, hipStream_t);
-hipError_t launch_bwd_cluster_k0_d0(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
-hipError_t launch_bwd_cluster_k0_d1(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
-hipError_t launch_bwd_cluster_k1_d0(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
-hipError_t launch_bwd_cluster_k1_d1(int, int, int, const BwdArgs&, const ClusterArgs&, int, hipStream_t);
-int occupancy_fwd_cluster_k0_d0(int, int, int);
-int occupancy_fwd_cluster_k0_d1(int, int, int);
-int occupancy_fwd_cluster_k1_d0(int, int, int);
-int occupancy_fwd_cluster_k1_d1(int, int, int);
-int occupancy_bwd_cluster_k0_d0(int, int, int);
-int occupancy_bwd_cluster_k0_d1(int, int, int);
-int occupancy_bwd_cluster_k1_d0(int, int, int);
-int occupancy_bwd_cluster_k1_d1(int, int, int);
-
-hipError_t launch_fwd_cluster(int kind, int dtype, int t, int vpl, int rows, const FwdArgs& a,
+hipError_t launch_fwd_cluster(int kind, int tc, int t, int vpl, int rows, const FwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s) {
-  if (kind == 0) {
-    return dtype ? launch_fwd_cluster_k0_d1(t, vpl, rows, a, c, grid, s)
-                 : launch_fwd_cluster_k0_d0(t, vpl, rows, a, c, grid, s);
-  }
-  return dtype ? launch_fwd_cluster_k1_d1(t, vpl, rows, a, c, grid, s)
-               : launch_fwd_cluster_k1_d0(t, vpl, rows, a, c, grid, s);
+  return kFwdCluster[kind][tc](t, vpl, rows, a, c, grid, s);
 }
-
-hipError_t launch_bwd_cluster(int kind, int dtype, int t, int vpl, int rows, const BwdArgs& a,
+hipError_t launch_bwd_cluster(int kind, int tc, int t, int vpl, int rows, const BwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s) {
-  if (kind == 0) {
-    return dtype ? launch_bwd_cluster_k0_d1(t, vpl, rows, a, c, grid, s)
-                 : launch_bwd_cluster_k0_d0(t, vpl, rows, a, c, grid, s);
+  return kBwdCluster[kind][tc](t, vpl, rows, a, c, grid, s);
+}
+int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows) {
+  return kFwdOcc[kind][tc](t, vpl, rows);
+}
+int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows) {
+  return kBwdOcc[kind][tc](t, vpl, rows);
+}
+
+// The public dtype code: the activation type in the low byte, optionally the parameter
+// type + 1 in the next byte (0: the activation type), see rownorm.h.
+struct DtypeInfo {
+  int x = -1;   // activation type (norm_dtype_t)
+  int p = -1;   // parameter type
+  int tc = -1;  // TypeCombo
+};
+
+DtypeInfo decode_dtype(norm_dtype_t code) {
+  DtypeInfo d;
+  const uint32_t c = static_cast<uint32_t>(code);
+  if (c >> 16) return d;
+  const int x = int(c & 0xFFu), pc = int((c >> 8) & 0xFFu);
+  const int p = pc ? pc - 1 : x;
+  const bool x_ok = x == NORM_DTYPE_F32 || x == NORM_DTYPE_BF16 || x == NORM_DTYPE_F16;
+  if (!x_ok) return d;
+  int tc = -1;
+  if (p == x) {
+    tc = x == NORM_DTYPE_F32 ? kTcF32 : x == NORM_DTYPE_BF16 ? kTcBF16 : kTcF16;
+  } else if (p == NORM_DTYPE_F32 && x == NORM_DTYPE_BF16) {
+    tc = kTcBF16F32;
+  } else if (p == NORM_DTYPE_F32 && x == NORM_DTYPE_F16) {
+    tc = kTcF16F32;
   }
-  return dtype ? launch_bwd_cluster_k1_d1(t, vpl, rows, a, c, grid, s)
-               : launch_bwd_cluster_k1_d0(t, vpl, rows, a, c, grid, s);
+  if (tc < 0) return d;
+  d.x = x;
+  d.p = p;
+  d.tc = tc;
+  return d;
 }
 
-int occupancy_fwd_cluster(int kind, int dtype, int t, int vpl, int rows) {
-  if (kind == 0) return dtype ? occupancy_fwd_cluster_k0_d1(t, vpl, rows) : occupancy_fwd_cluster_k0_d0(t, vpl, rows);
-  return dtype ? occupancy_fwd_cluster_k1_d1(t, vpl, rows) : occupancy_fwd_cluster_k1_d0(t, vpl, rows);
-}
-
-int occupancy_bwd_cluster(int kind, int dtype, int t, int vpl, int rows) {
-  if (kind == 0) return dtype ? occupancy_bwd_cluster_k0_d1(t, vpl, rows) : occupancy_bwd_cluster_k0_d0(t, vpl, rows);
-  return dtype ? occupancy_bwd_cluster_k1_d1(t, vpl, rows) : occupancy_bwd_cluster_k1_d0(t, vpl, rows);
-}
+uintptr_t elem_bytes(int t) { return t == NORM_DTYPE_F32 ? 4 : 2; }
 
 namespace {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 norm_status_t check_shape_dtype(int64_t M, int64_t N, norm_dtype_t dtype) {
-  if (dtype != NORM_DTYPE_F32 && dtype != NORM_DTYPE_BF16) return NORM_ERR_BAD_DTYPE;
+  if (decode_dtype(dtype).tc < 0) return NORM_ERR_BAD_DTYPE;
   if (M < 0 || N < 1 || N > INT32_MAX) return NORM_ERR_BAD_SHAPE;
   // Keep M*N*16 (the largest byte offset any kernel forms) within int64.
   if (M > 0 && M > (INT64_MAX / 16) / N) return NORM_ERR_BAD_SHAPE;
@@ -120,8 +137,8 @@ struct EventScope {
 }  // namespace
 
 // Workgroups of a cluster kernel the current device can hold at once (0 if unknown).
-// Cached per (device, direction, kind, dtype, threads, vectors, rows per step).
-int cluster_capacity(bool backward, int kind, int dtype, int t, int vpl, int rows) {
+// Cached per (device, direction, kind, type pair, threads, vectors, rows per step).
+int cluster_capacity(bool backward, int kind, int tc, int t, int vpl, int rows) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   static std::atomic<int> cus[64];
@@ -133,19 +150,19 @@ int cluster_capacity(bool backward, int kind, int dtype, int t, int vpl, int row
   }
   // occupancy depends only on the kernel and the device's per-CU limits
   static std::mutex mu;
-  // [dev][bwd][kind][dtype][t: 256/512/1024][vpl: 1/2/4][rows per step: 1/2]
-  static int cache[64][2][2][2][3][3][2];
+  // [dev][bwd][kind][type pair][t: 256/512/1024][vpl: 1/2/4][rows per step: 1/2]
+  static int cache[64][2][2][kNumTypeCombos][3][3][2];
   const int ti = t == 256 ? 0 : t == 512 ? 1 : 2;
   const int vi = vpl == 1 ? 0 : vpl == 2 ? 1 : 2;
   int occ;
   {
     std::lock_guard<std::mutex> lock(mu);
     const int ri = rows == 1 ? 0 : 1;
-    occ = cache[dev][backward][kind][dtype][ti][vi][ri];
+    occ = cache[dev][backward][kind][tc][ti][vi][ri];
     if (occ == 0) {
-      occ = backward ? occupancy_bwd_cluster(kind, dtype, t, vpl, rows)
-                     : occupancy_fwd_cluster(kind, dtype, t, vpl, rows);
-      cache[dev][backward][kind][dtype][ti][vi][ri] = occ > 0 ? occ : -1;
+      occ = backward ? occupancy_bwd_cluster(kind, tc, t, vpl, rows)
+                     : occupancy_fwd_cluster(kind, tc, t, vpl, rows);
+      cache[dev][backward][kind][tc][ti][vi][ri] = occ > 0 ? occ : -1;
     }
   }
   return occ > 0 ? occ * n : 0;
@@ -155,8 +172,8 @@ int cluster_capacity(bool backward, int kind, int dtype, int t, int vpl, int row
 // co-resident (fewer clusters also means fewer dgamma/dbeta partial rows, so the
 // workspace the plan sized still suffices).  Returns false when not even one cluster
 // fits; the caller then takes the fallback plan.
-bool fit_cluster(bool backward, int kind, int dtype, Plan& p) {
-  const int cap = cluster_capacity(backward, kind, dtype, p.lpr, p.vpl, p.rows_per_step);
+bool fit_cluster(bool backward, int kind, int tc, Plan& p) {
+  const int cap = cluster_capacity(backward, kind, tc, p.lpr, p.vpl, p.rows_per_step);
   if (cap < p.cluster) return false;
   if (p.grid > cap) {
     int ncl = cap / p.cluster;
@@ -206,14 +223,15 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   if (!gamma || (ln && !beta)) return NORM_ERR_NULL_PTR;
   if (M > 0 && (!x || !y)) return NORM_ERR_NULL_PTR;
   if (!std::isfinite(eps) || eps < 0.0f) return NORM_ERR_BAD_EPS;
-  const uintptr_t es = dtype == NORM_DTYPE_BF16 ? 2 : 4;
-  if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, es) || !aligned(beta, es) ||
+  const DtypeInfo dt = decode_dtype(dtype);
+  const uintptr_t es = elem_bytes(dt.x), ps = elem_bytes(dt.p);
+  if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, ps) || !aligned(beta, ps) ||
       !aligned(mean, 4) || !aligned(rstd, 4))
     return NORM_ERR_MISALIGNED;
   const bool a16 = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16);
 
   Plan p;
-  st = make_plan(false, ln, M, N, dtype, a16, opt, &p);
+  st = make_plan(false, ln, M, N, dt.x, a16, opt, &p);
   if (st != NORM_OK) return st;
   st = check_workspace(p, workspace, workspace_bytes_given);
   if (st != NORM_OK) return st;
@@ -234,11 +252,10 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   a.groups = p.groups;
 
   const int kind = ln ? 1 : 0;
-  const int dt = dtype == NORM_DTYPE_BF16 ? 1 : 0;
   EventScope ev{opt, stream};
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(false, kind, dt, p)) {
-    make_fallback_plan(false, ln, M, N, dtype, &p);
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(false, kind, dt.tc, p)) {
+    make_fallback_plan(false, ln, M, N, dt.x, &p);
   }
   hipError_t e = hipSuccess;
   if (p.path == NORM_PATH_CLUSTER) {
@@ -248,13 +265,14 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   if (ev.start() != hipSuccess) return NORM_ERR_HIP;
   switch (p.path) {
     case NORM_PATH_ROWS:
-      e = launch_fwd_rows(kind, dt, p.lpr, p.vpl, a, p.grid, stream);
+      e = launch_fwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
       break;
     case NORM_PATH_CLUSTER:
-      e = launch_fwd_cluster(kind, dt, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws), p.grid, stream);
+      e = launch_fwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws),
+                             p.grid, stream);
       break;
     default:
-      e = launch_fwd_generic(kind, dt, a, p.grid, stream);
+      e = launch_fwd_generic(kind, dt.tc, a, p.grid, stream);
   }
   if (e != hipSuccess) return NORM_ERR_HIP;
   return hip_status(ev.stop());
@@ -269,20 +287,20 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   if (st != NORM_OK) return st;
   if (!gamma || !dgamma || (ln && !dbeta)) return NORM_ERR_NULL_PTR;
   if (M > 0 && (!dy || !x || !rstd || !dx || (ln && !mean))) return NORM_ERR_NULL_PTR;
-  const uintptr_t es = dtype == NORM_DTYPE_BF16 ? 2 : 4;
-  if (!aligned(dy, es) || !aligned(x, es) || !aligned(gamma, es) || !aligned(dx, es) ||
+  const DtypeInfo dt = decode_dtype(dtype);
+  const uintptr_t es = elem_bytes(dt.x), ps = elem_bytes(dt.p);
+  if (!aligned(dy, es) || !aligned(x, es) || !aligned(gamma, ps) || !aligned(dx, es) ||
       !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4))
     return NORM_ERR_MISALIGNED;
   const bool a16 = aligned(dy, 16) && aligned(x, 16) && aligned(gamma, 16) && aligned(dx, 16);
 
   Plan p;
-  st = make_plan(true, ln, M, N, dtype, a16, opt, &p);
+  st = make_plan(true, ln, M, N, dt.x, a16, opt, &p);
   if (st != NORM_OK) return st;
   st = check_workspace(p, workspace, workspace_bytes_given);
   if (st != NORM_OK) return st;
 
   const int kind = ln ? 1 : 0;
-  const int dt = dtype == NORM_DTYPE_BF16 ? 1 : 0;
   const int mode = opt ? opt->dgamma_mode : NORM_DGAMMA_TWO_STAGE;
   float* const db = ln ? dbeta : nullptr;
 
@@ -291,8 +309,8 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   }
 
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(true, kind, dt, p)) {
-    make_fallback_plan(true, ln, M, N, dtype, &p);
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(true, kind, dt.tc, p)) {
+    make_fallback_plan(true, ln, M, N, dt.x, &p);
   }
   BwdArgs a;
   a.dy = dy;
@@ -327,14 +345,15 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   }
   if (ev.start() != hipSuccess) return NORM_ERR_HIP;
   if (p.path == NORM_PATH_ROWS) {
-    e = launch_bwd_rows(kind, dt, p.lpr, p.vpl, a, p.grid, stream);
+    e = launch_bwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
   } else if (p.path == NORM_PATH_CLUSTER) {
-    e = launch_bwd_cluster(kind, dt, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws), p.grid, stream);
+    e = launch_bwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws),
+                           p.grid, stream);
   } else {
     const bool vec = p.path == NORM_PATH_SPLIT;
-    e = launch_bwd_rowdot(kind, dt, vec, a, p.grid, stream);
+    e = launch_bwd_rowdot(kind, dt.tc, vec, a, p.grid, stream);
     if (e == hipSuccess)
-      e = launch_bwd_colslice(kind, dt, vec, a, p.slices, int(p.partial_rows), stream);
+      e = launch_bwd_colslice(kind, dt.tc, vec, a, p.slices, int(p.partial_rows), stream);
   }
   if (e != hipSuccess) return NORM_ERR_HIP;
   if (ev.stop() != hipSuccess) return NORM_ERR_HIP;
@@ -408,7 +427,8 @@ size_t norm_fwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtyp
 size_t norm_fwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
                                   const norm_options_t* opt) {
   if (rownorm::check_shape_dtype(M, N, dtype) != NORM_OK) return 0;
-  return rownorm::workspace_bytes(false, M, N, is_layernorm != 0, dtype, opt);
+  return rownorm::workspace_bytes(false, M, N, is_layernorm != 0, rownorm::decode_dtype(dtype).x,
+                                  opt);
 }
 
 size_t norm_bwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype) {
@@ -418,7 +438,8 @@ size_t norm_bwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtyp
 size_t norm_bwd_workspace_size_ex(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype,
                                   const norm_options_t* opt) {
   if (rownorm::check_shape_dtype(M, N, dtype) != NORM_OK) return 0;
-  return rownorm::workspace_bytes(true, M, N, is_layernorm != 0, dtype, opt);
+  return rownorm::workspace_bytes(true, M, N, is_layernorm != 0, rownorm::decode_dtype(dtype).x,
+                                  opt);
 }
 
 norm_status_t norm_rms_bwd(const void* dy, const void* x, const void* gamma, const float* rstd,
@@ -468,7 +489,8 @@ norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
   norm_status_t st = rownorm::check_shape_dtype(M, N, dtype);
   if (st != NORM_OK) return st;
   rownorm::Plan p;
-  st = rownorm::make_plan(is_backward != 0, is_layernorm != 0, M, N, dtype, aligned16 != 0, opt, &p);
+  st = rownorm::make_plan(is_backward != 0, is_layernorm != 0, M, N, rownorm::decode_dtype(dtype).x,
+                          aligned16 != 0, opt, &p);
   if (st != NORM_OK) return st;
   info->path = p.path;
   info->lanes_per_row = p.lpr;
@@ -487,14 +509,12 @@ norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
 int norm_cluster_resident(int is_backward, int is_layernorm, int64_t M, int64_t N,
                           norm_dtype_t dtype, const norm_options_t* opt) {
   if (rownorm::check_shape_dtype(M, N, dtype) != NORM_OK) return -1;
+  const rownorm::DtypeInfo dt = rownorm::decode_dtype(dtype);
   rownorm::Plan p;
-  if (rownorm::make_plan(is_backward != 0, is_layernorm != 0, M, N, dtype, true, opt, &p) != NORM_OK)
+  if (rownorm::make_plan(is_backward != 0, is_layernorm != 0, M, N, dt.x, true, opt, &p) != NORM_OK)
     return -1;
   if (p.path != NORM_PATH_CLUSTER) return 0;
-  return rownorm::fit_cluster(is_backward != 0, is_layernorm ? 1 : 0,
-                              dtype == NORM_DTYPE_BF16 ? 1 : 0, p)
-             ? 1
-             : 0;
+  return rownorm::fit_cluster(is_backward != 0, is_layernorm ? 1 : 0, dt.tc, p) ? 1 : 0;
 }
 
 const char* norm_status_string(norm_status_t s) {

@@ -52,7 +52,7 @@ __device__ inline void block_sum2(float& a, float& b, float* red, int& parity) {
 }
 
 // ----------------------------------------------------------------------- rowdot
-template <bool LN, typename D, bool VEC>
+template <bool LN, typename D, typename P, bool VEC>
 __global__ __launch_bounds__(kRowBlock) void rowdot_kernel(const BwdArgs a) {
   constexpr int EPV = D::kPerVec;
   __shared__ float red[2 * kRowWaves * 2];
@@ -68,11 +68,12 @@ __global__ __launch_bounds__(kRowBlock) void rowdot_kernel(const BwdArgs a) {
       for (int vi = tid; vi < a.nvec; vi += kRowBlock) {
         const u32x4 xv = ld16(a.x, vbase + vi);
         const u32x4 dv = ld16(a.dy, vbase + vi);
-        const u32x4 gv = ld16(a.gamma, vi);
+        Param<D, P> gv;
+        gv.load(a.gamma, vi);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           const float xh = (D::get(xv, e) - mu) * r;
-          const float g = D::get(dv, e) * D::get(gv, e);
+          const float g = D::get(dv, e) * gv.get(e);
           s1 = fmaf(g, xh, s1);
           if constexpr (LN) s2 += g;
         }
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kRowBlock) void rowdot_kernel(const BwdArgs a) {
 #pragma unroll 4
       for (int j = tid; j < a.N; j += kRowBlock) {
         const float xh = (D::scalar(a.x, base + j) - mu) * r;
-        const float g = D::scalar(a.dy, base + j) * D::scalar(a.gamma, j);
+        const float g = D::scalar(a.dy, base + j) * P::scalar(a.gamma, j);
         s1 = fmaf(g, xh, s1);
         if constexpr (LN) s2 += g;
       }
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(kRowBlock) void rowdot_kernel(const BwdArgs a) {
 }
 
 // --------------------------------------------------------------------- colslice
-template <bool LN, typename D, bool VEC>
+template <bool LN, typename D, typename P, bool VEC>
 __global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) {
   constexpr int EPV = VEC ? D::kPerVec : 1;
   constexpr int V = VEC ? kSliceVecs : 1;
@@ -118,11 +119,16 @@ __global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) 
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     if constexpr (VEC) {
-      const u32x4 gv = own[v] ? ld16(a.gamma, idx[v]) : zero16();
+      Param<D, P> gv;
+      if (own[v]) {
+        gv.load(a.gamma, idx[v]);
+      } else {
+        gv.clear();
+      }
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) gam[v][e] = D::get(gv, e);
+      for (int e = 0; e < EPV; ++e) gam[v][e] = gv.get(e);
     } else {
-      gam[v][0] = own[v] ? D::scalar(a.gamma, idx[v]) : 0.0f;
+      gam[v][0] = own[v] ? P::scalar(a.gamma, idx[v]) : 0.0f;
     }
   }
 
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void zero_kernel(float* a, float* b, int32_t N
 }
 
 // ------------------------------------------------------------------ fwd_generic
-template <bool LN, typename D>
+template <bool LN, typename D, typename P>
 __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a) {
   __shared__ float red[2 * kRowWaves * 2];
   int parity = 0;
@@ -289,10 +295,10 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
 #pragma unroll 4
     for (int j = tid; j < a.N; j += kRowBlock) {
       const float f = D::scalar(a.x, base + j);
-      const float gm = D::scalar(a.gamma, j);
+      const float gm = P::scalar(a.gamma, j);
       float o;
       if constexpr (LN) {
-        o = fmaf((f - mu) * r, gm, D::scalar(a.beta, j));
+        o = fmaf((f - mu) * r, gm, P::scalar(a.beta, j));
       } else {
         o = f * r * gm;
       }
@@ -304,54 +310,58 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
 }  // namespace
 
 // --------------------------------------------------------------------- launchers
-#define RN_DISPATCH_KD(kind, dtype, CALL)     \
-  do {                                        \
-    if (kind == 0 && dtype == 0) CALL(false, F32); \
-    if (kind == 0 && dtype == 1) CALL(false, BF16); \
-    if (kind == 1 && dtype == 0) CALL(true, F32);  \
-    if (kind == 1 && dtype == 1) CALL(true, BF16); \
+// (kind, type pair) -> CALL(LayerNorm?, activation type, parameter type).
+#define RN_DISPATCH_KT(kind, tc, CALL)                              \
+  do {                                                              \
+    const bool ln_ = kind == 1;                                     \
+    if (tc == kTcF32) { if (ln_) CALL(true, F32, F32) else CALL(false, F32, F32) }       \
+    if (tc == kTcBF16) { if (ln_) CALL(true, BF16, BF16) else CALL(false, BF16, BF16) }  \
+    if (tc == kTcF16) { if (ln_) CALL(true, F16, F16) else CALL(false, F16, F16) }       \
+    if (tc == kTcBF16F32) { if (ln_) CALL(true, BF16, F32) else CALL(false, BF16, F32) } \
+    if (tc == kTcF16F32) { if (ln_) CALL(true, F16, F32) else CALL(false, F16, F32) }    \
   } while (0)
 
-hipError_t launch_bwd_rowdot(int kind, int dtype, bool vec, const BwdArgs& a, int grid,
+hipError_t launch_bwd_rowdot(int kind, int tc, bool vec, const BwdArgs& a, int grid,
                              hipStream_t s) {
-#define RN_CALL(LN, D)                                                                    \
-  {                                                                                      \
-    if (vec) {                                                                           \
-      hipLaunchKernelGGL((rowdot_kernel<LN, D, true>), dim3(grid), dim3(kRowBlock), 0, s, a); \
-    } else {                                                                             \
-      hipLaunchKernelGGL((rowdot_kernel<LN, D, false>), dim3(grid), dim3(kRowBlock), 0, s, a); \
-    }                                                                                    \
-    return hipGetLastError();                                                            \
-  }
-  RN_DISPATCH_KD(kind, dtype, RN_CALL);
-#undef RN_CALL
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_bwd_colslice(int kind, int dtype, bool vec, const BwdArgs& a, int slices,
-                               int row_blocks, hipStream_t s) {
-  const dim3 grid(slices, row_blocks);
-#define RN_CALL(LN, D)                                                                       \
+#define RN_CALL(LN, D, P)                                                                    \
   {                                                                                         \
     if (vec) {                                                                              \
-      hipLaunchKernelGGL((colslice_kernel<LN, D, true>), grid, dim3(kSliceBlock), 0, s, a);  \
+      hipLaunchKernelGGL((rowdot_kernel<LN, D, P, true>), dim3(grid), dim3(kRowBlock), 0, s, a); \
     } else {                                                                                \
-      hipLaunchKernelGGL((colslice_kernel<LN, D, false>), grid, dim3(kSliceBlock), 0, s, a); \
+      hipLaunchKernelGGL((rowdot_kernel<LN, D, P, false>), dim3(grid), dim3(kRowBlock), 0, s,  \
+                         a);                                                                \
     }                                                                                       \
     return hipGetLastError();                                                               \
   }
-  RN_DISPATCH_KD(kind, dtype, RN_CALL);
+  RN_DISPATCH_KT(kind, tc, RN_CALL);
 #undef RN_CALL
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_generic(int kind, int dtype, const FwdArgs& a, int grid, hipStream_t s) {
-#define RN_CALL(LN, D)                                                                    \
-  {                                                                                      \
-    hipLaunchKernelGGL((fwd_generic_kernel<LN, D>), dim3(grid), dim3(kRowBlock), 0, s, a); \
-    return hipGetLastError();                                                            \
+hipError_t launch_bwd_colslice(int kind, int tc, bool vec, const BwdArgs& a, int slices,
+                               int row_blocks, hipStream_t s) {
+  const dim3 grid(slices, row_blocks);
+#define RN_CALL(LN, D, P)                                                                        \
+  {                                                                                             \
+    if (vec) {                                                                                  \
+      hipLaunchKernelGGL((colslice_kernel<LN, D, P, true>), grid, dim3(kSliceBlock), 0, s, a);   \
+    } else {                                                                                    \
+      hipLaunchKernelGGL((colslice_kernel<LN, D, P, false>), grid, dim3(kSliceBlock), 0, s, a);  \
+    }                                                                                           \
+    return hipGetLastError();                                                                   \
   }
-  RN_DISPATCH_KD(kind, dtype, RN_CALL);
+  RN_DISPATCH_KT(kind, tc, RN_CALL);
+#undef RN_CALL
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_generic(int kind, int tc, const FwdArgs& a, int grid, hipStream_t s) {
+#define RN_CALL(LN, D, P)                                                                    \
+  {                                                                                         \
+    hipLaunchKernelGGL((fwd_generic_kernel<LN, D, P>), dim3(grid), dim3(kRowBlock), 0, s, a); \
+    return hipGetLastError();                                                               \
+  }
+  RN_DISPATCH_KT(kind, tc, RN_CALL);
 #undef RN_CALL
   return hipErrorInvalidValue;
 }

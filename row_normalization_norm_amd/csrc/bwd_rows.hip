@@ -19,7 +19,7 @@
 // atomically adding every block's partial into one shared vector; the atomic variants
 // (per row, per workgroup) are kept for measurement only.
 //
-// Built once per (kind, dtype) from RN_KIND / RN_DTYPE on the command line.
+// Built once per (kind, type pair) from RN_KIND / RN_TC on the command line.
 #include <type_traits>
 
 #include "launch.h"
@@ -28,15 +28,16 @@
 #ifndef RN_KIND
 #error "RN_KIND must be defined"
 #endif
-#ifndef RN_DTYPE
-#error "RN_DTYPE must be defined"
+#ifndef RN_TC
+#error "RN_TC must be defined"
 #endif
 
 namespace rownorm {
 namespace {
 
-template <bool LN, typename D, int LPR, int VPL>
+template <bool LN, typename D, typename P, int LPR, int VPL>
 __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs a) {
+  using PV = Param<D, P>;
   constexpr int BLOCK = bwd_block(LPR);
   constexpr int EPV = D::kPerVec;
   constexpr int ROWS = BLOCK / LPR;
@@ -66,17 +67,22 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
   // for the shortest rows also unpacked to fp32.
   constexpr bool GREG = VPL <= 2;
   constexpr bool GUNP = GREG && VPL * EPV <= 16;
-  constexpr bool kBf16 = std::is_same<D, BF16>::value;
-  u32x4 greg[GREG ? VPL : 1];
+  // Sums of dy * gamma straight from packed 16-bit words (dy and gamma of one type).
+  constexpr bool kDot = !std::is_same<D, F32>::value && PV::kPacked;
+  PV greg[GREG ? VPL : 1];
   float gunp[GUNP ? VPL : 1][EPV];
   if constexpr (GREG) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
-      greg[v] = vi < nvec ? ld16(a.gamma, vi) : zero16();
+      if (vi < nvec) {
+        greg[v].load(a.gamma, vi);
+      } else {
+        greg[v].clear();
+      }
       if constexpr (GUNP) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) gunp[v][e] = D::get(greg[v], e);
+        for (int e = 0; e < EPV; ++e) gunp[v][e] = greg[v].get(e);
       }
     }
   }
@@ -105,7 +111,8 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     const bool row_ok = row < a.M;
     const int64_t vbase = row * nvec;
 
-    u32x4 xv[VPL], dv[VPL], gv[VPL];
+    u32x4 xv[VPL], dv[VPL];
+    PV gv[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
@@ -113,8 +120,10 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
       dv[v] = nd[v];
       if constexpr (GREG) {
         gv[v] = greg[v];
+      } else if (row_ok && vi < nvec) {
+        gv[v].load(a.gamma, vi);
       } else {
-        gv[v] = (row_ok && vi < nvec) ? ld16(a.gamma, vi) : zero16();
+        gv[v].clear();
       }
     }
     const float r = nr;
@@ -129,15 +138,15 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
-      // LayerNorm's sum of g = dy * gamma: for bf16 straight from the packed words.
-      if constexpr (LN && kBf16) s2 = D::dot(dv[v], gv[v], s2);
+      // LayerNorm's sum of g = dy * gamma: for 16-bit types straight from the packed words.
+      if constexpr (LN && kDot) s2 = D::dot(dv[v], gv[v].v, s2);
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
         const float xh = (D::get(xv[v], e) - mu) * r;
         const float d = D::get(dv[v], e);
-        const float g = d * (GUNP ? gunp[GUNP ? v : 0][e] : D::get(gv[v], e));
+        const float g = d * (GUNP ? gunp[GUNP ? v : 0][e] : gv[v].get(e));
         s1 = fmaf(g, xh, s1);
-        if constexpr (LN && !kBf16) s2 += g;
+        if constexpr (LN && !kDot) s2 += g;
         accg[v][e] = fmaf(d, xh, accg[v][e]);
         if constexpr (LN) accb[v][e] += d;
         if constexpr (KEEP) {
@@ -184,7 +193,7 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
             g = kg[v][e];
           } else {
             xh = (D::get_fresh(xv[v], e) - mu) * r;
-            g = D::get_fresh(dv[v], e) * D::get_fresh(gv[v], e);
+            g = D::get_fresh(dv[v], e) * gv[v].get_fresh(e);
           }
           o[e] = fmaf(g, r, fmaf(xh, nrc1, nrc2));
         }
@@ -262,10 +271,10 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
   }
 }
 
-template <bool LN, typename D, int LPR, int VPL>
+template <bool LN, typename D, typename P, int LPR, int VPL>
 hipError_t launch_one(const BwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_rows_kernel<LN, D, LPR, VPL>), dim3(grid), dim3(bwd_block(LPR)), 0, s,
-                     a);
+  hipLaunchKernelGGL((bwd_rows_kernel<LN, D, P, LPR, VPL>), dim3(grid), dim3(bwd_block(LPR)), 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -273,13 +282,14 @@ hipError_t launch_one(const BwdArgs& a, int grid, hipStream_t s) {
 
 #define RN_CAT_(a, b, c, d) a##b##c##d
 #define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
-#define RN_LAUNCHER RN_CAT(launch_bwd_rows_k, RN_KIND, _d, RN_DTYPE)
+#define RN_LAUNCHER RN_CAT(launch_bwd_rows_k, RN_KIND, _t, RN_TC)
 
 hipError_t RN_LAUNCHER(int lpr, int vpl, const BwdArgs& a, int grid, hipStream_t s) {
   constexpr bool kLN = RN_KIND == 1;
-  using D = typename std::conditional<RN_DTYPE == 1, BF16, F32>::type;
+  using D = Types<RN_TC>::D;
+  using P = Types<RN_TC>::P;
 #define RN_CASE(L, V) \
-  if (lpr == L && vpl == V) return launch_one<kLN, D, L, V>(a, grid, s);
+  if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, s);
   RN_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;

@@ -24,7 +24,7 @@
 // mean) with the pairwise-update formula of Chan, Golub and LeVeque, so the variance is
 // exact for constant rows and free of mean(x^2) - mean^2 cancellation.
 //
-// Built once per (kind, dtype) from RN_KIND / RN_DTYPE on the command line.
+// Built once per (kind, type pair) from RN_KIND / RN_TC on the command line.
 #include <type_traits>
 
 #include "launch.h"
@@ -33,8 +33,8 @@
 #ifndef RN_KIND
 #error "RN_KIND must be defined"
 #endif
-#ifndef RN_DTYPE
-#error "RN_DTYPE must be defined"
+#ifndef RN_TC
+#error "RN_TC must be defined"
 #endif
 
 namespace rownorm {
@@ -145,8 +145,9 @@ __device__ inline void gather_step(const ClusterArgs& c, int64_t step,
 // backward runs up to two steps ahead when its registers allow.
 
 // --------------------------------------------------------------------------- forward
-template <bool LN, typename D, int T, int VPL, int R>
+template <bool LN, typename D, typename P, int T, int VPL, int R>
 __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const ClusterArgs c) {
+  using PV = Param<D, P>;
   constexpr int EPV = D::kPerVec;
   constexpr int NW = T / 64;
   constexpr int K = (LN ? 2 : 1) * R;  // exchanged values per member and step
@@ -158,12 +159,17 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
   const int64_t nsteps = (a.M + R - 1) / R;
 
   bool own[VPL];
-  u32x4 g[VPL], b[LN ? VPL : 1];
+  PV g[VPL], b[LN ? VPL : 1];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     own[v] = v * T + tid < c.slice_vecs;
-    g[v] = own[v] ? ld16(a.gamma, vofs + v * T + tid) : zero16();
-    if constexpr (LN) b[v] = own[v] ? ld16(a.beta, vofs + v * T + tid) : zero16();
+    if (own[v]) {
+      g[v].load(a.gamma, vofs + v * T + tid);
+      if constexpr (LN) b[v].load(a.beta, vofs + v * T + tid);
+    } else {
+      g[v].clear();
+      if constexpr (LN) b[v].clear();
+    }
   }
 
   __shared__ float red[2 * NW * R];
@@ -281,9 +287,9 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
         for (int e = 0; e < EPV; ++e) {
           const float f = D::get_fresh(b0[i][v], e);
           if constexpr (LN) {
-            o[e] = fmaf((f - mu) * r, D::get_fresh(g[v], e), D::get_fresh(b[v], e));
+            o[e] = fmaf((f - mu) * r, g[v].get_fresh(e), b[v].get_fresh(e));
           } else {
-            o[e] = f * r * D::get_fresh(g[v], e);
+            o[e] = f * r * g[v].get_fresh(e);
           }
         }
         st16_stream(a.y, row * a.nvec + vofs + v * T + tid, D::pack(o));
@@ -300,12 +306,14 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
 }
 
 // -------------------------------------------------------------------------- backward
-template <bool LN, typename D, int T, int VPL, int R>
+template <bool LN, typename D, typename P, int T, int VPL, int R>
 __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const ClusterArgs c) {
+  using PV = Param<D, P>;
   constexpr int EPV = D::kPerVec;
   constexpr int NW = T / 64;
   constexpr int K = 2 * R;  // exchanged values per member and step: (sum g*xhat, sum g) x R
-  constexpr bool kBf16 = std::is_same<D, BF16>::value;
+  // Sums of dy * gamma straight from packed 16-bit words (dy and gamma of one type).
+  constexpr bool kDot = !std::is_same<D, F32>::value && PV::kPacked;
   const int tid = threadIdx.x;
   const int cl = blockIdx.x % c.nclusters;
   const int member = blockIdx.x / c.nclusters;
@@ -313,16 +321,20 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   const int64_t nsteps = (a.M + R - 1) / R;
 
   bool own[VPL];
-  u32x4 g[VPL];
+  PV g[VPL];
   float gf[VPL][EPV];  // gamma unpacked once: the slice is the same for every row
   float accg[VPL][EPV], accb[LN ? VPL : 1][EPV];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     own[v] = v * T + tid < c.slice_vecs;
-    g[v] = own[v] ? ld16(a.gamma, vofs + v * T + tid) : zero16();
+    if (own[v]) {
+      g[v].load(a.gamma, vofs + v * T + tid);
+    } else {
+      g[v].clear();
+    }
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      gf[v][e] = D::get(g[v], e);
+      gf[v][e] = g[v].get(e);
       accg[v][e] = 0.0f;
       if constexpr (LN) accb[v][e] = 0.0f;
     }
@@ -363,14 +375,14 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
       float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if constexpr (LN && kBf16) s2 = D::dot(sb.d[i][v], g[v], s2);
+        if constexpr (LN && kDot) s2 = D::dot(sb.d[i][v], g[v].v, s2);
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           const float xh = (D::get_fresh(sb.x[i][v], e) - mu) * r;
           const float d = D::get_fresh(sb.d[i][v], e);
           const float gg = d * gf[v][e];
           s1 = fmaf(gg, xh, s1);
-          if constexpr (LN && !kBf16) s2 += gg;
+          if constexpr (LN && !kDot) s2 += gg;
           accg[v][e] = fmaf(d, xh, accg[v][e]);
           if constexpr (LN) accb[v][e] += d;
         }
@@ -486,19 +498,20 @@ int occupancy(K kernel, int block) {
 
 #define RN_CAT_(a, b, c, d) a##b##c##d
 #define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
-#define RN_FWD_LAUNCHER RN_CAT(launch_fwd_cluster_k, RN_KIND, _d, RN_DTYPE)
-#define RN_BWD_LAUNCHER RN_CAT(launch_bwd_cluster_k, RN_KIND, _d, RN_DTYPE)
-#define RN_FWD_OCC RN_CAT(occupancy_fwd_cluster_k, RN_KIND, _d, RN_DTYPE)
-#define RN_BWD_OCC RN_CAT(occupancy_bwd_cluster_k, RN_KIND, _d, RN_DTYPE)
+#define RN_FWD_LAUNCHER RN_CAT(launch_fwd_cluster_k, RN_KIND, _t, RN_TC)
+#define RN_BWD_LAUNCHER RN_CAT(launch_bwd_cluster_k, RN_KIND, _t, RN_TC)
+#define RN_FWD_OCC RN_CAT(occupancy_fwd_cluster_k, RN_KIND, _t, RN_TC)
+#define RN_BWD_OCC RN_CAT(occupancy_bwd_cluster_k, RN_KIND, _t, RN_TC)
 
-using DT = std::conditional<RN_DTYPE == 1, BF16, F32>::type;
+using DT = Types<RN_TC>::D;
+using PT = Types<RN_TC>::P;
 constexpr bool kLN = RN_KIND == 1;
 
 hipError_t RN_FWD_LAUNCHER(int t, int vpl, int rows, const FwdArgs& a, const ClusterArgs& c, int grid,
                            hipStream_t s) {
 #define RN_CASE(T_, V_, R_)                                                              \
   if (t == T_ && vpl == V_ && rows == R_)                                                \
-    return launch_coop(fwd_cluster_kernel<kLN, DT, T_, V_, R_>, grid, T_, a, c, s);
+    return launch_coop(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, grid, T_, a, c, s);
   RN_CLUSTER_FWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;
@@ -508,7 +521,7 @@ hipError_t RN_BWD_LAUNCHER(int t, int vpl, int rows, const BwdArgs& a, const Clu
                            hipStream_t s) {
 #define RN_CASE(T_, V_, R_)                                                              \
   if (t == T_ && vpl == V_ && rows == R_)                                                \
-    return launch_coop(bwd_cluster_kernel<kLN, DT, T_, V_, R_>, grid, T_, a, c, s);
+    return launch_coop(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, grid, T_, a, c, s);
   RN_CLUSTER_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;
@@ -516,7 +529,7 @@ hipError_t RN_BWD_LAUNCHER(int t, int vpl, int rows, const BwdArgs& a, const Clu
 
 int RN_FWD_OCC(int t, int vpl, int rows) {
 #define RN_CASE(T_, V_, R_) \
-  if (t == T_ && vpl == V_ && rows == R_) return occupancy(fwd_cluster_kernel<kLN, DT, T_, V_, R_>, T_);
+  if (t == T_ && vpl == V_ && rows == R_) return occupancy(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, T_);
   RN_CLUSTER_FWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return 0;
@@ -524,7 +537,7 @@ int RN_FWD_OCC(int t, int vpl, int rows) {
 
 int RN_BWD_OCC(int t, int vpl, int rows) {
 #define RN_CASE(T_, V_, R_) \
-  if (t == T_ && vpl == V_ && rows == R_) return occupancy(bwd_cluster_kernel<kLN, DT, T_, V_, R_>, T_);
+  if (t == T_ && vpl == V_ && rows == R_) return occupancy(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, T_);
   RN_CLUSTER_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return 0;

@@ -19,8 +19,9 @@
 // takes row groups b, b + gridDim.x, ...  gamma (and beta) are loaded once per
 // workgroup and kept in registers when they fit.
 //
-// Built once per (kind, dtype): RN_KIND (0 RMSNorm, 1 LayerNorm) and RN_DTYPE
-// (0 fp32, 1 bf16) come from the compiler command line.
+// Built once per (kind, type pair): RN_KIND (0 RMSNorm, 1 LayerNorm) and RN_TC (the
+// activation/parameter type pair, TypeCombo in launch.h) come from the compiler command
+// line.
 #include <type_traits>
 
 #include "launch.h"
@@ -29,34 +30,41 @@
 #ifndef RN_KIND
 #error "RN_KIND must be defined"
 #endif
-#ifndef RN_DTYPE
-#error "RN_DTYPE must be defined"
+#ifndef RN_TC
+#error "RN_TC must be defined"
 #endif
 
 namespace rownorm {
 namespace {
 
-template <bool LN, typename D, int LPR, int VPL>
+template <bool LN, typename D, typename P, int LPR, int VPL>
 __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs a) {
   constexpr int BLOCK = fwd_block(LPR);
   constexpr int EPV = D::kPerVec;
   constexpr int ROWS = BLOCK / LPR;              // rows per workgroup per iteration
   constexpr int WPR = LPR > 64 ? LPR / 64 : 1;   // wavefronts per row
-  constexpr bool GREG = LN ? (VPL <= 4) : (VPL <= 8);  // gamma/beta kept in registers
+  using PV = Param<D, P>;
+  // gamma/beta kept in registers when they take at most 32 VGPRs
+  constexpr bool GREG = (PV::kPacked ? 4 : 8) * VPL * (LN ? 2 : 1) <= 32;
 
   const int tid = threadIdx.x;
   const int lane = tid % LPR;
   const int slot = tid / LPR;
   const int nvec = a.nvec;
 
-  u32x4 g[GREG ? VPL : 1];
-  u32x4 b[(GREG && LN) ? VPL : 1];
+  PV g[GREG ? VPL : 1];
+  PV b[(GREG && LN) ? VPL : 1];
   if constexpr (GREG) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
-      g[v] = vi < nvec ? ld16(a.gamma, vi) : zero16();
-      if constexpr (LN) b[v] = vi < nvec ? ld16(a.beta, vi) : zero16();
+      if (vi < nvec) {
+        g[v].load(a.gamma, vi);
+        if constexpr (LN) b[v].load(a.beta, vi);
+      } else {
+        g[v].clear();
+        if constexpr (LN) b[v].clear();
+      }
     }
   }
 
@@ -148,13 +156,13 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
       if (row_ok && vi < nvec) {
-        u32x4 gv, bv;
+        PV gv, bv;
         if constexpr (GREG) {
           gv = g[v];
           if constexpr (LN) bv = b[v];
         } else {
-          gv = ld16(a.gamma, vi);
-          if constexpr (LN) bv = ld16(a.beta, vi);
+          gv.load(a.gamma, vi);
+          if constexpr (LN) bv.load(a.beta, vi);
         }
         float o[EPV];
 #pragma unroll
@@ -163,9 +171,9 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
           // the packed words stay live across the reductions.
           if constexpr (LN) {
             const float d = KEEP ? dev[KEEP ? v : 0][e] : D::get_fresh(xv[v], e) - mu;
-            o[e] = fmaf(d * r, D::get_fresh(gv, e), D::get_fresh(bv, e));
+            o[e] = fmaf(d * r, gv.get_fresh(e), bv.get_fresh(e));
           } else {
-            o[e] = D::get_fresh(xv[v], e) * r * D::get_fresh(gv, e);
+            o[e] = D::get_fresh(xv[v], e) * r * gv.get_fresh(e);
           }
         }
         st16_stream(a.y, vbase + vi, D::pack(o));
@@ -174,10 +182,10 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
   }
 }
 
-template <bool LN, typename D, int LPR, int VPL>
+template <bool LN, typename D, typename P, int LPR, int VPL>
 hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_rows_kernel<LN, D, LPR, VPL>), dim3(grid), dim3(fwd_block(LPR)), 0, s,
-                     a);
+  hipLaunchKernelGGL((fwd_rows_kernel<LN, D, P, LPR, VPL>), dim3(grid), dim3(fwd_block(LPR)), 0,
+                     s, a);
   return hipGetLastError();
 }
 
@@ -185,13 +193,14 @@ hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t s) {
 
 #define RN_CAT_(a, b, c, d) a##b##c##d
 #define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
-#define RN_LAUNCHER RN_CAT(launch_fwd_rows_k, RN_KIND, _d, RN_DTYPE)
+#define RN_LAUNCHER RN_CAT(launch_fwd_rows_k, RN_KIND, _t, RN_TC)
 
 hipError_t RN_LAUNCHER(int lpr, int vpl, const FwdArgs& a, int grid, hipStream_t s) {
   constexpr bool kLN = RN_KIND == 1;
-  using D = typename std::conditional<RN_DTYPE == 1, BF16, F32>::type;
+  using D = Types<RN_TC>::D;
+  using P = Types<RN_TC>::P;
 #define RN_CASE(L, V) \
-  if (lpr == L && vpl == V) return launch_one<kLN, D, L, V>(a, grid, s);
+  if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, s);
   RN_FWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;

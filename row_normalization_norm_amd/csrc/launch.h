@@ -7,6 +7,20 @@
 
 namespace rownorm {
 
+// ------------------------------------------------------------- element types
+// Activations (x, y, dy, dx) and parameters (gamma, beta) may differ in type; these are
+// the supported pairs, each built as its own set of kernels.  The public dtype code
+// (rownorm.h) maps onto them in api.cpp.
+enum TypeCombo {
+  kTcF32 = 0,     // fp32 activations, fp32 parameters
+  kTcBF16 = 1,    // bf16, bf16
+  kTcF16 = 2,     // fp16, fp16
+  kTcBF16F32 = 3, // bf16 activations, fp32 parameters
+  kTcF16F32 = 4,  // fp16 activations, fp32 parameters
+};
+constexpr int kNumTypeCombos = 5;
+constexpr bool tc_is16(int tc) { return tc != kTcF32; }  // 16-bit activations
+
 // ------------------------------------------------------------ compiled mappings
 // (lanes per row, 16-byte vectors per lane).  8..64 lanes: several rows per
 // wavefront (a row is one aligned lane group); 128..1024 lanes: one row spans
@@ -15,11 +29,11 @@ namespace rownorm {
   X(8, 1) X(8, 2) X(8, 3) X(8, 4) X(8, 6) X(8, 8)                                      \
   X(16, 1) X(16, 2) X(16, 3) X(16, 4) X(16, 6) X(16, 8)                                \
   X(32, 1) X(32, 2) X(32, 3) X(32, 4) X(32, 6) X(32, 8)                                \
-  X(64, 1) X(64, 2) X(64, 3) X(64, 4) X(64, 6) X(64, 8) X(64, 12) X(64, 16)            \
-  X(128, 2) X(128, 3) X(128, 4) X(128, 6) X(128, 8) X(128, 12) X(128, 16)              \
-  X(256, 2) X(256, 3) X(256, 4) X(256, 6) X(256, 8) X(256, 12) X(256, 16)              \
-  X(512, 2) X(512, 3) X(512, 4) X(512, 6) X(512, 8) X(512, 12) X(512, 16)              \
-  X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 6) X(1024, 8) X(1024, 12) X(1024, 16)
+  X(64, 1) X(64, 2) X(64, 3) X(64, 4) X(64, 6) X(64, 8)                                \
+  X(128, 2) X(128, 3) X(128, 4) X(128, 6) X(128, 8)                                    \
+  X(256, 2) X(256, 3) X(256, 4) X(256, 6) X(256, 8)                                    \
+  X(512, 2) X(512, 3) X(512, 4) X(512, 6) X(512, 8)                                    \
+  X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 6) X(1024, 8)
 
 // The backward keeps x, dy and per-column fp32 partials of dgamma (and dbeta) in
 // registers; beyond 4 vectors per lane (1 at 1024 lanes, where a lane may use at
@@ -112,27 +126,27 @@ struct ClusterArgs {
 };
 
 // ------------------------------------------------------------------ launchers
-// kind: 0 = RMSNorm, 1 = LayerNorm.  dtype: 0 = fp32, 1 = bf16.  Each returns
-// hipErrorInvalidValue when the (lpr, vpl) mapping is not compiled.
-hipError_t launch_fwd_rows(int kind, int dtype, int lpr, int vpl, const FwdArgs& a, int grid,
+// kind: 0 = RMSNorm, 1 = LayerNorm.  tc: the activation/parameter type pair
+// (TypeCombo).  Each returns hipErrorInvalidValue when the mapping is not compiled.
+hipError_t launch_fwd_rows(int kind, int tc, int lpr, int vpl, const FwdArgs& a, int grid,
                            hipStream_t s);
-hipError_t launch_bwd_rows(int kind, int dtype, int lpr, int vpl, const BwdArgs& a, int grid,
+hipError_t launch_bwd_rows(int kind, int tc, int lpr, int vpl, const BwdArgs& a, int grid,
                            hipStream_t s);
 // SPLIT path (16-byte vectors): per-row reduction, then the column-sliced pass on a
 // (slices, row_blocks) grid.
-hipError_t launch_bwd_rowdot(int kind, int dtype, bool vec, const BwdArgs& a, int grid,
+hipError_t launch_bwd_rowdot(int kind, int tc, bool vec, const BwdArgs& a, int grid,
                              hipStream_t s);
-hipError_t launch_bwd_colslice(int kind, int dtype, bool vec, const BwdArgs& a, int slices,
+hipError_t launch_bwd_colslice(int kind, int tc, bool vec, const BwdArgs& a, int slices,
                                int row_blocks, hipStream_t s);
 // Split-row kernels (cooperative launch) and their occupancy (workgroups per CU).
-hipError_t launch_fwd_cluster(int kind, int dtype, int t, int vpl, int rows, const FwdArgs& a,
+hipError_t launch_fwd_cluster(int kind, int tc, int t, int vpl, int rows, const FwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s);
-hipError_t launch_bwd_cluster(int kind, int dtype, int t, int vpl, int rows, const BwdArgs& a,
+hipError_t launch_bwd_cluster(int kind, int tc, int t, int vpl, int rows, const BwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s);
-int occupancy_fwd_cluster(int kind, int dtype, int t, int vpl, int rows);
-int occupancy_bwd_cluster(int kind, int dtype, int t, int vpl, int rows);
+int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows);
+int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows);
 // GENERIC forward (scalar loads).
-hipError_t launch_fwd_generic(int kind, int dtype, const FwdArgs& a, int grid, hipStream_t s);
+hipError_t launch_fwd_generic(int kind, int tc, const FwdArgs& a, int grid, hipStream_t s);
 // Column reduce: out[j] = sum_p part[p*N + j] for dgamma (and dbeta if part_b).
 hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P, int32_t N,
                             float* dgamma, float* dbeta, hipStream_t s);

@@ -48,9 +48,8 @@ constexpr int kBwdGrid = 256;
 int fwd_target_vpl(int64_t nvec) { return nvec < 1024 ? 4 : 2; }
 int bwd_target_vpl(int64_t nvec) { return nvec <= 128 ? 2 : nvec <= 256 ? 1 : 4; }
 // Longest row (in 16-byte vectors) the forward keeps in one workgroup before splitting it
-// over a cluster; fp32 RMSNorm (no beta, 4 elements per vector) stays resident longer.
+// over a cluster (1024 lanes x 8 vectors; wider mappings spill).
 constexpr int64_t kFwdRowsMaxVecs = 8192;
-constexpr int64_t kFwdRowsMaxVecsF32Rms = 16384;
 constexpr int64_t kBwdRowsMaxVecs = 2048;  // same for the backward
 // Vectors per lane of the cluster kernels: beyond these the kernels need more than the
 // 128 VGPRs a 1024-thread workgroup may use (the backward also holds the per-column
@@ -179,7 +178,7 @@ bool plan_cluster(bool backward, bool layernorm, int64_t M, int64_t N, int64_t n
   const int max_vpl = backward ? kClusterBwdMaxVpl : kClusterFwdMaxVpl;
   const int rows = o.cluster_rows ? o.cluster_rows
                    : !backward               ? kClusterFwdRows
-                   : dtype == NORM_DTYPE_BF16 ? kClusterBwdRowsBf16
+                   : dtype != NORM_DTYPE_F32 ? kClusterBwdRowsBf16
                                               : kClusterBwdRowsF32;
   // The compiled (threads, vectors) pairs for this rows-per-step.
   Mapping list[32];
@@ -264,7 +263,7 @@ void plan_generic_fwd(int64_t M, const norm_options_t& o, Plan& p) {
 const TunedPlan* find_tuned(bool backward, bool layernorm, int dtype, int64_t nvec) {
   for (const TunedPlan& t : kTunedPlans) {
     if (t.backward == int(backward) && t.layernorm == int(layernorm) &&
-        t.bf16 == int(dtype == NORM_DTYPE_BF16) && t.nvec == nvec)
+        t.bf16 == int(dtype != NORM_DTYPE_F32) && t.nvec == nvec)
       return &t;
   }
   return nullptr;
@@ -284,7 +283,7 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
   const bool atomic = backward && o.dgamma_mode != NORM_DGAMMA_TWO_STAGE;
 
   Plan p;
-  const int epv = dtype == NORM_DTYPE_BF16 ? 8 : 4;
+  const int epv = dtype != NORM_DTYPE_F32 ? 8 : 4;
   const bool vec_ok = aligned16 && (N % epv == 0);
   const int64_t nvec = vec_ok ? N / epv : 0;
   p.nvec = int(nvec);
@@ -319,9 +318,7 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
           plan_generic_fwd(M, o, p);
         }
       } else if (atomic ||
-                 nvec <= (backward                                    ? kBwdRowsMaxVecs
-                          : (dtype == NORM_DTYPE_F32 && !layernorm) ? kFwdRowsMaxVecsF32Rms
-                                                                    : kFwdRowsMaxVecs)) {
+                 nvec <= (backward ? kBwdRowsMaxVecs : kFwdRowsMaxVecs)) {
         ok = plan_rows(backward, layernorm, M, N, nvec, o, atomic, p);
       } else if (!plan_cluster(backward, layernorm, M, N, nvec, dtype, o, p)) {
         if (backward) {
@@ -371,7 +368,7 @@ norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64
                                  Plan* out) {
   norm_options_t o = {};
   Plan p;
-  const int epv = dtype == NORM_DTYPE_BF16 ? 8 : 4;
+  const int epv = dtype != NORM_DTYPE_F32 ? 8 : 4;
   p.nvec = int(N / epv);
   if (backward) {
     plan_split(layernorm, M, N, p.nvec, true, o, p);

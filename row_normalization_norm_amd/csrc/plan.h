@@ -37,7 +37,9 @@ struct Plan {
   size_t off_xchg = 0, off_status = 0, xchg_bytes = 0;
 };
 
-// Returns NORM_OK or NORM_ERR_BAD_OPTION.  Shapes and dtype must already be valid.
+// Returns NORM_OK or NORM_ERR_BAD_OPTION.  Shapes and dtype must already be valid; dtype
+// here is the activation type (NORM_DTYPE_F32, _BF16 or _F16): the plan depends only on
+// the activations' element size.
 norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
                         bool aligned16, const norm_options_t* opt, Plan* out);
 

@@ -3,6 +3,8 @@
 //  * 16-byte vector loads and stores (one global_load/store_dwordx4 per lane);
 //  * bf16 <-> fp32: widening is exact (bf16 bits are the top half of an fp32);
 //    narrowing uses v_cvt_pk_bf16_f32 (round to nearest even, NaN stays NaN);
+//  * fp16 <-> fp32: widening is exact (v_cvt_f32_f16, or folded into v_fma_mix_f32 by
+//    the compiler); narrowing uses v_cvt_pk_f16_f32 (round to nearest even);
 //  * sums over aligned groups of 2..64 lanes with DPP (quad_perm, row_half_mirror,
 //    row_mirror) inside a 16-lane row and lane shuffles across rows.  Every lane of a
 //    group ends with the same bits, because each step adds the same two operands.
@@ -11,11 +13,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace rownorm {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------- element types
 struct F32 {
@@ -125,6 +130,84 @@ struct BF16 {
   }
 };
 
+struct F16 {
+  static constexpr int kBytes = 2;
+  static constexpr int kPerVec = 8;
+  // Element e of the vector lives in 32-bit word e/2: low half for even e.
+  __device__ static inline float get(const u32x4& v, int e) {
+    const uint32_t w = v[e >> 1];
+    return static_cast<float>(
+        __builtin_bit_cast(_Float16, static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xFFFFu))));
+  }
+  // Same value as get(), through an opaque instruction (see BF16::get_fresh).
+  __device__ static inline float get_fresh(const u32x4& v, int e) {
+    const uint32_t w = v[e >> 1];
+    float r;
+    if (e & 1) {
+      asm volatile("v_cvt_f32_f16_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1"
+                   : "=v"(r)
+                   : "v"(w));
+    } else {
+      asm volatile("v_cvt_f32_f16 %0, %1" : "=v"(r) : "v"(w));
+    }
+    return r;
+  }
+  __device__ static inline float scalar(const void* p, int64_t i) {
+    return static_cast<float>(static_cast<const _Float16*>(p)[i]);
+  }
+  __device__ static inline void put_scalar(void* p, int64_t i, float f) {
+    static_cast<_Float16*>(p)[i] = static_cast<_Float16>(f);
+  }
+  __device__ static inline f16x2 word(const u32x4& v, int w) {
+    const uint32_t u = v[w];
+    f16x2 h;
+    __builtin_memcpy(&h, &u, sizeof(h));
+    return h;
+  }
+  // Sum, sum of squares and dot product from the packed words (v_dot2_f32_f16: two exact
+  // fp16 products added to an fp32 accumulator).
+  __device__ static inline float sum(const u32x4& v, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = __builtin_amdgcn_fdot2(word(v, w), one, acc, false);
+    return acc;
+  }
+  __device__ static inline float sumsq(const u32x4& v, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const f16x2 h = word(v, w);
+      acc = __builtin_amdgcn_fdot2(h, h, acc, false);
+    }
+    return acc;
+  }
+  __device__ static inline float dot(const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) acc = __builtin_amdgcn_fdot2(word(a, w), word(b, w), acc, false);
+    return acc;
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    f32x2 f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+  }
+  __device__ static inline u32x4 pack(const float (&f)[8]) {
+    u32x4 r;
+    r[0] = pack2(f[0], f[1]);
+    r[1] = pack2(f[2], f[3]);
+    r[2] = pack2(f[4], f[5]);
+    r[3] = pack2(f[6], f[7]);
+    return r;
+  }
+};
+
+// The (activation, parameter) type pairs the kernels are built for, numbered as in
+// launch.h's TypeCombo: fp32/fp32, bf16/bf16, fp16/fp16, bf16/fp32, fp16/fp32.
+template <int TC> struct Types;
+template <> struct Types<0> { using D = F32; using P = F32; };
+template <> struct Types<1> { using D = BF16; using P = BF16; };
+template <> struct Types<2> { using D = F16; using P = F16; };
+template <> struct Types<3> { using D = BF16; using P = F32; };
+template <> struct Types<4> { using D = F16; using P = F32; };
+
 // ------------------------------------------------------------------ vector memory
 __device__ inline u32x4 ld16(const void* base, int64_t vec_index) {
   return static_cast<const u32x4*>(base)[vec_index];
@@ -144,6 +227,41 @@ __device__ inline u32x4 zero16() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return z;
 }
+
+// ------------------------------------------------------------- gamma and beta
+// The EPV parameters (gamma or beta) that go with one 16-byte vector of activations of
+// type D, stored as type P: one 16-byte vector when P is D, two when fp32 parameters go
+// with 16-bit activations (EPV = 8).
+template <typename D, typename P, bool kSame = std::is_same<D, P>::value>
+struct Param;
+
+template <typename D, typename P>
+struct Param<D, P, true> {
+  static constexpr bool kPacked = true;  // the same packing as the activations
+  u32x4 v;
+  __device__ inline void load(const void* base, int64_t vi) { v = ld16(base, vi); }
+  __device__ inline void clear() { v = zero16(); }
+  __device__ inline float get(int e) const { return D::get(v, e); }
+  __device__ inline float get_fresh(int e) const { return D::get_fresh(v, e); }
+};
+
+template <typename D, typename P>
+struct Param<D, P, false> {
+  static_assert(std::is_same<P, F32>::value && D::kPerVec == 8,
+                "mixed precision pairs 16-bit activations with fp32 parameters");
+  static constexpr bool kPacked = false;
+  u32x4 v[2];
+  __device__ inline void load(const void* base, int64_t vi) {
+    v[0] = ld16(base, 2 * vi);
+    v[1] = ld16(base, 2 * vi + 1);
+  }
+  __device__ inline void clear() {
+    v[0] = zero16();
+    v[1] = zero16();
+  }
+  __device__ inline float get(int e) const { return __uint_as_float(v[e >> 2][e & 3]); }
+  __device__ inline float get_fresh(int e) const { return get(e); }
+};
 
 // ------------------------------------------------------------------- reductions
 // DPP control codes (GFX9): quad_perm selectors, and the row mirrors.

@@ -156,10 +156,13 @@ def sweep(out_path, ns=SWEEP_N):
 def table(jsonl_paths):
     """C++ header with the fastest candidate per (direction, kind, dtype, row length)."""
     best = {}
+    compiled = {"fwd": set(mappings("fwd")), "bwd": set(mappings("bwd"))}
     for p in jsonl_paths:
         with open(p) as f:
             for line in f:
                 r = json.loads(line)
+                if r.get("path", 1) == 1 and (r["lpr"], r["vpl"]) not in compiled[r["dir"]]:
+                    continue  # a mapping no longer built
                 nvec = r.get("nvec") or r["N"] // (8 if r["dtype"] == "bf16" else 4)
                 key = (r["dir"] == "bwd", r["kind"] == "ln", r["dtype"] == "bf16", nvec)
                 if key not in best or r["GBs"] > best[key][1]["GBs"]:

@@ -13,7 +13,9 @@ What pins what:
   * central finite differences of the forward for dx, dgamma, dbeta;
   * torch.nn.functional.rms_norm / layer_norm with autograd in float64 on the CPU, an
     independent library implementation;
-  * consistency of the bf16 decode and of row selection.
+  * consistency of the bf16 decode and of row selection;
+  * the binary16 decode against numpy's float16 (an independent implementation), and
+    fp16 / mixed-precision inputs against the same values widened to fp32.
 """
 from __future__ import annotations
 
@@ -274,6 +276,57 @@ def pin_bf16_decode_and_rows(orc):
     assert np.max(np.abs(dg_all - (dg_a + dg_b))) < 1e-12, "dgamma is not a sum over rows"
 
 
+def pin_f16_decode(orc):
+    """binary16 bits decode to numpy's float16 values: LayerNorm of the two-element row
+    [h, 0] has mean h/2 exactly.  Normals, subnormals, the largest finite value, signed
+    zero and negative values."""
+    bits = np.array([0x3C00, 0xC000, 0x7BFF, 0x0400, 0x03FF, 0x0001, 0x8001, 0x3555, 0x0000,
+                     0x8000, 0x4248, 0xFBFF, 0x1234, 0x5678, 0x2E66], dtype=np.uint16)
+    h = bits.view(np.float16)
+    x = np.stack([h, np.zeros_like(h)], axis=1)
+    g = np.ones(2, np.float16)
+    b = np.zeros(2, np.float16)
+    _, mean, _ = orc.ln_fwd(x, g, b, 1e-5)
+    want = h.astype(np.float64) / 2.0
+    assert np.array_equal(mean, want), f"fp16 decode: {mean} vs {want}"
+
+
+def pin_f16_and_mixed_params(orc):
+    """fp16 activations, and bf16 / fp16 activations with fp32 gamma and beta, give the
+    results of the same values widened exactly to fp32 (the oracle works in double from
+    the decoded values, so any mix-up of which buffer has which type shows)."""
+    M, N = 6, 24
+    rng = np.random.default_rng(311)
+    for act in ("bf16", "f16"):
+        xv = (rng.standard_normal((M, N)) * 1.7 + 0.3).astype(np.float32)
+        dyv = rng.standard_normal((M, N)).astype(np.float32)
+        x = gen.round_to(xv, act)
+        dy = gen.round_to(dyv, act)
+        # fp32 parameters that are not representable in the 16-bit type
+        g32 = (1.0 + 0.1 * rng.standard_normal(N)).astype(np.float32) + np.float32(2.0 ** -13)
+        b32 = (0.1 * rng.standard_normal(N)).astype(np.float32) + np.float32(2.0 ** -14)
+        wide = (lambda a: gen.bf16_to_f32(a)) if act == "bf16" else (lambda a: a.astype(np.float32))
+        xf, dyf = wide(x), wide(dy)
+        for eps in (1e-5, 0.0):
+            got = orc.ln_fwd(x, g32, b32, eps)
+            want = orc.ln_fwd(xf, g32, b32, eps)
+            for a, w in zip(got, want):
+                assert np.array_equal(a, w), f"{act}+f32 LayerNorm forward"
+            got = orc.rms_fwd(x, g32, eps)
+            want = orc.rms_fwd(xf, g32, eps)
+            for a, w in zip(got, want):
+                assert np.array_equal(a, w), f"{act}+f32 RMSNorm forward"
+            assert np.array_equal(orc.ln_bwd_dx(dy, x, g32, eps), orc.ln_bwd_dx(dyf, xf, g32, eps))
+            assert np.array_equal(orc.rms_bwd_dx(dy, x, g32, eps),
+                                  orc.rms_bwd_dx(dyf, xf, g32, eps))
+        # same-type parameters: fp16 gamma equals its fp32 widening
+        g16 = gen.round_to(g32, act)
+        assert np.array_equal(orc.rms_fwd(x, g16, 1e-6)[0], orc.rms_fwd(xf, wide(g16), 1e-6)[0])
+        dg, _ = orc.rms_dgamma(dy, x, 1e-6)
+        dgf, _ = orc.rms_dgamma(dyf, xf, 1e-6)
+        assert np.array_equal(dg, dgf), f"{act} dgamma decode"
+
+
 ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_rms_unit_rms, pin_ln_moments,
             pin_invariance, pin_dx_orthogonality, pin_finite_differences, pin_torch_float64,
-            pin_bf16_decode_and_rows]
+            pin_bf16_decode_and_rows, pin_f16_decode, pin_f16_and_mixed_params]

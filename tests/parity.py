@@ -2,6 +2,8 @@
 
 Tolerances (the GPU result against the fp64 oracle, per element):
   * bf16 y / dx:   |gpu - ref| <= 2^-7 * max(1, |ref|)
+  * fp16 y / dx:   |gpu - ref| <= 2^-10 * max(1, |ref|): the bf16 rule carried over to
+                   binary16 (two half-units in the last place of its 11-bit significand)
   * fp32 y:        |gpu - ref| <= 1e-5 * max(1, |ref|)
   * fp32 dx:       |gpu - ref| <= 1e-5 * max(1, |ref|, rstd*(|g| + |c2| + |xhat*c1|)):
                    dx is a difference and can cancel (for N = 1, RMSNorm's dx is
@@ -26,6 +28,7 @@ import oracle
 import row_normalization_norm_amd as rn
 
 TOL_BF16 = 2.0 ** -7
+TOL_F16 = 2.0 ** -10
 TOL_F32 = 1e-5
 TOL_STAT = 1e-5
 TOL_DGAMMA = 1e-4
@@ -33,9 +36,13 @@ TOL_DGAMMA = 1e-4
 
 # ------------------------------------------------------------------ host <-> device
 def to_device(a: np.ndarray, dtype: str, device):
+    """Host bits (uint16 bf16, float16, float32) -> device tensor, bit-exact."""
     import torch
-    if dtype == "bf16":
-        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    elif a.dtype == np.float16:
+        t = torch.from_numpy(a)
     else:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return t.to(device)
@@ -88,8 +95,8 @@ class GpuRun:
         else:
             self.x = to_device(inputs["x"], w.dtype, device)
             self.dy = to_device(inputs["dy"], w.dtype, device)
-        self.gamma = to_device(inputs["gamma"], w.dtype, device)
-        self.beta = to_device(inputs["beta"], w.dtype, device) if w.kind == "ln" else None
+        self.gamma = to_device(inputs["gamma"], w.param_dtype, device)
+        self.beta = to_device(inputs["beta"], w.param_dtype, device) if w.kind == "ln" else None
         self.y = torch.empty_like(self.x)
         self.dx = torch.empty_like(self.x)
         self.mean = torch.empty(M, dtype=torch.float32, device=device) if w.kind == "ln" else None
@@ -139,7 +146,7 @@ def _check(name, got, ref, tol, floor=1.0, scale=None):
 
 
 def out_tol(dtype: str) -> float:
-    return TOL_BF16 if dtype == "bf16" else TOL_F32
+    return {"bf16": TOL_BF16, "f16": TOL_F16}.get(dtype, TOL_F32)
 
 
 def check_forward(run: GpuRun, inputs: dict, rows, orc=None):

@@ -13,7 +13,7 @@ import row_normalization_norm_amd as rn
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rownorm.h")
 
-BF16, F32 = rn.NORM_DTYPE_BF16, rn.NORM_DTYPE_F32
+BF16, F32, F16 = rn.NORM_DTYPE_BF16, rn.NORM_DTYPE_F32, rn.NORM_DTYPE_F16
 A = 0x10000  # a 16-byte-aligned fake address: only ever passed to calls that fail validation
 
 
@@ -105,6 +105,19 @@ def ln_bwd(**kw):
     (ln_bwd, dict(dbeta=None), rn.NORM_ERR_NULL_PTR),
     (ln_bwd, dict(dbeta=A + 1), rn.NORM_ERR_MISALIGNED),
     (ln_bwd, dict(ws_bytes=0), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
+    # type pairs: 16-bit activations may take fp32 gamma/beta; nothing else mixes
+    (rms_fwd, dict(dtype=rn.dtype_mixed(F32, BF16)), rn.NORM_ERR_BAD_DTYPE),
+    (rms_fwd, dict(dtype=rn.dtype_mixed(BF16, F16)), rn.NORM_ERR_BAD_DTYPE),
+    (rms_fwd, dict(dtype=rn.dtype_mixed(F16, BF16)), rn.NORM_ERR_BAD_DTYPE),
+    (rms_fwd, dict(dtype=rn.dtype_mixed(BF16, 3)), rn.NORM_ERR_BAD_DTYPE),
+    (rms_fwd, dict(dtype=3), rn.NORM_ERR_BAD_DTYPE),
+    (rms_fwd, dict(dtype=BF16 | (1 << 16)), rn.NORM_ERR_BAD_DTYPE),
+    (ln_bwd, dict(dtype=rn.dtype_mixed(F32, F16)), rn.NORM_ERR_BAD_DTYPE),
+    # fp32 parameters need 4-byte alignment even with 2-byte activations
+    (rms_fwd, dict(dtype=rn.dtype_mixed(BF16, F32), gamma=A + 2), rn.NORM_ERR_MISALIGNED),
+    (ln_fwd, dict(dtype=rn.dtype_mixed(F16, F32), beta=A + 2), rn.NORM_ERR_MISALIGNED),
+    (ln_bwd, dict(dtype=rn.dtype_mixed(F16, F32), gamma=A + 2), rn.NORM_ERR_MISALIGNED),
+    (rms_fwd, dict(dtype=F16, x=A + 1), rn.NORM_ERR_MISALIGNED),
 ])
 def test_validation_rejects(call, kw, status):
     assert call(**kw) == status
@@ -213,3 +226,18 @@ def test_cluster_plans():
     assert rn.norm_plan(False, True, 8192, 16384, BF16).path == rn.NORM_PATH_ROWS
     assert rn.norm_plan(True, True, 16384, 8192, BF16).path == rn.NORM_PATH_ROWS
     assert rn.norm_fwd_workspace_size(65536, 4096, True, BF16) == 0
+
+
+def test_type_pairs_plan_like_their_activations():
+    """The plan and the workspace depend on the activations' element size only: fp16 plans
+    like bf16, and fp32 gamma/beta beside 16-bit activations change neither."""
+    for bwd in (False, True):
+        for ln in (False, True):
+            for M, N in ((4096, 1024), (65536, 4096), (262144, 384), (2048, 131072), (77, 1000)):
+                ref = rn.norm_plan(bwd, ln, M, N, BF16)
+                for code in (F16, rn.dtype_mixed(BF16, F32), rn.dtype_mixed(F16, F32)):
+                    p = rn.norm_plan(bwd, ln, M, N, code)
+                    assert (p.path, p.lanes_per_row, p.vecs_per_lane, p.grid, p.cluster_size) == \
+                        (ref.path, ref.lanes_per_row, ref.vecs_per_lane, ref.grid, ref.cluster_size)
+                    size = rn.norm_bwd_workspace_size if bwd else rn.norm_fwd_workspace_size
+                    assert size(M, N, ln, code) == size(M, N, ln, BF16)

@@ -1,4 +1,5 @@
-"""The seeded input generator: determinism, prefix stability, distributions, bf16 rounding."""
+"""The seeded input generator: determinism, prefix stability, distributions, bf16 and fp16
+rounding, parameter types."""
 import numpy as np
 
 import gen
@@ -36,6 +37,40 @@ def test_round_bf16_nearest_even():
     assert np.array_equal(got, want)
     nan = gen.round_bf16(np.array([np.nan], dtype=np.float32))
     assert np.isnan(gen.bf16_to_f32(nan))[0]
+
+
+def test_f16_is_rounded_f32():
+    f = gen.fill(1 << 16, "f32", 7, 1.0, 0.1)
+    h = gen.fill(1 << 16, "f16", 7, 1.0, 0.1)
+    assert h.dtype == np.float16
+    assert np.array_equal(h.view(np.uint16), gen.round_f16(f).view(np.uint16))
+
+
+def test_round_f16_matches_numpy():
+    """The binary16 encoder against numpy's float32 -> float16 conversion (IEEE round to
+    nearest even): normals over many decades, subnormals, ties, overflow, signed zeros."""
+    rng = np.random.default_rng(0)
+    scale = np.float32(10.0) ** rng.integers(-9, 6, 200000).astype(np.float32)
+    vals = np.concatenate([
+        rng.standard_normal(200000).astype(np.float32) * scale,
+        np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.99, 65520.0, 65536.0, 2.0 ** -14,
+                  2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -25, 2.0 ** -26, 1 - 2.0 ** -12,
+                  1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, -(2.0 ** -15) * 1.5], dtype=np.float32)])
+    with np.errstate(over="ignore"):
+        want = vals.astype(np.float16)
+    assert np.array_equal(gen.round_f16(vals).view(np.uint16), want.view(np.uint16))
+    assert np.isnan(gen.round_f16(np.array([np.nan], dtype=np.float32)))[0]
+
+
+def test_mixed_parameter_type():
+    w = gen.Workload("t", "ln", "bf16", 4, 64, 1e-5, config=9, pdtype="f32")
+    d = gen.make_inputs(w)
+    assert d["x"].dtype == np.uint16 and d["gamma"].dtype == np.float32
+    assert d["beta"].dtype == np.float32
+    # the same seeds in bf16 round the fp32 parameters
+    same = gen.make_inputs(gen.Workload("t", "ln", "bf16", 4, 64, 1e-5, config=9))
+    assert np.array_equal(same["gamma"], gen.round_bf16(d["gamma"]))
+    assert np.array_equal(same["x"], d["x"])
 
 
 def test_outlier_mask():

@@ -17,19 +17,31 @@ SMALL_N = (1, 7, 64, 100, 256, 384, 512, 768, 1000, 1024, 2048, 4095, 4096, 8192
            65536, 131072)
 
 
-def small_workload(kind, dtype, N, M=None, eps=1e-6, x_mean=0.0, x_std=1.0):
+# (activation type, parameter type or None for the same): the configurations' bf16 and
+# fp32, fp16, and 16-bit activations with fp32 gamma/beta.
+PAIRS = [("bf16", None), ("f32", None), ("f16", None), ("bf16", "f32"), ("f16", "f32")]
+PAIR_IDS = ["bf16", "f32", "f16", "bf16+f32", "f16+f32"]
+_CODE = {"f32": rn.NORM_DTYPE_F32, "bf16": rn.NORM_DTYPE_BF16, "f16": rn.NORM_DTYPE_F16}
+
+
+def dtype_code(dtype, pdtype=None):
+    return rn.dtype_mixed(_CODE[dtype], _CODE[pdtype]) if pdtype else _CODE[dtype]
+
+
+def small_workload(kind, dtype, N, M=None, eps=1e-6, x_mean=0.0, x_std=1.0, pdtype=None):
     if M is None:
         # several row groups plus a ragged tail, within a few million elements
         M = max(3, min(1531, 3_000_000 // N))
-    return gen.Workload(f"{kind}_{dtype}_{M}x{N}", kind, dtype, M, N, eps, x_mean=x_mean,
-                        x_std=x_std, config=9)
+    return gen.Workload(f"{kind}_{dtype}{'+' + pdtype if pdtype else ''}_{M}x{N}", kind, dtype, M,
+                        N, eps, x_mean=x_mean, x_std=x_std, config=9, pdtype=pdtype)
 
 
 @pytest.mark.parametrize("N", SMALL_N)
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("kind", ["rms", "ln"])
-def test_small_shapes(device, kind, dtype, N):
-    w = small_workload(kind, dtype, N, x_mean=0.25 if kind == "ln" else 0.0, x_std=1.5)
+def test_small_shapes(device, kind, dtype, pdtype, N):
+    w = small_workload(kind, dtype, N, x_mean=0.25 if kind == "ln" else 0.0, x_std=1.5,
+                       pdtype=pdtype)
     full_check(w, device, rows=np.arange(w.M))
 
 
@@ -37,6 +49,17 @@ def test_small_shapes(device, kind, dtype, N):
 def test_workloads_full_size(device, name):
     """The named workloads at full size, in the launch configuration the benchmark times."""
     full_check(gen.WORKLOADS[name], device, rows=sample_rows(gen.WORKLOADS[name].M, 64))
+
+
+@pytest.mark.parametrize("dtype,pdtype", PAIRS[2:], ids=PAIR_IDS[2:])
+@pytest.mark.parametrize("name", ["rms1", "ln2", "rms3", "rms4"])
+def test_workloads_other_types(device, name, dtype, pdtype):
+    """The named workloads' shapes and distributions with fp16 activations, or with fp32
+    gamma/beta beside 16-bit activations."""
+    import dataclasses
+    w = dataclasses.replace(gen.WORKLOADS[name], dtype=dtype, pdtype=pdtype,
+                            name=f"{name}_{dtype}_{pdtype}")
+    full_check(w, device, rows=sample_rows(w.M, 32))
 
 
 @pytest.mark.parametrize("N", gen.SWEEP_N)
@@ -64,16 +87,16 @@ MAPPINGS = _mapping_cases()
 
 @pytest.mark.parametrize("direction,lpr,vpl", MAPPINGS,
                          ids=[f"{d}-{l}x{v}" for d, l, v in MAPPINGS])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("kind", ["rms", "ln"])
-def test_every_mapping(device, kind, dtype, direction, lpr, vpl):
+def test_every_mapping(device, kind, dtype, pdtype, direction, lpr, vpl):
     """Force each compiled (lanes per row, vectors per lane) mapping on a row that leaves
     the last vector slot partly empty, with a ragged final row group."""
-    epv = 8 if dtype == "bf16" else 4
+    epv = 4 if dtype == "f32" else 8
     nvec = lpr * vpl - max(1, lpr // 3) if lpr * vpl > 1 else 1
     N = nvec * epv
     M = max(5, min(301, 400_000 // N))
-    w = small_workload(kind, dtype, N, M=M, x_mean=0.1)
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.1, pdtype=pdtype)
     opt = rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=lpr, vecs_per_lane=vpl)
     inputs = gen.make_inputs(w)
     run = GpuRun(w, inputs, device)
@@ -89,11 +112,11 @@ def test_every_mapping(device, kind, dtype, direction, lpr, vpl):
 
 
 @pytest.mark.parametrize("path", [rn.NORM_PATH_SPLIT, rn.NORM_PATH_GENERIC])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("kind", ["rms", "ln"])
 @pytest.mark.parametrize("N", [256, 384, 4096, 12288])
-def test_forced_paths(device, kind, dtype, N, path):
-    w = small_workload(kind, dtype, N, M=517)
+def test_forced_paths(device, kind, dtype, pdtype, N, path):
+    w = small_workload(kind, dtype, N, M=517, pdtype=pdtype)
     fwd_opt = rn.Options(path=rn.NORM_PATH_GENERIC) if path == rn.NORM_PATH_GENERIC else None
     full_check(w, device, rows=np.arange(w.M), fwd_options=fwd_opt,
                bwd_options=rn.Options(path=path))
@@ -105,18 +128,18 @@ CLUSTER_CASES = [(N, C) for N in (2048, 8192, 65536) for C in (2, 4, 8, 16, 32)
 
 @pytest.mark.parametrize("R", [1, 2])
 @pytest.mark.parametrize("N,C", CLUSTER_CASES, ids=[f"N{n}-C{c}" for n, c in CLUSTER_CASES])
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("kind", ["rms", "ln"])
-def test_cluster_path(device, kind, dtype, N, C, R):
+def test_cluster_path(device, kind, dtype, pdtype, N, C, R):
     """Rows split over C co-resident workgroups (cooperative launch), forward and backward,
     with a row count that leaves the clusters unevenly loaded."""
-    epv = 8 if dtype == "bf16" else 4
+    epv = 4 if dtype == "f32" else 8
     if (N // epv) % C:
         pytest.skip("row does not split evenly")
     M = max(3, min(997, 2_000_000 // N))
-    w = small_workload(kind, dtype, N, M=M, x_mean=0.3, x_std=1.2)
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.3, x_std=1.2, pdtype=pdtype)
     opt = rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=C, cluster_rows=R)
-    code = rn.NORM_DTYPE_BF16 if dtype == "bf16" else rn.NORM_DTYPE_F32
+    code = dtype_code(dtype, pdtype)
     try:
         rn.norm_plan(False, kind == "ln", M, N, code, options=opt)
         rn.norm_plan(True, kind == "ln", M, N, code, options=opt)
@@ -194,10 +217,11 @@ def test_backward_with_oracle_stats(device, kind):
     check_backward(run, inputs, np.arange(w.M))
 
 
+@pytest.mark.parametrize("dtype,pdtype", [("bf16", None), ("f16", "f32")], ids=["bf16", "f16+f32"])
 @pytest.mark.parametrize("offset", [1, 3])
 @pytest.mark.parametrize("kind", ["rms", "ln"])
-def test_misaligned_inputs(device, kind, offset):
-    w = small_workload(kind, "bf16", 1024, M=300)
+def test_misaligned_inputs(device, kind, offset, dtype, pdtype):
+    w = small_workload(kind, dtype, 1024, M=300, pdtype=pdtype)
     full_check(w, device, rows=np.arange(w.M), x_offset=offset)
 
 

@@ -24,10 +24,22 @@ MUTATIONS = [
     ("ln_drop_eps", "*rstd_out = 1.0 / sqrt(var + eps);", "*rstd_out = 1.0 / sqrt(var);"),
     ("ln_var_about_zero", "double d = elem(x, dtype, base + j) - mu;",
      "double d = elem(x, dtype, base + j);"),
-    ("ln_beta_sign", "y[k * N + j] = xhat * elem(gamma, dtype, j) + elem(beta, dtype, j);",
-     "y[k * N + j] = xhat * elem(gamma, dtype, j) - elem(beta, dtype, j);"),
-    ("rms_gamma_reversed", "y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, dtype, j);",
-     "y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, dtype, N - 1 - j);"),
+    ("ln_beta_sign", "y[k * N + j] = xhat * elem(gamma, gdtype, j) + elem(beta, gdtype, j);",
+     "y[k * N + j] = xhat * elem(gamma, gdtype, j) - elem(beta, gdtype, j);"),
+    ("rms_gamma_reversed",
+     "y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, gdtype, j);",
+     "y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, gdtype, N - 1 - j);"),
+    ("rms_gamma_read_as_x_type",
+     "y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, gdtype, j);",
+     "y[k * N + j] = elem(x, dtype, row * N + j) * r * elem(gamma, dtype, j);"),
+    ("ln_beta_read_as_x_type", "xhat * elem(gamma, gdtype, j) + elem(beta, gdtype, j);",
+     "xhat * elem(gamma, gdtype, j) + elem(beta, dtype, j);"),
+    ("f16_exponent_bias", "v = ldexp((double)(frac + 1024), e - 25);",
+     "v = ldexp((double)(frac + 1024), e - 24);"),
+    ("f16_no_implicit_bit", "v = ldexp((double)(frac + 1024), e - 25);",
+     "v = ldexp((double)frac, e - 25);"),
+    ("f16_subnormal_scale", "v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
+    ("f16_sign_dropped", "return (h & 0x8000) ? -v : v;", "return v;"),
     ("rms_dx_sign", "dx[k * N + j] = r * (g - xhat * c1);", "dx[k * N + j] = r * (g + xhat * c1);"),
     ("ln_dx_drop_c2", "dx[k * N + j] = r * (g - c2 - xhat * c1);",
      "dx[k * N + j] = r * (g - xhat * c1);"),
