@@ -34,16 +34,33 @@ MALL_BYTES = 256 << 20
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_bwd_rows_ln2.json")
 
 
-def ideal_bytes(kind, M, N, s):
+def ideal_bytes(kind, M, N, s, ps=None):
+    """Algorithmic bytes of the forward and of the backward call: s bytes per activation,
+    ps per gamma/beta element (default s)."""
+    ps = s if ps is None else ps
     if kind == "rms":
-        return 2 * M * N * s + N * s + 4 * M, 3 * M * N * s + N * s + 4 * M + 4 * N
-    return 2 * M * N * s + 2 * N * s + 8 * M, 3 * M * N * s + N * s + 8 * M + 8 * N
+        return 2 * M * N * s + N * ps + 4 * M, 3 * M * N * s + N * ps + 4 * M + 4 * N
+    return 2 * M * N * s + 2 * N * ps + 8 * M, 3 * M * N * s + N * ps + 8 * M + 8 * N
 
 
-def main_bwd_kernel_bytes(kind, M, N, s):
+def main_bwd_kernel_bytes(kind, M, N, s, ps=None):
     """Bytes the backward's main kernel must move: read x, dy, gamma, the saved statistics,
     write dx (the dgamma/dbeta output is written by the column reduce)."""
-    return 3 * M * N * s + N * s + (4 if kind == "rms" else 8) * M
+    ps = s if ps is None else ps
+    return 3 * M * N * s + N * ps + (4 if kind == "rms" else 8) * M
+
+
+def elem_bytes(dtype):
+    return 4 if dtype == "f32" else 2
+
+
+def lib_dtype(w):
+    """The library's dtype code for a workload (activations, and gamma/beta if different)."""
+    import row_normalization_norm_amd as rn
+    code = {"f32": rn.NORM_DTYPE_F32, "bf16": rn.NORM_DTYPE_BF16, "f16": rn.NORM_DTYPE_F16}
+    if w.pdtype and w.pdtype != w.dtype:
+        return rn.dtype_mixed(code[w.dtype], code[w.pdtype])
+    return code[w.dtype]
 
 
 def kernel_source_hash():
@@ -57,18 +74,22 @@ def kernel_source_hash():
 
 def describe(w):
     dist = f"N({w.x_mean:g},{w.x_std:g})"
+    types = w.dtype if not w.pdtype else f"{w.dtype} (gamma/beta {w.pdtype})"
     if w.outlier_p:
         dist += f" with {w.outlier_p:.0%} of entries x{w.outlier_scale:g}"
     kind = "RMSNorm" if w.kind == "rms" else "LayerNorm"
-    return f"{kind} fwd+bwd x[{w.M},{w.N}] {w.dtype} {dist}, eps={w.eps:g}"
+    return f"{kind} fwd+bwd x[{w.M},{w.N}] {types} {dist}, eps={w.eps:g}"
 
 
 def to_device(a, dtype, device):
-    """Host array of raw bits (uint16 bf16 / float32) -> device tensor, bit-exact."""
+    """Host array of raw bits (uint16 bf16, float16, float32) -> device tensor, bit-exact."""
     import numpy as np
     import torch
+    a = np.ascontiguousarray(a)
     if dtype == "bf16":
-        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f16":
+        t = torch.from_numpy(a.view(np.float16))
     else:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
     return t.to(device)
@@ -84,13 +105,13 @@ class Bench:
         self.w, self.device, self.rn = w, device, rn
         t0 = time.time()
         inputs = gen.make_inputs(w)
-        s = 2 if w.dtype == "bf16" else 4
+        s = elem_bytes(w.dtype)
         per_set = 4 * w.M * w.N * s  # x, y, dy, dx
         self.sets = max(1, math.ceil(2 * MALL_BYTES / per_set))
         x0 = to_device(inputs["x"], w.dtype, device)
         dy0 = to_device(inputs["dy"], w.dtype, device)
-        self.gamma = to_device(inputs["gamma"], w.dtype, device)
-        self.beta = to_device(inputs["beta"], w.dtype, device) if w.kind == "ln" else None
+        self.gamma = to_device(inputs["gamma"], w.param_dtype, device)
+        self.beta = to_device(inputs["beta"], w.param_dtype, device) if w.kind == "ln" else None
         self.bufs = []
         for i in range(self.sets):
             x = x0 if i == 0 else x0.clone()
@@ -101,7 +122,7 @@ class Bench:
                 rstd=torch.empty(w.M, device=device)))
         self.dgamma = torch.empty(w.N, device=device)
         self.dbeta = torch.empty(w.N, device=device) if w.kind == "ln" else None
-        dt = rn.NORM_DTYPE_BF16 if w.dtype == "bf16" else rn.NORM_DTYPE_F32
+        dt = lib_dtype(w)
         ws = rn.norm_bwd_workspace_size(w.M, w.N, w.kind == "ln", dt)
         self.ws = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         fws = rn.norm_fwd_workspace_size(w.M, w.N, w.kind == "ln", dt)
@@ -229,8 +250,7 @@ def cpu_baseline(w, target_s=12.0):
         one_pass(inp)
         dt = (dt * passes + time.perf_counter() - t0) / (passes + 1)
         passes += 1
-    s = 2 if w.dtype == "bf16" else 4
-    f, bwd = ideal_bytes(w.kind, rows, w.N, s)
+    f, bwd = ideal_bytes(w.kind, rows, w.N, elem_bytes(w.dtype), elem_bytes(w.param_dtype))
     return {"value": round((f + bwd) / dt / 1e9, 3), "unit": "GB/s", "cores": orc.num_threads(),
             "kind": "oracle",
             "sample": f"first {rows} of {w.M} rows of the same workload (fp64 C oracle, "
@@ -302,9 +322,9 @@ def summarize(d, workload, warmup, steps, copy_bytes):
                 lds.setdefault(k, {})[name] = v
     import gen
     wl = gen.WORKLOADS[w]
-    s = 2 if wl.dtype == "bf16" else 4
-    fwd_b, bwd_b = ideal_bytes(wl.kind, wl.M, wl.N, s)
-    main_b = main_bwd_kernel_bytes(wl.kind, wl.M, wl.N, s)
+    s, ps = elem_bytes(wl.dtype), elem_bytes(wl.param_dtype)
+    fwd_b, bwd_b = ideal_bytes(wl.kind, wl.M, wl.N, s, ps)
+    main_b = main_bwd_kernel_bytes(wl.kind, wl.M, wl.N, s, ps)
     algo = {"fwd_rows_kernel": fwd_b, "bwd_rows_kernel": main_b,
             "colreduce_kernel": bwd_b - main_b}
     clines = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes read | bytes written | "
@@ -431,15 +451,14 @@ def main():
         return
 
     w = gen.WORKLOADS[args.workload]
-    s = 2 if w.dtype == "bf16" else 4
-    fwd_b, bwd_b = ideal_bytes(w.kind, w.M, w.N, s)
+    s, ps = elem_bytes(w.dtype), elem_bytes(w.param_dtype)
+    fwd_b, bwd_b = ideal_bytes(w.kind, w.M, w.N, s, ps)
     r = run_gpu(w, args.steps, args.warmup, device)
     value = (fwd_b + bwd_b) / (r["ms_per_step"] * 1e-3) / 1e9
 
-    main_bytes = main_bwd_kernel_bytes(w.kind, w.M, w.N, s)
+    main_bytes = main_bwd_kernel_bytes(w.kind, w.M, w.N, s, ps)
     achieved = main_bytes / (r["bwd_main_kernel_ms"] * 1e-3) / 1e9
-    plan = rn.norm_plan(True, w.kind == "ln", w.M, w.N,
-                        rn.NORM_DTYPE_BF16 if w.dtype == "bf16" else rn.NORM_DTYPE_F32)
+    plan = rn.norm_plan(True, w.kind == "ln", w.M, w.N, lib_dtype(w))
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -479,13 +498,18 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w)
     if args.all:
         table = []
+        import dataclasses
         sweep = [gen.sweep_workload(k, d, n) for k in ("rms", "ln") for d in ("bf16", "f32")
                  for n in gen.SWEEP_N]
-        for wl in list(gen.WORKLOADS.values()) + sweep:
+        # the benchmark workload with fp16 activations and with fp32 gamma/beta
+        other = [dataclasses.replace(gen.WORKLOADS[DEFAULT_WORKLOAD], dtype=d, pdtype=p,
+                                     name=f"{DEFAULT_WORKLOAD}_{d}" + (f"_{p}" if p else ""))
+                 for d, p in (("f16", None), ("bf16", "f32"), ("f16", "f32"))]
+        for wl in list(gen.WORKLOADS.values()) + other + sweep:
             name = wl.name
             rr = run_gpu(wl, max(5, args.steps // 2), 3, device)
-            ss = 2 if wl.dtype == "bf16" else 4
-            fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, ss)
+            fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, elem_bytes(wl.dtype),
+                                 elem_bytes(wl.param_dtype))
             table.append({"workload": name, "desc": describe(wl),
                           **{k: round(v, 5) for k, v in rr.items()},
                           "fwd_GBs": fb / (rr["fwd_kernel_ms"] * 1e-3) / 1e9,

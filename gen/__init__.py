@@ -18,7 +18,9 @@ sweep  both    [floor(2^27/N), N]  N(0, 1); bf16 and fp32             1e-6
 =====  ======  ==================  =================================  ======
 
 gamma = 1 + 0.1*N(0,1), beta = 0.1*N(0,1), dy = N(0,1), all in the dtype of x.
-Seeds: ``0x5EED0000 + 16*config + tensor_id`` with tensor ids x=0, gamma=1, beta=2, dy=3.
+Seeds: ``0x5EED0000 + 16*config + tensor_id`` with tensor ids x=0, gamma=1, beta=2, dy=3,
+and for the residual-add entry points res=4 (the residual, N(0, 1)) and dsum=5 (the
+gradient arriving at the sum, 0.5*N(0, 1)).
 """
 from __future__ import annotations
 
@@ -40,7 +42,7 @@ _DTYPES = {"f32": F32, "fp32": F32, "float32": F32, "bf16": BF16, "bfloat16": BF
 # host array dtype of each element type: bf16 as raw uint16 bits, fp16 as numpy float16
 _NP = {F32: np.float32, BF16: np.uint16, F16: np.float16}
 
-TENSOR_IDS = {"x": 0, "gamma": 1, "beta": 2, "dy": 3}
+TENSOR_IDS = {"x": 0, "gamma": 1, "beta": 2, "dy": 3, "res": 4, "dsum": 5}
 SEED_BASE = 0x5EED0000
 
 
@@ -169,8 +171,9 @@ def sweep_workload(kind: str, dtype: str, N: int) -> Workload:
     return Workload(f"sweep_{kind}_{dtype}_N{N}", kind, dtype, (1 << 27) // N, N, 1e-6, config=5)
 
 
-def make_inputs(w: Workload, rows: int | None = None) -> dict:
-    """Host arrays x [M,N], gamma [N], beta [N] (LayerNorm only), dy [M,N].
+def make_inputs(w: Workload, rows: int | None = None, residual: bool = False) -> dict:
+    """Host arrays x [M,N], gamma [N], beta [N] (LayerNorm only), dy [M,N]; with
+    ``residual`` also res [M,N] and dsum [M,N].
 
     ``rows`` limits x and dy to their first ``rows`` rows (the draws are counter based,
     so the first rows of a larger workload are bit-identical to the full one's).
@@ -185,4 +188,7 @@ def make_inputs(w: Workload, rows: int | None = None) -> dict:
     }
     if w.kind == "ln":
         out["beta"] = fill(w.N, w.param_dtype, w.seed("beta"), 0.0, 0.1)
+    if residual:
+        out["res"] = fill(n, w.dtype, w.seed("res"), 0.0, 1.0).reshape(M, w.N)
+        out["dsum"] = fill(n, w.dtype, w.seed("dsum"), 0.0, 0.5).reshape(M, w.N)
     return out

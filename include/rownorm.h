@@ -231,6 +231,39 @@ norm_status_t norm_ln_bwd_ex(const void* dy, const void* x, const void* gamma,
                              void* workspace, size_t workspace_bytes, hipStream_t stream,
                              const norm_options_t* opt);
 
+/* ------------------------------------------------------------ residual add fused
+ * The residual add that feeds a norm, fused into it (the "SOTA normalization performance
+ * with torch.compile" page credits automatic fusion of neighbouring kernels for the
+ * end-to-end gains; this is the plainest such neighbour of a norm):
+ *     sum = x + residual, rounded to the activation type, is written out (the updated
+ *     residual stream) and is the row that is normalized: y = norm(sum).
+ * In the backward, `sum` takes the place of x, and dsum (the gradient arriving at the
+ * sum from its other uses; NULL means zero) is added to the result, which is then the
+ * gradient of both addends:  dx = d norm(sum) / d sum (dy) + dsum.
+ * Bytes: the forward also reads `residual` and writes `sum`; the backward also reads
+ * `dsum`.  Everything else -- arguments, layouts, types, workspace, alignment (now
+ * including residual, sum and dsum), errors -- is as for norm_*_fwd / norm_*_bwd, and
+ * `opt` (may be NULL) as for the _ex variants.  sum must not overlap x or residual. */
+norm_status_t norm_rms_fwd_add(const void* x, const void* residual, const void* gamma, void* y,
+                               void* sum, float* rstd, int64_t M, int64_t N, float eps,
+                               norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, const norm_options_t* opt);
+norm_status_t norm_ln_fwd_add(const void* x, const void* residual, const void* gamma,
+                              const void* beta, void* y, void* sum, float* mean, float* rstd,
+                              int64_t M, int64_t N, float eps, norm_dtype_t dtype,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              const norm_options_t* opt);
+norm_status_t norm_rms_bwd_add(const void* dy, const void* sum, const void* gamma,
+                               const float* rstd, const void* dsum, void* dx, float* dgamma,
+                               int64_t M, int64_t N, norm_dtype_t dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream,
+                               const norm_options_t* opt);
+norm_status_t norm_ln_bwd_add(const void* dy, const void* sum, const void* gamma,
+                              const float* mean, const float* rstd, const void* dsum, void* dx,
+                              float* dgamma, float* dbeta, int64_t M, int64_t N,
+                              norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const norm_options_t* opt);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,6 +69,8 @@ class Oracle:
         lib.oracle_ln_bwd_dx.argtypes = [_P, _P, _P, _INT, _INT, _I64, _D, _P, _I64, _P]
         lib.oracle_rms_bwd_dgamma.argtypes = [_P, _P, _INT, _I64, _I64, _D, _P, _P]
         lib.oracle_ln_bwd_dgamma_dbeta.argtypes = [_P, _P, _INT, _I64, _I64, _D, _P, _P, _P, _P]
+        lib.oracle_residual_sum.argtypes = [_P, _P, _INT, _I64, _P, _I64, _P]
+        lib.oracle_residual_sum.restype = None
         for name in ("oracle_rms_fwd", "oracle_ln_fwd", "oracle_rms_bwd_dx", "oracle_ln_bwd_dx",
                      "oracle_rms_bwd_dgamma", "oracle_ln_bwd_dgamma_dbeta"):
             getattr(lib, name).restype = None
@@ -166,6 +168,15 @@ class Oracle:
                                   k, _ptr(dx))
         return dx
 
+    def residual_sum(self, x, res, rows=None):
+        """Rows of s = x + res rounded to x's type, float64 [k, N]."""
+        x, dt, (res,) = self._prep(x, res)
+        M, N = x.shape
+        r, k = self._rows(rows, M)
+        s = np.empty((k, N), np.float64)
+        self.lib.oracle_residual_sum(_ptr(x), _ptr(res), dt, N, _ptr(r), k, _ptr(s))
+        return s
+
     def rms_dgamma(self, dy, x, eps):
         """-> (dgamma [N], scale [N]) float64."""
         x, dt, (dy,) = self._prep(x, dy)
@@ -183,6 +194,25 @@ class Oracle:
         self.lib.oracle_ln_bwd_dgamma_dbeta(_ptr(dy), _ptr(x), dt, M, N, float(eps), _ptr(dg),
                                             _ptr(db), _ptr(sg), _ptr(sb))
         return dg, db, sg, sb
+
+
+def as_type_bits(values: np.ndarray, dtype: int) -> np.ndarray:
+    """float64 values that are exactly representable in `dtype` -> host arrays of raw bits
+    (uint16 bfloat16, float16, float32), as the oracle's inputs expect."""
+    v = np.asarray(values, np.float64)
+    f = v.astype(np.float32)
+    if dtype == F32:
+        out = f
+    elif dtype == F16:
+        out = v.astype(np.float16)
+    else:
+        out = (f.view(np.uint32) >> 16).astype(np.uint16)
+    back = out.astype(np.float64) if dtype != BF16 else \
+        (out.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ok = (back == v) | (np.isnan(back) & np.isnan(v))
+    if not np.all(ok):
+        raise ValueError("values are not representable in the element type")
+    return out
 
 
 _default = None

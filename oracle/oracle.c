@@ -48,6 +48,31 @@ static double elem(const void* p, int dtype, int64_t i) {
 
 static int64_t pick_row(const int64_t* rows, int64_t k) { return rows ? rows[k] : k; }
 
+/* Round a double to the nearest value of the element type, ties to even: p significant
+ * bits, smallest normal exponent emin, largest finite value (2 - 2^(1-p)) * 2^emax;
+ * below 2^emin the spacing stays 2^(emin - p + 1) (subnormals); at or beyond the
+ * midpoint between the largest finite value and 2^(emax+1) the result is infinite. */
+static double round_to_type(double v, int dtype) {
+  int p, emin, emax;
+  if (dtype == ORACLE_BF16) {
+    p = 8, emin = -126, emax = 127;
+  } else if (dtype == ORACLE_F16) {
+    p = 11, emin = -14, emax = 15;
+  } else {
+    p = 24, emin = -126, emax = 127;
+  }
+  if (v == 0.0 || isnan(v) || isinf(v)) return v;
+  const double a = fabs(v);
+  if (a >= ldexp(2.0 - ldexp(1.0, -p), emax)) return v > 0 ? INFINITY : -INFINITY;
+  int k;
+  frexp(a, &k); /* a = m * 2^k, 0.5 <= m < 1, so the leading bit is 2^(k-1) */
+  int e = k - 1;
+  if (e < emin) e = emin;
+  const double q = ldexp(1.0, e - p + 1); /* spacing of the type around a */
+  const double n = nearbyint(a / q);      /* exact quotient, rounded half to even */
+  return copysign(n * q, v);
+}
+
 /* ---------------------------------------------------------------- statistics */
 
 /* RMSNorm: mean of squares, add eps, reciprocal square root. */
@@ -247,4 +272,20 @@ int oracle_num_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* --------------------------------------------------------------- residual add */
+
+/* s = x + res for the selected rows, rounded to the activation type: the stored sum
+ * that a residual add in front of the norm produces and normalizes. */
+void oracle_residual_sum(const void* x, const void* res, int dtype, int64_t N,
+                         const int64_t* rows, int64_t nrows, double* s) {
+#pragma omp parallel for schedule(static)
+  for (int64_t k = 0; k < nrows; ++k) {
+    const int64_t row = pick_row(rows, k);
+    for (int64_t j = 0; j < N; ++j) {
+      s[k * N + j] = round_to_type(elem(x, dtype, row * N + j) + elem(res, dtype, row * N + j),
+                                   dtype);
+    }
+  }
 }

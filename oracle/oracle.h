@@ -63,6 +63,12 @@ void oracle_ln_bwd_dgamma_dbeta(const void* dy, const void* x, int dtype, int64_
                                 double eps, double* dgamma, double* dbeta,
                                 double* dgamma_scale, double* dbeta_scale);
 
+/* Residual add in front of the norm: s[k,:] = x[row,:] + res[row,:], rounded to the
+ * activation type `dtype` (nearest, ties to even).  The fused forward normalizes s and
+ * stores it; the plainest reading of fusing the residual add that feeds a norm. */
+void oracle_residual_sum(const void* x, const void* res, int dtype, int64_t N,
+                         const int64_t* rows, int64_t nrows, double* s);
+
 /* OpenMP threads the row loops use. */
 int oracle_num_threads(void);
 

@@ -96,6 +96,12 @@ SIGNATURES = {
     "norm_rms_bwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P, _OPT]),
     "norm_ln_bwd_ex": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P,
                               _OPT]),
+    "norm_rms_fwd_add": (_INT, [_P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _SZ, _P, _OPT]),
+    "norm_ln_fwd_add": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _F, _INT, _P, _SZ, _P,
+                               _OPT]),
+    "norm_rms_bwd_add": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P, _OPT]),
+    "norm_ln_bwd_add": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P,
+                               _OPT]),
 }
 
 _lib = None
@@ -341,3 +347,82 @@ def norm_cluster_resident(is_backward: bool, is_layernorm: bool, M: int, N: int,
     """1 if the call would run on the CLUSTER path on the current device, else 0."""
     return int(lib().norm_cluster_resident(int(bool(is_backward)), int(bool(is_layernorm)), M, N,
                                            dtype, _opt(options)))
+
+
+# ------------------------------------------------------------- residual add fused
+def norm_rms_fwd_add(x, residual, gamma, y, sum_out, rstd=None, eps: float = 1e-6,
+                     workspace=None, stream=None, options=None):
+    """sum_out = x + residual (rounded to x's type); y = RMSNorm(sum_out)."""
+    torch = _torch()
+    M, N = _shape(x)
+    for t, n in ((x, "x"), (residual, "residual"), (y, "y"), (sum_out, "sum_out")):
+        _need(t, n, M * N, x.dtype, x.device)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
+    _need(rstd, "rstd", M, torch.float32, x.device)
+    dt = _types(x, gamma)
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options)
+    _check(lib().norm_rms_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(sum_out),
+                                  _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
+                                  _stream(x.device, stream), _opt(options)), "norm_rms_fwd_add")
+    return y, sum_out
+
+
+def norm_ln_fwd_add(x, residual, gamma, beta, y, sum_out, mean=None, rstd=None,
+                    eps: float = 1e-5, workspace=None, stream=None, options=None):
+    """sum_out = x + residual (rounded to x's type); y = LayerNorm(sum_out)."""
+    torch = _torch()
+    M, N = _shape(x)
+    for t, n in ((x, "x"), (residual, "residual"), (y, "y"), (sum_out, "sum_out")):
+        _need(t, n, M * N, x.dtype, x.device)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
+    _need(beta, "beta", N, _pdtype(x, gamma), x.device)
+    _need(mean, "mean", M, torch.float32, x.device)
+    _need(rstd, "rstd", M, torch.float32, x.device)
+    dt = _types(x, gamma)
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options)
+    _check(lib().norm_ln_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
+                                 _ptr(sum_out), _ptr(mean), _ptr(rstd), M, N, float(eps), dt,
+                                 _ptr(ws), ws_bytes, _stream(x.device, stream), _opt(options)),
+           "norm_ln_fwd_add")
+    return y, sum_out
+
+
+def norm_rms_bwd_add(dy, sum_in, gamma, rstd, dsum, dx, dgamma, workspace=None, stream=None,
+                     options=None):
+    """dx = RMSNorm backward at sum_in (+ dsum, the gradient arriving at the sum, if given);
+    dgamma overwritten."""
+    torch = _torch()
+    M, N = _shape(sum_in)
+    for t, n in ((dy, "dy"), (sum_in, "sum_in"), (dsum, "dsum"), (dx, "dx")):
+        _need(t, n, M * N, sum_in.dtype, sum_in.device)
+    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), sum_in.device)
+    _need(rstd, "rstd", M, torch.float32, sum_in.device)
+    _need(dgamma, "dgamma", N, torch.float32, sum_in.device)
+    dt = _types(sum_in, gamma)
+    ws, ws_bytes = _workspace(M, N, False, dt, sum_in.device, workspace, options)
+    _check(lib().norm_rms_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(rstd), _ptr(dsum),
+                                  _ptr(dx), _ptr(dgamma), M, N, dt, _ptr(ws), ws_bytes,
+                                  _stream(sum_in.device, stream), _opt(options)),
+           "norm_rms_bwd_add")
+    return dx, dgamma
+
+
+def norm_ln_bwd_add(dy, sum_in, gamma, mean, rstd, dsum, dx, dgamma, dbeta, workspace=None,
+                    stream=None, options=None):
+    """dx = LayerNorm backward at sum_in (+ dsum if given); dgamma, dbeta overwritten."""
+    torch = _torch()
+    M, N = _shape(sum_in)
+    for t, n in ((dy, "dy"), (sum_in, "sum_in"), (dsum, "dsum"), (dx, "dx")):
+        _need(t, n, M * N, sum_in.dtype, sum_in.device)
+    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), sum_in.device)
+    for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
+                    (dbeta, "dbeta", N)):
+        _need(t, n, k, torch.float32, sum_in.device)
+    dt = _types(sum_in, gamma)
+    ws, ws_bytes = _workspace(M, N, True, dt, sum_in.device, workspace, options)
+    _check(lib().norm_ln_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(mean), _ptr(rstd),
+                                 _ptr(dsum), _ptr(dx), _ptr(dgamma), _ptr(dbeta), M, N, dt,
+                                 _ptr(ws), ws_bytes, _stream(sum_in.device, stream),
+                                 _opt(options)), "norm_ln_bwd_add")
+    return dx, dgamma, dbeta
+

@@ -23,8 +23,8 @@ namespace rownorm {
                                             int, hipStream_t);                             \
   hipError_t launch_bwd_cluster_k##K##_t##T(int, int, int, const BwdArgs&, const ClusterArgs&, \
                                             int, hipStream_t);                             \
-  int occupancy_fwd_cluster_k##K##_t##T(int, int, int);                                    \
-  int occupancy_bwd_cluster_k##K##_t##T(int, int, int);
+  int occupancy_fwd_cluster_k##K##_t##T(int, int, int, bool);                              \
+  int occupancy_bwd_cluster_k##K##_t##T(int, int, int, bool);
 RN_DECL_TU(0, 0) RN_DECL_TU(0, 1) RN_DECL_TU(0, 2) RN_DECL_TU(0, 3) RN_DECL_TU(0, 4)
 RN_DECL_TU(1, 0) RN_DECL_TU(1, 1) RN_DECL_TU(1, 2) RN_DECL_TU(1, 3) RN_DECL_TU(1, 4)
 #undef RN_DECL_TU
@@ -43,7 +43,7 @@ using FwdClusterFn = hipError_t (*)(int, int, int, const FwdArgs&, const Cluster
                                     hipStream_t);
 using BwdClusterFn = hipError_t (*)(int, int, int, const BwdArgs&, const ClusterArgs&, int,
                                     hipStream_t);
-using OccFn = int (*)(int, int, int);
+using OccFn = int (*)(int, int, int, bool);
 const FwdRowsFn kFwdRows[2][kNumTypeCombos] = RN_TABLE(launch_fwd_rows);
 const BwdRowsFn kBwdRows[2][kNumTypeCombos] = RN_TABLE(launch_bwd_rows);
 const FwdClusterFn kFwdCluster[2][kNumTypeCombos] = RN_TABLE(launch_fwd_cluster);
@@ -69,11 +69,11 @@ hipError_t launch_bwd_cluster(int kind, int tc, int t, int vpl, int rows, const 
                               const ClusterArgs& c, int grid, hipStream_t s) {
   return kBwdCluster[kind][tc](t, vpl, rows, a, c, grid, s);
 }
-int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows) {
-  return kFwdOcc[kind][tc](t, vpl, rows);
+int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add) {
+  return kFwdOcc[kind][tc](t, vpl, rows, add);
 }
-int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows) {
-  return kBwdOcc[kind][tc](t, vpl, rows);
+int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add) {
+  return kBwdOcc[kind][tc](t, vpl, rows, add);
 }
 
 // The public dtype code: the activation type in the low byte, optionally the parameter
@@ -137,8 +137,9 @@ struct EventScope {
 }  // namespace
 
 // Workgroups of a cluster kernel the current device can hold at once (0 if unknown).
-// Cached per (device, direction, kind, type pair, threads, vectors, rows per step).
-int cluster_capacity(bool backward, int kind, int tc, int t, int vpl, int rows) {
+// Cached per (device, direction, kind, type pair, fused add, threads, vectors, rows per
+// step).
+int cluster_capacity(bool backward, int kind, int tc, bool add, int t, int vpl, int rows) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   static std::atomic<int> cus[64];
@@ -150,19 +151,19 @@ int cluster_capacity(bool backward, int kind, int tc, int t, int vpl, int rows) 
   }
   // occupancy depends only on the kernel and the device's per-CU limits
   static std::mutex mu;
-  // [dev][bwd][kind][type pair][t: 256/512/1024][vpl: 1/2/4][rows per step: 1/2]
-  static int cache[64][2][2][kNumTypeCombos][3][3][2];
+  // [dev][bwd][kind][type pair][add][t: 256/512/1024][vpl: 1/2/4][rows per step: 1/2]
+  static int cache[64][2][2][kNumTypeCombos][2][3][3][2];
   const int ti = t == 256 ? 0 : t == 512 ? 1 : 2;
   const int vi = vpl == 1 ? 0 : vpl == 2 ? 1 : 2;
   int occ;
   {
     std::lock_guard<std::mutex> lock(mu);
     const int ri = rows == 1 ? 0 : 1;
-    occ = cache[dev][backward][kind][tc][ti][vi][ri];
+    occ = cache[dev][backward][kind][tc][add][ti][vi][ri];
     if (occ == 0) {
-      occ = backward ? occupancy_bwd_cluster(kind, tc, t, vpl, rows)
-                     : occupancy_fwd_cluster(kind, tc, t, vpl, rows);
-      cache[dev][backward][kind][tc][ti][vi][ri] = occ > 0 ? occ : -1;
+      occ = backward ? occupancy_bwd_cluster(kind, tc, t, vpl, rows, add)
+                     : occupancy_fwd_cluster(kind, tc, t, vpl, rows, add);
+      cache[dev][backward][kind][tc][add][ti][vi][ri] = occ > 0 ? occ : -1;
     }
   }
   return occ > 0 ? occ * n : 0;
@@ -172,8 +173,8 @@ int cluster_capacity(bool backward, int kind, int tc, int t, int vpl, int rows) 
 // co-resident (fewer clusters also means fewer dgamma/dbeta partial rows, so the
 // workspace the plan sized still suffices).  Returns false when not even one cluster
 // fits; the caller then takes the fallback plan.
-bool fit_cluster(bool backward, int kind, int tc, Plan& p) {
-  const int cap = cluster_capacity(backward, kind, tc, p.lpr, p.vpl, p.rows_per_step);
+bool fit_cluster(bool backward, int kind, int tc, bool add, Plan& p) {
+  const int cap = cluster_capacity(backward, kind, tc, add, p.lpr, p.vpl, p.rows_per_step);
   if (cap < p.cluster) return false;
   if (p.grid > cap) {
     int ncl = cap / p.cluster;
@@ -214,21 +215,25 @@ norm_status_t check_workspace(const Plan& p, void* workspace, size_t given) {
   return NORM_OK;
 }
 
+// fused: the residual-add entry points (res and sum required when M > 0).
 norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* beta, void* y,
                        float* mean, float* rstd, int64_t M, int64_t N, float eps,
                        norm_dtype_t dtype, void* workspace, size_t workspace_bytes_given,
-                       hipStream_t stream, const norm_options_t* opt) {
+                       hipStream_t stream, const norm_options_t* opt, bool fused = false,
+                       const void* res = nullptr, void* sum = nullptr) {
   norm_status_t st = check_shape_dtype(M, N, dtype);
   if (st != NORM_OK) return st;
   if (!gamma || (ln && !beta)) return NORM_ERR_NULL_PTR;
   if (M > 0 && (!x || !y)) return NORM_ERR_NULL_PTR;
+  if (fused && M > 0 && (!res || !sum)) return NORM_ERR_NULL_PTR;
   if (!std::isfinite(eps) || eps < 0.0f) return NORM_ERR_BAD_EPS;
   const DtypeInfo dt = decode_dtype(dtype);
   const uintptr_t es = elem_bytes(dt.x), ps = elem_bytes(dt.p);
   if (!aligned(x, es) || !aligned(y, es) || !aligned(gamma, ps) || !aligned(beta, ps) ||
-      !aligned(mean, 4) || !aligned(rstd, 4))
+      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(res, es) || !aligned(sum, es))
     return NORM_ERR_MISALIGNED;
-  const bool a16 = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16);
+  const bool a16 = aligned(x, 16) && aligned(y, 16) && aligned(gamma, 16) && aligned(beta, 16) &&
+                   aligned(res, 16) && aligned(sum, 16);
 
   Plan p;
   st = make_plan(false, ln, M, N, dt.x, a16, opt, &p);
@@ -250,11 +255,13 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   a.eps = eps;
   a.inv_n = 1.0f / float(N);
   a.groups = p.groups;
+  a.res = fused ? res : nullptr;
+  a.sum = fused ? sum : nullptr;
 
   const int kind = ln ? 1 : 0;
   EventScope ev{opt, stream};
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(false, kind, dt.tc, p)) {
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(false, kind, dt.tc, fused, p)) {
     make_fallback_plan(false, ln, M, N, dt.x, &p);
   }
   hipError_t e = hipSuccess;
@@ -278,11 +285,12 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   return hip_status(ev.stop());
 }
 
+// dres: the residual-add entry points' gradient arriving at the sum (may be NULL).
 norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma,
                        const float* mean, const float* rstd, void* dx, float* dgamma,
                        float* dbeta, int64_t M, int64_t N, norm_dtype_t dtype, void* workspace,
                        size_t workspace_bytes_given, hipStream_t stream,
-                       const norm_options_t* opt) {
+                       const norm_options_t* opt, const void* dres = nullptr) {
   norm_status_t st = check_shape_dtype(M, N, dtype);
   if (st != NORM_OK) return st;
   if (!gamma || !dgamma || (ln && !dbeta)) return NORM_ERR_NULL_PTR;
@@ -290,9 +298,11 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   const DtypeInfo dt = decode_dtype(dtype);
   const uintptr_t es = elem_bytes(dt.x), ps = elem_bytes(dt.p);
   if (!aligned(dy, es) || !aligned(x, es) || !aligned(gamma, ps) || !aligned(dx, es) ||
-      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4))
+      !aligned(mean, 4) || !aligned(rstd, 4) || !aligned(dgamma, 4) || !aligned(dbeta, 4) ||
+      !aligned(dres, es))
     return NORM_ERR_MISALIGNED;
-  const bool a16 = aligned(dy, 16) && aligned(x, 16) && aligned(gamma, 16) && aligned(dx, 16);
+  const bool a16 = aligned(dy, 16) && aligned(x, 16) && aligned(gamma, 16) && aligned(dx, 16) &&
+                   aligned(dres, 16);
 
   Plan p;
   st = make_plan(true, ln, M, N, dt.x, a16, opt, &p);
@@ -309,7 +319,7 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   }
 
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(true, kind, dt.tc, p)) {
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(true, kind, dt.tc, dres != nullptr, p)) {
     make_fallback_plan(true, ln, M, N, dt.x, &p);
   }
   BwdArgs a;
@@ -332,6 +342,7 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   a.mode = mode;
   a.groups = p.groups;
   a.rows_per_block = p.rows_per_block;
+  a.dres = dres;
 
   EventScope ev{opt, stream};
   hipError_t e = hipSuccess;
@@ -482,6 +493,49 @@ norm_status_t norm_ln_bwd_ex(const void* dy, const void* x, const void* gamma,
   });
 }
 
+norm_status_t norm_rms_fwd_add(const void* x, const void* residual, const void* gamma, void* y,
+                               void* sum, float* rstd, int64_t M, int64_t N, float eps,
+                               norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, const norm_options_t* opt) {
+  return guarded([&] {
+    return fwd_impl(false, x, gamma, nullptr, y, nullptr, rstd, M, N, eps, dtype, workspace,
+                    workspace_bytes, stream, opt, true, residual, sum);
+  });
+}
+
+norm_status_t norm_ln_fwd_add(const void* x, const void* residual, const void* gamma,
+                              const void* beta, void* y, void* sum, float* mean, float* rstd,
+                              int64_t M, int64_t N, float eps, norm_dtype_t dtype,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream,
+                              const norm_options_t* opt) {
+  return guarded([&] {
+    return fwd_impl(true, x, gamma, beta, y, mean, rstd, M, N, eps, dtype, workspace,
+                    workspace_bytes, stream, opt, true, residual, sum);
+  });
+}
+
+norm_status_t norm_rms_bwd_add(const void* dy, const void* sum, const void* gamma,
+                               const float* rstd, const void* dsum, void* dx, float* dgamma,
+                               int64_t M, int64_t N, norm_dtype_t dtype, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream,
+                               const norm_options_t* opt) {
+  return guarded([&] {
+    return bwd_impl(false, dy, sum, gamma, nullptr, rstd, dx, dgamma, nullptr, M, N, dtype,
+                    workspace, workspace_bytes, stream, opt, dsum);
+  });
+}
+
+norm_status_t norm_ln_bwd_add(const void* dy, const void* sum, const void* gamma,
+                              const float* mean, const float* rstd, const void* dsum, void* dx,
+                              float* dgamma, float* dbeta, int64_t M, int64_t N,
+                              norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, const norm_options_t* opt) {
+  return guarded([&] {
+    return bwd_impl(true, dy, sum, gamma, mean, rstd, dx, dgamma, dbeta, M, N, dtype, workspace,
+                    workspace_bytes, stream, opt, dsum);
+  });
+}
+
 norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
                         norm_dtype_t dtype, int aligned16, const norm_options_t* opt,
                         norm_plan_info_t* info) {
@@ -514,7 +568,7 @@ int norm_cluster_resident(int is_backward, int is_layernorm, int64_t M, int64_t 
   if (rownorm::make_plan(is_backward != 0, is_layernorm != 0, M, N, dt.x, true, opt, &p) != NORM_OK)
     return -1;
   if (p.path != NORM_PATH_CLUSTER) return 0;
-  return rownorm::fit_cluster(is_backward != 0, is_layernorm ? 1 : 0, dt.tc, p) ? 1 : 0;
+  return rownorm::fit_cluster(is_backward != 0, is_layernorm ? 1 : 0, dt.tc, false, p) ? 1 : 0;
 }
 
 const char* norm_status_string(norm_status_t s) {

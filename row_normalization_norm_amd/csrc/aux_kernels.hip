@@ -175,6 +175,15 @@ __global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) 
         accg[v][e] = fmaf(ds[e], xh, accg[v][e]);
         if constexpr (LN) accb[v][e] += ds[e];
       }
+      if (a.dres) {  // gradient arriving at a fused residual sum
+        if constexpr (VEC) {
+          const u32x4 gv = ld16_stream(a.dres, row * a.nvec + idx[v]);
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) o[e] += D::get(gv, e);
+        } else {
+          o[0] += D::scalar(a.dres, row * a.N + idx[v]);
+        }
+      }
       if constexpr (VEC) {
         st16_stream(a.dx, row * a.nvec + idx[v], D::pack(o));
       } else {
@@ -256,6 +265,12 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
   __shared__ float red[2 * kRowWaves * 2];
   int parity = 0;
   const int tid = threadIdx.x;
+  // Element j of the row normalized: x, or with a fused residual add the sum x + res
+  // rounded to the activation type (formed again on each pass, written on the last).
+  auto elem = [&](int64_t i) {
+    const float f = D::scalar(a.x, i);
+    return a.res ? D::round(f + D::scalar(a.res, i)) : f;
+  };
   for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
     const int64_t base = row * a.N;
     // RMSNorm: mean of squares.  LayerNorm: mean, then mean squared deviation (a second,
@@ -264,13 +279,13 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
     if constexpr (LN) {
       float s = 0.0f, unused = 0.0f;
 #pragma unroll 4
-      for (int j = tid; j < a.N; j += kRowBlock) s += D::scalar(a.x, base + j);
+      for (int j = tid; j < a.N; j += kRowBlock) s += elem(base + j);
       block_sum2(s, unused, red, parity);
       mu = s * a.inv_n;
       float ss = 0.0f;
 #pragma unroll 4
       for (int j = tid; j < a.N; j += kRowBlock) {
-        const float d = D::scalar(a.x, base + j) - mu;
+        const float d = elem(base + j) - mu;
         ss = fmaf(d, d, ss);
       }
       block_sum2(ss, unused, red, parity);
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
       float ss = 0.0f, unused = 0.0f;
 #pragma unroll 4
       for (int j = tid; j < a.N; j += kRowBlock) {
-        const float f = D::scalar(a.x, base + j);
+        const float f = elem(base + j);
         ss = fmaf(f, f, ss);
       }
       block_sum2(ss, unused, red, parity);
@@ -294,7 +309,8 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
     }
 #pragma unroll 4
     for (int j = tid; j < a.N; j += kRowBlock) {
-      const float f = D::scalar(a.x, base + j);
+      const float f = elem(base + j);
+      if (a.res) D::put_scalar(a.sum, base + j, f);
       const float gm = P::scalar(a.gamma, j);
       float o;
       if constexpr (LN) {

@@ -35,7 +35,7 @@
 namespace rownorm {
 namespace {
 
-template <bool LN, typename D, typename P, int LPR, int VPL>
+template <bool LN, typename D, typename P, int LPR, int VPL, bool ADD>
 __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs a) {
   using PV = Param<D, P>;
   constexpr int BLOCK = bwd_block(LPR);
@@ -89,7 +89,10 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
 
   // The next row group's x, dy and saved statistics are loaded before the current one is
   // reduced, so HBM reads stay in flight through the reduction and the dx stores.
-  auto load = [&](int64_t grp, u32x4 (&xb)[VPL], u32x4 (&db)[VPL], float& rb, float& mb) {
+  // With ADD the gradient arriving at the residual sum comes with x and dy, and is
+  // added to dx.
+  auto load = [&](int64_t grp, u32x4 (&xb)[VPL], u32x4 (&db)[VPL], u32x4 (&gb)[ADD ? VPL : 1],
+                  float& rb, float& mb) {
     const int64_t row = grp * ROWS + slot;
     const bool rok = row < a.M;
 #pragma unroll
@@ -98,26 +101,28 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
       const bool ok = rok && vi < nvec;
       xb[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
       db[v] = ok ? ld16_stream(a.dy, row * nvec + vi) : zero16();
+      if constexpr (ADD) gb[v] = ok ? ld16_stream(a.dres, row * nvec + vi) : zero16();
     }
     rb = rok ? a.rstd[row] : 0.0f;
     mb = (LN && rok) ? a.mean[row] : 0.0f;
   };
-  u32x4 nx[VPL], nd[VPL];
+  u32x4 nx[VPL], nd[VPL], ng[ADD ? VPL : 1];
   float nr = 0.0f, nmu = 0.0f;
-  if (blockIdx.x < a.groups) load(blockIdx.x, nx, nd, nr, nmu);
+  if (blockIdx.x < a.groups) load(blockIdx.x, nx, nd, ng, nr, nmu);
 
   for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
     const int64_t row = grp * ROWS + slot;
     const bool row_ok = row < a.M;
     const int64_t vbase = row * nvec;
 
-    u32x4 xv[VPL], dv[VPL];
+    u32x4 xv[VPL], dv[VPL], rg[ADD ? VPL : 1];
     PV gv[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
       xv[v] = nx[v];
       dv[v] = nd[v];
+      if constexpr (ADD) rg[v] = ng[v];
       if constexpr (GREG) {
         gv[v] = greg[v];
       } else if (row_ok && vi < nvec) {
@@ -128,7 +133,7 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     }
     const float r = nr;
     const float mu = nmu;
-    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd, nr, nmu);
+    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd, ng, nr, nmu);
 
     // Row sums, and the per-column contributions (which do not need the row sums).
     // Short rows keep xhat and g in registers for the dx pass; longer ones unpack the
@@ -196,6 +201,7 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
             g = D::get_fresh(dv[v], e) * gv[v].get_fresh(e);
           }
           o[e] = fmaf(g, r, fmaf(xh, nrc1, nrc2));
+          if constexpr (ADD) o[e] += D::get_fresh(rg[v], e);
         }
         st16_stream(a.dx, vbase + vi, D::pack(o));
         if (mode == kAtomicRow) {
@@ -273,8 +279,13 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
 
 template <bool LN, typename D, typename P, int LPR, int VPL>
 hipError_t launch_one(const BwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((bwd_rows_kernel<LN, D, P, LPR, VPL>), dim3(grid), dim3(bwd_block(LPR)), 0,
-                     s, a);
+  if (a.dres) {
+    hipLaunchKernelGGL((bwd_rows_kernel<LN, D, P, LPR, VPL, true>), dim3(grid),
+                       dim3(bwd_block(LPR)), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((bwd_rows_kernel<LN, D, P, LPR, VPL, false>), dim3(grid),
+                       dim3(bwd_block(LPR)), 0, s, a);
+  }
   return hipGetLastError();
 }
 

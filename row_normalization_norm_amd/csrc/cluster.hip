@@ -145,7 +145,7 @@ __device__ inline void gather_step(const ClusterArgs& c, int64_t step,
 // backward runs up to two steps ahead when its registers allow.
 
 // --------------------------------------------------------------------------- forward
-template <bool LN, typename D, typename P, int T, int VPL, int R>
+template <bool LN, typename D, typename P, int T, int VPL, int R, bool ADD>
 __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const ClusterArgs c) {
   using PV = Param<D, P>;
   constexpr int EPV = D::kPerVec;
@@ -176,14 +176,32 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
   __shared__ float xin[2][kMaxCluster * K];
   int parity = 0, xp = 0;
 
-  auto load = [&](int64_t st, u32x4 (&buf)[R][VPL]) {
+  // With ADD a step's residual slices come with x's and are added in before the step's
+  // partial sums (the row normalized is the rounded sum, which is also written out).
+  auto load = [&](int64_t st, u32x4 (&buf)[R][VPL], u32x4 (&rbuf)[ADD ? R : 1][VPL]) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = st * R + i;
 #pragma unroll
-      for (int v = 0; v < VPL; ++v)
-        buf[i][v] = (own[v] && row < a.M) ? ld16_stream(a.x, row * a.nvec + vofs + v * T + tid)
-                                          : zero16();
+      for (int v = 0; v < VPL; ++v) {
+        const bool ok = own[v] && row < a.M;
+        const int64_t idx = row * a.nvec + vofs + v * T + tid;
+        buf[i][v] = ok ? ld16_stream(a.x, idx) : zero16();
+        if constexpr (ADD) rbuf[i][v] = ok ? ld16_stream(a.res, idx) : zero16();
+      }
+    }
+  };
+  auto form_sum = [&](int64_t st, u32x4 (&buf)[R][VPL], const u32x4 (&rbuf)[ADD ? R : 1][VPL]) {
+    if constexpr (ADD) {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int64_t row = st * R + i;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+          buf[i][v] = D::add(buf[i][v], rbuf[i][v]);
+          if (own[v] && row < a.M) st16_stream(a.sum, row * a.nvec + vofs + v * T + tid, buf[i][v]);
+        }
+      }
     }
   };
   // This member's partial sums of a step's rows: RMSNorm sums of squares; LayerNorm slice
@@ -229,12 +247,14 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
   };
 
   u32x4 b0[R][VPL], b1[R][VPL], b2[R][VPL];
+  u32x4 r0[ADD ? R : 1][VPL], r1[ADD ? R : 1][VPL], r2[ADD ? R : 1][VPL];
   int64_t st = cl;
   if (st >= nsteps) return;
-  load(st, b0);
-  if (st + c.nclusters < nsteps) load(st + c.nclusters, b1);
+  load(st, b0, r0);
+  if (st + c.nclusters < nsteps) load(st + c.nclusters, b1, r1);
   {
     float mine[K];
+    form_sum(st, b0, r0);
     partial(b0, mine);
     publish_step<K>(c, member, st, mine);
   }
@@ -244,10 +264,11 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
     prefetch_step<K>(c, st, pre);
     if (s1 < nsteps) {
       float mine[K];
+      form_sum(s1, b1, r1);
       partial(b1, mine);
       publish_step<K>(c, member, s1, mine);
     }
-    if (s2 < nsteps) load(s2, b2);
+    if (s2 < nsteps) load(s2, b2, r2);
 
     float* xs = xin[xp];
     xp ^= 1;
@@ -301,12 +322,16 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
       for (int v = 0; v < VPL; ++v) {
         b0[i][v] = b1[i][v];
         b1[i][v] = b2[i][v];
+        if constexpr (ADD) {
+          r0[i][v] = r1[i][v];
+          r1[i][v] = r2[i][v];
+        }
       }
   }
 }
 
 // -------------------------------------------------------------------------- backward
-template <bool LN, typename D, typename P, int T, int VPL, int R>
+template <bool LN, typename D, typename P, int T, int VPL, int R, bool ADD>
 __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const ClusterArgs c) {
   using PV = Param<D, P>;
   constexpr int EPV = D::kPerVec;
@@ -347,6 +372,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   // A step's x and dy slices and its rows' saved statistics, loaded together.
   struct Stage {
     u32x4 x[R][VPL], d[R][VPL];
+    u32x4 g2[ADD ? R : 1][VPL];  // ADD: gradient arriving at the residual sum
     float r[R], mu[R];
   };
   auto load = [&](int64_t st, Stage& sb) {
@@ -359,6 +385,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
         const int64_t idx = row * a.nvec + vofs + v * T + tid;
         sb.x[i][v] = ok ? ld16_stream(a.x, idx) : zero16();
         sb.d[i][v] = ok ? ld16_stream(a.dy, idx) : zero16();
+        if constexpr (ADD) sb.g2[i][v] = ok ? ld16_stream(a.dres, idx) : zero16();
       }
       sb.r[i] = row < a.M ? a.rstd[row] : 0.0f;
       sb.mu[i] = (LN && row < a.M) ? a.mean[row] : 0.0f;
@@ -396,7 +423,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   // S steps live in registers: b[0] waits for the exchange, b[1 .. S-3] are published,
   // b[S-2] is reduced and published this iteration and b[S-1] is being loaded, so the
   // exchange round trip of a step overlaps S-2 steps of work.
-  constexpr int S = (T <= 512 && VPL * R <= 2) ? 4 : 3;
+  constexpr int S = (T <= 512 && VPL * R <= 2 && !ADD) ? 4 : 3;
   Stage b[S];
   int64_t st = cl;
   if (st < nsteps) {
@@ -452,6 +479,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
           const float xh = (D::get_fresh(b[0].x[i][v], e) - mu) * r;
           const float gg = D::get_fresh(b[0].d[i][v], e) * gf[v][e];
           o[e] = fmaf(gg, r, fmaf(xh, nrc1, nrc2));
+          if constexpr (ADD) o[e] += D::get_fresh(b[0].g2[i][v], e);
         }
         st16_stream(a.dx, row * a.nvec + vofs + v * T + tid, D::pack(o));
       }
@@ -511,7 +539,10 @@ hipError_t RN_FWD_LAUNCHER(int t, int vpl, int rows, const FwdArgs& a, const Clu
                            hipStream_t s) {
 #define RN_CASE(T_, V_, R_)                                                              \
   if (t == T_ && vpl == V_ && rows == R_)                                                \
-    return launch_coop(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, grid, T_, a, c, s);
+    return a.res ? launch_coop(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, grid, T_, a, \
+                               c, s)                                                     \
+                 : launch_coop(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, grid, T_, a, \
+                               c, s);
   RN_CLUSTER_FWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;
@@ -521,23 +552,30 @@ hipError_t RN_BWD_LAUNCHER(int t, int vpl, int rows, const BwdArgs& a, const Clu
                            hipStream_t s) {
 #define RN_CASE(T_, V_, R_)                                                              \
   if (t == T_ && vpl == V_ && rows == R_)                                                \
-    return launch_coop(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, grid, T_, a, c, s);
+    return a.dres ? launch_coop(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, grid, T_, a, \
+                                c, s)                                                    \
+                  : launch_coop(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, grid, T_, a, \
+                                c, s);
   RN_CLUSTER_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;
 }
 
-int RN_FWD_OCC(int t, int vpl, int rows) {
-#define RN_CASE(T_, V_, R_) \
-  if (t == T_ && vpl == V_ && rows == R_) return occupancy(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, T_);
+int RN_FWD_OCC(int t, int vpl, int rows, bool add) {
+#define RN_CASE(T_, V_, R_)                                                         \
+  if (t == T_ && vpl == V_ && rows == R_)                                           \
+    return add ? occupancy(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, T_)   \
+               : occupancy(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, T_);
   RN_CLUSTER_FWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return 0;
 }
 
-int RN_BWD_OCC(int t, int vpl, int rows) {
-#define RN_CASE(T_, V_, R_) \
-  if (t == T_ && vpl == V_ && rows == R_) return occupancy(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_>, T_);
+int RN_BWD_OCC(int t, int vpl, int rows, bool add) {
+#define RN_CASE(T_, V_, R_)                                                         \
+  if (t == T_ && vpl == V_ && rows == R_)                                           \
+    return add ? occupancy(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, T_)   \
+               : occupancy(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, T_);
   RN_CLUSTER_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return 0;

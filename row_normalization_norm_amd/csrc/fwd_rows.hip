@@ -37,7 +37,7 @@
 namespace rownorm {
 namespace {
 
-template <bool LN, typename D, typename P, int LPR, int VPL>
+template <bool LN, typename D, typename P, int LPR, int VPL, bool ADD>
 __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs a) {
   constexpr int BLOCK = fwd_block(LPR);
   constexpr int EPV = D::kPerVec;
@@ -90,16 +90,19 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
 
   // The next row group's loads are issued before the current one is reduced, so HBM
   // reads stay in flight through the reduction and the stores.
-  auto load = [&](int64_t grp, u32x4 (&buf)[VPL]) {
+  // With ADD the residual's vectors come with x's.
+  auto load = [&](int64_t grp, u32x4 (&buf)[VPL], u32x4 (&rbuf)[ADD ? VPL : 1]) {
     const int64_t row = grp * ROWS + slot;
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
-      buf[v] = (row < a.M && vi < nvec) ? ld16_stream(a.x, row * nvec + vi) : zero16();
+      const bool ok = row < a.M && vi < nvec;
+      buf[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
+      if constexpr (ADD) rbuf[v] = ok ? ld16_stream(a.res, row * nvec + vi) : zero16();
     }
   };
-  u32x4 nx[VPL];
-  if (blockIdx.x < a.groups) load(blockIdx.x, nx);
+  u32x4 nx[VPL], nr[ADD ? VPL : 1];
+  if (blockIdx.x < a.groups) load(blockIdx.x, nx, nr);
 
   for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
     const int64_t row = grp * ROWS + slot;
@@ -109,7 +112,17 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
     u32x4 xv[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) xv[v] = nx[v];
-    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx);
+    if constexpr (ADD) {
+      // The row normalized is the residual sum, rounded to the activation type and
+      // written out as it is formed.
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int vi = v * LPR + lane;
+        xv[v] = D::add(xv[v], nr[v]);
+        if (row_ok && vi < nvec) st16_stream(a.sum, vbase + vi, xv[v]);
+      }
+    }
+    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nr);
 
     // RMSNorm: mean of squares.  LayerNorm: the mean, then the mean squared deviation
     // from it, both reduced from the registers (the row is read from memory once).
@@ -184,8 +197,13 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
 
 template <bool LN, typename D, typename P, int LPR, int VPL>
 hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((fwd_rows_kernel<LN, D, P, LPR, VPL>), dim3(grid), dim3(fwd_block(LPR)), 0,
-                     s, a);
+  if (a.res) {
+    hipLaunchKernelGGL((fwd_rows_kernel<LN, D, P, LPR, VPL, true>), dim3(grid),
+                       dim3(fwd_block(LPR)), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((fwd_rows_kernel<LN, D, P, LPR, VPL, false>), dim3(grid),
+                       dim3(fwd_block(LPR)), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -91,6 +91,10 @@ struct FwdArgs {
   float eps;
   float inv_n;
   int64_t groups;  // row groups = ceil(M / rows per workgroup iteration)
+  // Residual add in front of the norm (NULL when not fused): the row normalized is
+  // s = x + res rounded to the activation type, and s is written to `sum`.
+  const void* res;
+  void* sum;
 };
 
 struct BwdArgs {
@@ -112,6 +116,9 @@ struct BwdArgs {
   int32_t mode;    // DgammaMode
   int64_t groups;
   int64_t rows_per_block;  // SPLIT / GENERIC column pass: rows per row block
+  // Gradient arriving at the residual sum from later uses (NULL when not fused): it is
+  // added to dx, the gradient of both addends.
+  const void* dres;
 };
 
 struct ClusterArgs {
@@ -143,8 +150,9 @@ hipError_t launch_fwd_cluster(int kind, int tc, int t, int vpl, int rows, const 
                               const ClusterArgs& c, int grid, hipStream_t s);
 hipError_t launch_bwd_cluster(int kind, int tc, int t, int vpl, int rows, const BwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s);
-int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows);
-int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows);
+// add: the variant with the fused residual add (forward) or residual gradient (backward).
+int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add);
+int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add);
 // GENERIC forward (scalar loads).
 hipError_t launch_fwd_generic(int kind, int tc, const FwdArgs& a, int grid, hipStream_t s);
 // Column reduce: out[j] = sum_p part[p*N + j] for dgamma (and dbeta if part_b).

@@ -48,6 +48,14 @@ struct F32 {
     for (int e = 0; e < 4; ++e) acc = fmaf(get(a, e), get(b, e), acc);
     return acc;
   }
+  // a + b element by element, rounded to this type (the residual sum).
+  __device__ static inline u32x4 add(const u32x4& a, const u32x4& b) {
+    u32x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = __float_as_uint(get(a, e) + get(b, e));
+    return r;
+  }
+  __device__ static inline float round(float f) { return f; }
   __device__ static inline u32x4 pack(const float (&f)[4]) {
     u32x4 r;
     r[0] = __float_as_uint(f[0]);
@@ -120,6 +128,7 @@ struct BF16 {
   __device__ static inline void put_scalar(void* p, int64_t i, float f) {
     static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack2(f, 0.0f) & 0xFFFFu);
   }
+  __device__ static inline float round(float f) { return __uint_as_float(pack2(0.0f, f) & 0xFFFF0000u); }
   __device__ static inline u32x4 pack(const float (&f)[8]) {
     u32x4 r;
     r[0] = pack2(f[0], f[1]);
@@ -127,6 +136,13 @@ struct BF16 {
     r[2] = pack2(f[4], f[5]);
     r[3] = pack2(f[6], f[7]);
     return r;
+  }
+  // a + b element by element in fp32, rounded to this type (the residual sum).
+  __device__ static inline u32x4 add(const u32x4& a, const u32x4& b) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = get(a, e) + get(b, e);
+    return pack(f);
   }
 };
 
@@ -158,6 +174,7 @@ struct F16 {
   __device__ static inline void put_scalar(void* p, int64_t i, float f) {
     static_cast<_Float16*>(p)[i] = static_cast<_Float16>(f);
   }
+  __device__ static inline float round(float f) { return static_cast<float>(static_cast<_Float16>(f)); }
   __device__ static inline f16x2 word(const u32x4& v, int w) {
     const uint32_t u = v[w];
     f16x2 h;
@@ -196,6 +213,13 @@ struct F16 {
     r[2] = pack2(f[4], f[5]);
     r[3] = pack2(f[6], f[7]);
     return r;
+  }
+  // a + b element by element in fp32, rounded to this type (the residual sum).
+  __device__ static inline u32x4 add(const u32x4& a, const u32x4& b) {
+    float f[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = get(a, e) + get(b, e);
+    return pack(f);
   }
 };
 

@@ -327,6 +327,49 @@ def pin_f16_and_mixed_params(orc):
         assert np.array_equal(dg, dgf), f"{act} dgamma decode"
 
 
+def pin_residual_sum(orc):
+    """The residual sum rounded to the activation type: numpy's float64 -> float32 and
+    float64 -> float16 conversions (round to nearest, ties to even) for fp32 and fp16; for
+    bf16, sums exact in fp32 rounded by the generator's bf16 encoder, and hand-made ties,
+    overflow and subnormal cases for all three."""
+    rng = np.random.default_rng(404)
+    M, N = 8, 64
+    scale = 2.0 ** rng.integers(-20, 20, (M, N))
+    a32 = (rng.standard_normal((M, N)) * scale).astype(np.float32)
+    b32 = (rng.standard_normal((M, N)) * scale[:, ::-1]).astype(np.float32)
+    want = (a32.astype(np.float64) + b32.astype(np.float64)).astype(np.float32)
+    assert np.array_equal(orc.residual_sum(a32, b32), want.astype(np.float64)), "fp32 sum"
+    a16 = (rng.standard_normal((M, N)) * 2.0 ** rng.integers(-12, 10, (M, N))).astype(np.float16)
+    b16 = (rng.standard_normal((M, N)) * 2.0 ** rng.integers(-12, 10, (M, N))).astype(np.float16)
+    with np.errstate(over="ignore"):
+        want = (a16.astype(np.float64) + b16.astype(np.float64)).astype(np.float16)
+    assert np.array_equal(orc.residual_sum(a16, b16), want.astype(np.float64)), "fp16 sum"
+    ab = gen.round_bf16(rng.standard_normal((M, N)).astype(np.float32) * 3)
+    bb = gen.round_bf16(rng.standard_normal((M, N)).astype(np.float32))
+    exact = gen.bf16_to_f32(ab) + gen.bf16_to_f32(bb)  # exact: exponents close
+    want = gen.bf16_to_f32(gen.round_bf16(exact)).astype(np.float64)
+    assert np.array_equal(orc.residual_sum(ab, bb), want), "bf16 sum"
+    # hand cases: (a, b, bf16 result, fp16 result)
+    cases = [(1.0, 2.0 ** -8, 1.0, 1.0 + 2.0 ** -8),            # bf16 tie -> even
+             (1.0 + 2.0 ** -7, 2.0 ** -8, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7 + 2.0 ** -8),
+             (1.0, 2.0 ** -11, 1.0, 1.0),                       # fp16 tie -> even
+             (1.0 + 2.0 ** -10, 2.0 ** -11, 1.0, 1.0 + 2.0 ** -9),
+             (65504.0, 16.0, 65536.0, np.inf),                  # fp16 overflow
+             (65504.0, 8.0, 65536.0, 65504.0),
+             (2.0 ** -24, 2.0 ** -24, 2.0 ** -23, 2.0 ** -23),   # fp16 subnormals
+             (-3.0, 3.0, 0.0, 0.0)]
+    for a, b, want_b, want_h in cases:
+        xa = gen.round_bf16(np.array([[a]], np.float32))
+        xb = gen.round_bf16(np.array([[b]], np.float32))
+        assert orc.residual_sum(xa, xb)[0, 0] == want_b, f"bf16 {a} + {b}"
+        ha = np.array([[a]], np.float16)
+        hb = np.array([[b]], np.float16)
+        assert orc.residual_sum(ha, hb)[0, 0] == want_h, f"fp16 {a} + {b}"
+    big = gen.round_bf16(np.array([[3.38e38]], np.float32))
+    assert np.isinf(orc.residual_sum(big, big)[0, 0]), "bf16 overflow"
+
+
 ALL_PINS = [pin_golden_forward, pin_golden_backward, pin_rms_unit_rms, pin_ln_moments,
             pin_invariance, pin_dx_orthogonality, pin_finite_differences, pin_torch_float64,
-            pin_bf16_decode_and_rows, pin_f16_decode, pin_f16_and_mixed_params]
+            pin_bf16_decode_and_rows, pin_f16_decode, pin_f16_and_mixed_params,
+            pin_residual_sum]

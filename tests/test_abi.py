@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     lib = rn.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in rownorm.h but not exported"
@@ -121,6 +121,29 @@ def ln_bwd(**kw):
 ])
 def test_validation_rejects(call, kw, status):
     assert call(**kw) == status
+
+
+def test_fused_residual_validation():
+    """The residual-add entry points check their extra pointers like the others."""
+    lib = rn.lib()
+    fwd = lambda **kw: lib.norm_rms_fwd_add(kw.get("x", A), kw.get("res", A), A, A,
+                                            kw.get("sum", A), A, kw.get("M", 4), 64, 1e-6, BF16,
+                                            None, 0, None, None)
+    lnf = lambda **kw: lib.norm_ln_fwd_add(A, kw.get("res", A), A, A, A, kw.get("sum", A), A, A,
+                                           kw.get("M", 4), 64, 1e-6, BF16, None, 0, None, None)
+    bwd = lambda **kw: lib.norm_rms_bwd_add(A, A, A, A, kw.get("dsum", A), A, A, 4, 64, BF16, A,
+                                            1 << 30, None, None)
+    lnb = lambda **kw: lib.norm_ln_bwd_add(A, A, A, A, A, kw.get("dsum", A), A, A, A, 4, 64,
+                                           kw.get("dtype", BF16), A, 1 << 30, None, None)
+    assert fwd(res=None) == rn.NORM_ERR_NULL_PTR
+    assert fwd(sum=None) == rn.NORM_ERR_NULL_PTR
+    assert lnf(res=None) == rn.NORM_ERR_NULL_PTR
+    assert fwd(res=A + 1) == rn.NORM_ERR_MISALIGNED
+    assert lnf(sum=A + 1) == rn.NORM_ERR_MISALIGNED
+    assert bwd(dsum=A + 1) == rn.NORM_ERR_MISALIGNED
+    assert lnb(dtype=rn.dtype_mixed(F32, F16)) == rn.NORM_ERR_BAD_DTYPE
+    # an empty batch needs no residual buffers and enqueues nothing
+    assert fwd(M=0, x=None, res=None, sum=None) == rn.NORM_OK
 
 
 def test_bad_options_rejected():

@@ -40,6 +40,14 @@ MUTATIONS = [
      "v = ldexp((double)frac, e - 25);"),
     ("f16_subnormal_scale", "v = ldexp((double)frac, -24);", "v = ldexp((double)frac, -25);"),
     ("f16_sign_dropped", "return (h & 0x8000) ? -v : v;", "return v;"),
+    ("round_exponent_off", "int e = k - 1;", "int e = k;"),
+    ("round_bf16_precision", "p = 8, emin = -126, emax = 127;", "p = 9, emin = -126, emax = 127;"),
+    ("round_f16_range", "p = 11, emin = -14, emax = 15;", "p = 11, emin = -14, emax = 14;"),
+    ("round_ties_away", "const double n = nearbyint(a / q);", "const double n = round(a / q);"),
+    ("round_no_overflow", "if (a >= ldexp(2.0 - ldexp(1.0, -p), emax)) return v > 0 ? INFINITY : -INFINITY;",
+     "if (a >= ldexp(4.0, emax)) return v > 0 ? INFINITY : -INFINITY;"),
+    ("residual_dropped", "elem(x, dtype, row * N + j) + elem(res, dtype, row * N + j)",
+     "elem(x, dtype, row * N + j)"),
     ("rms_dx_sign", "dx[k * N + j] = r * (g - xhat * c1);", "dx[k * N + j] = r * (g + xhat * c1);"),
     ("ln_dx_drop_c2", "dx[k * N + j] = r * (g - c2 - xhat * c1);",
      "dx[k * N + j] = r * (g - xhat * c1);"),
