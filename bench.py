@@ -98,15 +98,15 @@ def to_device(a, dtype, device):
 class Bench:
     """Device buffers (rotating sets when one set would fit in the MALL) for a workload."""
 
-    def __init__(self, w, device):
+    def __init__(self, w, device, fused=False):
         import torch
         import gen
         import row_normalization_norm_amd as rn
-        self.w, self.device, self.rn = w, device, rn
+        self.w, self.device, self.rn, self.fused = w, device, rn, fused
         t0 = time.time()
-        inputs = gen.make_inputs(w)
+        inputs = gen.make_inputs(w, residual=fused)
         s = elem_bytes(w.dtype)
-        per_set = 4 * w.M * w.N * s  # x, y, dy, dx
+        per_set = (7 if fused else 4) * w.M * w.N * s  # x, y, dy, dx (+ res, sum, dsum)
         self.sets = max(1, math.ceil(2 * MALL_BYTES / per_set))
         x0 = to_device(inputs["x"], w.dtype, device)
         dy0 = to_device(inputs["dy"], w.dtype, device)
@@ -120,6 +120,10 @@ class Bench:
                 x=x, dy=dy, y=torch.empty_like(x), dx=torch.empty_like(x),
                 mean=torch.empty(w.M, device=device) if w.kind == "ln" else None,
                 rstd=torch.empty(w.M, device=device)))
+            if fused:
+                self.bufs[-1].update(res=to_device(inputs["res"], w.dtype, device),
+                                     dsum=to_device(inputs["dsum"], w.dtype, device),
+                                     sum=torch.empty_like(x))
         self.dgamma = torch.empty(w.N, device=device)
         self.dbeta = torch.empty(w.N, device=device) if w.kind == "ln" else None
         dt = lib_dtype(w)
@@ -132,6 +136,20 @@ class Bench:
 
     def step(self, k, fwd_opt=None, bwd_opt=None):
         rn, w, b = self.rn, self.w, self.bufs[k % self.sets]
+        if self.fused:
+            if w.kind == "rms":
+                rn.norm_rms_fwd_add(b["x"], b["res"], self.gamma, b["y"], b["sum"], b["rstd"],
+                                    eps=w.eps, workspace=self.fws, options=fwd_opt)
+                rn.norm_rms_bwd_add(b["dy"], b["sum"], self.gamma, b["rstd"], b["dsum"], b["dx"],
+                                    self.dgamma, workspace=self.ws, options=bwd_opt)
+            else:
+                rn.norm_ln_fwd_add(b["x"], b["res"], self.gamma, self.beta, b["y"], b["sum"],
+                                   b["mean"], b["rstd"], eps=w.eps, workspace=self.fws,
+                                   options=fwd_opt)
+                rn.norm_ln_bwd_add(b["dy"], b["sum"], self.gamma, b["mean"], b["rstd"], b["dsum"],
+                                   b["dx"], self.dgamma, self.dbeta, workspace=self.ws,
+                                   options=bwd_opt)
+            return
         if w.kind == "rms":
             rn.norm_rms_fwd(b["x"], self.gamma, b["y"], b["rstd"], eps=w.eps, workspace=self.fws,
                             options=fwd_opt)
@@ -154,7 +172,7 @@ def make_events(n):
     return evs
 
 
-def run_gpu(w, steps, warmup, device):
+def run_gpu(w, steps, warmup, device, fused=False):
     """Two timed passes of `steps` steps each, after `warmup` untimed steps:
     pass A records events only before and after the K steps (the step time); pass B also
     records HIP events around every launch of the forward kernel and of the backward's
@@ -162,7 +180,7 @@ def run_gpu(w, steps, warmup, device):
     events add a few microseconds of gap each, which is why the step time comes from A."""
     import torch
     import row_normalization_norm_amd as rn
-    b = Bench(w, device)
+    b = Bench(w, device, fused)
     for k in range(warmup):
         b.step(k)
     torch.cuda.synchronize()
@@ -505,12 +523,22 @@ def main():
         other = [dataclasses.replace(gen.WORKLOADS[DEFAULT_WORKLOAD], dtype=d, pdtype=p,
                                      name=f"{DEFAULT_WORKLOAD}_{d}" + (f"_{p}" if p else ""))
                  for d, p in (("f16", None), ("bf16", "f32"), ("f16", "f32"))]
-        for wl in list(gen.WORKLOADS.values()) + other + sweep:
+        fused_names = set()
+        fused = []
+        for base in (DEFAULT_WORKLOAD, "rms1"):
+            f = dataclasses.replace(gen.WORKLOADS[base], name=f"{base}_residual_add")
+            fused.append(f)
+            fused_names.add(f.name)
+        for wl in list(gen.WORKLOADS.values()) + other + fused + sweep:
             name = wl.name
-            rr = run_gpu(wl, max(5, args.steps // 2), 3, device)
-            fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, elem_bytes(wl.dtype),
-                                 elem_bytes(wl.param_dtype))
-            table.append({"workload": name, "desc": describe(wl),
+            is_fused = name in fused_names
+            rr = run_gpu(wl, max(5, args.steps // 2), 3, device, fused=is_fused)
+            es = elem_bytes(wl.dtype)
+            fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, es, elem_bytes(wl.param_dtype))
+            if is_fused:  # + read residual, write sum; + read dsum
+                fb, bb = fb + 2 * wl.M * wl.N * es, bb + wl.M * wl.N * es
+            table.append({"workload": name,
+                          "desc": describe(wl) + (", residual add fused" if is_fused else ""),
                           **{k: round(v, 5) for k, v in rr.items()},
                           "fwd_GBs": fb / (rr["fwd_kernel_ms"] * 1e-3) / 1e9,
                           "bwd_GBs": bb / ((rr["ms_per_step"] - rr["fwd_kernel_ms"]) * 1e-3) / 1e9,

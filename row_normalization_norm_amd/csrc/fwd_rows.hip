@@ -44,8 +44,10 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
   constexpr int ROWS = BLOCK / LPR;              // rows per workgroup per iteration
   constexpr int WPR = LPR > 64 ? LPR / 64 : 1;   // wavefronts per row
   using PV = Param<D, P>;
-  // gamma/beta kept in registers when they take at most 32 VGPRs
-  constexpr bool GREG = (PV::kPacked ? 4 : 8) * VPL * (LN ? 2 : 1) <= 32;
+  // gamma/beta kept in registers when they take at most 32 VGPRs; fp32 parameters beside
+  // 16-bit activations take twice that, which workgroups below 512 lanes can afford.
+  constexpr int kParamRegs = (PV::kPacked ? 4 : 8) * VPL * (LN ? 2 : 1);
+  constexpr bool GREG = kParamRegs <= 32 || (!PV::kPacked && LPR < 512 && kParamRegs <= 64);
 
   const int tid = threadIdx.x;
   const int lane = tid % LPR;
