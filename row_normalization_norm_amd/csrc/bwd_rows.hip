@@ -12,8 +12,10 @@
 // dx is computed the way the forward computes y: the rows of x and dy are loaded once
 // into registers (16-byte loads), the two row sums are reduced across the row's lanes,
 // and dx is written once.  The column sums stay in fp32 registers for every row the
-// workgroup handles; at the end the workgroup's row slots are combined through LDS in
-// a fixed order and written as ONE partial row of a [P, N] workspace.  A separate
+// workgroup handles (for wide one-row workgroups in LDS, each lane owning its columns'
+// words, which frees the registers for more resident waves); at the end the
+// workgroup's row slots are combined in a fixed order and written as ONE partial row
+// of a [P, N] workspace.  A separate
 // column-reduce kernel then adds the P partial rows.  That is the atomic-free two-stage
 // scheme the "Fused RMSNorm" page (aryanashta.me, "What didn't work") contrasts with
 // atomically adding every block's partial into one shared vector; the atomic variants
@@ -49,14 +51,32 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
   const int nvec = a.nvec;
   const int mode = a.mode;
 
-  float accg[VPL][EPV];
-  float accb[LN ? VPL : 1][EPV];
+  // Per-column partial sums: registers, or (LACC) LDS words private to each lane, laid
+  // out [dgamma|dbeta][vector][4-column chunk][lane] so that a wave's 16-byte accesses
+  // are contiguous.
+  constexpr bool LACC = bwd_lds_acc(LN, EPV, LPR, VPL);
+  static_assert(!LACC || ROWS == 1, "LDS partials assume one row per workgroup");
+  constexpr int CH = EPV / 4;
+  constexpr int RV = LACC ? 1 : VPL;
+  float accg[RV][EPV];
+  float accb[LN ? RV : 1][EPV];
+  __shared__ float4 lacc[LACC ? (LN ? 2 : 1) * VPL * CH * LPR : 1];
+  auto lidx = [&](int which, int v, int h) { return ((which * VPL + v) * CH + h) * LPR + lane; };
+  if constexpr (LACC) {
 #pragma unroll
-  for (int v = 0; v < VPL; ++v) {
+    for (int w = 0; w < (LN ? 2 : 1); ++w)
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      accg[v][e] = 0.0f;
-      if constexpr (LN) accb[v][e] = 0.0f;
+      for (int v = 0; v < VPL; ++v)
+#pragma unroll
+        for (int h = 0; h < CH; ++h) lacc[lidx(w, v, h)] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        accg[v][e] = 0.0f;
+        if constexpr (LN) accb[v][e] = 0.0f;
+      }
     }
   }
 
@@ -106,6 +126,9 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     rb = rok ? a.rstd[row] : 0.0f;
     mb = (LN && rok) ? a.mean[row] : 0.0f;
   };
+  // 1024-lane workgroups with 4 vectors per lane have no registers left for a second
+  // row; their 16 waves per CU keep enough loads in flight without it.
+  constexpr bool PF = !(LPR == 1024 && VPL > 2);
   u32x4 nx[VPL], nd[VPL], ng[ADD ? VPL : 1];
   float nr = 0.0f, nmu = 0.0f;
   if (blockIdx.x < a.groups) load(blockIdx.x, nx, nd, ng, nr, nmu);
@@ -133,7 +156,7 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     }
     const float r = nr;
     const float mu = nmu;
-    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd, ng, nr, nmu);
+    if (PF && grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd, ng, nr, nmu);
 
     // Row sums, and the per-column contributions (which do not need the row sums).
     // Short rows keep xhat and g in registers for the dx pass; longer ones unpack the
@@ -145,6 +168,7 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     for (int v = 0; v < VPL; ++v) {
       // LayerNorm's sum of g = dy * gamma: for 16-bit types straight from the packed words.
       if constexpr (LN && kDot) s2 = D::dot(dv[v], gv[v].v, s2);
+      float xs[EPV], ds[EPV];
 #pragma unroll
       for (int e = 0; e < EPV; ++e) {
         const float xh = (D::get(xv[v], e) - mu) * r;
@@ -152,11 +176,35 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
         const float g = d * (GUNP ? gunp[GUNP ? v : 0][e] : gv[v].get(e));
         s1 = fmaf(g, xh, s1);
         if constexpr (LN && !kDot) s2 += g;
-        accg[v][e] = fmaf(d, xh, accg[v][e]);
-        if constexpr (LN) accb[v][e] += d;
+        xs[e] = xh;
+        ds[e] = d;
+        if constexpr (!LACC) {
+          accg[v][e] = fmaf(d, xh, accg[v][e]);
+          if constexpr (LN) accb[v][e] += d;
+        }
         if constexpr (KEEP) {
           kxh[v][e] = xh;
           kg[v][e] = g;
+        }
+      }
+      if constexpr (LACC) {
+        // Rows past M contribute zeros (x and dy load as zeros there).
+#pragma unroll
+        for (int h = 0; h < CH; ++h) {
+          float4 t = lacc[lidx(0, v, h)];
+          t.x = fmaf(ds[4 * h], xs[4 * h], t.x);
+          t.y = fmaf(ds[4 * h + 1], xs[4 * h + 1], t.y);
+          t.z = fmaf(ds[4 * h + 2], xs[4 * h + 2], t.z);
+          t.w = fmaf(ds[4 * h + 3], xs[4 * h + 3], t.w);
+          lacc[lidx(0, v, h)] = t;
+          if constexpr (LN) {
+            float4 u = lacc[lidx(1, v, h)];
+            u.x += ds[4 * h];
+            u.y += ds[4 * h + 1];
+            u.z += ds[4 * h + 2];
+            u.w += ds[4 * h + 3];
+            lacc[lidx(1, v, h)] = u;
+          }
         }
       }
     }
@@ -215,6 +263,7 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
         }
       }
     }
+    if (!PF && grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nd, ng, nr, nmu);
   }
 
   if (mode == kAtomicRow) return;
@@ -223,7 +272,32 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
   // atomic mode, add it into dgamma/dbeta).
   float* const out_g = mode == kTwoStage ? a.part_g + (int64_t)blockIdx.x * a.N : a.dgamma;
   float* const out_b = mode == kTwoStage ? a.part_b + (int64_t)blockIdx.x * a.N : a.dbeta;
-  if constexpr (ROWS == 1) {
+  if constexpr (LACC) {
+    // Each lane reads back only the LDS words it wrote: no barrier is needed.
+#pragma unroll
+    for (int w = 0; w < (LN ? 2 : 1); ++w) {
+      float* const out = w == 0 ? out_g : out_b;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int vi = v * LPR + lane;
+        if (vi < nvec) {
+#pragma unroll
+          for (int h = 0; h < CH; ++h) {
+            const float4 t = lacc[lidx(w, v, h)];
+            const int col = vi * EPV + 4 * h;
+            if (mode == kTwoStage) {
+              *reinterpret_cast<float4*>(out + col) = t;
+            } else {
+              unsafeAtomicAdd(out + col, t.x);
+              unsafeAtomicAdd(out + col + 1, t.y);
+              unsafeAtomicAdd(out + col + 2, t.z);
+              unsafeAtomicAdd(out + col + 3, t.w);
+            }
+          }
+        }
+      }
+    }
+  } else if constexpr (ROWS == 1) {
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
@@ -299,8 +373,10 @@ hipError_t RN_LAUNCHER(int lpr, int vpl, const BwdArgs& a, int grid, hipStream_t
   constexpr bool kLN = RN_KIND == 1;
   using D = Types<RN_TC>::D;
   using P = Types<RN_TC>::P;
-#define RN_CASE(L, V) \
-  if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, s);
+#define RN_CASE(L, V)                                                \
+  if constexpr (bwd_mapping_built(kLN, D::kPerVec, L, V)) {          \
+    if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, s); \
+  }
   RN_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;

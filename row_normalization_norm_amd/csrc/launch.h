@@ -36,8 +36,9 @@ constexpr bool tc_is16(int tc) { return tc != kTcF32; }  // 16-bit activations
   X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 6) X(1024, 8)
 
 // The backward keeps x, dy and per-column fp32 partials of dgamma (and dbeta) in
-// registers; beyond 4 vectors per lane (1 at 1024 lanes, where a lane may use at
-// most 128 VGPRs) the kernel spills, so those mappings are not built.
+// registers.  Wide one-row workgroups keep the partials in LDS instead (bwd_lds_acc);
+// 1024-lane mappings with more than one vector per lane exist only in that form (in
+// registers they would exceed the 128 VGPRs a 1024-thread workgroup's lanes may use).
 #define RN_BWD_MAPPINGS(X)                                                             \
   X(8, 1) X(8, 2) X(8, 3) X(8, 4)                                                      \
   X(16, 1) X(16, 2) X(16, 3) X(16, 4)                                                  \
@@ -46,7 +47,24 @@ constexpr bool tc_is16(int tc) { return tc != kTcF32; }  // 16-bit activations
   X(128, 1) X(128, 2) X(128, 3) X(128, 4)                                              \
   X(256, 1) X(256, 2) X(256, 3) X(256, 4)                                              \
   X(512, 1) X(512, 2) X(512, 3) X(512, 4)                                              \
-  X(1024, 1)
+  X(1024, 1) X(1024, 2) X(1024, 4)
+
+constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup (and per CU) on gfx950
+// fp32 partial sums per lane of a backward row mapping; epv = elements per 16-byte vector.
+constexpr int bwd_acc_floats(bool ln, int epv, int vpl) { return vpl * epv * (ln ? 2 : 1); }
+// Whether the backward row mapping keeps its per-column partials in LDS: one-row
+// workgroups (512+ lanes) whose partials take 16 or more registers per lane, when they
+// fit.  Measured on MI355X this is never slower, and it is what lets 1024-lane
+// workgroups hold 2 or 4 vectors per lane (LayerNorm bf16 at N = 16384: 5.4 TB/s
+// against 4.0 TB/s for the best split-row configuration).
+constexpr bool bwd_lds_acc(bool ln, int epv, int lpr, int vpl) {
+  return lpr >= 512 && bwd_acc_floats(ln, epv, vpl) >= 16 &&
+         lpr * bwd_acc_floats(ln, epv, vpl) * 4 <= kLdsBytes;
+}
+// Whether the backward row mapping is built for this kind and element width.
+constexpr bool bwd_mapping_built(bool ln, int epv, int lpr, int vpl) {
+  return lpr < 1024 || vpl == 1 || bwd_lds_acc(ln, epv, lpr, vpl);
+}
 
 // Split-row (cluster) kernels: (threads per member workgroup, vectors per lane, rows
 // per step).

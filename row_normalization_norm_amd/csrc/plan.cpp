@@ -51,6 +51,9 @@ int bwd_target_vpl(int64_t nvec) { return nvec <= 128 ? 2 : nvec <= 256 ? 1 : 4;
 // over a cluster (1024 lanes x 8 vectors; wider mappings spill).
 constexpr int64_t kFwdRowsMaxVecs = 8192;
 constexpr int64_t kBwdRowsMaxVecs = 2048;  // same for the backward
+// Up to this length the backward also tries the 1024-lane mappings that keep their
+// per-column partials in LDS (built for some kinds and element widths only).
+constexpr int64_t kBwdRowsLdsMaxVecs = 4096;
 // Vectors per lane of the cluster kernels: beyond these the kernels need more than the
 // 128 VGPRs a 1024-thread workgroup may use (the backward also holds the per-column
 // partial sums and a prefetched row of x and dy).
@@ -73,14 +76,15 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // lane closest to `target`, then the fewest lanes (with `distance_first`, closeness to the
 // target ranks before padding).  Mappings whose last vector slot would be empty in every
 // lane are not considered.
-template <size_t K>
+template <size_t K, typename Built>
 bool choose_mapping(const Mapping (&list)[K], int64_t units, int target, int max_vpl, int req_lpr,
-                    int req_vpl, bool distance_first, Mapping* out) {
+                    int req_vpl, bool distance_first, Built built, Mapping* out) {
   bool found = false;
   Mapping best{0, 0};
   int64_t best_waste = 0;
   int best_dist = 0;
   for (const Mapping& m : list) {
+    if (!built(m)) continue;
     if (req_lpr && m.lpr != req_lpr) continue;
     if (req_vpl && m.vpl != req_vpl) continue;
     if (!req_vpl && m.vpl > max_vpl) continue;
@@ -139,10 +143,17 @@ bool choose_mapping_n(const Mapping* list, int n, int64_t units, int target, int
 bool plan_rows(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec,
                const norm_options_t& o, bool atomic, Plan& p) {
   Mapping m{0, 0};
-  const bool ok = backward ? choose_mapping(kBwdMappings, nvec, bwd_target_vpl(nvec), 1 << 30,
-                                            o.lanes_per_row, o.vecs_per_lane, true, &m)
-                           : choose_mapping(kFwdMappings, nvec, fwd_target_vpl(nvec), 1 << 30,
-                                            o.lanes_per_row, o.vecs_per_lane, false, &m);
+  const int epv = nvec > 0 ? int(N / nvec) : 8;  // elements per 16-byte vector
+  const bool ok =
+      backward
+          ? choose_mapping(kBwdMappings, nvec, bwd_target_vpl(nvec), 1 << 30, o.lanes_per_row,
+                           o.vecs_per_lane, true,
+                           [&](const Mapping& c) {
+                             return bwd_mapping_built(layernorm, epv, c.lpr, c.vpl);
+                           },
+                           &m)
+          : choose_mapping(kFwdMappings, nvec, fwd_target_vpl(nvec), 1 << 30, o.lanes_per_row,
+                           o.vecs_per_lane, false, [](const Mapping&) { return true; }, &m);
   if (!ok) return false;
   p.path = NORM_PATH_ROWS;
   p.lpr = m.lpr;
@@ -320,6 +331,9 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
       } else if (atomic ||
                  nvec <= (backward ? kBwdRowsMaxVecs : kFwdRowsMaxVecs)) {
         ok = plan_rows(backward, layernorm, M, N, nvec, o, atomic, p);
+      } else if (backward && nvec <= kBwdRowsLdsMaxVecs && !o.lanes_per_row &&
+                 !o.vecs_per_lane && plan_rows(true, layernorm, M, N, nvec, o, false, p)) {
+        // a 1024-lane mapping with LDS partials covers the row
       } else if (!plan_cluster(backward, layernorm, M, N, nvec, dtype, o, p)) {
         if (backward) {
           plan_split(layernorm, M, N, nvec, true, o, p);

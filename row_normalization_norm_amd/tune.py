@@ -113,6 +113,10 @@ def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 1024), grids_b=(0, 256, 512),
             for grid in grids:
                 opt = rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=lanes, vecs_per_lane=vecs,
                                  grid=grid)
+                try:
+                    rn.norm_plan(bwd, ln, M, N, code, options=opt)
+                except rn.NormError:
+                    break  # mapping not built for this kind and element width
                 record(direction, opt, rn.NORM_PATH_ROWS, lanes, vecs, grid)
         if not cluster or nvec <= 1024:
             continue
@@ -154,10 +158,13 @@ def sweep(out_path, ns=SWEEP_N):
 
 
 def table(jsonl_paths):
-    """C++ header with the fastest candidate per (direction, kind, dtype, row length)."""
+    """C++ header with the fastest candidate per (direction, kind, dtype, row length).
+    A shape measured in a later file is taken from that file alone (its kernels may have
+    changed since the earlier measurement)."""
     best = {}
     compiled = {"fwd": set(mappings("fwd")), "bwd": set(mappings("bwd"))}
     for p in jsonl_paths:
+        mine = {}
         with open(p) as f:
             for line in f:
                 r = json.loads(line)
@@ -165,8 +172,9 @@ def table(jsonl_paths):
                     continue  # a mapping no longer built
                 nvec = r.get("nvec") or r["N"] // (8 if r["dtype"] == "bf16" else 4)
                 key = (r["dir"] == "bwd", r["kind"] == "ln", r["dtype"] == "bf16", nvec)
-                if key not in best or r["GBs"] > best[key][1]["GBs"]:
-                    best[key] = (r["N"], r)
+                if key not in mine or r["GBs"] > mine[key][1]["GBs"]:
+                    mine[key] = (r["N"], r)
+        best.update(mine)
     lines = []
     for key in sorted(best, key=lambda k: (-k[0], -k[1], -k[2], k[3])):
         N, r = best[key]
@@ -188,7 +196,8 @@ def main():
     ap.add_argument("--n", type=int, nargs="+", default=list(SWEEP_N),
                     help="row lengths to sweep (default: all)")
     ap.add_argument("--table", metavar="IN.jsonl", nargs="+",
-                    help="print csrc/tuned.h built from sweep results (later files win ties)")
+                    help="print csrc/tuned.h built from sweep results (a shape in a later "
+                         "file replaces the earlier files' results for it)")
     args = ap.parse_args()
     if args.sweep:
         sys.path.insert(0, os.path.dirname(HERE))

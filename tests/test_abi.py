@@ -232,7 +232,7 @@ def test_cluster_plans():
     """Rows longer than one workgroup's registers are split over a cluster of workgroups,
     each owning a column slice; forward and backward both, bf16 and fp32."""
     cases = [(False, BF16, 131072), (False, F32, 65536), (True, BF16, 131072), (True, BF16, 65536),
-             (True, BF16, 32768), (True, F32, 65536), (True, F32, 32768), (True, F32, 16384)]
+             (True, BF16, 32768), (True, F32, 65536), (True, F32, 32768)]
     for bwd, dt, N in cases:
             M = (1 << 27) // N
             p = rn.norm_plan(bwd, True, M, N, dt)
@@ -248,6 +248,42 @@ def test_cluster_plans():
     # shorter rows stay in one workgroup's registers (no forward workspace)
     assert rn.norm_plan(False, True, 8192, 16384, BF16).path == rn.NORM_PATH_ROWS
     assert rn.norm_plan(True, True, 16384, 8192, BF16).path == rn.NORM_PATH_ROWS
+
+
+def test_lds_partial_mappings():
+    """1024-lane backward mappings with 2 or 4 vectors per lane keep their per-column
+    partials in LDS; they exist where those partials fit in 160 KiB (4 bytes x 1024 lanes
+    x vectors x elements per vector x 1 or 2 sums), and the planner uses them for rows
+    up to 4096 vectors, else splits the row over a cluster."""
+    rows = rn.NORM_PATH_ROWS
+
+    def built(ln, dt, lpr, vpl):
+        epv = 8 if dt == BF16 else 4
+        N = (lpr * vpl - 7) * epv
+        try:
+            rn.norm_plan(True, ln, 1000, N, dt,
+                         options=rn.Options(path=rows, lanes_per_row=lpr, vecs_per_lane=vpl))
+            return True
+        except rn.NormError:
+            return False
+
+    for ln in (False, True):
+        for dt in (BF16, F32):
+            epv = 8 if dt == BF16 else 4
+            for vpl in (2, 4):
+                lds = 4 * 1024 * vpl * epv * (2 if ln else 1)
+                assert built(ln, dt, 1024, vpl) == (lds <= 160 * 1024 and vpl * epv * (2 if ln else 1) >= 16), \
+                    (ln, dt, vpl)
+    # tuned long rows that now stay in one workgroup
+    p = rn.norm_plan(True, True, 8192, 16384, BF16)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rows, 1024, 2)
+    p = rn.norm_plan(True, True, 8192, 16384, F32)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rows, 1024, 4)
+    # untuned lengths: 3500 vectors fit 1024 x 4 where it is built (RMSNorm bf16), not for
+    # LayerNorm bf16; 2500 vectors have no 1024 x 3 mapping
+    assert rn.norm_plan(True, False, 4096, 3500 * 8, BF16).path == rows
+    assert rn.norm_plan(True, True, 4096, 3500 * 8, BF16).path == rn.NORM_PATH_CLUSTER
+    assert rn.norm_plan(True, False, 4096, 2500 * 8, BF16).path == rn.NORM_PATH_CLUSTER
     assert rn.norm_fwd_workspace_size(65536, 4096, True, BF16) == 0
 
 
