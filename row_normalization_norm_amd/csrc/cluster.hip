@@ -345,10 +345,21 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   const int64_t vofs = static_cast<int64_t>(member) * c.slice_vecs;
   const int64_t nsteps = (a.M + R - 1) / R;
 
+  // Per-column partial sums of the member's slice: registers, or (LACC, wide members)
+  // LDS words private to each lane, [dgamma|dbeta][vector][4-column chunk][lane].
+  constexpr bool LACC = bwd_lds_acc(LN, EPV, T, VPL);
+  constexpr int CH = EPV / 4;
+  constexpr int RV = LACC ? 1 : VPL;
+  __shared__ float4 lacc[LACC ? (LN ? 2 : 1) * VPL * CH * T : 1];
+  auto lidx = [&](int which, int v, int h) { return ((which * VPL + v) * CH + h) * T + tid; };
+
   bool own[VPL];
   PV g[VPL];
-  float gf[VPL][EPV];  // gamma unpacked once: the slice is the same for every row
-  float accg[VPL][EPV], accb[LN ? VPL : 1][EPV];
+  // gamma unpacked once (the slice is the same for every row), except in 1024-lane
+  // members holding 16+ elements per lane, which have no registers for it
+  constexpr bool GF = !(T == 1024 && VPL * EPV >= 16);
+  float gf[GF ? VPL : 1][EPV];
+  float accg[RV][EPV], accb[LN ? RV : 1][EPV];
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     own[v] = v * T + tid < c.slice_vecs;
@@ -359,9 +370,19 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     }
 #pragma unroll
     for (int e = 0; e < EPV; ++e) {
-      gf[v][e] = g[v].get(e);
-      accg[v][e] = 0.0f;
-      if constexpr (LN) accb[v][e] = 0.0f;
+      if constexpr (GF) gf[v][e] = g[v].get(e);
+    }
+    if constexpr (LACC) {
+#pragma unroll
+      for (int w = 0; w < (LN ? 2 : 1); ++w)
+#pragma unroll
+        for (int h = 0; h < CH; ++h) lacc[lidx(w, v, h)] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        accg[v][e] = 0.0f;
+        if constexpr (LN) accb[v][e] = 0.0f;
+      }
     }
   }
 
@@ -403,15 +424,39 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         if constexpr (LN && kDot) s2 = D::dot(sb.d[i][v], g[v].v, s2);
+        float xs[EPV], ds[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           const float xh = (D::get_fresh(sb.x[i][v], e) - mu) * r;
           const float d = D::get_fresh(sb.d[i][v], e);
-          const float gg = d * gf[v][e];
+          const float gg = d * (GF ? gf[GF ? v : 0][e] : g[v].get_fresh(e));
           s1 = fmaf(gg, xh, s1);
           if constexpr (LN && !kDot) s2 += gg;
-          accg[v][e] = fmaf(d, xh, accg[v][e]);
-          if constexpr (LN) accb[v][e] += d;
+          xs[e] = xh;
+          ds[e] = d;
+          if constexpr (!LACC) {
+            accg[v][e] = fmaf(d, xh, accg[v][e]);
+            if constexpr (LN) accb[v][e] += d;
+          }
+        }
+        if constexpr (LACC) {
+#pragma unroll
+          for (int h = 0; h < CH; ++h) {
+            float4 t = lacc[lidx(0, v, h)];
+            t.x = fmaf(ds[4 * h], xs[4 * h], t.x);
+            t.y = fmaf(ds[4 * h + 1], xs[4 * h + 1], t.y);
+            t.z = fmaf(ds[4 * h + 2], xs[4 * h + 2], t.z);
+            t.w = fmaf(ds[4 * h + 3], xs[4 * h + 3], t.w);
+            lacc[lidx(0, v, h)] = t;
+            if constexpr (LN) {
+              float4 u = lacc[lidx(1, v, h)];
+              u.x += ds[4 * h];
+              u.y += ds[4 * h + 1];
+              u.z += ds[4 * h + 2];
+              u.w += ds[4 * h + 3];
+              lacc[lidx(1, v, h)] = u;
+            }
+          }
         }
       }
       out[2 * i] = s1;
@@ -477,7 +522,8 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
           const float xh = (D::get_fresh(b[0].x[i][v], e) - mu) * r;
-          const float gg = D::get_fresh(b[0].d[i][v], e) * gf[v][e];
+          const float gg =
+              D::get_fresh(b[0].d[i][v], e) * (GF ? gf[GF ? v : 0][e] : g[v].get_fresh(e));
           o[e] = fmaf(gg, r, fmaf(xh, nrc1, nrc2));
           if constexpr (ADD) o[e] += D::get_fresh(b[0].g2[i][v], e);
         }
@@ -495,10 +541,19 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   for (int v = 0; v < VPL; ++v) {
     if (!own[v]) continue;
     const int64_t col0 = (vofs + v * T + tid) * EPV;
+    if constexpr (LACC) {
+      // each lane reads back only the LDS words it wrote
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      out_g[col0 + e] = accg[v][e];
-      if constexpr (LN) out_b[col0 + e] = accb[v][e];
+      for (int h = 0; h < CH; ++h) {
+        *reinterpret_cast<float4*>(out_g + col0 + 4 * h) = lacc[lidx(0, v, h)];
+        if constexpr (LN) *reinterpret_cast<float4*>(out_b + col0 + 4 * h) = lacc[lidx(1, v, h)];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        out_g[col0 + e] = accg[v][e];
+        if constexpr (LN) out_b[col0 + e] = accb[v][e];
+      }
     }
   }
 }

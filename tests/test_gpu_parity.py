@@ -156,6 +156,60 @@ def test_cluster_path(device, kind, dtype, pdtype, N, C, R):
     full_check(w, device, rows=np.arange(M), fwd_options=opt, bwd_options=opt)
 
 
+def _cluster_mapping_cases():
+    import re
+    src = open(rn.__file__.replace("__init__.py", "csrc/launch.h")).read()
+    cases = []
+    for direction, macro in (("fwd", "RN_CLUSTER_FWD_MAPPINGS"), ("bwd", "RN_CLUSTER_BWD_MAPPINGS")):
+        lines = src[src.index(f"#define {macro}"):].splitlines()
+        end = next(i for i, line in enumerate(lines) if not line.rstrip().endswith("\\"))
+        body = "\n".join(lines[:end + 1])
+        for t, v, r in re.findall(r"X\((\d+), (\d+), (\d+)\)", body):
+            cases.append((direction, int(t), int(v), int(r)))
+    return cases
+
+
+CLUSTER_MAPPINGS = _cluster_mapping_cases()
+
+
+@pytest.mark.parametrize("direction,T,V,R", CLUSTER_MAPPINGS,
+                         ids=[f"{d}-{t}x{v}r{r}" for d, t, v, r in CLUSTER_MAPPINGS])
+@pytest.mark.parametrize("dtype,pdtype", [("bf16", None), ("f32", None), ("f16", "f32")],
+                         ids=["bf16", "f32", "f16+f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_every_cluster_mapping(device, kind, dtype, pdtype, direction, T, V, R):
+    """Force each compiled split-row mapping (threads, vectors per lane, rows per step) on
+    a 2-member cluster whose slice leaves the last vector slot partly empty, with a row
+    count that leaves the last step and the clusters unevenly loaded."""
+    epv = 4 if dtype == "f32" else 8
+    C = 2
+    slice_vecs = T * V - max(1, T // 3)
+    N = C * slice_vecs * epv
+    M = 37
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.3, x_std=1.2, pdtype=pdtype)
+    opt = rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=C, lanes_per_row=T, vecs_per_lane=V,
+                     cluster_rows=R)
+    code = dtype_code(dtype, pdtype)
+    bwd = direction == "bwd"
+    try:
+        rn.norm_plan(bwd, kind == "ln", M, N, code, options=opt)
+    except rn.NormError:
+        pytest.skip("mapping not built for this direction")
+    if rn.norm_cluster_resident(bwd, kind == "ln", M, N, code, opt) != 1:
+        pytest.skip("cooperative grid does not fit")
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    if not bwd:
+        run.forward(opt)
+        run.sync()
+        check_forward(run, inputs, np.arange(M))
+    else:
+        run.forward()
+        run.backward(opt)
+        run.sync()
+        check_backward(run, inputs, np.arange(M))
+
+
 @pytest.mark.parametrize("name", ["rms4"])
 def test_long_rows_run_on_cluster_path(device, name):
     w = gen.WORKLOADS[name]
