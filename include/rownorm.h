@@ -34,6 +34,11 @@
  *     valid once the stream has synchronised.  The workspace must stay alive until
  *     the backward has completed on that stream.  Calls on one stream are ordered;
  *     concurrent calls on different streams must not share a workspace.
+ *   - Graph capture: a call may be captured into a HIP graph (stream capture).  It
+ *     enqueues kernels only (no memset, copy, allocation or synchronisation).  Under
+ *     capture the split-row path, whose kernels need a cooperative launch, is replaced
+ *     by its fallback (the column-sliced backward, the scalar forward): same results
+ *     within the stated tolerances, more bytes moved.
  *   - Errors: every argument check runs on the host before any HIP call; on an
  *     invalid argument the call returns its status and enqueues nothing.  A failed
  *     launch returns NORM_ERR_HIP.  No C++ exception crosses the boundary.

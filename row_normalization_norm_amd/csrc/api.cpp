@@ -188,6 +188,20 @@ bool fit_cluster(bool backward, int kind, int tc, bool add, Plan& p) {
 
 namespace {
 
+// Whether work enqueued on `stream` is being captured into a graph.  The split-row
+// kernels need a cooperative launch, which a captured graph does not take, so under
+// capture a CLUSTER plan is replaced by its fallback (the split backward, the scalar
+// forward).  A failed query is read as capturing, and its error is cleared so that it
+// does not surface from the next launch.
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
 ClusterArgs cluster_args(const Plan& p, char* ws) {
   ClusterArgs c;
   c.C = p.cluster;
@@ -261,7 +275,8 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   const int kind = ln ? 1 : 0;
   EventScope ev{opt, stream};
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(false, kind, dt.tc, fused, p)) {
+  if (p.path == NORM_PATH_CLUSTER &&
+      (capturing(stream) || !fit_cluster(false, kind, dt.tc, fused, p))) {
     make_fallback_plan(false, ln, M, N, dt.x, &p);
   }
   hipError_t e = hipSuccess;
@@ -319,7 +334,8 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   }
 
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(true, kind, dt.tc, dres != nullptr, p)) {
+  if (p.path == NORM_PATH_CLUSTER &&
+      (capturing(stream) || !fit_cluster(true, kind, dt.tc, dres != nullptr, p))) {
     make_fallback_plan(true, ln, M, N, dt.x, &p);
   }
   BwdArgs a;

@@ -1,0 +1,112 @@
+"""Entry points captured into a HIP graph (torch.cuda.graph, stream capture) and replayed.
+
+Each case runs forward + backward eagerly for the reference outputs, captures the same
+calls into a graph, then replays it several times with unrelated eager work and
+synchronisations between the replays (the outputs are cleared by fill kernels before
+each replay), and requires every replay to reproduce the eager outputs bit for bit.
+Under capture the split-row plans, which need a cooperative launch, are replaced by
+their fallbacks (the split backward, the scalar forward); for those shapes the eager
+reference is computed with the same fallback paths forced.
+"""
+import numpy as np
+import pytest
+
+import gen
+import row_normalization_norm_amd as rn
+from parity import to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # kind, dtype, M, N, fused
+    ("rms", "bf16", 4096, 1024, False),    # the small benchmark shape (row-resident path)
+    ("ln", "bf16", 1000, 4096, False),
+    ("ln", "f32", 96, 65536, False),       # backward on the split-row path when eager
+    ("rms", "bf16", 16, 131072, False),    # forward and backward on the split-row path
+    ("ln", "bf16", 333, 1000, False),      # N not a multiple of 8: scalar and split paths
+    ("ln", "bf16", 512, 4096, True),       # residual-add entry points
+    ("rms", "f32", 700, 12288, True),
+]
+_CODE = {"bf16": rn.NORM_DTYPE_BF16, "f32": rn.NORM_DTYPE_F32}
+
+
+def _capture_options(backward, kind, M, N, dtype):
+    """Options that make the eager call take the path the captured call takes."""
+    p = rn.norm_plan(backward, kind == "ln", M, N, _CODE[dtype])
+    if p.path != rn.NORM_PATH_CLUSTER:
+        return None
+    return rn.Options(path=rn.NORM_PATH_SPLIT if backward else rn.NORM_PATH_GENERIC)
+
+
+@pytest.mark.parametrize("kind,dtype,M,N,fused", CASES,
+                         ids=[f"{k}-{d}-{m}x{n}{'-add' if f else ''}" for k, d, m, n, f in CASES])
+@pytest.mark.parametrize("own_workspace", [True, False], ids=["workspace", "alloc"])
+def test_graph_replay_matches_eager(device, kind, dtype, M, N, fused, own_workspace):
+    import torch
+    w = gen.Workload(f"graph_{kind}_{dtype}_{M}x{N}", kind, dtype, M, N, 1e-5, x_mean=0.1,
+                     x_std=1.1, config=21)
+    inp = gen.make_inputs(w, residual=fused)
+    ln = kind == "ln"
+    x = to_device(inp["x"], dtype, device)
+    dy = to_device(inp["dy"], dtype, device)
+    g = to_device(inp["gamma"], dtype, device)
+    b = to_device(inp["beta"], dtype, device) if ln else None
+    res = to_device(inp["res"], dtype, device) if fused else None
+    dsum = to_device(inp["dsum"], dtype, device) if fused else None
+    out = dict(y=torch.empty_like(x), dx=torch.empty_like(x), rstd=torch.empty(M, device=device),
+               dg=torch.empty(N, device=device))
+    if ln:
+        out.update(mean=torch.empty(M, device=device), db=torch.empty(N, device=device))
+    if fused:
+        out["s"] = torch.empty_like(x)
+    fopt = _capture_options(False, kind, M, N, dtype)
+    bopt = _capture_options(True, kind, M, N, dtype)
+    code = _CODE[dtype]
+    if own_workspace:
+        fws_n = rn.norm_fwd_workspace_size(M, N, ln, code)
+        fws = torch.empty(fws_n, dtype=torch.uint8, device=device) if fws_n else None
+        bws = torch.empty(max(rn.norm_bwd_workspace_size(M, N, ln, code), 1), dtype=torch.uint8,
+                          device=device)
+    else:
+        fws = bws = None
+
+    def step(fo, bo):
+        o = out
+        if fused:
+            if ln:
+                rn.norm_ln_fwd_add(x, res, g, b, o["y"], o["s"], o["mean"], o["rstd"], eps=w.eps,
+                                   workspace=fws, options=fo)
+                rn.norm_ln_bwd_add(dy, o["s"], g, o["mean"], o["rstd"], dsum, o["dx"], o["dg"],
+                                   o["db"], workspace=bws, options=bo)
+            else:
+                rn.norm_rms_fwd_add(x, res, g, o["y"], o["s"], o["rstd"], eps=w.eps,
+                                    workspace=fws, options=fo)
+                rn.norm_rms_bwd_add(dy, o["s"], g, o["rstd"], dsum, o["dx"], o["dg"],
+                                    workspace=bws, options=bo)
+        elif ln:
+            rn.norm_ln_fwd(x, g, b, o["y"], o["mean"], o["rstd"], eps=w.eps, workspace=fws,
+                           options=fo)
+            rn.norm_ln_bwd(dy, x, g, o["mean"], o["rstd"], o["dx"], o["dg"], o["db"],
+                           workspace=bws, options=bo)
+        else:
+            rn.norm_rms_fwd(x, g, o["y"], o["rstd"], eps=w.eps, workspace=fws, options=fo)
+            rn.norm_rms_bwd(dy, x, g, o["rstd"], o["dx"], o["dg"], workspace=bws, options=bo)
+
+    step(fopt, bopt)
+    torch.cuda.synchronize(device)
+    ref = {k: v.clone() for k, v in out.items()}
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(None, None)
+    scratch = torch.empty(1 << 20, device=device)
+    for rep in range(3):
+        for v in out.values():
+            v.zero_()
+        scratch.normal_()  # unrelated eager work between replays
+        torch.cuda.synchronize(device)
+        graph.replay()
+        torch.cuda.synchronize(device)
+        for k, v in out.items():
+            assert torch.equal(v, ref[k]), f"replay {rep}: {k} differs from the eager result"
+    assert np.isfinite(out["dg"].cpu().numpy()).all()
