@@ -212,6 +212,18 @@ def run_gpu(w, steps, warmup, device, fused=False):
                 wall_s=wall, sets=b.sets, setup_s=b.setup_s)
 
 
+def workload_by_name(name):
+    """A named workload, or a sweep point written sweep_{rms|ln}_{bf16|f32}_N{N}."""
+    import gen
+    if name in gen.WORKLOADS:
+        return gen.WORKLOADS[name]
+    parts = name.split("_")
+    if len(parts) == 4 and parts[0] == "sweep" and parts[1] in ("rms", "ln") and \
+            parts[2] in ("bf16", "f32", "f16") and parts[3].startswith("N") and parts[3][1:].isdigit():
+        return gen.sweep_workload(parts[1], parts[2], int(parts[3][1:]))
+    raise SystemExit(f"unknown workload {name!r}")
+
+
 def graph_step_ms(w, device, fused=False, replays=20):
     """Step time with the host out of the loop: one step per rotating buffer set captured
     into a HIP graph (torch.cuda.graph), replayed `replays` times."""
@@ -234,6 +246,31 @@ def graph_step_ms(w, device, fused=False, replays=20):
     stop.record()
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / (replays * b.sets)
+
+
+def copy_reference_ms(nbytes, device, reps=10):
+    """A plain device copy (torch's copy kernel) of nbytes, with rotating buffer pairs so
+    that the working set is at least twice the MALL: the achievable time for moving the
+    forward's bytes (read nbytes, write nbytes) at this size."""
+    import torch
+    sets = max(1, math.ceil(2 * MALL_BYTES / (2 * nbytes)))
+    src = [torch.empty(nbytes, dtype=torch.uint8, device=device).fill_(1) for _ in range(sets)]
+    dst = [torch.empty_like(t) for t in src]
+    for d, t in zip(dst, src):
+        d.copy_(t)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        for d, t in zip(dst, src):
+            d.copy_(t)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / (reps * sets)
+    del src, dst
+    torch.cuda.empty_cache()
+    return ms
 
 
 def copy_probe(nbytes, steps, device):
@@ -363,7 +400,7 @@ def summarize(d, workload, warmup, steps, copy_bytes):
             for k, v in counter("LDS", f"{w}_counter_collection.csv", name).items():
                 lds.setdefault(k, {})[name] = v
     import gen
-    wl = gen.WORKLOADS[w]
+    wl = workload_by_name(w)
     s, ps = elem_bytes(wl.dtype), elem_bytes(wl.param_dtype)
     fwd_b, bwd_b = ideal_bytes(wl.kind, wl.M, wl.N, s, ps)
     main_b = main_bwd_kernel_bytes(wl.kind, wl.M, wl.N, s, ps)
@@ -492,7 +529,7 @@ def main():
         print(json.dumps(copy_probe(args.copy_probe, args.steps, device)), flush=True)
         return
 
-    w = gen.WORKLOADS[args.workload]
+    w = workload_by_name(args.workload)
     s, ps = elem_bytes(w.dtype), elem_bytes(w.param_dtype)
     fwd_b, bwd_b = ideal_bytes(w.kind, w.M, w.N, s, ps)
     r = run_gpu(w, args.steps, args.warmup, device)
@@ -567,6 +604,10 @@ def main():
                           "fwd_GBs": fb / (rr["fwd_kernel_ms"] * 1e-3) / 1e9,
                           "bwd_GBs": bb / ((rr["ms_per_step"] - rr["fwd_kernel_ms"]) * 1e-3) / 1e9,
                           "step_GBs": (fb + bb) / (rr["ms_per_step"] * 1e-3) / 1e9})
+            # a plain copy of the forward's bytes (read and write M*N elements)
+            cms = copy_reference_ms(wl.M * wl.N * es, device)
+            table[-1]["copy_ms"] = round(cms, 5)
+            table[-1]["copy_GBs"] = 2 * wl.M * wl.N * es / (cms * 1e-3) / 1e9
             if rr["ms_per_step"] < 0.1:
                 # launch-bound: also the step replayed from a captured graph
                 gms = graph_step_ms(wl, device, fused=is_fused)

@@ -95,36 +95,64 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
   // With ADD the residual's vectors come with x's.
   auto load = [&](int64_t grp, u32x4 (&buf)[VPL], u32x4 (&rbuf)[ADD ? VPL : 1]) {
     const int64_t row = grp * ROWS + slot;
+    if constexpr (VPL > 8) {
+      // The widest mappings address the row from one opaque per-lane pointer.
+      const u32x4* xp = opaque_ptr(static_cast<const u32x4*>(a.x) + (row * nvec + lane));
+      const u32x4* rp =
+          ADD ? opaque_ptr(static_cast<const u32x4*>(a.res) + (row * nvec + lane)) : nullptr;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int vi = v * LPR + lane;
-      const bool ok = row < a.M && vi < nvec;
-      buf[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
-      if constexpr (ADD) rbuf[v] = ok ? ld16_stream(a.res, row * nvec + vi) : zero16();
+      for (int v = 0; v < VPL; ++v) {
+        const bool ok = row < a.M && v * LPR + lane < nvec;
+        buf[v] = ok ? ld16_stream(xp, v * LPR) : zero16();
+        if constexpr (ADD) rbuf[v] = ok ? ld16_stream(rp, v * LPR) : zero16();
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int vi = v * LPR + lane;
+        const bool ok = row < a.M && vi < nvec;
+        buf[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
+        if constexpr (ADD) rbuf[v] = ok ? ld16_stream(a.res, row * nvec + vi) : zero16();
+      }
     }
   };
-  u32x4 nx[VPL], nr[ADD ? VPL : 1];
-  if (blockIdx.x < a.groups) load(blockIdx.x, nx, nr);
+  // Mappings with more than 8 vectors per lane (a whole 256 KiB row in one workgroup)
+  // have no registers for a second row: each row is loaded at the top of its iteration,
+  // and the other resident waves keep HBM busy meanwhile.
+  constexpr bool PF = VPL <= 8;
+  u32x4 nx[PF ? VPL : 1], nr[(PF && ADD) ? VPL : 1];
+  if constexpr (PF) {
+    if (blockIdx.x < a.groups) load(blockIdx.x, nx, nr);
+  }
 
   for (int64_t grp = blockIdx.x; grp < a.groups; grp += gridDim.x) {
     const int64_t row = grp * ROWS + slot;
     const bool row_ok = row < a.M;
     const int64_t vbase = row * nvec;
 
-    u32x4 xv[VPL];
+    u32x4 xv[VPL], rv[ADD ? VPL : 1];
+    if constexpr (PF) {
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) xv[v] = nx[v];
+      for (int v = 0; v < VPL; ++v) {
+        xv[v] = nx[v];
+        if constexpr (ADD) rv[v] = nr[v];
+      }
+    } else {
+      load(grp, xv, rv);
+    }
     if constexpr (ADD) {
       // The row normalized is the residual sum, rounded to the activation type and
       // written out as it is formed.
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         const int vi = v * LPR + lane;
-        xv[v] = D::add(xv[v], nr[v]);
+        xv[v] = D::add(xv[v], rv[v]);
         if (row_ok && vi < nvec) st16_stream(a.sum, vbase + vi, xv[v]);
       }
     }
-    if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nr);
+    if constexpr (PF) {
+      if (grp + gridDim.x < a.groups) load(grp + gridDim.x, nx, nr);
+    }
 
     // RMSNorm: mean of squares.  LayerNorm: the mean, then the mean squared deviation
     // from it, both reduced from the registers (the row is read from memory once).
@@ -167,6 +195,13 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
       }
     }
 
+    // The widest mappings read gamma/beta per vector from opaque per-lane bases.
+    constexpr int kPB = PV::kPacked ? 16 : 32;  // parameter bytes per 16-byte vector
+    const char* gp = VPL > 8 ? opaque_ptr(static_cast<const char*>(a.gamma) + lane * kPB)
+                             : static_cast<const char*>(a.gamma);
+    const char* bp = (VPL > 8 && LN) ? opaque_ptr(static_cast<const char*>(a.beta) + lane * kPB)
+                                     : static_cast<const char*>(a.beta);
+    constexpr int kGS = VPL > 8 ? 0 : 1;  // lane term of the vector index for the plain bases
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
       const int vi = v * LPR + lane;
@@ -176,8 +211,8 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_rows_kernel(const FwdArgs 
           gv = g[v];
           if constexpr (LN) bv = b[v];
         } else {
-          gv.load(a.gamma, vi);
-          if constexpr (LN) bv.load(a.beta, vi);
+          gv.load(gp, v * LPR + kGS * lane);
+          if constexpr (LN) bv.load(bp, v * LPR + kGS * lane);
         }
         float o[EPV];
 #pragma unroll

@@ -48,8 +48,10 @@ constexpr int kBwdGrid = 256;
 int fwd_target_vpl(int64_t nvec) { return nvec < 1024 ? 4 : 2; }
 int bwd_target_vpl(int64_t nvec) { return nvec <= 128 ? 2 : nvec <= 256 ? 1 : 4; }
 // Longest row (in 16-byte vectors) the forward keeps in one workgroup before splitting it
-// over a cluster (1024 lanes x 8 vectors; wider mappings spill).
+// over a cluster (1024 lanes x 8 vectors), and the longest it tries the no-prefetch
+// 12- and 16-vector mappings for (1024 x 16: a whole 256 KiB row per workgroup).
 constexpr int64_t kFwdRowsMaxVecs = 8192;
+constexpr int64_t kFwdRowsWideMaxVecs = 16384;
 constexpr int64_t kBwdRowsMaxVecs = 2048;  // same for the backward
 // Up to this length the backward also tries the 1024-lane mappings that keep their
 // per-column partials in LDS (built for some kinds and element widths only).
@@ -334,6 +336,9 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
       } else if (backward && nvec <= kBwdRowsLdsMaxVecs && !o.lanes_per_row &&
                  !o.vecs_per_lane && plan_rows(true, layernorm, M, N, nvec, o, false, p)) {
         // a 1024-lane mapping with LDS partials covers the row
+      } else if (!backward && nvec <= kFwdRowsWideMaxVecs && !o.lanes_per_row &&
+                 !o.vecs_per_lane && plan_rows(false, layernorm, M, N, nvec, o, false, p)) {
+        // a 12- or 16-vector mapping covers the row
       } else if (!plan_cluster(backward, layernorm, M, N, nvec, dtype, o, p)) {
         if (backward) {
           plan_split(layernorm, M, N, nvec, true, o, p);

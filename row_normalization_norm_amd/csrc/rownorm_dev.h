@@ -241,6 +241,15 @@ __device__ inline void st16(void* base, int64_t vec_index, const u32x4& v) {
 }
 // Streaming variants for data touched once (x, dy, y, dx): non-temporal hint, so the
 // stream does not evict gamma/beta and the partial rows from the caches.
+// The same pointer, opaque to the optimiser: addresses formed from it inside a loop are
+// not hoisted out of the loop as one live 64-bit address per vector (which spills the
+// widest mappings).
+template <typename T>
+__device__ inline T* opaque_ptr(T* p) {
+  asm volatile("" : "+v"(p));
+  return p;
+}
+
 __device__ inline u32x4 ld16_stream(const void* base, int64_t vec_index) {
   return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + vec_index);
 }

@@ -90,9 +90,9 @@ def ln_bwd(**kw):
     (ln_fwd, dict(beta=None), rn.NORM_ERR_NULL_PTR),
     (ln_fwd, dict(mean=A + 1), rn.NORM_ERR_MISALIGNED),
     # rows long enough to be split over a cluster of workgroups need a forward workspace
-    (rms_fwd, dict(M=2048, N=131072), rn.NORM_ERR_NULL_PTR),
-    (rms_fwd, dict(M=2048, N=131072, ws=A, ws_bytes=64), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
-    (ln_fwd, dict(M=2048, N=131072, ws=A + 8, ws_bytes=1 << 20), rn.NORM_ERR_MISALIGNED),
+    (rms_fwd, dict(M=1024, N=262144), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(M=1024, N=262144, ws=A, ws_bytes=64), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
+    (ln_fwd, dict(M=1024, N=262144, ws=A + 8, ws_bytes=1 << 20), rn.NORM_ERR_MISALIGNED),
     (rms_bwd, dict(dy=None), rn.NORM_ERR_NULL_PTR),
     (rms_bwd, dict(rstd=None), rn.NORM_ERR_NULL_PTR),
     (rms_bwd, dict(dgamma=None), rn.NORM_ERR_NULL_PTR),
@@ -181,9 +181,10 @@ def test_plan_shape_classes():
         cover = p.lanes_per_row * p.vecs_per_lane
         assert p.path == rn.NORM_PATH_ROWS and 48 <= cover < 48 + p.lanes_per_row
         assert p.lanes_per_row <= 32
-    # very long rows are split over a cluster of workgroups, forward and backward
-    for bwd in (False, True):
-        p = rn.norm_plan(bwd, False, 2048, 131072, BF16)
+    # very long rows are split over a cluster of workgroups (the backward from 131072
+    # bf16 columns, the forward beyond one workgroup's 16 vectors per lane)
+    for bwd, N in ((False, 262144), (True, 131072)):
+        p = rn.norm_plan(bwd, False, 2048, N, BF16)
         assert p.path == rn.NORM_PATH_CLUSTER and p.cluster_size >= 2 and p.cluster_rows >= 1
     # the two-pass column-sliced backward remains available
     p = rn.norm_plan(True, False, 2048, 131072, BF16, options=rn.Options(path=rn.NORM_PATH_SPLIT))
@@ -231,7 +232,7 @@ def test_workspace_size():
 def test_cluster_plans():
     """Rows longer than one workgroup's registers are split over a cluster of workgroups,
     each owning a column slice; forward and backward both, bf16 and fp32."""
-    cases = [(False, BF16, 131072), (False, F32, 65536), (True, BF16, 131072), (True, BF16, 65536),
+    cases = [(False, BF16, 262144), (False, F32, 131072), (True, BF16, 131072), (True, BF16, 65536),
              (True, BF16, 32768), (True, F32, 65536), (True, F32, 32768)]
     for bwd, dt, N in cases:
             M = (1 << 27) // N
@@ -245,8 +246,15 @@ def test_cluster_plans():
                 assert p.partial_rows == p.grid // p.cluster_size
             ws = (rn.norm_bwd_workspace_size if bwd else rn.norm_fwd_workspace_size)(M, N, True, dt)
             assert ws >= p.workspace_bytes > 0
-    # shorter rows stay in one workgroup's registers (no forward workspace)
+    # shorter rows stay in one workgroup's registers (no forward workspace); the forward
+    # keeps a whole 256 KiB row (1024 lanes x 16 vectors)
     assert rn.norm_plan(False, True, 8192, 16384, BF16).path == rn.NORM_PATH_ROWS
+    for dt, N in ((BF16, 131072), (F32, 65536)):
+        p = rn.norm_plan(False, False, 2048, N, dt)
+        assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 1024, 16)
+    # untuned: 12000 vectors fit 1024 x 12; 10000 vectors fit no wide mapping
+    assert rn.norm_plan(False, True, 64, 12000 * 8, BF16).vecs_per_lane == 12
+    assert rn.norm_plan(False, True, 64, 10000 * 8, BF16).path == rn.NORM_PATH_CLUSTER
     assert rn.norm_plan(True, True, 16384, 8192, BF16).path == rn.NORM_PATH_ROWS
 
 

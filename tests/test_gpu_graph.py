@@ -22,7 +22,8 @@ CASES = [
     ("rms", "bf16", 4096, 1024, False),    # the small benchmark shape (row-resident path)
     ("ln", "bf16", 1000, 4096, False),
     ("ln", "f32", 96, 65536, False),       # backward on the split-row path when eager
-    ("rms", "bf16", 16, 131072, False),    # forward and backward on the split-row path
+    ("rms", "bf16", 16, 131072, False),    # a whole row per workgroup forward
+    ("rms", "bf16", 8, 262144, False),     # forward and backward on the split-row path
     ("ln", "bf16", 333, 1000, False),      # N not a multiple of 8: scalar and split paths
     ("ln", "bf16", 512, 4096, True),       # residual-add entry points
     ("rms", "f32", 700, 12288, True),

@@ -212,11 +212,15 @@ def test_every_cluster_mapping(device, kind, dtype, pdtype, direction, T, V, R):
 
 @pytest.mark.parametrize("name", ["rms4"])
 def test_long_rows_run_on_cluster_path(device, name):
+    """The 131072-column workload: the forward holds a whole row per 1024-lane workgroup
+    (16 vectors per lane); the backward, which also keeps per-column partial sums, splits
+    the row over a co-resident cluster."""
     w = gen.WORKLOADS[name]
     code = rn.NORM_DTYPE_BF16 if w.dtype == "bf16" else rn.NORM_DTYPE_F32
-    for bwd in (False, True):
-        assert rn.norm_plan(bwd, w.kind == "ln", w.M, w.N, code).path == rn.NORM_PATH_CLUSTER
-        assert rn.norm_cluster_resident(bwd, w.kind == "ln", w.M, w.N, code) == 1
+    p = rn.norm_plan(False, w.kind == "ln", w.M, w.N, code)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 1024, 16)
+    assert rn.norm_plan(True, w.kind == "ln", w.M, w.N, code).path == rn.NORM_PATH_CLUSTER
+    assert rn.norm_cluster_resident(True, w.kind == "ln", w.M, w.N, code) == 1
 
 
 @pytest.mark.parametrize("grid", [1, 3, 64])
