@@ -248,27 +248,36 @@ def graph_step_ms(w, device, fused=False, replays=20):
     return start.elapsed_time(stop) / (replays * b.sets)
 
 
-def copy_reference_ms(nbytes, device, reps=10):
-    """A plain device copy (torch's copy kernel) of nbytes, with rotating buffer pairs so
-    that the working set is at least twice the MALL: the achievable time for moving the
-    forward's bytes (read nbytes, write nbytes) at this size."""
+def stream_reference_ms(nbytes, device, two_reads=False, reps=10):
+    """The library's streaming reference kernel over nbytes per stream (copy: read a,
+    write d; two_reads: read a and b, write d), with rotating buffers so that the working
+    set is at least twice the MALL: the achievable time for moving the forward's (copy)
+    or the backward's (two reads, one write) element bytes at this size."""
     import torch
-    sets = max(1, math.ceil(2 * MALL_BYTES / (2 * nbytes)))
-    src = [torch.empty(nbytes, dtype=torch.uint8, device=device).fill_(1) for _ in range(sets)]
-    dst = [torch.empty_like(t) for t in src]
-    for d, t in zip(dst, src):
-        d.copy_(t)
+    import row_normalization_norm_amd as rn
+    nbytes = (nbytes + 15) // 16 * 16
+    streams = 3 if two_reads else 2
+    sets = max(1, math.ceil(2 * MALL_BYTES / (streams * nbytes)))
+    bufs = [[torch.empty(nbytes, dtype=torch.uint8, device=device).fill_(1)
+             for _ in range(streams)] for _ in range(sets)]
+
+    def run(bs):
+        rn.norm_stream_reference(1 if two_reads else 0, bs[0], bs[1] if two_reads else None,
+                                 bs[-1])
+
+    for bs in bufs:
+        run(bs)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record()
     for _ in range(reps):
-        for d, t in zip(dst, src):
-            d.copy_(t)
+        for bs in bufs:
+            run(bs)
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / (reps * sets)
-    del src, dst
+    del bufs
     torch.cuda.empty_cache()
     return ms
 
@@ -604,10 +613,13 @@ def main():
                           "fwd_GBs": fb / (rr["fwd_kernel_ms"] * 1e-3) / 1e9,
                           "bwd_GBs": bb / ((rr["ms_per_step"] - rr["fwd_kernel_ms"]) * 1e-3) / 1e9,
                           "step_GBs": (fb + bb) / (rr["ms_per_step"] * 1e-3) / 1e9})
-            # a plain copy of the forward's bytes (read and write M*N elements)
-            cms = copy_reference_ms(wl.M * wl.N * es, device)
-            table[-1]["copy_ms"] = round(cms, 5)
-            table[-1]["copy_GBs"] = 2 * wl.M * wl.N * es / (cms * 1e-3) / 1e9
+            # the streaming reference at the forward's (1 read + 1 write of M*N elements)
+            # and the backward's (2 reads + 1 write) element bytes
+            nb = wl.M * wl.N * es
+            cms = stream_reference_ms(nb, device)
+            tms = stream_reference_ms(nb, device, two_reads=True)
+            table[-1].update(copy_ms=round(cms, 5), copy_GBs=2 * nb / (cms * 1e-3) / 1e9,
+                             two_read_ms=round(tms, 5), two_read_GBs=3 * nb / (tms * 1e-3) / 1e9)
             if rr["ms_per_step"] < 0.1:
                 # launch-bound: also the step replayed from a captured graph
                 gms = graph_step_ms(wl, device, fused=is_fused)

@@ -269,6 +269,20 @@ norm_status_t norm_ln_bwd_add(const void* dy, const void* sum, const void* gamma
                               norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, const norm_options_t* opt);
 
+/* ------------------------------------------------------------ measurement aid
+ * Not part of the normalization path: the achievable-bandwidth reference the benchmark
+ * quotes beside the norm kernels.  A plain streaming kernel over n 16-byte vectors with
+ * the same 16-byte non-temporal loads and stores:
+ *     kind 0 (copy, one read and one write per vector, the forward's mix): dst = a;
+ *     kind 1 (two reads and one write, the backward's mix): dst = a + b, as 32-bit
+ *     unsigned integers lane by lane.
+ * a, b (kind 1 only; ignored for kind 0) and dst are device pointers aligned to 16
+ * bytes; dst must not overlap a or b.  n >= 0 (n = 0 enqueues nothing).  Errors:
+ * NORM_ERR_BAD_OPTION for another kind, NORM_ERR_BAD_SHAPE for n < 0,
+ * NORM_ERR_NULL_PTR, NORM_ERR_MISALIGNED; a failed launch is NORM_ERR_HIP. */
+norm_status_t norm_stream_reference(int kind, const void* a, const void* b, void* dst, int64_t n,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

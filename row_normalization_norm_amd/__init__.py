@@ -102,6 +102,7 @@ SIGNATURES = {
     "norm_rms_bwd_add": (_INT, [_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P, _OPT]),
     "norm_ln_bwd_add": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P,
                                _OPT]),
+    "norm_stream_reference": (_INT, [_INT, _P, _P, _P, _I64, _P]),
 }
 
 _lib = None
@@ -426,3 +427,21 @@ def norm_ln_bwd_add(dy, sum_in, gamma, mean, rstd, dsum, dx, dgamma, dbeta, work
                                  _opt(options)), "norm_ln_bwd_add")
     return dx, dgamma, dbeta
 
+
+# ------------------------------------------------------------------ measurement aid
+def norm_stream_reference(kind: int, a, b, dst, stream=None):
+    """Streaming reference kernel over dst's bytes (16-byte vectors): kind 0 copies a
+    into dst, kind 1 writes a + b (32-bit lanes).  Not part of the normalization path:
+    the achievable-bandwidth reference for the benchmark."""
+    nbytes = dst.numel() * dst.element_size()
+    if nbytes % 16:
+        raise ValueError("dst must hold a whole number of 16-byte vectors")
+    for t, n in ((a, "a"), (b, "b")):
+        if t is None:
+            continue
+        if t.numel() * t.element_size() < nbytes or not t.is_contiguous():
+            raise ValueError(f"{n} must be contiguous and at least as large as dst")
+    _check(lib().norm_stream_reference(int(kind), a.data_ptr(),
+                                       b.data_ptr() if b is not None else None, dst.data_ptr(),
+                                       nbytes // 16, _stream(dst.device, stream)),
+           "norm_stream_reference")

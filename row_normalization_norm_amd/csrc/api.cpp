@@ -587,6 +587,21 @@ int norm_cluster_resident(int is_backward, int is_layernorm, int64_t M, int64_t 
   return rownorm::fit_cluster(is_backward != 0, is_layernorm ? 1 : 0, dt.tc, false, p) ? 1 : 0;
 }
 
+norm_status_t norm_stream_reference(int kind, const void* a, const void* b, void* dst, int64_t n,
+                                    hipStream_t stream) {
+  return rownorm::guarded([&] {
+    if (kind != 0 && kind != 1) return NORM_ERR_BAD_OPTION;
+    if (n < 0) return NORM_ERR_BAD_SHAPE;
+    if (n == 0) return NORM_OK;
+    if (!a || !dst || (kind == 1 && !b)) return NORM_ERR_NULL_PTR;
+    if (!rownorm::aligned(a, 16) || !rownorm::aligned(dst, 16) ||
+        (kind == 1 && !rownorm::aligned(b, 16)))
+      return NORM_ERR_MISALIGNED;
+    return rownorm::hip_status(
+        rownorm::launch_stream_reference(kind == 1, a, b, dst, n, stream));
+  });
+}
+
 const char* norm_status_string(norm_status_t s) {
   switch (s) {
     case NORM_OK: return "ok";

@@ -400,6 +400,49 @@ hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P,
   return hipGetLastError();
 }
 
+// Streaming reference (a measurement aid, not on the normalization path): each workgroup
+// owns a contiguous chunk of 256 x kStreamVecs 16-byte vectors, issues all its loads,
+// then all its stores, with the norm kernels' non-temporal hints.
+constexpr int kStreamVecs = 4;
+
+template <bool TWO>
+__global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ a,
+                                                     const u32x4* __restrict__ b,
+                                                     u32x4* __restrict__ d, int64_t n) {
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * 256 * kStreamVecs + threadIdx.x;
+  u32x4 r[kStreamVecs];
+#pragma unroll
+  for (int v = 0; v < kStreamVecs; ++v) {
+    const int64_t i = base + v * 256;
+    r[v] = i < n ? ld16_stream(a, i) : zero16();
+    if constexpr (TWO) {
+      if (i < n) r[v] += ld16_stream(b, i);
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < kStreamVecs; ++v) {
+    const int64_t i = base + v * 256;
+    if (i < n) st16_stream(d, i, r[v]);
+  }
+}
+
+hipError_t launch_stream_reference(bool two_reads, const void* a, const void* b, void* d,
+                                   int64_t n, hipStream_t s) {
+  const int64_t per_block = 256 * kStreamVecs;
+  const int64_t grid = (n + per_block - 1) / per_block;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  const u32x4* pa = static_cast<const u32x4*>(a);
+  const u32x4* pb = static_cast<const u32x4*>(b);
+  u32x4* pd = static_cast<u32x4*>(d);
+  if (two_reads) {
+    hipLaunchKernelGGL((stream_kernel<true>), dim3(unsigned(grid)), dim3(256), 0, s, pa, pb, pd, n);
+  } else {
+    hipLaunchKernelGGL((stream_kernel<false>), dim3(unsigned(grid)), dim3(256), 0, s, pa, pb, pd,
+                       n);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(float* a, float* b, int32_t N, hipStream_t s) {
   int grid = (N + 255) / 256;
   if (grid > 1024) grid = 1024;

@@ -179,5 +179,8 @@ hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P,
                             float* dgamma, float* dbeta, hipStream_t s);
 // dgamma (and dbeta) <- 0, for the atomic modes.
 hipError_t launch_zero(float* a, float* b, int32_t N, hipStream_t s);
+// Measurement aid: d = a (copy) or d = a + b over n 16-byte vectors.
+hipError_t launch_stream_reference(bool two_reads, const void* a, const void* b, void* d,
+                                   int64_t n, hipStream_t s);
 
 }  // namespace rownorm

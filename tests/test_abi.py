@@ -26,11 +26,23 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     lib = rn.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in rownorm.h but not exported"
     assert set(names) == set(rn.SIGNATURES), "binding signatures out of sync with the header"
+
+
+def test_stream_reference_validation():
+    """The measurement aid checks its arguments on the host like the norm entry points."""
+    f = rn.lib().norm_stream_reference
+    assert f(2, A, A, A, 16, None) == rn.NORM_ERR_BAD_OPTION
+    assert f(0, A, None, A, -1, None) == rn.NORM_ERR_BAD_SHAPE
+    assert f(0, A, None, A, 0, None) == rn.NORM_OK  # nothing to do, nothing enqueued
+    assert f(0, None, None, A, 16, None) == rn.NORM_ERR_NULL_PTR
+    assert f(1, A, None, A, 16, None) == rn.NORM_ERR_NULL_PTR
+    assert f(0, A + 8, None, A, 16, None) == rn.NORM_ERR_MISALIGNED
+    assert f(1, A, A + 4, A, 16, None) == rn.NORM_ERR_MISALIGNED
 
 
 def test_status_strings():

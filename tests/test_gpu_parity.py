@@ -388,3 +388,20 @@ def test_events_and_streams(device):
     assert e0.elapsed_time(e1) > 0
     check_forward(run, inputs, sample_rows(w.M))
     check_backward(run, inputs, sample_rows(w.M))
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096 + 16, (1 << 20) + 48])
+def test_stream_reference(device, nbytes):
+    """The benchmark's streaming reference kernel: copy and a + b over 16-byte vectors,
+    including a ragged last workgroup."""
+    import torch
+    n = nbytes // 4
+    a = torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device=device)
+    b = torch.randint(0, 1 << 30, (n,), dtype=torch.int32, device=device)
+    d = torch.full((n,), -1, dtype=torch.int32, device=device)
+    rn.norm_stream_reference(0, a, None, d)
+    torch.cuda.synchronize(device)
+    assert torch.equal(d, a)
+    rn.norm_stream_reference(1, a, b, d)
+    torch.cuda.synchronize(device)
+    assert torch.equal(d, a + b)
