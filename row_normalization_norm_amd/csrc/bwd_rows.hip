@@ -107,6 +107,10 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
     }
   }
 
+  // 1024-lane workgroups with 4 vectors per lane have no registers left for a second
+  // row; their 16 waves per CU keep enough loads in flight without it.
+  constexpr bool PF = !(LPR == 1024 && VPL > 2);
+  constexpr bool OP = !PF;
   // The next row group's x, dy and saved statistics are loaded before the current one is
   // reduced, so HBM reads stay in flight through the reduction and the dx stores.
   // With ADD the gradient arriving at the residual sum comes with x and dy, and is
@@ -115,20 +119,33 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
                   float& rb, float& mb) {
     const int64_t row = grp * ROWS + slot;
     const bool rok = row < a.M;
+    if constexpr (OP) {
+      // The widest mapping addresses the row from opaque per-lane pointers (no per-vector
+      // 64-bit addresses hoisted out of the row loop).
+      const int64_t lofs = row * nvec + lane;
+      const u32x4* xp = opaque_ptr(static_cast<const u32x4*>(a.x) + lofs);
+      const u32x4* dp = opaque_ptr(static_cast<const u32x4*>(a.dy) + lofs);
+      const u32x4* rp = ADD ? opaque_ptr(static_cast<const u32x4*>(a.dres) + lofs) : nullptr;
 #pragma unroll
-    for (int v = 0; v < VPL; ++v) {
-      const int vi = v * LPR + lane;
-      const bool ok = rok && vi < nvec;
-      xb[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
-      db[v] = ok ? ld16_stream(a.dy, row * nvec + vi) : zero16();
-      if constexpr (ADD) gb[v] = ok ? ld16_stream(a.dres, row * nvec + vi) : zero16();
+      for (int v = 0; v < VPL; ++v) {
+        const bool ok = rok && v * LPR + lane < nvec;
+        xb[v] = ok ? ld16_stream(xp, v * LPR) : zero16();
+        db[v] = ok ? ld16_stream(dp, v * LPR) : zero16();
+        if constexpr (ADD) gb[v] = ok ? ld16_stream(rp, v * LPR) : zero16();
+      }
+    } else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int vi = v * LPR + lane;
+        const bool ok = rok && vi < nvec;
+        xb[v] = ok ? ld16_stream(a.x, row * nvec + vi) : zero16();
+        db[v] = ok ? ld16_stream(a.dy, row * nvec + vi) : zero16();
+        if constexpr (ADD) gb[v] = ok ? ld16_stream(a.dres, row * nvec + vi) : zero16();
+      }
     }
     rb = rok ? a.rstd[row] : 0.0f;
     mb = (LN && rok) ? a.mean[row] : 0.0f;
   };
-  // 1024-lane workgroups with 4 vectors per lane have no registers left for a second
-  // row; their 16 waves per CU keep enough loads in flight without it.
-  constexpr bool PF = !(LPR == 1024 && VPL > 2);
   u32x4 nx[VPL], nd[VPL], ng[ADD ? VPL : 1];
   float nr = 0.0f, nmu = 0.0f;
   if (blockIdx.x < a.groups) load(blockIdx.x, nx, nd, ng, nr, nmu);
