@@ -35,10 +35,7 @@
  *     the backward has completed on that stream.  Calls on one stream are ordered;
  *     concurrent calls on different streams must not share a workspace.
  *   - Graph capture: a call may be captured into a HIP graph (stream capture).  It
- *     enqueues kernels only (no memset, copy, allocation or synchronisation).  Under
- *     capture the split-row path, whose kernels need a cooperative launch, is replaced
- *     by its fallback (the column-sliced backward, the scalar forward): same results
- *     within the stated tolerances, more bytes moved.
+ *     enqueues kernels only (no memset, copy, allocation or synchronisation).
  *   - Errors: every argument check runs on the host before any HIP call; on an
  *     invalid argument the call returns its status and enqueues nothing.  A failed
  *     launch returns NORM_ERR_HIP.  No C++ exception crosses the boundary.
@@ -160,9 +157,10 @@ typedef enum norm_path {
                               registers: a per-row reduction pass, then a
                               column-sliced pass for dx and the partials */
   NORM_PATH_GENERIC = 3,   /* scalar loads, any N and alignment */
-  NORM_PATH_CLUSTER = 4    /* long rows split over a cluster of co-resident workgroups
-                              (cooperative launch), each owning a column slice and
-                              exchanging per-row partial sums through the workspace */
+  NORM_PATH_CLUSTER = 4    /* long rows split over a cluster of workgroups, each owning
+                              a column slice and exchanging per-row partial sums through
+                              the workspace (a member that waits too long for another's
+                              sums computes them itself, with the same result bits) */
 } norm_path_t;
 
 /* Options for the *_ex entry points; zero-initialise for defaults.  Used by tests and
@@ -181,6 +179,9 @@ typedef struct norm_options {
   int cluster_rows;    /* CLUSTER path: rows per exchange step (1 or 2); 0 = planner */
   hipEvent_t ev_start; /* if non-NULL, recorded on `stream` just before the main kernel */
   hipEvent_t ev_stop;  /* if non-NULL, recorded on `stream` just after the main kernel */
+  int cluster_wait;    /* CLUSTER path: polls of another member's partial sums before
+                          computing them locally; 0 = default, -1 = never wait (every
+                          member computes every partial itself: for tests) */
 } norm_options_t;
 
 /* What the planner chose for a call (filled by norm_plan). */

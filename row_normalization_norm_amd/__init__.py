@@ -60,7 +60,7 @@ class Options(ctypes.Structure):
                 ("vecs_per_lane", ctypes.c_int), ("dgamma_mode", ctypes.c_int),
                 ("grid", ctypes.c_int), ("cluster_size", ctypes.c_int),
                 ("cluster_rows", ctypes.c_int), ("ev_start", ctypes.c_void_p),
-                ("ev_stop", ctypes.c_void_p)]
+                ("ev_stop", ctypes.c_void_p), ("cluster_wait", ctypes.c_int)]
 
 
 class PlanInfo(ctypes.Structure):

@@ -188,37 +188,23 @@ bool fit_cluster(bool backward, int kind, int tc, bool add, Plan& p) {
 
 namespace {
 
-// Whether work enqueued on `stream` is being captured into a graph.  The split-row
-// kernels need a cooperative launch, which a captured graph does not take, so under
-// capture a CLUSTER plan is replaced by its fallback (the split backward, the scalar
-// forward).  A failed query is read as capturing, and its error is cleared so that it
-// does not surface from the next launch.
-bool capturing(hipStream_t stream) {
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cs) != hipSuccess) {
-    (void)hipGetLastError();
-    return true;
-  }
-  return cs != hipStreamCaptureStatusNone;
-}
-
-ClusterArgs cluster_args(const Plan& p, char* ws) {
+ClusterArgs cluster_args(const Plan& p, char* ws, const norm_options_t* opt) {
   ClusterArgs c;
   c.C = p.cluster;
   c.nclusters = p.nclusters;
   c.slice_vecs = p.slice_vecs;
   c.rows_per_step = p.rows_per_step;
-  c.spin_limit = kSpinLimit;
+  const int wait = opt ? opt->cluster_wait : 0;
+  c.spin_limit = wait > 0 ? uint32_t(wait) : wait < 0 ? 0u : kSpinLimit;
   c.xchg = reinterpret_cast<unsigned long long*>(ws + p.off_xchg);
-  c.status = reinterpret_cast<unsigned*>(ws + p.off_status);
   return c;
 }
 
-// Zero the exchange slots and the status word before a cluster launch.  A fill kernel
-// rather than a memset, so the call stays safe to capture in a graph.
+// Zero the exchange slots before a cluster launch.  A fill kernel rather than a memset,
+// so the call stays safe to capture in a graph.
 hipError_t clear_exchange(const Plan& p, char* ws, hipStream_t s) {
   return launch_zero(reinterpret_cast<float*>(ws + p.off_xchg), nullptr,
-                     int32_t((p.off_status + 256 - p.off_xchg) / 4), s);
+                     int32_t(p.xchg_bytes / 4), s);
 }
 
 norm_status_t check_workspace(const Plan& p, void* workspace, size_t given) {
@@ -275,8 +261,7 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   const int kind = ln ? 1 : 0;
   EventScope ev{opt, stream};
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER &&
-      (capturing(stream) || !fit_cluster(false, kind, dt.tc, fused, p))) {
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(false, kind, dt.tc, fused, p)) {
     make_fallback_plan(false, ln, M, N, dt.x, &p);
   }
   hipError_t e = hipSuccess;
@@ -290,7 +275,7 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
       e = launch_fwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
       break;
     case NORM_PATH_CLUSTER:
-      e = launch_fwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws),
+      e = launch_fwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws, opt),
                              p.grid, stream);
       break;
     default:
@@ -334,8 +319,7 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   }
 
   char* ws = static_cast<char*>(workspace);
-  if (p.path == NORM_PATH_CLUSTER &&
-      (capturing(stream) || !fit_cluster(true, kind, dt.tc, dres != nullptr, p))) {
+  if (p.path == NORM_PATH_CLUSTER && !fit_cluster(true, kind, dt.tc, dres != nullptr, p)) {
     make_fallback_plan(true, ln, M, N, dt.x, &p);
   }
   BwdArgs a;
@@ -374,7 +358,7 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   if (p.path == NORM_PATH_ROWS) {
     e = launch_bwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
   } else if (p.path == NORM_PATH_CLUSTER) {
-    e = launch_bwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws),
+    e = launch_bwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws, opt),
                            p.grid, stream);
   } else {
     const bool vec = p.path == NORM_PATH_SPLIT;

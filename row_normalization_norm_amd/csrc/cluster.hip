@@ -2,8 +2,8 @@
 //
 // The pages note that very long rows cost Triton on H100 because it cannot reduce a
 // row across cooperating SMs ("SOTA normalization performance with torch.compile",
-// theaicatchup.com, "How Did Torch.compile Catch Quack?").  Here C co-resident
-// workgroups share each row: workgroup k of a cluster owns the k-th column slice of every
+// theaicatchup.com, "How Did Torch.compile Catch Quack?").  Here C workgroups share
+// each row: workgroup k of a cluster owns the k-th column slice of every
 // row the cluster handles, keeps its slice of gamma (and beta) in registers for all of
 // them, and, in the backward, its slice's dgamma/dbeta column sums as well.  Per row, each
 // member reduces its slice inside the workgroup (DPP + LDS), publishes the partial sums,
@@ -17,8 +17,13 @@
 // atomic loads until the tag matches, so every word validates itself and no ordering
 // between different words is needed.  The slots are zeroed by a fill kernel before each
 // launch and each is written once per launch.
-// Co-residency of all workgroups is guaranteed by a cooperative launch; every wait is
-// bounded, and a timed-out wait yields NaN (and sets a status word) instead of hanging.
+//
+// The kernels are launched like any other (a cooperative launch costs about 25 us of
+// idle device time around every call on this platform), with a grid the device can hold
+// at once, so the members of a cluster normally run together.  Nothing depends on it:
+// a member that has polled another's words `spin_limit` times computes that member's
+// partial sums itself, from the same data with the same code (floating-point
+// contraction off), so the result has the same bits and every wait ends.
 //
 // LayerNorm statistics merge per-slice (sum, sum of squared deviations about the slice
 // mean) with the pairwise-update formula of Chan, Golub and LeVeque, so the variance is
@@ -49,23 +54,18 @@ __device__ inline void publish(unsigned long long* slot, uint32_t tag, float v) 
   __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until the slot carries `tag`.  Gives up after `limit` polls, or as soon as any
-// wait of the launch has given up (the status word is sticky), so a failed exchange
-// costs one time-out per launch, not one per row; the result is then NaN.
-__device__ inline float wait_for(unsigned long long* slot, uint32_t tag, uint32_t limit,
-                                 unsigned* status) {
-  for (uint32_t n = 0;; ++n) {
+// Poll the slot until it carries `tag`, at most `limit` times; the value on success.
+__device__ inline bool poll_for(unsigned long long* slot, uint32_t tag, uint32_t limit,
+                                float* out) {
+  for (uint32_t n = 0; n < limit; ++n) {
     const unsigned long long w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (static_cast<uint32_t>(w >> 32) == tag) return __uint_as_float(static_cast<uint32_t>(w));
-    if (n >= limit) {
-      atomicOr(status, 1u);
-      return __builtin_nanf("");
+    if (static_cast<uint32_t>(w >> 32) == tag) {
+      *out = __uint_as_float(static_cast<uint32_t>(w));
+      return true;
     }
-    if ((n & 63) == 63 &&
-        __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-      return __builtin_nanf("");
     __builtin_amdgcn_s_sleep(2);
   }
+  return false;
 }
 
 // Sum of K values over the workgroup at once (one barrier), identical in every thread.
@@ -121,22 +121,241 @@ __device__ inline void prefetch_step(const ClusterArgs& c, int64_t step,
 
 // Gather every member's K partials of `step` into xin[member * K + j]; visible to the whole
 // workgroup after the barrier.  A prefetched word that already carries the step's tag is
-// used as is; otherwise the thread polls.  The caller alternates between two xin buffers,
-// so values are never overwritten before every thread has read them.
+// used as is; otherwise the thread polls.  Returns the members whose words did not arrive
+// within the poll limit (a bit per member, the same in every thread): the caller computes
+// those partials itself.  The caller alternates between two xin / xok buffers, so values
+// are never overwritten before every thread has read them.
 template <int K>
-__device__ inline void gather_step(const ClusterArgs& c, int64_t step,
-                                   const unsigned long long (&pre)[K], float* xin) {
+__device__ inline unsigned gather_step(const ClusterArgs& c, int64_t step,
+                                       const unsigned long long (&pre)[K], float* xin, int* xok) {
   if (threadIdx.x < c.C) {
-    unsigned long long* base = c.xchg + step * c.C * K;
+    unsigned long long* base = c.xchg + (step * c.C + threadIdx.x) * K;
     const uint32_t tag = row_tag(step);
+    bool ok = c.spin_limit != 0;
 #pragma unroll
-    for (int j = 0; j < K; ++j)
-      xin[threadIdx.x * K + j] =
-          static_cast<uint32_t>(pre[j] >> 32) == tag
-              ? __uint_as_float(static_cast<uint32_t>(pre[j]))
-              : wait_for(base + threadIdx.x * K + j, tag, c.spin_limit, c.status);
+    for (int j = 0; j < K; ++j) {
+      float v = 0.0f;
+      if (ok) {
+        if (static_cast<uint32_t>(pre[j] >> 32) == tag) {
+          v = __uint_as_float(static_cast<uint32_t>(pre[j]));
+        } else {
+          ok = poll_for(base + j, tag, c.spin_limit, &v);
+        }
+      }
+      xin[threadIdx.x * K + j] = v;
+    }
+    xok[threadIdx.x] = ok ? 1 : 0;
   }
   __syncthreads();
+  unsigned miss = 0;
+  for (int m = 0; m < c.C; ++m) miss |= xok[m] ? 0u : (1u << m);
+  return miss;
+}
+
+// ------------------------------------------------------------------ partial row sums
+// A member whose partners' words do not arrive computes their partial sums itself
+// (fwd_missing / bwd_missing).  Both it and the partner perform the same operations in the
+// same order with floating-point contraction off, so the result has the same bits either
+// way.  The missing-partner paths are cold: their vector loops stay rolled (one vector
+// live at a time) so that they take next to no registers from the pipelined step loop.
+
+// Forward partial sums of a step's R rows over one slice, from an accessor X(i, v) of
+// its vectors: RMSNorm sums of squares; LayerNorm slice sums and sums of squared
+// deviations about the slice mean.  Reduced over the workgroup (identical in every thread).
+template <bool LN, typename D, int T, int VPL, int R, typename XF>
+__device__ __forceinline__ void fwd_partial(XF&& X, int slice_vecs, float slice_n,
+                                            float (&out)[(LN ? 2 : 1) * R], float* red,
+                                            int& parity) {
+#pragma clang fp contract(off)
+  constexpr int EPV = D::kPerVec;
+  constexpr int NW = T / 64;
+  constexpr int K = (LN ? 2 : 1) * R;
+  if constexpr (LN) {
+    float s[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      s[i] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) s[i] = D::sum(X(i, v), s[i]);
+    }
+    block_sum_n<NW, R>(s, red, parity);
+    float m2[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const float m_k = s[i] / slice_n;
+      m2[i] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const u32x4 xv = X(i, v);
+        const bool mine = v * T + static_cast<int>(threadIdx.x) < slice_vecs;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float d = mine ? D::get_fresh(xv, e) - m_k : 0.0f;
+          m2[i] = fmaf(d, d, m2[i]);
+        }
+      }
+    }
+    block_sum_n<NW, R>(m2, red, parity);
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      out[2 * i] = s[i];
+      out[2 * i + 1] = m2[i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      out[i] = 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) out[i] = D::sumsq(X(i, v), out[i]);
+    }
+    block_sum_n<NW, K>(out, red, parity);
+  }
+}
+
+// The forward partials of the members in `miss` (a bit per member) for step st, computed
+// from their slices (with ADD, the rounded residual sum those members write out), into
+// xs[member * K + j]: fwd_partial's operations in its order.  Returns the updated
+// reduction-buffer parity.
+template <bool LN, typename D, int T, int VPL, int R, bool ADD>
+__device__ __forceinline__ int fwd_missing(const FwdArgs& a, const ClusterArgs& c, unsigned miss,
+                                           int64_t st, float slice_n, float* red, float* xs,
+                                           int parity) {
+#pragma clang fp contract(off)
+  constexpr int EPV = D::kPerVec;
+  constexpr int NW = T / 64;
+  constexpr int K = (LN ? 2 : 1) * R;
+  const int tid = threadIdx.x;
+  for (int m = 0; m < c.C; ++m) {
+    if (!((miss >> m) & 1u)) continue;
+    const int64_t mofs = static_cast<int64_t>(m) * c.slice_vecs;
+    auto vec = [&](int i, int v) -> u32x4 {
+      const int64_t row = st * R + i;
+      const bool ok = v * T + tid < c.slice_vecs && row < a.M;
+      const int64_t idx = row * a.nvec + mofs + v * T + tid;
+      u32x4 xv = ok ? ld16_stream(a.x, idx) : zero16();
+      if constexpr (ADD) xv = D::add(xv, ok ? ld16_stream(a.res, idx) : zero16());
+      return xv;
+    };
+    float t[K];
+    if constexpr (LN) {
+      float sm[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        sm[i] = 0.0f;
+#pragma unroll 1
+        for (int v = 0; v < VPL; ++v) sm[i] = D::sum(vec(i, v), sm[i]);
+      }
+      block_sum_n<NW, R>(sm, red, parity);
+      float m2[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const float m_k = sm[i] / slice_n;
+        m2[i] = 0.0f;
+#pragma unroll 1
+        for (int v = 0; v < VPL; ++v) {
+          const u32x4 xv = vec(i, v);
+          const bool mine = v * T + tid < c.slice_vecs;
+#pragma unroll
+          for (int e = 0; e < EPV; ++e) {
+            const float d = mine ? D::get_fresh(xv, e) - m_k : 0.0f;
+            m2[i] = fmaf(d, d, m2[i]);
+          }
+        }
+      }
+      block_sum_n<NW, R>(m2, red, parity);
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        t[2 * i] = sm[i];
+        t[2 * i + 1] = m2[i];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        t[i] = 0.0f;
+#pragma unroll 1
+        for (int v = 0; v < VPL; ++v) t[i] = D::sumsq(vec(i, v), t[i]);
+      }
+      block_sum_n<NW, K>(t, red, parity);
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) xs[m * K + j] = t[j];
+    }
+  }
+  __syncthreads();
+  return parity;
+}
+
+// Backward row-sum terms of one 16-byte vector of a slice: s1 += g * xhat, s2 += g
+// (g = dy * gamma; gfv, when given, is gamma unpacked), and the unpacked xhat and dy.
+template <bool LN, bool kDot, typename D, typename PV>
+__device__ __forceinline__ void bwd_vec_sums(const u32x4& xv, const u32x4& dv, const PV& gv,
+                                             const float* gfv, float r, float mu, float& s1,
+                                             float& s2, float (&xs)[D::kPerVec],
+                                             float (&ds)[D::kPerVec]) {
+#pragma clang fp contract(off)
+  if constexpr (LN && kDot) s2 = D::dot(dv, gv.v, s2);
+#pragma unroll
+  for (int e = 0; e < D::kPerVec; ++e) {
+    const float xh = (D::get_fresh(xv, e) - mu) * r;
+    const float d = D::get_fresh(dv, e);
+    const float gg = d * (gfv ? gfv[e] : gv.get_fresh(e));
+    s1 = fmaf(gg, xh, s1);
+    if constexpr (LN && !kDot) s2 += gg;
+    xs[e] = xh;
+    ds[e] = d;
+  }
+}
+
+// The backward partial row sums of the members in `miss` for step st, computed from their
+// slices of x, dy and gamma (no column sums: those are each member's own), into
+// xs[member * K + j].  Returns the updated reduction-buffer parity.
+template <bool LN, typename D, typename P, int T, int VPL, int R>
+__device__ __forceinline__ int bwd_missing(const BwdArgs& a, const ClusterArgs& c, unsigned miss,
+                                        int64_t st, float* red, float* xs, int parity) {
+  using PV = Param<D, P>;
+  constexpr int EPV = D::kPerVec;
+  constexpr int NW = T / 64;
+  constexpr int K = 2 * R;
+  constexpr bool kDot = !std::is_same<D, F32>::value && PV::kPacked;
+  const int tid = threadIdx.x;
+  for (int m = 0; m < c.C; ++m) {
+    if (!((miss >> m) & 1u)) continue;
+    const int64_t mofs = static_cast<int64_t>(m) * c.slice_vecs;
+    float out[K];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = st * R + i;
+      const float r = row < a.M ? a.rstd[row] : 0.0f;
+      const float mu = (LN && row < a.M) ? a.mean[row] : 0.0f;
+      float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll 1
+      for (int v = 0; v < VPL; ++v) {
+        const bool mine = v * T + tid < c.slice_vecs;
+        const bool ok = mine && row < a.M;
+        const int64_t idx = row * a.nvec + mofs + v * T + tid;
+        const u32x4 xv = ok ? ld16_stream(a.x, idx) : zero16();
+        const u32x4 dv = ok ? ld16_stream(a.dy, idx) : zero16();
+        PV gv;
+        if (mine) {
+          gv.load(a.gamma, mofs + v * T + tid);
+        } else {
+          gv.clear();
+        }
+        float xs_[EPV], ds_[EPV];
+        bwd_vec_sums<LN, kDot, D>(xv, dv, gv, nullptr, r, mu, s1, s2, xs_, ds_);
+      }
+      out[2 * i] = s1;
+      out[2 * i + 1] = s2;
+    }
+    block_sum_n<NW, K>(out, red, parity);
+    if (tid == 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j) xs[m * K + j] = out[j];
+    }
+  }
+  __syncthreads();
+  return parity;
 }
 
 // Each workgroup keeps several steps in registers: the forward publishes step t+1's partial
@@ -174,6 +393,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
 
   __shared__ float red[2 * NW * R];
   __shared__ float xin[2][kMaxCluster * K];
+  __shared__ int xok[2][kMaxCluster];
   int parity = 0, xp = 0;
 
   // With ADD a step's residual slices come with x's and are added in before the step's
@@ -182,12 +402,16 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = st * R + i;
+      // the row's slice is addressed from opaque per-lane pointers (no per-vector 64-bit
+      // addresses kept live across the step loop)
+      const int64_t lofs = row * a.nvec + vofs + tid;
+      const u32x4* xp = opaque_ptr(static_cast<const u32x4*>(a.x) + lofs);
+      const u32x4* rp = ADD ? opaque_ptr(static_cast<const u32x4*>(a.res) + lofs) : nullptr;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         const bool ok = own[v] && row < a.M;
-        const int64_t idx = row * a.nvec + vofs + v * T + tid;
-        buf[i][v] = ok ? ld16_stream(a.x, idx) : zero16();
-        if constexpr (ADD) rbuf[i][v] = ok ? ld16_stream(a.res, idx) : zero16();
+        buf[i][v] = ok ? ld16_stream(xp, v * T) : zero16();
+        if constexpr (ADD) rbuf[i][v] = ok ? ld16_stream(rp, v * T) : zero16();
       }
     }
   };
@@ -204,46 +428,10 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
       }
     }
   };
-  // This member's partial sums of a step's rows: RMSNorm sums of squares; LayerNorm slice
-  // sums and sums of squared deviations about the slice means.
+  // This member's partial sums of a step's rows (fwd_partial).
   auto partial = [&](const u32x4 (&buf)[R][VPL], float (&out)[K]) {
-    if constexpr (LN) {
-      float s[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        s[i] = 0.0f;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) s[i] = D::sum(buf[i][v], s[i]);
-      }
-      block_sum_n<NW, R>(s, red, parity);
-      float m2[R];
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        const float m_k = s[i] / slice_n;
-        m2[i] = 0.0f;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v)
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) {
-            const float d = own[v] ? D::get_fresh(buf[i][v], e) - m_k : 0.0f;
-            m2[i] = fmaf(d, d, m2[i]);
-          }
-      }
-      block_sum_n<NW, R>(m2, red, parity);
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        out[2 * i] = s[i];
-        out[2 * i + 1] = m2[i];
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < R; ++i) {
-        out[i] = 0.0f;
-#pragma unroll
-        for (int v = 0; v < VPL; ++v) out[i] = D::sumsq(buf[i][v], out[i]);
-      }
-      block_sum_n<NW, K>(out, red, parity);
-    }
+    fwd_partial<LN, D, T, VPL, R>([&](int i, int v) -> u32x4 { return buf[i][v]; },
+                                  c.slice_vecs, slice_n, out, red, parity);
   };
 
   u32x4 b0[R][VPL], b1[R][VPL], b2[R][VPL];
@@ -258,21 +446,10 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
     partial(b0, mine);
     publish_step<K>(c, member, st, mine);
   }
-  for (; st < nsteps; st += c.nclusters) {
-    const int64_t s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
-    unsigned long long pre[K];
-    prefetch_step<K>(c, st, pre);
-    if (s1 < nsteps) {
-      float mine[K];
-      form_sum(s1, b1, r1);
-      partial(b1, mine);
-      publish_step<K>(c, member, s1, mine);
-    }
-    if (s2 < nsteps) load(s2, b2, r2);
-
-    float* xs = xin[xp];
-    xp ^= 1;
-    gather_step<K>(c, st, pre, xs);
+  // y of a step's rows from the gathered partials of every member (contraction off: the
+  // statistics come out the same wherever this runs).
+  auto emit_y = [&](const u32x4 (&buf)[R][VPL], int64_t st, const float* xs) {
+#pragma clang fp contract(off)
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = st * R + i;
@@ -306,7 +483,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float f = D::get_fresh(b0[i][v], e);
+          const float f = D::get_fresh(buf[i][v], e);
           if constexpr (LN) {
             o[e] = fmaf((f - mu) * r, g[v].get_fresh(e), b[v].get_fresh(e));
           } else {
@@ -316,6 +493,25 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
         st16_stream(a.y, row * a.nvec + vofs + v * T + tid, D::pack(o));
       }
     }
+  };
+
+  for (; st < nsteps; st += c.nclusters) {
+    const int64_t s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
+    unsigned long long pre[K];
+    prefetch_step<K>(c, st, pre);
+    if (s1 < nsteps) {
+      float mine[K];
+      form_sum(s1, b1, r1);
+      partial(b1, mine);
+      publish_step<K>(c, member, s1, mine);
+    }
+    if (s2 < nsteps) load(s2, b2, r2);
+
+    float* xs = xin[xp];
+    int* xk = xok[xp];
+    xp ^= 1;
+    if (gather_step<K>(c, st, pre, xs, xk)) break;  // a partner is late: finish below
+    emit_y(b0, st, xs);
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
@@ -327,6 +523,31 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
           r1[i][v] = r2[i][v];
         }
       }
+  }
+  // The rest of the steps, one at a time, computing any partial that does not arrive
+  // (reached only when a partner's words are late).  Steps before `done` have had this
+  // member's partials formed and published by the loop above; the residual sum of a step
+  // is formed again (and written again, with the same values).
+  if (st < nsteps) {
+    const int64_t done = st + 2 * c.nclusters;
+    for (; st < nsteps; st += c.nclusters) {
+      u32x4 sb[R][VPL], rb[ADD ? R : 1][VPL];
+      load(st, sb, rb);
+      form_sum(st, sb, rb);
+      if (st >= done) {
+        float mine[K];
+        partial(sb, mine);
+        publish_step<K>(c, member, st, mine);
+      }
+      unsigned long long pre[K];
+      prefetch_step<K>(c, st, pre);
+      float* xs = xin[xp];
+      int* xk = xok[xp];
+      xp ^= 1;
+      const unsigned miss = gather_step<K>(c, st, pre, xs, xk);
+      if (miss) parity = fwd_missing<LN, D, T, VPL, R, ADD>(a, c, miss, st, slice_n, red, xs, parity);
+      emit_y(sb, st, xs);
+    }
   }
 }
 
@@ -354,10 +575,10 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   auto lidx = [&](int which, int v, int h) { return ((which * VPL + v) * CH + h) * T + tid; };
 
   bool own[VPL];
-  PV g[VPL];
-  // gamma unpacked once (the slice is the same for every row), except in 1024-lane
-  // members holding 16+ elements per lane, which have no registers for it
+  // gamma kept in registers (the slice is the same for every row), also unpacked except
+  // in 1024-lane members holding 16+ elements per lane, which have no registers for that
   constexpr bool GF = !(T == 1024 && VPL * EPV >= 16);
+  PV g[VPL];
   float gf[GF ? VPL : 1][EPV];
   float accg[RV][EPV], accb[LN ? RV : 1][EPV];
 #pragma unroll
@@ -368,9 +589,9 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     } else {
       g[v].clear();
     }
+    if constexpr (GF) {
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      if constexpr (GF) gf[v][e] = g[v].get(e);
+      for (int e = 0; e < EPV; ++e) gf[v][e] = g[v].get(e);
     }
     if constexpr (LACC) {
 #pragma unroll
@@ -388,6 +609,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
 
   __shared__ float red[2 * NW * K];
   __shared__ float xin[2][kMaxCluster * K];
+  __shared__ int xok[2][kMaxCluster];
   int parity = 0, xp = 0;
 
   // A step's x and dy slices and its rows' saved statistics, loaded together.
@@ -400,13 +622,18 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const int64_t row = st * R + i;
+      // the row's slice is addressed from opaque per-lane pointers, so that no per-vector
+      // 64-bit addresses are kept live across the step loop
+      const int64_t lofs = row * a.nvec + vofs + tid;
+      const u32x4* xp = opaque_ptr(static_cast<const u32x4*>(a.x) + lofs);
+      const u32x4* dp = opaque_ptr(static_cast<const u32x4*>(a.dy) + lofs);
+      const u32x4* rp = ADD ? opaque_ptr(static_cast<const u32x4*>(a.dres) + lofs) : nullptr;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
         const bool ok = own[v] && row < a.M;
-        const int64_t idx = row * a.nvec + vofs + v * T + tid;
-        sb.x[i][v] = ok ? ld16_stream(a.x, idx) : zero16();
-        sb.d[i][v] = ok ? ld16_stream(a.dy, idx) : zero16();
-        if constexpr (ADD) sb.g2[i][v] = ok ? ld16_stream(a.dres, idx) : zero16();
+        sb.x[i][v] = ok ? ld16_stream(xp, v * T) : zero16();
+        sb.d[i][v] = ok ? ld16_stream(dp, v * T) : zero16();
+        if constexpr (ADD) sb.g2[i][v] = ok ? ld16_stream(rp, v * T) : zero16();
       }
       sb.r[i] = row < a.M ? a.rstd[row] : 0.0f;
       sb.mu[i] = (LN && row < a.M) ? a.mean[row] : 0.0f;
@@ -423,20 +650,14 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
       float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if constexpr (LN && kDot) s2 = D::dot(sb.d[i][v], g[v].v, s2);
         float xs[EPV], ds[EPV];
+        bwd_vec_sums<LN, kDot, D>(sb.x[i][v], sb.d[i][v], g[v], GF ? gf[GF ? v : 0] : nullptr, r,
+                                  mu, s1, s2, xs, ds);
+        if constexpr (!LACC) {
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float xh = (D::get_fresh(sb.x[i][v], e) - mu) * r;
-          const float d = D::get_fresh(sb.d[i][v], e);
-          const float gg = d * (GF ? gf[GF ? v : 0][e] : g[v].get_fresh(e));
-          s1 = fmaf(gg, xh, s1);
-          if constexpr (LN && !kDot) s2 += gg;
-          xs[e] = xh;
-          ds[e] = d;
-          if constexpr (!LACC) {
-            accg[v][e] = fmaf(d, xh, accg[v][e]);
-            if constexpr (LN) accb[v][e] += d;
+          for (int e = 0; e < EPV; ++e) {
+            accg[v][e] = fmaf(ds[e], xs[e], accg[v][e]);
+            if constexpr (LN) accb[v][e] += ds[e];
           }
         }
         if constexpr (LACC) {
@@ -464,7 +685,6 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     }
     block_sum_n<NW, K>(out, red, parity);
   };
-
   // S steps live in registers: b[0] waits for the exchange, b[1 .. S-3] are published,
   // b[S-2] is reduced and published this iteration and b[S-1] is being loaded, so the
   // exchange round trip of a step overlaps S-2 steps of work.
@@ -487,6 +707,41 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
       }
     }
   }
+  // dx of a step's rows from the gathered partials of every member (contraction off, as
+  // for the partials).
+  auto emit_dx = [&](const Stage& sb, int64_t st, const float* xs) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int64_t row = st * R + i;
+      if (row >= a.M) break;
+      float t1 = 0.0f, t2 = 0.0f;
+      for (int j = 0; j < c.C; ++j) {
+        t1 += xs[j * K + 2 * i];
+        t2 += xs[j * K + 2 * i + 1];
+      }
+      const float r = sb.r[i];
+      const float mu = sb.mu[i];
+      // dx = r * (g - c2 - xhat * c1) = g * r + (xhat * (-r * c1) + (-r * c2)).
+      const float nrc1 = -r * (t1 * a.inv_n);
+      const float nrc2 = LN ? -r * (t2 * a.inv_n) : 0.0f;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        if (!own[v]) continue;
+        float o[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const float xh = (D::get_fresh(sb.x[i][v], e) - mu) * r;
+          const float gg =
+              D::get_fresh(sb.d[i][v], e) * (GF ? gf[GF ? v : 0][e] : g[v].get_fresh(e));
+          o[e] = fmaf(gg, r, fmaf(xh, nrc1, nrc2));
+          if constexpr (ADD) o[e] += D::get_fresh(sb.g2[i][v], e);
+        }
+        st16_stream(a.dx, row * a.nvec + vofs + v * T + tid, D::pack(o));
+      }
+    }
+  };
+
   for (; st < nsteps; st += c.nclusters) {
     const int64_t sp = st + (S - 2) * c.nclusters, sl = st + (S - 1) * c.nclusters;
     unsigned long long pre[K];
@@ -499,39 +754,35 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     if (sl < nsteps) load(sl, b[S - 1]);
 
     float* xs = xin[xp];
+    int* xk = xok[xp];
     xp ^= 1;
-    gather_step<K>(c, st, pre, xs);
-#pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const int64_t row = st * R + i;
-      if (row >= a.M) break;
-      float t1 = 0.0f, t2 = 0.0f;
-      for (int j = 0; j < c.C; ++j) {
-        t1 += xs[j * K + 2 * i];
-        t2 += xs[j * K + 2 * i + 1];
-      }
-      const float r = b[0].r[i];
-      const float mu = b[0].mu[i];
-      // dx = r * (g - c2 - xhat * c1) = g * r + (xhat * (-r * c1) + (-r * c2)).
-      const float nrc1 = -r * (t1 * a.inv_n);
-      const float nrc2 = LN ? -r * (t2 * a.inv_n) : 0.0f;
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        if (!own[v]) continue;
-        float o[EPV];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float xh = (D::get_fresh(b[0].x[i][v], e) - mu) * r;
-          const float gg =
-              D::get_fresh(b[0].d[i][v], e) * (GF ? gf[GF ? v : 0][e] : g[v].get_fresh(e));
-          o[e] = fmaf(gg, r, fmaf(xh, nrc1, nrc2));
-          if constexpr (ADD) o[e] += D::get_fresh(b[0].g2[i][v], e);
-        }
-        st16_stream(a.dx, row * a.nvec + vofs + v * T + tid, D::pack(o));
-      }
-    }
+    if (gather_step<K>(c, st, pre, xs, xk)) break;  // a partner is late: finish below
+    emit_dx(b[0], st, xs);
 #pragma unroll
     for (int k = 0; k < S - 1; ++k) b[k] = b[k + 1];
+  }
+  // The rest of the steps, one at a time, computing any partial that does not arrive
+  // (reached only when a partner's words are late).  Steps before `done` have had this
+  // member's partial (and column sums) formed and published by the loop above.
+  if (st < nsteps) {
+    const int64_t done = st + (S - 1) * c.nclusters;
+    for (; st < nsteps; st += c.nclusters) {
+      Stage sb;
+      load(st, sb);
+      if (st >= done) {
+        float mine[K];
+        partial(sb, mine);
+        publish_step<K>(c, member, st, mine);
+      }
+      unsigned long long pre[K];
+      prefetch_step<K>(c, st, pre);
+      float* xs = xin[xp];
+      int* xk = xok[xp];
+      xp ^= 1;
+      const unsigned miss = gather_step<K>(c, st, pre, xs, xk);
+      if (miss) parity = bwd_missing<LN, D, P, T, VPL, R>(a, c, miss, st, red, xs, parity);
+      emit_dx(sb, st, xs);
+    }
   }
 
   // This member's slice of the cluster's partial row.
@@ -559,13 +810,10 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
 }
 
 template <typename K, typename A>
-hipError_t launch_coop(K kernel, int grid, int block, const A& a, const ClusterArgs& c,
-                       hipStream_t s) {
-  A a_copy = a;
-  ClusterArgs c_copy = c;
-  void* args[] = {&a_copy, &c_copy};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kernel), dim3(grid), dim3(block),
-                                    args, 0, s);
+hipError_t launch_split(K kernel, int grid, int block, const A& a, const ClusterArgs& c,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(kernel, dim3(grid), dim3(block), 0, s, a, c);
+  return hipGetLastError();
 }
 
 template <typename K>
@@ -594,9 +842,9 @@ hipError_t RN_FWD_LAUNCHER(int t, int vpl, int rows, const FwdArgs& a, const Clu
                            hipStream_t s) {
 #define RN_CASE(T_, V_, R_)                                                              \
   if (t == T_ && vpl == V_ && rows == R_)                                                \
-    return a.res ? launch_coop(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, grid, T_, a, \
+    return a.res ? launch_split(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, grid, T_, a, \
                                c, s)                                                     \
-                 : launch_coop(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, grid, T_, a, \
+                 : launch_split(fwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, grid, T_, a, \
                                c, s);
   RN_CLUSTER_FWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
@@ -607,9 +855,9 @@ hipError_t RN_BWD_LAUNCHER(int t, int vpl, int rows, const BwdArgs& a, const Clu
                            hipStream_t s) {
 #define RN_CASE(T_, V_, R_)                                                              \
   if (t == T_ && vpl == V_ && rows == R_)                                                \
-    return a.dres ? launch_coop(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, grid, T_, a, \
+    return a.dres ? launch_split(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, true>, grid, T_, a, \
                                 c, s)                                                    \
-                  : launch_coop(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, grid, T_, a, \
+                  : launch_split(bwd_cluster_kernel<kLN, DT, PT, T_, V_, R_, false>, grid, T_, a, \
                                 c, s);
   RN_CLUSTER_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE

@@ -77,7 +77,8 @@ constexpr bool bwd_mapping_built(bool ln, int epv, int lpr, int vpl) {
   X(256, 1, 1) X(256, 2, 1) X(512, 1, 1) X(512, 2, 1) X(1024, 1, 1) X(1024, 2, 1)         \
   X(256, 1, 2) X(512, 1, 2) X(1024, 1, 2) X(256, 2, 2) X(512, 2, 2)
 constexpr int kMaxCluster = 32;            // workgroups sharing one row, at most
-constexpr uint32_t kSpinLimit = 1u << 20;  // polls before a cluster wait gives up
+constexpr uint32_t kSpinLimit = 1u << 16;  // polls of a member's partials before a
+                                           // waiting member computes them itself
 
 // Threads per workgroup for a row mapping.
 constexpr int fwd_block(int lpr) { return lpr >= 256 ? lpr : 256; }
@@ -146,9 +147,8 @@ struct ClusterArgs {
                              // b % nclusters
   int32_t slice_vecs;        // 16-byte vectors of a row each member owns (nvec / C)
   int32_t rows_per_step;     // R: rows one reduction and one exchange serve
-  uint32_t spin_limit;
+  uint32_t spin_limit;       // polls before computing a missing partial locally; 0: never poll
   unsigned long long* xchg;  // [steps][C][2R] tagged partial sums, zeroed before each launch
-  unsigned* status;          // set to nonzero when a wait gave up
 };
 
 // ------------------------------------------------------------------ launchers
@@ -164,7 +164,7 @@ hipError_t launch_bwd_rowdot(int kind, int tc, bool vec, const BwdArgs& a, int g
                              hipStream_t s);
 hipError_t launch_bwd_colslice(int kind, int tc, bool vec, const BwdArgs& a, int slices,
                                int row_blocks, hipStream_t s);
-// Split-row kernels (cooperative launch) and their occupancy (workgroups per CU).
+// Split-row kernels and their occupancy (workgroups per CU).
 hipError_t launch_fwd_cluster(int kind, int tc, int t, int vpl, int rows, const FwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s);
 hipError_t launch_bwd_cluster(int kind, int tc, int t, int vpl, int rows, const BwdArgs& a,

@@ -231,9 +231,8 @@ bool plan_cluster(bool backward, bool layernorm, int64_t M, int64_t N, int64_t n
   p.grid = int(ncl * C);
   p.off_xchg = 0;
   // every step of rows has its own exchange slots: 2 values per row and member
-  p.xchg_bytes = size_t(M + rows) * C * 2 * 8;
-  p.off_status = align256(p.xchg_bytes);
-  size_t end = p.off_status + 256;
+  p.xchg_bytes = align256(size_t(M + rows) * C * 2 * 8);
+  size_t end = p.xchg_bytes;
   if (backward) {
     p.partial_rows = ncl;
     const size_t part = align256(size_t(ncl) * size_t(N) * 4);

@@ -34,7 +34,7 @@ struct Plan {
   size_t ws_bytes = 0;        // bytes this plan uses
   size_t ws_need = 0;         // bytes the call requires (covers the fallback plan too)
   size_t off_part_g = 0, off_part_b = 0, off_rowc = 0;  // byte offsets into the workspace
-  size_t off_xchg = 0, off_status = 0, xchg_bytes = 0;
+  size_t off_xchg = 0, xchg_bytes = 0;
 };
 
 // Returns NORM_OK or NORM_ERR_BAD_OPTION.  Shapes and dtype must already be valid; dtype
@@ -44,7 +44,7 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
                         bool aligned16, const norm_options_t* opt, Plan* out);
 
 // The SPLIT (bwd) or GENERIC (fwd) plan a CLUSTER plan falls back to when the device
-// cannot hold the cooperative grid.
+// cannot hold one cluster's workgroups at once.
 norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
                                  Plan* out);
 

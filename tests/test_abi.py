@@ -262,7 +262,7 @@ def test_cluster_plans():
     # keeps a whole 256 KiB row (1024 lanes x 16 vectors)
     assert rn.norm_plan(False, True, 8192, 16384, BF16).path == rn.NORM_PATH_ROWS
     for dt, N in ((BF16, 131072), (F32, 65536)):
-        p = rn.norm_plan(False, False, 2048, N, dt)
+        p = rn.norm_plan(False, True, 2048, N, dt)
         assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 1024, 16)
     # untuned: 12000 vectors fit 1024 x 12; 10000 vectors fit no wide mapping
     assert rn.norm_plan(False, True, 64, 12000 * 8, BF16).vecs_per_lane == 12
@@ -297,8 +297,8 @@ def test_lds_partial_mappings():
     # tuned long rows that now stay in one workgroup
     p = rn.norm_plan(True, True, 8192, 16384, BF16)
     assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rows, 1024, 2)
-    p = rn.norm_plan(True, True, 8192, 16384, F32)
-    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rows, 1024, 4)
+    p = rn.norm_plan(True, False, 8192, 16384, BF16)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rows, 1024, 2)
     # untuned lengths: 3500 vectors fit 1024 x 4 where it is built (RMSNorm bf16), not for
     # LayerNorm bf16; 2500 vectors have no 1024 x 3 mapping
     assert rn.norm_plan(True, False, 4096, 3500 * 8, BF16).path == rows

@@ -9,7 +9,7 @@ import pytest
 
 import gen
 import row_normalization_norm_amd as rn
-from parity import GpuRun, check_backward, check_forward, full_check, sample_rows
+from parity import GpuRun, check_backward, check_forward, full_check, sample_rows, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -136,8 +136,8 @@ CLUSTER_CASES = [(N, C) for N in (2048, 8192, 65536) for C in (2, 4, 8, 16, 32)
 @pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("kind", ["rms", "ln"])
 def test_cluster_path(device, kind, dtype, pdtype, N, C, R):
-    """Rows split over C co-resident workgroups (cooperative launch), forward and backward,
-    with a row count that leaves the clusters unevenly loaded."""
+    """Rows split over C workgroups, forward and backward, with a row count that leaves
+    the clusters unevenly loaded."""
     epv = 4 if dtype == "f32" else 8
     if (N // epv) % C:
         pytest.skip("row does not split evenly")
@@ -152,7 +152,7 @@ def test_cluster_path(device, kind, dtype, pdtype, N, C, R):
         pytest.skip("no compiled cluster mapping covers this slice")
     for bwd in (False, True):
         assert rn.norm_cluster_resident(bwd, kind == "ln", M, N, code, opt) == 1, \
-            "the cooperative grid must fit (otherwise the call silently takes another path)"
+            "one cluster must fit the device (otherwise the call silently takes another path)"
     full_check(w, device, rows=np.arange(M), fwd_options=opt, bwd_options=opt)
 
 
@@ -196,7 +196,7 @@ def test_every_cluster_mapping(device, kind, dtype, pdtype, direction, T, V, R):
     except rn.NormError:
         pytest.skip("mapping not built for this direction")
     if rn.norm_cluster_resident(bwd, kind == "ln", M, N, code, opt) != 1:
-        pytest.skip("cooperative grid does not fit")
+        pytest.skip("a cluster does not fit the device")
     inputs = gen.make_inputs(w)
     run = GpuRun(w, inputs, device)
     if not bwd:
@@ -210,17 +210,70 @@ def test_every_cluster_mapping(device, kind, dtype, pdtype, direction, T, V, R):
         check_backward(run, inputs, np.arange(M))
 
 
+SELF_CASES = [("ln", "bf16", None, 65536, 4, 1), ("rms", "bf16", None, 131072, 8, 1),
+              ("ln", "f32", None, 32768, 4, 2), ("rms", "f16", "f32", 65536, 8, 2),
+              ("ln", "bf16", None, 262144, 8, 1)]
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["plain", "residual"])
+@pytest.mark.parametrize("kind,dtype,pdtype,N,C,R", SELF_CASES,
+                         ids=[f"{k}-{d}{'+' + p if p else ''}-N{n}-C{c}-R{r}"
+                              for k, d, p, n, c, r in SELF_CASES])
+def test_cluster_partials_computed_locally(device, kind, dtype, pdtype, N, C, R, fused):
+    """A split-row member that does not receive another member's partial sums computes
+    them itself.  Forcing that for every member and step (cluster_wait = -1) must give
+    the same bits as the exchange, forward and backward."""
+    import torch
+    M = 37
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.2, x_std=1.1, pdtype=pdtype)
+    code = dtype_code(dtype, pdtype)
+    outs = []
+    for wait in (0, -1):
+        opt = rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=C, cluster_rows=R,
+                         cluster_wait=wait)
+        try:
+            for bwd in (False, True):
+                rn.norm_plan(bwd, kind == "ln", M, N, code, options=opt)
+        except rn.NormError:
+            pytest.skip("no compiled split-row mapping covers this slice")
+        inputs = gen.make_inputs(w, residual=fused)
+        run = GpuRun(w, inputs, device)
+        if fused:
+            res = to_device(inputs["res"], dtype, device)
+            dsum = to_device(inputs["dsum"], dtype, device)
+            s = torch.empty_like(run.x)
+            if kind == "rms":
+                rn.norm_rms_fwd_add(run.x, res, run.gamma, run.y, s, run.rstd, eps=w.eps,
+                                    options=opt)
+                rn.norm_rms_bwd_add(run.dy, s, run.gamma, run.rstd, dsum, run.dx, run.dgamma,
+                                    options=opt)
+            else:
+                rn.norm_ln_fwd_add(run.x, res, run.gamma, run.beta, run.y, s, run.mean,
+                                   run.rstd, eps=w.eps, options=opt)
+                rn.norm_ln_bwd_add(run.dy, s, run.gamma, run.mean, run.rstd, dsum, run.dx,
+                                   run.dgamma, run.dbeta, options=opt)
+        else:
+            run.forward(opt)
+            run.backward(opt)
+        run.sync()
+        outs.append({k: getattr(run, k).clone() for k in ("y", "dx", "rstd", "dgamma", "mean",
+                                                          "dbeta") if getattr(run, k) is not None})
+        if wait == 0 and not fused:
+            check_forward(run, inputs, np.arange(M))
+            check_backward(run, inputs, np.arange(M))
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), f"{k}: locally computed partials differ"
+
+
 @pytest.mark.parametrize("name", ["rms4"])
 def test_long_rows_run_on_cluster_path(device, name):
-    """The 131072-column workload: the forward holds a whole row per 1024-lane workgroup
-    (16 vectors per lane); the backward, which also keeps per-column partial sums, splits
-    the row over a co-resident cluster."""
+    """The 131072-column workload splits its rows over a cluster of workgroups, forward
+    and backward, and every cluster fits the device at once."""
     w = gen.WORKLOADS[name]
     code = rn.NORM_DTYPE_BF16 if w.dtype == "bf16" else rn.NORM_DTYPE_F32
-    p = rn.norm_plan(False, w.kind == "ln", w.M, w.N, code)
-    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, 1024, 16)
-    assert rn.norm_plan(True, w.kind == "ln", w.M, w.N, code).path == rn.NORM_PATH_CLUSTER
-    assert rn.norm_cluster_resident(True, w.kind == "ln", w.M, w.N, code) == 1
+    for bwd in (False, True):
+        assert rn.norm_plan(bwd, w.kind == "ln", w.M, w.N, code).path == rn.NORM_PATH_CLUSTER
+        assert rn.norm_cluster_resident(bwd, w.kind == "ln", w.M, w.N, code) == 1
 
 
 @pytest.mark.parametrize("grid", [1, 3, 64])
