@@ -164,7 +164,9 @@ bool plan_rows(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec
     p.block = fwd_block(m.lpr);
     p.groups = ceil_div(M, p.block / m.lpr);
     int64_t grid = p.groups < kFwdGrid ? p.groups : kFwdGrid;
-    if (o.grid) grid = o.grid;
+    // An explicit grid larger than the row groups gives one group per workgroup.
+    if (o.grid) grid = o.grid < p.groups ? o.grid : p.groups;
+    if (grid < 1) grid = 1;
     p.grid = int(grid);
   } else {
     p.block = bwd_block(m.lpr);

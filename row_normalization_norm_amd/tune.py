@@ -59,8 +59,10 @@ def _time(fn, iters=20, warm=3):
     return e0.elapsed_time(e1) / iters
 
 
-def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 1024), grids_b=(0, 256, 512), cluster=True):
-    """Time every candidate for one shape; returns a list of result dicts."""
+def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 1024, -1), grids_b=(0, 256, 512), cluster=True,
+               dirs=("fwd", "bwd")):
+    """Time every candidate for one shape; returns a list of result dicts.  A forward grid
+    of -1 stands for one row group per workgroup (the grid recorded is that count)."""
     import torch
     import row_normalization_norm_amd as rn
     dev = torch.device("cuda:0")
@@ -106,11 +108,19 @@ def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 1024), grids_b=(0, 256, 512),
     torch.cuda.synchronize()
     for direction, maps, grids, cl_list in (("fwd", mappings("fwd"), grids_f, CL_FWD),
                                             ("bwd", mappings("bwd"), grids_b, CL_BWD)):
+        if direction not in dirs:
+            continue
         bwd = direction == "bwd"
         for lanes, vecs in maps:
             if lanes * vecs < nvec or lanes * vecs - nvec >= lanes:
                 continue
+            rows_per_wg = (max(256, lanes) if not bwd else max(512, lanes)) // lanes
+            groups = (M + rows_per_wg - 1) // rows_per_wg
             for grid in grids:
+                if grid == -1:
+                    grid = groups
+                    if grid in grids:
+                        continue
                 opt = rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=lanes, vecs_per_lane=vecs,
                                  grid=grid)
                 try:
@@ -141,16 +151,16 @@ def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 1024), grids_b=(0, 256, 512),
     return res
 
 
-def sweep(out_path, ns=SWEEP_N):
+def sweep(out_path, ns=SWEEP_N, dirs=("fwd", "bwd")):
     with open(out_path, "w") as out:
         for kind in ("rms", "ln"):
             for dtype in ("bf16", "f32"):
                 for N in ns:
-                    res = tune_shape(kind, dtype, (1 << 27) // N, N)
+                    res = tune_shape(kind, dtype, (1 << 27) // N, N, dirs=dirs)
                     for r in res:
                         out.write(json.dumps(r) + "\n")
                     out.flush()
-                    for d in ("fwd", "bwd"):
+                    for d in dirs:
                         best = max((r for r in res if r["dir"] == d), key=lambda r: r["GBs"])
                         print(f"{kind} {dtype} N={N} {d}: path {best['path']} "
                               f"{best['lpr']}x{best['vpl']} grid {best['grid']} C{best['C']} "
@@ -195,13 +205,15 @@ def main():
     ap.add_argument("--sweep", metavar="OUT.jsonl", help="time the sweep on cuda:0")
     ap.add_argument("--n", type=int, nargs="+", default=list(SWEEP_N),
                     help="row lengths to sweep (default: all)")
+    ap.add_argument("--dirs", nargs="+", default=["fwd", "bwd"], choices=["fwd", "bwd"],
+                    help="directions to sweep (default: both)")
     ap.add_argument("--table", metavar="IN.jsonl", nargs="+",
                     help="print csrc/tuned.h built from sweep results (a shape in a later "
                          "file replaces the earlier files' results for it)")
     args = ap.parse_args()
     if args.sweep:
         sys.path.insert(0, os.path.dirname(HERE))
-        sweep(args.sweep, args.n)
+        sweep(args.sweep, args.n, tuple(args.dirs))
     elif args.table:
         sys.stdout.write(table(args.table))
     else:
