@@ -21,9 +21,10 @@
 // The kernels are launched like any other (a cooperative launch costs about 25 us of
 // idle device time around every call on this platform), with a grid the device can hold
 // at once, so the members of a cluster normally run together.  Nothing depends on it:
-// a member that has polled another's words `spin_limit` times computes that member's
-// partial sums itself, from the same data with the same code (floating-point
-// contraction off), so the result has the same bits and every wait ends.
+// a member that has polled another's words `spin_limit` times leaves the pipelined loop,
+// finishes its steps one at a time (polling 256 times fewer per word) and computes any
+// partial sums that do not arrive itself, from the same data with the same operations
+// (floating-point contraction off), so the result has the same bits and every wait ends.
 //
 // LayerNorm statistics merge per-slice (sum, sum of squared deviations about the slice
 // mean) with the pairwise-update formula of Chan, Golub and LeVeque, so the variance is
@@ -122,16 +123,17 @@ __device__ inline void prefetch_step(const ClusterArgs& c, int64_t step,
 // Gather every member's K partials of `step` into xin[member * K + j]; visible to the whole
 // workgroup after the barrier.  A prefetched word that already carries the step's tag is
 // used as is; otherwise the thread polls.  Returns the members whose words did not arrive
-// within the poll limit (a bit per member, the same in every thread): the caller computes
+// within `limit` polls (a bit per member, the same in every thread): the caller computes
 // those partials itself.  The caller alternates between two xin / xok buffers, so values
 // are never overwritten before every thread has read them.
 template <int K>
 __device__ inline unsigned gather_step(const ClusterArgs& c, int64_t step,
-                                       const unsigned long long (&pre)[K], float* xin, int* xok) {
+                                       const unsigned long long (&pre)[K], float* xin, int* xok,
+                                       uint32_t limit) {
   if (threadIdx.x < c.C) {
     unsigned long long* base = c.xchg + (step * c.C + threadIdx.x) * K;
     const uint32_t tag = row_tag(step);
-    bool ok = c.spin_limit != 0;
+    bool ok = limit != 0;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       float v = 0.0f;
@@ -139,7 +141,7 @@ __device__ inline unsigned gather_step(const ClusterArgs& c, int64_t step,
         if (static_cast<uint32_t>(pre[j] >> 32) == tag) {
           v = __uint_as_float(static_cast<uint32_t>(pre[j]));
         } else {
-          ok = poll_for(base + j, tag, c.spin_limit, &v);
+          ok = poll_for(base + j, tag, limit, &v);
         }
       }
       xin[threadIdx.x * K + j] = v;
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
     float* xs = xin[xp];
     int* xk = xok[xp];
     xp ^= 1;
-    if (gather_step<K>(c, st, pre, xs, xk)) break;  // a partner is late: finish below
+    if (gather_step<K>(c, st, pre, xs, xk, c.spin_limit)) break;  // a partner is late
     emit_y(b0, st, xs);
 #pragma unroll
     for (int i = 0; i < R; ++i)
@@ -530,6 +532,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
   // is formed again (and written again, with the same values).
   if (st < nsteps) {
     const int64_t done = st + 2 * c.nclusters;
+    const uint32_t tail_limit = c.spin_limit >> 8;  // a late partner: wait less from now on
     for (; st < nsteps; st += c.nclusters) {
       u32x4 sb[R][VPL], rb[ADD ? R : 1][VPL];
       load(st, sb, rb);
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
       float* xs = xin[xp];
       int* xk = xok[xp];
       xp ^= 1;
-      const unsigned miss = gather_step<K>(c, st, pre, xs, xk);
+      const unsigned miss = gather_step<K>(c, st, pre, xs, xk, tail_limit);
       if (miss) parity = fwd_missing<LN, D, T, VPL, R, ADD>(a, c, miss, st, slice_n, red, xs, parity);
       emit_y(sb, st, xs);
     }
@@ -756,7 +759,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     float* xs = xin[xp];
     int* xk = xok[xp];
     xp ^= 1;
-    if (gather_step<K>(c, st, pre, xs, xk)) break;  // a partner is late: finish below
+    if (gather_step<K>(c, st, pre, xs, xk, c.spin_limit)) break;  // a partner is late
     emit_dx(b[0], st, xs);
 #pragma unroll
     for (int k = 0; k < S - 1; ++k) b[k] = b[k + 1];
@@ -766,6 +769,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   // member's partial (and column sums) formed and published by the loop above.
   if (st < nsteps) {
     const int64_t done = st + (S - 1) * c.nclusters;
+    const uint32_t tail_limit = c.spin_limit >> 8;  // a late partner: wait less from now on
     for (; st < nsteps; st += c.nclusters) {
       Stage sb;
       load(st, sb);
@@ -779,7 +783,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
       float* xs = xin[xp];
       int* xk = xok[xp];
       xp ^= 1;
-      const unsigned miss = gather_step<K>(c, st, pre, xs, xk);
+      const unsigned miss = gather_step<K>(c, st, pre, xs, xk, tail_limit);
       if (miss) parity = bwd_missing<LN, D, P, T, VPL, R>(a, c, miss, st, red, xs, parity);
       emit_dx(sb, st, xs);
     }
