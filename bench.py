@@ -599,9 +599,15 @@ def main():
             f = dataclasses.replace(gen.WORKLOADS[base], name=f"{base}_residual_add")
             fused.append(f)
             fused_names.add(f.name)
+        import gc
+        import torch
         for wl in list(gen.WORKLOADS.values()) + other + fused + sweep:
             name = wl.name
             is_fused = name in fused_names
+            # release the previous workload's buffers, so each starts from the same
+            # (empty) caching-allocator state
+            gc.collect()
+            torch.cuda.empty_cache()
             rr = run_gpu(wl, max(5, args.steps // 2), 3, device, fused=is_fused)
             es = elem_bytes(wl.dtype)
             fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, es, elem_bytes(wl.param_dtype))
