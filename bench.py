@@ -414,6 +414,7 @@ def summarize(d, workload, warmup, steps, copy_bytes):
     fwd_b, bwd_b = ideal_bytes(wl.kind, wl.M, wl.N, s, ps)
     main_b = main_bwd_kernel_bytes(wl.kind, wl.M, wl.N, s, ps)
     algo = {"fwd_rows_kernel": fwd_b, "bwd_rows_kernel": main_b,
+            "fwd_cluster_kernel": fwd_b, "bwd_cluster_kernel": main_b,
             "colreduce_kernel": bwd_b - main_b}
     clines = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes read | bytes written | "
               "traffic | algorithmic | traffic / algorithmic | LDS instr | LDS bank conflicts |",
@@ -433,7 +434,9 @@ def summarize(d, workload, warmup, steps, copy_bytes):
                       f"{li.get('SQ_INSTS_LDS', float('nan')):.0f} | "
                       f"{li.get('SQ_LDS_BANK_CONFLICT', float('nan')):.0f} |")
     src_hash = None
-    log = os.path.join(d, "FETCH_SIZE.log")
+    log = os.path.join(d, f"FETCH_SIZE_{w}.log")
+    if not os.path.exists(log):
+        log = os.path.join(d, "FETCH_SIZE.log")
     if os.path.exists(log):
         for line in open(log):
             if line.startswith("{"):
@@ -446,7 +449,7 @@ PROFILE_STEPS = (
     "rocprofv3 --kernel-trace --stats --output-format csv -d $D/trace -o {w} -- "
     "python3 $R/bench.py --workload {w} --steps 10 --warmup 3 --no-cpu",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE -o {w} -- "
-    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu > $D/FETCH_SIZE.log",
+    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu > $D/FETCH_SIZE_{w}.log",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $D/WRITE_SIZE -o {w} -- "
     "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE_copy -o copy -- "
