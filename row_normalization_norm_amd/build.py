@@ -28,7 +28,7 @@ def _units():
     # kind (0 RMSNorm, 1 LayerNorm) x type pair (TypeCombo in csrc/launch.h)
     for k in (0, 1):
         for tc in range(5):
-            for name in ("fwd_rows", "bwd_rows", "cluster"):
+            for name in ("fwd_rows", "bwd_rows", "cluster", "grows"):
                 units.append((os.path.join(CSRC, f"{name}.hip"),
                               os.path.join(BUILD_DIR, f"{name}_k{k}_t{tc}.o"),
                               [f"-DRN_KIND={k}", f"-DRN_TC={tc}"]))

@@ -24,7 +24,9 @@ namespace rownorm {
   hipError_t launch_bwd_cluster_k##K##_t##T(int, int, int, const BwdArgs&, const ClusterArgs&, \
                                             int, hipStream_t);                             \
   int occupancy_fwd_cluster_k##K##_t##T(int, int, int, bool);                              \
-  int occupancy_bwd_cluster_k##K##_t##T(int, int, int, bool);
+  int occupancy_bwd_cluster_k##K##_t##T(int, int, int, bool);                              \
+  hipError_t launch_fwd_grows_k##K##_t##T(int, const FwdArgs&, int, hipStream_t);          \
+  hipError_t launch_bwd_grows_k##K##_t##T(int, const BwdArgs&, int, hipStream_t);
 RN_DECL_TU(0, 0) RN_DECL_TU(0, 1) RN_DECL_TU(0, 2) RN_DECL_TU(0, 3) RN_DECL_TU(0, 4)
 RN_DECL_TU(1, 0) RN_DECL_TU(1, 1) RN_DECL_TU(1, 2) RN_DECL_TU(1, 3) RN_DECL_TU(1, 4)
 #undef RN_DECL_TU
@@ -44,6 +46,10 @@ using FwdClusterFn = hipError_t (*)(int, int, int, const FwdArgs&, const Cluster
 using BwdClusterFn = hipError_t (*)(int, int, int, const BwdArgs&, const ClusterArgs&, int,
                                     hipStream_t);
 using OccFn = int (*)(int, int, int, bool);
+using FwdGrowsFn = hipError_t (*)(int, const FwdArgs&, int, hipStream_t);
+using BwdGrowsFn = hipError_t (*)(int, const BwdArgs&, int, hipStream_t);
+const FwdGrowsFn kFwdGrows[2][kNumTypeCombos] = RN_TABLE(launch_fwd_grows);
+const BwdGrowsFn kBwdGrows[2][kNumTypeCombos] = RN_TABLE(launch_bwd_grows);
 const FwdRowsFn kFwdRows[2][kNumTypeCombos] = RN_TABLE(launch_fwd_rows);
 const BwdRowsFn kBwdRows[2][kNumTypeCombos] = RN_TABLE(launch_bwd_rows);
 const FwdClusterFn kFwdCluster[2][kNumTypeCombos] = RN_TABLE(launch_fwd_cluster);
@@ -56,6 +62,14 @@ const OccFn kBwdOcc[2][kNumTypeCombos] = RN_TABLE(occupancy_bwd_cluster);
 hipError_t launch_fwd_rows(int kind, int tc, int lpr, int vpl, const FwdArgs& a, int grid,
                            hipStream_t s) {
   return kFwdRows[kind][tc](lpr, vpl, a, grid, s);
+}
+hipError_t launch_fwd_grows(int kind, int tc, int epl, const FwdArgs& a, int grid,
+                            hipStream_t s) {
+  return kFwdGrows[kind][tc](epl, a, grid, s);
+}
+hipError_t launch_bwd_grows(int kind, int tc, int epl, const BwdArgs& a, int grid,
+                            hipStream_t s) {
+  return kBwdGrows[kind][tc](epl, a, grid, s);
 }
 hipError_t launch_bwd_rows(int kind, int tc, int lpr, int vpl, const BwdArgs& a, int grid,
                            hipStream_t s) {
@@ -279,7 +293,8 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
                              p.grid, stream);
       break;
     default:
-      e = launch_fwd_generic(kind, dt.tc, a, p.grid, stream);
+      e = p.vpl > 0 ? launch_fwd_grows(kind, dt.tc, p.vpl, a, p.grid, stream)
+                    : launch_fwd_generic(kind, dt.tc, a, p.grid, stream);
   }
   if (e != hipSuccess) return NORM_ERR_HIP;
   return hip_status(ev.stop());
@@ -333,7 +348,10 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   a.part_b = (p.ws_bytes && ln) ? reinterpret_cast<float*>(ws + p.off_part_b) : nullptr;
   a.dgamma = dgamma;
   a.dbeta = db;
-  const bool two_pass = p.path == NORM_PATH_SPLIT || p.path == NORM_PATH_GENERIC;
+  // the split paths: a per-row pass, then a column-sliced pass (GENERIC rows too long for
+  // the register-resident scalar kernel, whose plan has vpl = 0)
+  const bool two_pass =
+      p.path == NORM_PATH_SPLIT || (p.path == NORM_PATH_GENERIC && p.vpl == 0);
   a.rowc = two_pass ? reinterpret_cast<float*>(ws + p.off_rowc) : nullptr;
   a.M = M;
   a.N = int32_t(N);
@@ -360,6 +378,8 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   } else if (p.path == NORM_PATH_CLUSTER) {
     e = launch_bwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws, opt),
                            p.grid, stream);
+  } else if (!two_pass) {
+    e = launch_bwd_grows(kind, dt.tc, p.vpl, a, p.grid, stream);
   } else {
     const bool vec = p.path == NORM_PATH_SPLIT;
     e = launch_bwd_rowdot(kind, dt.tc, vec, a, p.grid, stream);

@@ -80,6 +80,22 @@ constexpr int kMaxCluster = 32;            // workgroups sharing one row, at mos
 constexpr uint32_t kSpinLimit = 1u << 16;  // polls of a member's partials before a
                                            // waiting member computes them itself
 
+// Register-resident scalar kernels (GENERIC path) for rows that are not whole 16-byte
+// vectors: one row per 256-thread workgroup, this many elements per lane.  Element loads
+// keep them well below the vector kernels; measured on MI355X they beat the looping
+// forward (2.1-2.7 against 0.7-1.4 TB/s) up to 3072 elements and the two-pass scalar
+// backward (1.6-1.9 against 1.2-1.6 TB/s) up to 1024, and lose beyond.
+#define RN_GROWS_EPL(X) X(1) X(2) X(3) X(4) X(6) X(8) X(12)
+constexpr int kGrowsBlock = 256;
+constexpr int kGrowsFwdMaxElems = kGrowsBlock * 12;
+constexpr int kGrowsBwdMaxElems = kGrowsBlock * 4;
+// Smallest elements-per-lane entry of RN_GROWS_EPL covering n elements (0: none).
+constexpr int grows_epl(int64_t n) {
+  const int64_t e = (n + kGrowsBlock - 1) / kGrowsBlock;
+  return e <= 1 ? 1 : e <= 2 ? 2 : e <= 3 ? 3 : e <= 4 ? 4 : e <= 6 ? 6 : e <= 8 ? 8
+       : e <= 12 ? 12 : 0;
+}
+
 // Threads per workgroup for a row mapping.
 constexpr int fwd_block(int lpr) { return lpr >= 256 ? lpr : 256; }
 constexpr int bwd_block(int lpr) { return lpr >= 512 ? lpr : 512; }
@@ -172,8 +188,13 @@ hipError_t launch_bwd_cluster(int kind, int tc, int t, int vpl, int rows, const 
 // add: the variant with the fused residual add (forward) or residual gradient (backward).
 int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add);
 int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add);
-// GENERIC forward (scalar loads).
+// GENERIC forward (scalar loads): looping kernel for any N, register-resident kernel
+// (epl elements per lane, RN_GROWS_EPL) for N up to kGrowsFwdMaxElems; and the
+// register-resident GENERIC backward (one partial row per workgroup, like the ROWS path)
+// for N up to kGrowsBwdMaxElems.
 hipError_t launch_fwd_generic(int kind, int tc, const FwdArgs& a, int grid, hipStream_t s);
+hipError_t launch_fwd_grows(int kind, int tc, int epl, const FwdArgs& a, int grid, hipStream_t s);
+hipError_t launch_bwd_grows(int kind, int tc, int epl, const BwdArgs& a, int grid, hipStream_t s);
 // Column reduce: out[j] = sum_p part[p*N + j] for dgamma (and dbeta if part_b).
 hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P, int32_t N,
                             float* dgamma, float* dbeta, hipStream_t s);

@@ -70,6 +70,9 @@ constexpr int kClusterBwdRowsF32 = 1;
 constexpr int kSplitTargetBlocks = 2048;
 constexpr int kSplitMaxRowBlocks = 256;
 constexpr int kRowPassMaxGrid = 2048;
+// Register-resident scalar backward: workgroups (and partial rows); its element loads
+// need many waves in flight.
+constexpr int kGenericBwdGrid = 2048;
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -267,11 +270,40 @@ void plan_split(bool layernorm, int64_t M, int64_t N, int64_t nvec, bool vec,
   p.ws_bytes = layernorm ? p.off_part_b + part : p.off_part_b;
 }
 
-void plan_generic_fwd(int64_t M, const norm_options_t& o, Plan& p) {
+// GENERIC forward: the register-resident scalar kernel (vpl = elements per lane) for rows
+// up to kGrowsFwdMaxElems, else the looping kernel (vpl = 0).
+void plan_generic_fwd(int64_t M, int64_t N, const norm_options_t& o, Plan& p) {
   p.path = NORM_PATH_GENERIC;
   p.block = kRowBlock;
+  p.vpl = N <= kGrowsFwdMaxElems ? grows_epl(N) : 0;
+  p.lpr = p.vpl ? kGrowsBlock : 0;
   p.grid = int(M < kRowPassMaxGrid ? M : kRowPassMaxGrid);
   if (o.grid) p.grid = o.grid;
+}
+
+// GENERIC backward: the register-resident scalar kernel with one dgamma/dbeta partial row
+// per workgroup for rows up to kGrowsBwdMaxElems, else the scalar split path.
+void plan_generic_bwd(bool layernorm, int64_t M, int64_t N, int64_t nvec, bool atomic,
+                      const norm_options_t& o, Plan& p) {
+  const int epl = N <= kGrowsBwdMaxElems ? grows_epl(N) : 0;
+  if (!epl) {
+    plan_split(layernorm, M, N, nvec, false, o, p);
+    return;
+  }
+  p.path = NORM_PATH_GENERIC;
+  p.block = kGrowsBlock;
+  p.lpr = kGrowsBlock;
+  p.vpl = epl;
+  int64_t grid = M < kGenericBwdGrid ? M : kGenericBwdGrid;
+  if (o.grid) grid = o.grid < M ? o.grid : M;
+  if (grid < 1) grid = 1;
+  p.grid = int(grid);
+  if (!atomic) {
+    p.partial_rows = grid;
+    p.off_part_g = 0;
+    p.off_part_b = align256(size_t(grid) * size_t(N) * 4);
+    p.ws_bytes = layernorm ? 2 * p.off_part_b : p.off_part_b;
+  }
 }
 
 const TunedPlan* find_tuned(bool backward, bool layernorm, int dtype, int64_t nvec) {
@@ -327,9 +359,9 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
       }
       if (!vec_ok) {
         if (backward) {
-          plan_split(layernorm, M, N, nvec, false, o, p);
+          plan_generic_bwd(layernorm, M, N, nvec, atomic, o, p);
         } else {
-          plan_generic_fwd(M, o, p);
+          plan_generic_fwd(M, N, o, p);
         }
       } else if (atomic ||
                  nvec <= (backward ? kBwdRowsMaxVecs : kFwdRowsMaxVecs)) {
@@ -344,7 +376,7 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
         if (backward) {
           plan_split(layernorm, M, N, nvec, true, o, p);
         } else if (!plan_rows(false, layernorm, M, N, nvec, o, false, p)) {
-          plan_generic_fwd(M, o, p);
+          plan_generic_fwd(M, N, o, p);
         }
       }
       break;
@@ -360,9 +392,9 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
       break;
     case NORM_PATH_GENERIC:
       if (backward) {
-        plan_split(layernorm, M, N, nvec, false, o, p);
+        plan_generic_bwd(layernorm, M, N, nvec, atomic, o, p);
       } else {
-        plan_generic_fwd(M, o, p);
+        plan_generic_fwd(M, N, o, p);
       }
       break;
   }
@@ -393,7 +425,7 @@ norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64
   if (backward) {
     plan_split(layernorm, M, N, p.nvec, true, o, p);
   } else {
-    plan_generic_fwd(M, o, p);
+    plan_generic_fwd(M, N, o, p);
   }
   if (M == 0) p.grid = 0;
   p.ws_need = p.ws_bytes;

@@ -13,8 +13,8 @@ from parity import GpuRun, check_backward, check_forward, full_check, sample_row
 
 pytestmark = pytest.mark.gpu
 
-SMALL_N = (1, 7, 64, 100, 256, 384, 512, 768, 1000, 1024, 2048, 4095, 4096, 8192, 16384, 32768,
-           65536, 131072)
+SMALL_N = (1, 7, 64, 100, 256, 384, 512, 768, 770, 1000, 1024, 2048, 4095, 4096, 8190, 8192,
+           8195, 16384, 32768, 65536, 131072)
 
 
 # (activation type, parameter type or None for the same): the configurations' bf16 and
