@@ -97,41 +97,48 @@ __device__ inline void block_sum_n(float (&v)[K], float* red, int& parity) {
 // cluster cl takes steps cl, cl + nclusters, ...  One reduction and one exchange serve
 // all R rows of a step.  Every step has its own exchange slots: [member][K] 64-bit words.
 template <int K>
-__device__ inline void publish_step(const ClusterArgs& c, int member, int64_t step,
+__device__ inline void publish_step(const ClusterArgs& c, int member, int step,
                                     const float (&mine)[K]) {
   if (threadIdx.x == 0) {
-    unsigned long long* base = c.xchg + step * c.C * K;
+    unsigned long long* base = c.xchg + static_cast<int64_t>(step) * c.C * K;
 #pragma unroll
     for (int j = 0; j < K; ++j) publish(base + member * K + j, row_tag(step), mine[j]);
   }
 }
 
+// Word j of member m's slots for `step`: a uniform base for the step plus a 32-bit offset
+// that is opaque to the optimiser, so that no 64-bit per-lane address is kept live (and
+// spilled) across the step loop, and the address is formed only where it is used.
+template <int K>
+__device__ inline unsigned long long* slot_ptr(const ClusterArgs& c, int step, uint32_t m, int j) {
+  uint32_t ofs = (m * K + j) * 8u;
+  asm volatile("" : "+v"(ofs));
+  char* base = reinterpret_cast<char*>(c.xchg + static_cast<int64_t>(step) * c.C * K);
+  return reinterpret_cast<unsigned long long*>(base + ofs);
+}
+
 // Thread m < C reads member m's K words of `step` ahead of the gather, so the round trip
 // of the first poll overlaps other work instead of stalling the whole workgroup.
 template <int K>
-__device__ inline void prefetch_step(const ClusterArgs& c, int64_t step,
+__device__ inline void prefetch_step(const ClusterArgs& c, int step,
                                      unsigned long long (&pre)[K]) {
   if (threadIdx.x < c.C) {
-    unsigned long long* base = c.xchg + step * c.C * K;
 #pragma unroll
     for (int j = 0; j < K; ++j)
-      pre[j] = __hip_atomic_load(base + threadIdx.x * K + j, __ATOMIC_RELAXED,
+      pre[j] = __hip_atomic_load(slot_ptr<K>(c, step, threadIdx.x, j), __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Gather every member's K partials of `step` into xin[member * K + j]; visible to the whole
-// workgroup after the barrier.  A prefetched word that already carries the step's tag is
-// used as is; otherwise the thread polls.  Returns the members whose words did not arrive
-// within `limit` polls (a bit per member, the same in every thread): the caller computes
-// those partials itself.  The caller alternates between two xin / xok buffers, so values
-// are never overwritten before every thread has read them.
+// Every member's K partials of `step` into xin[member * K + j] (thread m < C handles member
+// m).  A prefetched word that already carries the step's tag is used as is; otherwise the
+// thread polls, at most `limit` times.  xok[m] records whether member m's words arrived.
+// The results are visible to the workgroup after its next barrier.
 template <int K>
-__device__ inline unsigned gather_step(const ClusterArgs& c, int64_t step,
-                                       const unsigned long long (&pre)[K], float* xin, int* xok,
-                                       uint32_t limit) {
+__device__ inline void resolve_step(const ClusterArgs& c, int step,
+                                    const unsigned long long (&pre)[K], float* xin, int* xok,
+                                    uint32_t limit) {
   if (threadIdx.x < c.C) {
-    unsigned long long* base = c.xchg + (step * c.C + threadIdx.x) * K;
     const uint32_t tag = row_tag(step);
     bool ok = limit != 0;
 #pragma unroll
@@ -141,17 +148,34 @@ __device__ inline unsigned gather_step(const ClusterArgs& c, int64_t step,
         if (static_cast<uint32_t>(pre[j] >> 32) == tag) {
           v = __uint_as_float(static_cast<uint32_t>(pre[j]));
         } else {
-          ok = poll_for(base + j, tag, limit, &v);
+          ok = poll_for(slot_ptr<K>(c, step, threadIdx.x, j), tag, limit, &v);
         }
       }
       xin[threadIdx.x * K + j] = v;
     }
     xok[threadIdx.x] = ok ? 1 : 0;
   }
-  __syncthreads();
+}
+
+// The members whose words did not arrive (a bit per member, the same in every thread),
+// read after the barrier that follows resolve_step: the caller computes those partials
+// itself.
+__device__ inline unsigned missing_members(const ClusterArgs& c, const int* xok) {
   unsigned miss = 0;
   for (int m = 0; m < c.C; ++m) miss |= xok[m] ? 0u : (1u << m);
   return miss;
+}
+
+// resolve_step and missing_members with a barrier of their own.  The caller alternates
+// between two xin / xok buffers, so values are never overwritten before every thread has
+// read them.
+template <int K>
+__device__ inline unsigned gather_step(const ClusterArgs& c, int step,
+                                       const unsigned long long (&pre)[K], float* xin, int* xok,
+                                       uint32_t limit) {
+  resolve_step<K>(c, step, pre, xin, xok, limit);
+  __syncthreads();
+  return missing_members(c, xok);
 }
 
 // ------------------------------------------------------------------ partial row sums
@@ -220,7 +244,7 @@ __device__ __forceinline__ void fwd_partial(XF&& X, int slice_vecs, float slice_
 // reduction-buffer parity.
 template <bool LN, typename D, int T, int VPL, int R, bool ADD>
 __device__ __forceinline__ int fwd_missing(const FwdArgs& a, const ClusterArgs& c, unsigned miss,
-                                           int64_t st, float slice_n, float* red, float* xs,
+                                           int st, float slice_n, float* red, float* xs,
                                            int parity) {
 #pragma clang fp contract(off)
   constexpr int EPV = D::kPerVec;
@@ -231,7 +255,7 @@ __device__ __forceinline__ int fwd_missing(const FwdArgs& a, const ClusterArgs& 
     if (!((miss >> m) & 1u)) continue;
     const int64_t mofs = static_cast<int64_t>(m) * c.slice_vecs;
     auto vec = [&](int i, int v) -> u32x4 {
-      const int64_t row = st * R + i;
+      const int64_t row = static_cast<int64_t>(st) * R + i;
       const bool ok = v * T + tid < c.slice_vecs && row < a.M;
       const int64_t idx = row * a.nvec + mofs + v * T + tid;
       u32x4 xv = ok ? ld16_stream(a.x, idx) : zero16();
@@ -314,7 +338,7 @@ __device__ __forceinline__ void bwd_vec_sums(const u32x4& xv, const u32x4& dv, c
 // xs[member * K + j].  Returns the updated reduction-buffer parity.
 template <bool LN, typename D, typename P, int T, int VPL, int R>
 __device__ __forceinline__ int bwd_missing(const BwdArgs& a, const ClusterArgs& c, unsigned miss,
-                                        int64_t st, float* red, float* xs, int parity) {
+                                        int st, float* red, float* xs, int parity) {
   using PV = Param<D, P>;
   constexpr int EPV = D::kPerVec;
   constexpr int NW = T / 64;
@@ -327,7 +351,7 @@ __device__ __forceinline__ int bwd_missing(const BwdArgs& a, const ClusterArgs& 
     float out[K];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int64_t row = st * R + i;
+      const int64_t row = static_cast<int64_t>(st) * R + i;
       const float r = row < a.M ? a.rstd[row] : 0.0f;
       const float mu = (LN && row < a.M) ? a.mean[row] : 0.0f;
       float s1 = 0.0f, s2 = 0.0f;
@@ -377,7 +401,8 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
   const int member = blockIdx.x / c.nclusters;
   const int64_t vofs = static_cast<int64_t>(member) * c.slice_vecs;
   const float slice_n = static_cast<float>(c.slice_vecs) * EPV;
-  const int64_t nsteps = (a.M + R - 1) / R;
+  // steps and step indices are 32-bit (the planner keeps M below 2^31)
+  const int nsteps = static_cast<int>((a.M + R - 1) / R);
 
   bool own[VPL];
   PV g[VPL], b[LN ? VPL : 1];
@@ -398,64 +423,60 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
   __shared__ int xok[2][kMaxCluster];
   int parity = 0, xp = 0;
 
-  // With ADD a step's residual slices come with x's and are added in before the step's
-  // partial sums (the row normalized is the rounded sum, which is also written out).
-  auto load = [&](int64_t st, u32x4 (&buf)[R][VPL], u32x4 (&rbuf)[ADD ? R : 1][VPL]) {
+  // A step's x slices (with ADD, and the residual's): every access goes through a buffer
+  // resource of the row's slice (rows past M get an empty one), so the loads are
+  // unconditional and read zero where there is no data, and stores there are dropped.
+  struct Stage {
+    u32x4 x[R][VPL];
+    u32x4 r[ADD ? R : 1][VPL];
+  };
+  const uint32_t slice_bytes = static_cast<uint32_t>(c.slice_vecs) * 16u;
+  const int M32 = static_cast<int>(a.M);
+  auto slice = [&](const void* base, int row) {
+    return make_rsrc(static_cast<const char*>(base) + (static_cast<int64_t>(row) * a.nvec + vofs) * 16,
+                     row < M32 ? slice_bytes : 0u);
+  };
+  const uint32_t lane_ofs = static_cast<uint32_t>(tid) * 16u;
+  auto load = [&](int st, Stage& sb) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int64_t row = st * R + i;
-      // the row's slice is addressed from opaque per-lane pointers (no per-vector 64-bit
-      // addresses kept live across the step loop)
-      const int64_t lofs = row * a.nvec + vofs + tid;
-      const u32x4* xp = opaque_ptr(static_cast<const u32x4*>(a.x) + lofs);
-      const u32x4* rp = ADD ? opaque_ptr(static_cast<const u32x4*>(a.res) + lofs) : nullptr;
+      const int row = st * R + i;
+      const rsrc_t rx = slice(a.x, row);
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        const bool ok = own[v] && row < a.M;
-        buf[i][v] = ok ? ld16_stream(xp, v * T) : zero16();
-        if constexpr (ADD) rbuf[i][v] = ok ? ld16_stream(rp, v * T) : zero16();
+      for (int v = 0; v < VPL; ++v) sb.x[i][v] = buf_ld16(rx, lane_ofs + v * T * 16);
+      if constexpr (ADD) {
+        const rsrc_t rr = slice(a.res, row);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) sb.r[i][v] = buf_ld16(rr, lane_ofs + v * T * 16);
       }
     }
   };
-  auto form_sum = [&](int64_t st, u32x4 (&buf)[R][VPL], const u32x4 (&rbuf)[ADD ? R : 1][VPL]) {
+  // With ADD the row normalized is the rounded sum x + res, which is also written out.
+  auto form_sum = [&](int st, Stage& sb) {
     if constexpr (ADD) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int64_t row = st * R + i;
+        const rsrc_t rs = slice(a.sum, st * R + i);
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
-          buf[i][v] = D::add(buf[i][v], rbuf[i][v]);
-          if (own[v] && row < a.M) st16_stream(a.sum, row * a.nvec + vofs + v * T + tid, buf[i][v]);
+          sb.x[i][v] = D::add(sb.x[i][v], sb.r[i][v]);
+          buf_st16(rs, lane_ofs + v * T * 16, sb.x[i][v]);
         }
       }
     }
   };
-  // This member's partial sums of a step's rows (fwd_partial).
-  auto partial = [&](const u32x4 (&buf)[R][VPL], float (&out)[K]) {
-    fwd_partial<LN, D, T, VPL, R>([&](int i, int v) -> u32x4 { return buf[i][v]; },
+  // This member's partial sums of a step's rows (fwd_partial, reduced over the workgroup).
+  auto partial = [&](const Stage& sb, float (&out)[K]) {
+    fwd_partial<LN, D, T, VPL, R>([&](int i, int v) -> u32x4 { return sb.x[i][v]; },
                                   c.slice_vecs, slice_n, out, red, parity);
   };
-
-  u32x4 b0[R][VPL], b1[R][VPL], b2[R][VPL];
-  u32x4 r0[ADD ? R : 1][VPL], r1[ADD ? R : 1][VPL], r2[ADD ? R : 1][VPL];
-  int64_t st = cl;
-  if (st >= nsteps) return;
-  load(st, b0, r0);
-  if (st + c.nclusters < nsteps) load(st + c.nclusters, b1, r1);
-  {
-    float mine[K];
-    form_sum(st, b0, r0);
-    partial(b0, mine);
-    publish_step<K>(c, member, st, mine);
-  }
   // y of a step's rows from the gathered partials of every member (contraction off: the
   // statistics come out the same wherever this runs).
-  auto emit_y = [&](const u32x4 (&buf)[R][VPL], int64_t st, const float* xs) {
+  auto emit_y = [&](const Stage& sb, int st, const float* xs) {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int64_t row = st * R + i;
-      if (row >= a.M) break;
+      const int row = st * R + i;
       float mu = 0.0f, var;
       if constexpr (LN) {
         float tot = 0.0f;
@@ -473,70 +494,88 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
         var = tot * a.inv_n;
       }
       const float r = rsqrtf(var + a.eps);
-      if (member == 0 && tid == 0) {
+      if (member == 0 && tid == 0 && row < M32) {
         if (a.rstd) a.rstd[row] = r;
         if constexpr (LN) {
           if (a.mean) a.mean[row] = mu;
         }
       }
+      const rsrc_t ry = slice(a.y, row);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (!own[v]) continue;
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-          const float f = D::get_fresh(buf[i][v], e);
+          const float f = D::get_fresh(sb.x[i][v], e);
           if constexpr (LN) {
             o[e] = fmaf((f - mu) * r, g[v].get_fresh(e), b[v].get_fresh(e));
           } else {
             o[e] = f * r * g[v].get_fresh(e);
           }
         }
-        st16_stream(a.y, row * a.nvec + vofs + v * T + tid, D::pack(o));
+        buf_st16(ry, lane_ofs + v * T * 16, D::pack(o));
       }
     }
   };
 
-  for (; st < nsteps; st += c.nclusters) {
-    const int64_t s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
+  // Three steps live in registers: b[k0] waits for the exchange, b[k1] is reduced and
+  // published this iteration and b[k2] is being loaded, so the exchange round trip of a
+  // step overlaps a step of work.  The roles rotate through fixed registers (the loop body
+  // is unrolled three times), so no step's data is copied while its loads are in flight.
+  constexpr int S = 3;
+  Stage sg[S];
+  int st = cl;
+  if (st >= nsteps) return;
+  load(st, sg[0]);
+  load(st + c.nclusters, sg[1]);
+  {
+    float mine[K];
+    form_sum(st, sg[0]);
+    partial(sg[0], mine);
+    publish_step<K>(c, member, st, mine);
+  }
+  // Where step s2's loads are issued: before step s1's reduction (so they are in flight
+  // during it), or after its publication (1024-lane members).
+  constexpr bool kLoadFirst = T < 1024;
+  // One pipelined step with compile-time stage roles; false when the loop is to end (no
+  // steps left, or a partner is late: then st is the step to finish in the tail).
+  auto pipe_step = [&](auto k0_) -> bool {
+    constexpr int k0 = decltype(k0_)::value;
+    constexpr int k1 = (k0 + 1) % S, k2 = (k0 + 2) % S;
+    if (st >= nsteps) return false;
+    const int s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
     unsigned long long pre[K];
     prefetch_step<K>(c, st, pre);
-    if (s1 < nsteps) {
+    if constexpr (kLoadFirst) load(s2, sg[k2]);
+    {
       float mine[K];
-      form_sum(s1, b1, r1);
-      partial(b1, mine);
-      publish_step<K>(c, member, s1, mine);
+      form_sum(s1, sg[k1]);
+      partial(sg[k1], mine);
+      if (s1 < nsteps) publish_step<K>(c, member, s1, mine);
     }
-    if (s2 < nsteps) load(s2, b2, r2);
-
+    if constexpr (!kLoadFirst) load(s2, sg[k2]);
     float* xs = xin[xp];
     int* xk = xok[xp];
     xp ^= 1;
-    if (gather_step<K>(c, st, pre, xs, xk, c.spin_limit)) break;  // a partner is late
-    emit_y(b0, st, xs);
-#pragma unroll
-    for (int i = 0; i < R; ++i)
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) {
-        b0[i][v] = b1[i][v];
-        b1[i][v] = b2[i][v];
-        if constexpr (ADD) {
-          r0[i][v] = r1[i][v];
-          r1[i][v] = r2[i][v];
-        }
-      }
+    if (gather_step<K>(c, st, pre, xs, xk, c.spin_limit)) return false;  // a partner is late
+    emit_y(sg[k0], st, xs);
+    st += c.nclusters;
+    return true;
+  };
+  while (pipe_step(std::integral_constant<int, 0>{}) && pipe_step(std::integral_constant<int, 1>{}) &&
+         pipe_step(std::integral_constant<int, 2>{})) {
   }
   // The rest of the steps, one at a time, computing any partial that does not arrive
   // (reached only when a partner's words are late).  Steps before `done` have had this
   // member's partials formed and published by the loop above; the residual sum of a step
   // is formed again (and written again, with the same values).
   if (st < nsteps) {
-    const int64_t done = st + 2 * c.nclusters;
+    const int done = st + 2 * c.nclusters;
     const uint32_t tail_limit = c.spin_limit >> 8;  // a late partner: wait less from now on
     for (; st < nsteps; st += c.nclusters) {
-      u32x4 sb[R][VPL], rb[ADD ? R : 1][VPL];
-      load(st, sb, rb);
-      form_sum(st, sb, rb);
+      Stage sb;
+      load(st, sb);
+      form_sum(st, sb);
       if (st >= done) {
         float mine[K];
         partial(sb, mine);
@@ -567,7 +606,8 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   const int cl = blockIdx.x % c.nclusters;
   const int member = blockIdx.x / c.nclusters;
   const int64_t vofs = static_cast<int64_t>(member) * c.slice_vecs;
-  const int64_t nsteps = (a.M + R - 1) / R;
+  // steps and step indices are 32-bit (the planner keeps M below 2^31)
+  const int nsteps = static_cast<int>((a.M + R - 1) / R);
 
   // Per-column partial sums of the member's slice: registers, or (LACC, wide members)
   // LDS words private to each lane, [dgamma|dbeta][vector][4-column chunk][lane].
@@ -615,37 +655,46 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
   __shared__ int xok[2][kMaxCluster];
   int parity = 0, xp = 0;
 
-  // A step's x and dy slices and its rows' saved statistics, loaded together.
+  // A step's x and dy slices and its rows' saved statistics, loaded together.  Every
+  // access goes through a buffer resource of the row's slice (rows past M get an empty
+  // one), so the loads are unconditional and read zero where there is no data.
   struct Stage {
     u32x4 x[R][VPL], d[R][VPL];
     u32x4 g2[ADD ? R : 1][VPL];  // ADD: gradient arriving at the residual sum
     float r[R], mu[R];
   };
-  auto load = [&](int64_t st, Stage& sb) {
+  const uint32_t slice_bytes = static_cast<uint32_t>(c.slice_vecs) * 16u;
+  const int M32 = static_cast<int>(a.M);
+  auto slice = [&](const void* base, int row) {
+    return make_rsrc(static_cast<const char*>(base) + (static_cast<int64_t>(row) * a.nvec + vofs) * 16,
+                     row < M32 ? slice_bytes : 0u);
+  };
+  const uint32_t lane_ofs = static_cast<uint32_t>(tid) * 16u;
+  auto load = [&](int st, Stage& sb) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int64_t row = st * R + i;
-      // the row's slice is addressed from opaque per-lane pointers, so that no per-vector
-      // 64-bit addresses are kept live across the step loop
-      const int64_t lofs = row * a.nvec + vofs + tid;
-      const u32x4* xp = opaque_ptr(static_cast<const u32x4*>(a.x) + lofs);
-      const u32x4* dp = opaque_ptr(static_cast<const u32x4*>(a.dy) + lofs);
-      const u32x4* rp = ADD ? opaque_ptr(static_cast<const u32x4*>(a.dres) + lofs) : nullptr;
+      const int row = st * R + i;
+      const rsrc_t rx = slice(a.x, row), rd = slice(a.dy, row);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        const bool ok = own[v] && row < a.M;
-        sb.x[i][v] = ok ? ld16_stream(xp, v * T) : zero16();
-        sb.d[i][v] = ok ? ld16_stream(dp, v * T) : zero16();
-        if constexpr (ADD) sb.g2[i][v] = ok ? ld16_stream(rp, v * T) : zero16();
+        sb.x[i][v] = buf_ld16(rx, lane_ofs + v * T * 16);
+        sb.d[i][v] = buf_ld16(rd, lane_ofs + v * T * 16);
       }
-      sb.r[i] = row < a.M ? a.rstd[row] : 0.0f;
-      sb.mu[i] = (LN && row < a.M) ? a.mean[row] : 0.0f;
+      if constexpr (ADD) {
+        const rsrc_t rg = slice(a.dres, row);
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) sb.g2[i][v] = buf_ld16(rg, lane_ofs + v * T * 16);
+      }
+      const uint32_t sn = row < M32 ? 4u : 0u;
+      sb.r[i] = buf_ldf(make_rsrc(a.rstd + row, sn), 0);
+      sb.mu[i] = LN ? buf_ldf(make_rsrc(a.mean + row, sn), 0) : 0.0f;
     }
   };
-  // Partial row sums of g*xhat and g over this member's slice, for each row of the step,
-  // and the slice's column contributions to dgamma/dbeta (which need no row sums).
-  // Rows past M have zero x and dy, so they add nothing.
-  auto partial = [&](const Stage& sb, float (&out)[K]) {
+  // This thread's partial row sums of g*xhat and g over the member's slice, for each row
+  // of the step, and the slice's column contributions to dgamma/dbeta (which need no row
+  // sums); the caller reduces the row sums over the workgroup.  Rows past M have zero x
+  // and dy, so they add nothing.
+  auto partial_sums = [&](const Stage& sb, float (&out)[K]) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
       const float r = sb.r[i];
@@ -686,23 +735,25 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
       out[2 * i] = s1;
       out[2 * i + 1] = s2;
     }
+  };
+  auto partial = [&](const Stage& sb, float (&out)[K]) {
+    partial_sums(sb, out);
     block_sum_n<NW, K>(out, red, parity);
   };
-  // S steps live in registers: b[0] waits for the exchange, b[1 .. S-3] are published,
-  // b[S-2] is reduced and published this iteration and b[S-1] is being loaded, so the
-  // exchange round trip of a step overlaps S-2 steps of work.
+  // S steps live in registers: b[k0] waits for the exchange, the next S-3 are published,
+  // one is reduced and published this iteration and one is being loaded, so the exchange
+  // round trip of a step overlaps S-2 steps of work.  The stage roles rotate through
+  // fixed registers (the loop body is unrolled S times), so no step's data is copied
+  // while its loads are still in flight.
   constexpr int S = (T <= 512 && VPL * R <= 2 && !ADD) ? 4 : 3;
   Stage b[S];
-  int64_t st = cl;
+  int st = cl;
   if (st < nsteps) {
 #pragma unroll
-    for (int k = 0; k < S - 1; ++k) {
-      const int64_t sk = st + k * c.nclusters;
-      if (sk < nsteps) load(sk, b[k]);
-    }
+    for (int k = 0; k < S - 1; ++k) load(st + k * c.nclusters, b[k]);
 #pragma unroll
     for (int k = 0; k < S - 2; ++k) {
-      const int64_t sk = st + k * c.nclusters;
+      const int sk = st + k * c.nclusters;
       if (sk < nsteps) {
         float mine[K];
         partial(b[k], mine);
@@ -711,13 +762,12 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     }
   }
   // dx of a step's rows from the gathered partials of every member (contraction off, as
-  // for the partials).
-  auto emit_dx = [&](const Stage& sb, int64_t st, const float* xs) {
+  // for the partials).  Stores past the slice or past M are dropped by the range check.
+  auto emit_dx = [&](const Stage& sb, int st, const float* xs) {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int64_t row = st * R + i;
-      if (row >= a.M) break;
+      const int row = st * R + i;
       float t1 = 0.0f, t2 = 0.0f;
       for (int j = 0; j < c.C; ++j) {
         t1 += xs[j * K + 2 * i];
@@ -728,9 +778,9 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
       // dx = r * (g - c2 - xhat * c1) = g * r + (xhat * (-r * c1) + (-r * c2)).
       const float nrc1 = -r * (t1 * a.inv_n);
       const float nrc2 = LN ? -r * (t2 * a.inv_n) : 0.0f;
+      const rsrc_t ro = slice(a.dx, row);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) {
-        if (!own[v]) continue;
         float o[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
@@ -740,35 +790,50 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
           o[e] = fmaf(gg, r, fmaf(xh, nrc1, nrc2));
           if constexpr (ADD) o[e] += D::get_fresh(sb.g2[i][v], e);
         }
-        st16_stream(a.dx, row * a.nvec + vofs + v * T + tid, D::pack(o));
+        buf_st16(ro, lane_ofs + v * T * 16, D::pack(o));
       }
     }
   };
 
-  for (; st < nsteps; st += c.nclusters) {
-    const int64_t sp = st + (S - 2) * c.nclusters, sl = st + (S - 1) * c.nclusters;
+  // One pipelined step with compile-time stage roles; false when the loop is to end
+  // (no steps left, or a partner is late: then st is the step to finish in the tail).
+  // Order: wave 0 reads step st's exchange words, then step sl's loads are issued, then
+  // step sp is reduced (in waves other than 0 it waits only for its own loads, issued one
+  // step earlier) and published, and only then does wave 0 wait for the other members'
+  // words of step st: a late partner never delays this member's own publication.
+  // Where step sl's loads are issued: before step sp's reduction (so they are in flight
+  // during it), or after its publication (1024-lane members, which measure faster so).
+  constexpr bool kLoadFirst = T < 1024;
+  auto pipe_step = [&](auto k0_) -> bool {
+    constexpr int k0 = decltype(k0_)::value;
+    constexpr int kp = (k0 + S - 2) % S, kl = (k0 + S - 1) % S;
+    if (st >= nsteps) return false;
+    const int sp = st + (S - 2) * c.nclusters, sl = st + (S - 1) * c.nclusters;
     unsigned long long pre[K];
     prefetch_step<K>(c, st, pre);
-    if (sp < nsteps) {
-      float mine[K];
-      partial(b[S - 2], mine);
-      publish_step<K>(c, member, sp, mine);
-    }
-    if (sl < nsteps) load(sl, b[S - 1]);
-
+    if constexpr (kLoadFirst) load(sl, b[kl]);
+    float mine[K];
+    partial_sums(b[kp], mine);
+    block_sum_n<NW, K>(mine, red, parity);
+    if (sp < nsteps) publish_step<K>(c, member, sp, mine);
+    if constexpr (!kLoadFirst) load(sl, b[kl]);
     float* xs = xin[xp];
     int* xk = xok[xp];
     xp ^= 1;
-    if (gather_step<K>(c, st, pre, xs, xk, c.spin_limit)) break;  // a partner is late
-    emit_dx(b[0], st, xs);
-#pragma unroll
-    for (int k = 0; k < S - 1; ++k) b[k] = b[k + 1];
+    if (gather_step<K>(c, st, pre, xs, xk, c.spin_limit)) return false;  // a partner is late
+    emit_dx(b[k0], st, xs);
+    st += c.nclusters;
+    return true;
+  };
+  while (pipe_step(std::integral_constant<int, 0>{}) && pipe_step(std::integral_constant<int, 1>{}) &&
+         (S < 3 || pipe_step(std::integral_constant<int, 2 % S>{})) &&
+         (S < 4 || pipe_step(std::integral_constant<int, 3 % S>{}))) {
   }
   // The rest of the steps, one at a time, computing any partial that does not arrive
   // (reached only when a partner's words are late).  Steps before `done` have had this
   // member's partial (and column sums) formed and published by the loop above.
   if (st < nsteps) {
-    const int64_t done = st + (S - 1) * c.nclusters;
+    const int done = st + (S - 1) * c.nclusters;
     const uint32_t tail_limit = c.spin_limit >> 8;  // a late partner: wait less from now on
     for (; st < nsteps; st += c.nclusters) {
       Stage sb;

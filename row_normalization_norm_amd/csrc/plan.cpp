@@ -193,6 +193,8 @@ bool plan_rows(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec
 
 bool plan_cluster(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec, int dtype,
                   const norm_options_t& o, Plan& p) {
+  // the kernels index steps and rows with 32-bit integers
+  if (M > int64_t(INT32_MAX) - 2) return false;
   const int max_vpl = backward ? kClusterBwdMaxVpl : kClusterFwdMaxVpl;
   const int rows = o.cluster_rows ? o.cluster_rows
                    : !backward               ? kClusterFwdRows

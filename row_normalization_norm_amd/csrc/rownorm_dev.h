@@ -239,23 +239,51 @@ __device__ inline u32x4 ld16(const void* base, int64_t vec_index) {
 __device__ inline void st16(void* base, int64_t vec_index, const u32x4& v) {
   static_cast<u32x4*>(base)[vec_index] = v;
 }
-// Streaming variants for data touched once (x, dy, y, dx): non-temporal hint, so the
-// stream does not evict gamma/beta and the partial rows from the caches.
 // The same pointer, opaque to the optimiser: addresses formed from it inside a loop are
 // not hoisted out of the loop as one live 64-bit address per vector (which spills the
-// widest mappings).
+// widest mappings).  It passes through the empty asm as a global (address space 1)
+// pointer, so the loads made through it are global loads: a flat load would also count
+// against the LDS wait counter, and every later LDS access would then wait for the row's
+// HBM reads.
 template <typename T>
 __device__ inline T* opaque_ptr(T* p) {
-  asm volatile("" : "+v"(p));
-  return p;
+  auto g = (__attribute__((address_space(1))) T*)p;
+  asm volatile("" : "+v"(g));
+  return (T*)g;
 }
 
+// Streaming variants for data touched once (x, dy, y, dx): non-temporal hint, so the
+// stream does not evict gamma/beta and the partial rows from the caches.
 __device__ inline u32x4 ld16_stream(const void* base, int64_t vec_index) {
   return __builtin_nontemporal_load(static_cast<const u32x4*>(base) + vec_index);
 }
 __device__ inline void st16_stream(void* base, int64_t vec_index, const u32x4& v) {
   __builtin_nontemporal_store(v, static_cast<u32x4*>(base) + vec_index);
 }
+
+// Raw buffer access (CDNA buffer resource: 48-bit base, byte size, no stride).  A load at
+// or past the end reads zero and a store there is dropped, by the hardware's range check,
+// so ragged slices and rows past the last need no branch around the access.  Without
+// branches the compiler can count the loads still in flight exactly and wait for just
+// the ones a computation needs (a load under a branch makes it wait for all of them).
+// The resource has to be uniform across the workgroup (it lives in scalar registers).
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+constexpr int kBufferFlags = 0x00020000;  // raw 32-bit data, the GFX9-family encoding
+constexpr int kBufferNT = 2;              // non-temporal cache policy (GFX940 family)
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kBufferFlags);
+}
+__device__ inline u32x4 buf_ld16(rsrc_t r, uint32_t byte_ofs) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_ofs, 0, kBufferNT);
+}
+__device__ inline void buf_st16(rsrc_t r, uint32_t byte_ofs, const u32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_ofs, 0, kBufferNT);
+}
+__device__ inline float buf_ldf(rsrc_t r, uint32_t byte_ofs) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_ofs, 0, 0));
+}
+
 __device__ inline u32x4 zero16() {
   u32x4 z = {0u, 0u, 0u, 0u};
   return z;
