@@ -30,10 +30,10 @@ constexpr bool tc_is16(int tc) { return tc != kTcF32; }  // 16-bit activations
   X(16, 1) X(16, 2) X(16, 3) X(16, 4) X(16, 6) X(16, 8)                                \
   X(32, 1) X(32, 2) X(32, 3) X(32, 4) X(32, 6) X(32, 8)                                \
   X(64, 1) X(64, 2) X(64, 3) X(64, 4) X(64, 6) X(64, 8)                                \
-  X(128, 2) X(128, 3) X(128, 4) X(128, 6) X(128, 8)                                    \
-  X(256, 2) X(256, 3) X(256, 4) X(256, 6) X(256, 8)                                    \
-  X(512, 2) X(512, 3) X(512, 4) X(512, 6) X(512, 8)                                    \
-  X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 6) X(1024, 8)                               \
+  X(128, 1) X(128, 2) X(128, 3) X(128, 4) X(128, 6) X(128, 8)                          \
+  X(256, 1) X(256, 2) X(256, 3) X(256, 4) X(256, 6) X(256, 8)                          \
+  X(512, 1) X(512, 2) X(512, 3) X(512, 4) X(512, 6) X(512, 8)                          \
+  X(1024, 1) X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 6) X(1024, 8)                    \
   X(512, 16) X(1024, 12) X(1024, 16)
 
 // The backward keeps x, dy and per-column fp32 partials of dgamma (and dbeta) in
