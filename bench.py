@@ -345,6 +345,81 @@ def cpu_baseline(w, target_s=12.0):
                       f"forward + dx + dgamma/dbeta), {passes} pass(es) of {dt:.2f} s"}
 
 
+def dgamma_compare(w, device, reps=5):
+    """The backward call with each way of reducing dgamma/dbeta over the rows: the two-stage
+    reduction (per-workgroup partial rows, then the column-reduce kernel) on the tuned plan
+    and on the atomic variants' own mapping, against fp32 atomicAdd of every row's
+    contribution (ATOMIC_ROW, M*N adds per output vector) and of one partial per workgroup
+    (ATOMIC_WG, grid*N adds).  Each variant is timed over `reps` calls per rotating buffer
+    set (HIP events around the calls, so the atomic variants' zero fill is included), after
+    one forward per set has saved the statistics.  Also reports how far each variant's
+    dgamma is from the tuned two-stage result."""
+    import torch
+    import row_normalization_norm_amd as rn
+    b = Bench(w, device)
+    for k in range(b.sets):
+        b.step(k)
+    torch.cuda.synchronize()
+    dt = lib_dtype(w)
+    ln = w.kind == "ln"
+    s, ps = elem_bytes(w.dtype), elem_bytes(w.param_dtype)
+    _, bwd_b = ideal_bytes(w.kind, w.M, w.N, s, ps)
+    apl = rn.norm_plan(True, ln, w.M, w.N, dt,
+                       options=rn.Options(dgamma_mode=rn.NORM_DGAMMA_ATOMIC_WG))
+    variants = [
+        ("two_stage", None),
+        ("two_stage_same_mapping", rn.Options(path=rn.NORM_PATH_ROWS,
+                                              lanes_per_row=apl.lanes_per_row,
+                                              vecs_per_lane=apl.vecs_per_lane, grid=apl.grid)),
+        ("atomic_wg", rn.Options(dgamma_mode=rn.NORM_DGAMMA_ATOMIC_WG)),
+        ("atomic_row", rn.Options(dgamma_mode=rn.NORM_DGAMMA_ATOMIC_ROW)),
+    ]
+
+    def bwd(buf, opt, ws):
+        if ln:
+            rn.norm_ln_bwd(buf["dy"], buf["x"], b.gamma, buf["mean"], buf["rstd"], buf["dx"],
+                           b.dgamma, b.dbeta, workspace=ws, options=opt)
+        else:
+            rn.norm_rms_bwd(buf["dy"], buf["x"], b.gamma, buf["rstd"], buf["dx"], b.dgamma,
+                            workspace=ws, options=opt)
+
+    rows, ref = [], None
+    for name, opt in variants:
+        pl = rn.norm_plan(True, ln, w.M, w.N, dt, options=opt)
+        need = rn.norm_bwd_workspace_size(w.M, w.N, ln, dt, opt)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        bwd(b.bufs[0], opt, ws)  # warm-up
+        torch.cuda.synchronize()
+        dg = b.dgamma.clone()
+        db = b.dbeta.clone() if ln else None
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for buf in b.bufs:
+                bwd(buf, opt, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (reps * b.sets)
+        if ref is None:
+            ref = (dg, db)
+
+        def rel(a, r):
+            return float(((a - r).abs().max() / r.abs().max().clamp_min(1e-30)).item())
+
+        row = {"variant": name, "ms": round(ms, 5), "GBs": round(bwd_b / (ms * 1e-3) / 1e9, 1),
+               "mapping": f"{pl.lanes_per_row}x{pl.vecs_per_lane}, grid {pl.grid}",
+               "atomic_adds_per_output_vector": (w.M if name == "atomic_row" else
+                                                 pl.grid if name == "atomic_wg" else 0) * w.N,
+               "dgamma_max_rel_diff_vs_two_stage": rel(dg, ref[0])}
+        if ln:
+            row["dbeta_max_rel_diff_vs_two_stage"] = rel(db, ref[1])
+        rows.append(row)
+        del ws
+    del b
+    return {"workload": w.name, "desc": describe(w), "variants": rows}
+
+
 def _read_csv(path):
     import csv
     with open(path, newline="") as f:
@@ -516,6 +591,10 @@ def main():
     ap.add_argument("--all", metavar="JSON", help="also time every workload, write a table")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only time a plain device copy of BYTES and print it")
+    ap.add_argument("--dgamma-compare", metavar="JSON",
+                    help="only time the backward with the two-stage and the atomic dgamma "
+                         "reductions on rms1, ln2, rms3 and sweep points up to N=8192, "
+                         "write a table")
     ap.add_argument("--summarize", metavar="DIR",
                     help="only write the profiles/ summaries from a profiling session in DIR")
     args = ap.parse_args()
@@ -539,6 +618,22 @@ def main():
     device = torch.device("cuda:0")
     if args.copy_probe:
         print(json.dumps(copy_probe(args.copy_probe, args.steps, device)), flush=True)
+        return
+
+    if args.dgamma_compare:
+        import gc
+        names = ["rms1", "ln2", "rms3"] + [f"sweep_{k}_bf16_N{n}" for k in ("rms", "ln")
+                                           for n in (1024, 4096, 8192)]
+        res = []
+        for name in names:
+            gc.collect()
+            torch.cuda.empty_cache()
+            res.append(dgamma_compare(workload_by_name(name), device))
+            print("# " + name + ": " + ", ".join(f"{v['variant']} {v['GBs']:.0f} GB/s"
+                                                 for v in res[-1]["variants"]),
+                  file=sys.stderr, flush=True)
+        with open(args.dgamma_compare, "w") as f:
+            json.dump(res, f, indent=1)
         return
 
     w = workload_by_name(args.workload)
