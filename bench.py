@@ -134,33 +134,49 @@ class Bench:
         torch.cuda.synchronize()
         self.setup_s = time.time() - t0
 
-    def step(self, k, fwd_opt=None, bwd_opt=None):
+    def step(self, k, fwd_opt=None, bwd_opt=None, bwd_events=None):
+        """One forward + backward on buffer set k; with bwd_events = (e0, e1), events
+        recorded on the launch stream just before and just after the backward call."""
+        self.forward(k, fwd_opt)
+        if bwd_events:
+            bwd_events[0].record()
+        self.backward(k, bwd_opt)
+        if bwd_events:
+            bwd_events[1].record()
+
+    def forward(self, k, opt=None):
         rn, w, b = self.rn, self.w, self.bufs[k % self.sets]
         if self.fused:
             if w.kind == "rms":
                 rn.norm_rms_fwd_add(b["x"], b["res"], self.gamma, b["y"], b["sum"], b["rstd"],
-                                    eps=w.eps, workspace=self.fws, options=fwd_opt)
-                rn.norm_rms_bwd_add(b["dy"], b["sum"], self.gamma, b["rstd"], b["dsum"], b["dx"],
-                                    self.dgamma, workspace=self.ws, options=bwd_opt)
+                                    eps=w.eps, workspace=self.fws, options=opt)
             else:
                 rn.norm_ln_fwd_add(b["x"], b["res"], self.gamma, self.beta, b["y"], b["sum"],
                                    b["mean"], b["rstd"], eps=w.eps, workspace=self.fws,
-                                   options=fwd_opt)
-                rn.norm_ln_bwd_add(b["dy"], b["sum"], self.gamma, b["mean"], b["rstd"], b["dsum"],
-                                   b["dx"], self.dgamma, self.dbeta, workspace=self.ws,
-                                   options=bwd_opt)
-            return
-        if w.kind == "rms":
+                                   options=opt)
+        elif w.kind == "rms":
             rn.norm_rms_fwd(b["x"], self.gamma, b["y"], b["rstd"], eps=w.eps, workspace=self.fws,
-                            options=fwd_opt)
-            rn.norm_rms_bwd(b["dy"], b["x"], self.gamma, b["rstd"], b["dx"], self.dgamma,
-                            workspace=self.ws, options=bwd_opt)
+                            options=opt)
         else:
             rn.norm_ln_fwd(b["x"], self.gamma, self.beta, b["y"], b["mean"], b["rstd"], eps=w.eps,
-                           workspace=self.fws, options=fwd_opt)
-            rn.norm_ln_bwd(b["dy"], b["x"], self.gamma, b["mean"], b["rstd"], b["dx"], self.dgamma,
-                           self.dbeta, workspace=self.ws, options=bwd_opt)
+                           workspace=self.fws, options=opt)
 
+    def backward(self, k, opt=None):
+        rn, w, b = self.rn, self.w, self.bufs[k % self.sets]
+        if self.fused:
+            if w.kind == "rms":
+                rn.norm_rms_bwd_add(b["dy"], b["sum"], self.gamma, b["rstd"], b["dsum"], b["dx"],
+                                    self.dgamma, workspace=self.ws, options=opt)
+            else:
+                rn.norm_ln_bwd_add(b["dy"], b["sum"], self.gamma, b["mean"], b["rstd"], b["dsum"],
+                                   b["dx"], self.dgamma, self.dbeta, workspace=self.ws,
+                                   options=opt)
+        elif w.kind == "rms":
+            rn.norm_rms_bwd(b["dy"], b["x"], self.gamma, b["rstd"], b["dx"], self.dgamma,
+                            workspace=self.ws, options=opt)
+        else:
+            rn.norm_ln_bwd(b["dy"], b["x"], self.gamma, b["mean"], b["rstd"], b["dx"], self.dgamma,
+                           self.dbeta, workspace=self.ws, options=opt)
 
 def make_events(n):
     import torch
@@ -198,18 +214,20 @@ def run_gpu(w, steps, warmup, device, fused=False):
 
     fev = make_events(2 * steps)
     bev = make_events(2 * steps)
+    cev = make_events(2 * steps)
     fopts = [rn.Options(ev_start=fev[2 * i].cuda_event, ev_stop=fev[2 * i + 1].cuda_event)
              for i in range(steps)]
     bopts = [rn.Options(ev_start=bev[2 * i].cuda_event, ev_stop=bev[2 * i + 1].cuda_event)
              for i in range(steps)]
     torch.cuda.synchronize()
     for k in range(steps):
-        b.step(warmup + steps + k, fopts[k], bopts[k])
+        b.step(warmup + steps + k, fopts[k], bopts[k], (cev[2 * k], cev[2 * k + 1]))
     torch.cuda.synchronize()
     fwd_ms = sum(fev[2 * i].elapsed_time(fev[2 * i + 1]) for i in range(steps)) / steps
     bwd_ms = sum(bev[2 * i].elapsed_time(bev[2 * i + 1]) for i in range(steps)) / steps
+    call_ms = sum(cev[2 * i].elapsed_time(cev[2 * i + 1]) for i in range(steps)) / steps
     return dict(ms_per_step=total_ms / steps, fwd_kernel_ms=fwd_ms, bwd_main_kernel_ms=bwd_ms,
-                wall_s=wall, sets=b.sets, setup_s=b.setup_s)
+                bwd_call_ms=call_ms, wall_s=wall, sets=b.sets, setup_s=b.setup_s)
 
 
 def workload_by_name(name):
@@ -663,6 +681,7 @@ def main():
         "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "fwd_GBs": round(fwd_b / (r["fwd_kernel_ms"] * 1e-3) / 1e9, 1),
         "bwd_GBs": round(bwd_b / ((r["ms_per_step"] - r["fwd_kernel_ms"]) * 1e-3) / 1e9, 1),
+        "bwd_call_GBs": round(bwd_b / (r["bwd_call_ms"] * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
             "kernel": f"bwd_rows_kernel (dx + dgamma/dbeta partials), "
@@ -716,6 +735,7 @@ def main():
                           **{k: round(v, 5) for k, v in rr.items()},
                           "fwd_GBs": fb / (rr["fwd_kernel_ms"] * 1e-3) / 1e9,
                           "bwd_GBs": bb / ((rr["ms_per_step"] - rr["fwd_kernel_ms"]) * 1e-3) / 1e9,
+                          "bwd_call_GBs": bb / (rr["bwd_call_ms"] * 1e-3) / 1e9,
                           "step_GBs": (fb + bb) / (rr["ms_per_step"] * 1e-3) / 1e9})
             # the streaming reference at the forward's (1 read + 1 write of M*N elements)
             # and the backward's (2 reads + 1 write) element bytes

@@ -151,10 +151,10 @@ def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 1024, -1), grids_b=(0, 256, 5
     return res
 
 
-def sweep(out_path, ns=SWEEP_N, dirs=("fwd", "bwd")):
+def sweep(out_path, ns=SWEEP_N, dirs=("fwd", "bwd"), kinds=("rms", "ln"), dtypes=("bf16", "f32")):
     with open(out_path, "w") as out:
-        for kind in ("rms", "ln"):
-            for dtype in ("bf16", "f32"):
+        for kind in kinds:
+            for dtype in dtypes:
                 for N in ns:
                     res = tune_shape(kind, dtype, (1 << 27) // N, N, dirs=dirs)
                     for r in res:
@@ -207,13 +207,17 @@ def main():
                     help="row lengths to sweep (default: all)")
     ap.add_argument("--dirs", nargs="+", default=["fwd", "bwd"], choices=["fwd", "bwd"],
                     help="directions to sweep (default: both)")
+    ap.add_argument("--kinds", nargs="+", default=["rms", "ln"], choices=["rms", "ln"],
+                    help="normalizations to sweep (default: both)")
+    ap.add_argument("--dtypes", nargs="+", default=["bf16", "f32"], choices=["bf16", "f32"],
+                    help="element types to sweep (default: both)")
     ap.add_argument("--table", metavar="IN.jsonl", nargs="+",
                     help="print csrc/tuned.h built from sweep results (a shape in a later "
                          "file replaces the earlier files' results for it)")
     args = ap.parse_args()
     if args.sweep:
         sys.path.insert(0, os.path.dirname(HERE))
-        sweep(args.sweep, args.n, tuple(args.dirs))
+        sweep(args.sweep, args.n, tuple(args.dirs), tuple(args.kinds), tuple(args.dtypes))
     elif args.table:
         sys.stdout.write(table(args.table))
     else:
