@@ -538,7 +538,7 @@ def summarize(d, workload, warmup, steps, copy_bytes):
 
 
 PROFILE_STEPS = (
-    "cd /tmp && export TMPDIR=/tmp; R=/root/repo; D=$R/gpurun_out/prof",
+    "cd /tmp && export TMPDIR=/tmp; R=/root/repo; D=${{PROF_OUT:-$R/prof_out}}; mkdir -p $D",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $D/trace -o {w} -- "
     "python3 $R/bench.py --workload {w} --steps 10 --warmup 3 --no-cpu",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE -o {w} -- "
