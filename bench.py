@@ -725,7 +725,7 @@ def main():
             # (empty) caching-allocator state
             gc.collect()
             torch.cuda.empty_cache()
-            rr = run_gpu(wl, max(5, args.steps // 2), 3, device, fused=is_fused)
+            rr = run_gpu(wl, max(5, args.steps // 2), 10, device, fused=is_fused)
             es = elem_bytes(wl.dtype)
             fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, es, elem_bytes(wl.param_dtype))
             if is_fused:  # + read residual, write sum; + read dsum
