@@ -188,7 +188,7 @@ def make_events(n):
     return evs
 
 
-def run_gpu(w, steps, warmup, device, fused=False):
+def run_gpu(w, steps, warmup, device, fused=False, warmup_s=0.0):
     """Two timed passes of `steps` steps each, after `warmup` untimed steps:
     pass A records events only before and after the K steps (the step time); pass B also
     records HIP events around every launch of the forward kernel and of the backward's
@@ -197,9 +197,18 @@ def run_gpu(w, steps, warmup, device, fused=False):
     import torch
     import row_normalization_norm_amd as rn
     b = Bench(w, device, fused)
-    for k in range(warmup):
+    # `warmup` steps, continued (when warmup_s is set) until that much wall time has gone
+    # by: on MI355X the first tens of milliseconds of sustained traffic run slower than
+    # the steady state (a short step's first 50 timed steps up to 13 % slower)
+    t0 = time.perf_counter()
+    k = 0
+    while k < warmup or time.perf_counter() - t0 < warmup_s:
         b.step(k)
+        k += 1
+        if k % 16 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warmup = k
 
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -603,7 +612,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--all", metavar="JSON", help="also time every workload, write a table")
@@ -725,7 +734,7 @@ def main():
             # (empty) caching-allocator state
             gc.collect()
             torch.cuda.empty_cache()
-            rr = run_gpu(wl, max(5, args.steps // 2), 10, device, fused=is_fused)
+            rr = run_gpu(wl, max(5, args.steps // 2), 10, device, fused=is_fused, warmup_s=0.3)
             es = elem_bytes(wl.dtype)
             fb, bb = ideal_bytes(wl.kind, wl.M, wl.N, es, elem_bytes(wl.param_dtype))
             if is_fused:  # + read residual, write sum; + read dsum
