@@ -402,8 +402,10 @@ hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P,
 
 // Streaming reference (a measurement aid, not on the normalization path): each workgroup
 // owns a contiguous chunk of 256 x kStreamVecs 16-byte vectors, issues all its loads,
-// then all its stores, with the norm kernels' non-temporal hints.
-constexpr int kStreamVecs = 4;
+// then all its stores, with the norm kernels' non-temporal hints.  One vector per thread
+// is the fastest form measured on MI355X (copy 6.5-6.6 TB/s and two reads + one write
+// 6.4-6.5 TB/s over 256 MiB-1 GiB streams, against 6.1-6.25 with four per thread).
+constexpr int kStreamVecs = 1;
 
 template <bool TWO>
 __global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ a,
