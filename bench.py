@@ -410,6 +410,19 @@ def dgamma_compare(w, device, reps=5):
             rn.norm_rms_bwd(buf["dy"], buf["x"], b.gamma, buf["rstd"], buf["dx"], b.dgamma,
                             workspace=ws, options=opt)
 
+    # warm the device up first (sustained traffic for 0.3 s), so that the first variant
+    # timed is not measured before the steady state
+    ws0 = torch.empty(max(rn.norm_bwd_workspace_size(w.M, w.N, ln, dt), 1), dtype=torch.uint8,
+                      device=device)
+    t0 = time.perf_counter()
+    k = 0
+    while time.perf_counter() - t0 < 0.3:
+        bwd(b.bufs[k % b.sets], None, ws0)
+        k += 1
+        if k % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    del ws0
     rows, ref = [], None
     for name, opt in variants:
         pl = rn.norm_plan(True, ln, w.M, w.N, dt, options=opt)
@@ -615,6 +628,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-only", action="store_true",
+                    help="only time the oracle CPU baseline of --workload (no GPU needed)")
+    ap.add_argument("--cpu-threads", type=int, metavar="T",
+                    help="host threads for the oracle (default: OpenMP's, all cores)")
     ap.add_argument("--all", metavar="JSON", help="also time every workload, write a table")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only time a plain device copy of BYTES and print it")
@@ -627,6 +644,14 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         write_summaries(args.summarize, args.workload)
+        return
+    if args.cpu_threads:
+        # read by the OpenMP runtime when the oracle library is loaded
+        os.environ["OMP_NUM_THREADS"] = str(args.cpu_threads)
+    if args.cpu_only:
+        out = cpu_baseline(workload_by_name(args.workload))
+        out["workload"] = args.workload
+        print(json.dumps(out), flush=True)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
