@@ -30,6 +30,8 @@ sys.path.insert(0, ROOT)
 METRIC = "RMSNorm/LayerNorm fwd+bwd effective GB/s and % of MI355X HBM peak, bf16"
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "ln2"
+DEFAULT_STEPS = 50
+DEFAULT_WARMUP = 100
 MALL_BYTES = 256 << 20
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_bwd_rows_ln2.json")
 
@@ -562,7 +564,7 @@ def summarize(d, workload, warmup, steps, copy_bytes):
 PROFILE_STEPS = (
     "cd /tmp && export TMPDIR=/tmp; R=/root/repo; D=${{PROF_OUT:-$R/prof_out}}; mkdir -p $D",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $D/trace -o {w} -- "
-    "python3 $R/bench.py --workload {w} --steps 10 --warmup 3 --no-cpu",
+    "python3 $R/bench.py --workload {w} --no-cpu",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE -o {w} -- "
     "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu > $D/FETCH_SIZE_{w}.log",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $D/WRITE_SIZE -o {w} -- "
@@ -577,7 +579,7 @@ PROFILE_STEPS = (
 )
 
 
-def write_summaries(d, w, warmup=3, steps=10, copy_bytes=1 << 30):
+def write_summaries(d, w, warmup=DEFAULT_WARMUP, steps=DEFAULT_STEPS, copy_bytes=1 << 30):
     """--summarize: write profiles/<w>_kernel_trace.md, profiles/<w>_hbm_counters.md and
     (for the benchmark's own workload) the counter file bench.py reports traffic from."""
     tt, tavg, ct, fs, ws_, bwd_traffic, src_hash = summarize(d, w, warmup, steps, copy_bytes)
@@ -624,8 +626,8 @@ def load_counters(w):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
+    ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-only", action="store_true",
