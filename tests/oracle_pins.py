@@ -7,7 +7,8 @@ source (at least one must fail for every planted mistake).
 
 What pins what:
   * hand-derived worked examples (tests/golden/hand_examples.json) -- forward values,
-    eps placement, gamma/beta indexing, row indexing, degenerate rows, backward values;
+    eps placement, gamma/beta indexing, row indexing, degenerate rows, backward values,
+    and the root-sum-square magnitudes that size the dgamma/dbeta parity bound;
   * invariants: RMS of y is 1 at gamma=1, eps=0; LayerNorm y has mean 0 and variance 1;
     scale (and, for LayerNorm, shift) invariance; dx orthogonality relations at eps=0;
   * central finite differences of the forward for dx, dgamma, dbeta;
@@ -87,13 +88,17 @@ def pin_golden_backward(orc):
             dy = _as_dtype(c["dy"], dtype)
             if c["kind"] == "rms":
                 dx = orc.rms_bwd_dx(dy, x, g, c["eps"])
-                dg, _ = orc.rms_dgamma(dy, x, c["eps"])
+                dg, sg = orc.rms_dgamma(dy, x, c["eps"])
             else:
                 dx = orc.ln_bwd_dx(dy, x, g, c["eps"])
-                dg, db, _, _ = orc.ln_dgamma_dbeta(dy, x, c["eps"])
+                dg, db, sg, sb = orc.ln_dgamma_dbeta(dy, x, c["eps"])
                 _close(db, _exprs(c["dbeta"]), 1e-14, f"{c['name']} dbeta")
+                # the size of the dbeta parity bound: root-sum-square of the summed dy
+                _close(sb, _exprs(c["dbeta_scale"]), 1e-14, f"{c['name']} dbeta_scale")
             _close(dx, _exprs(c["dx"]), 1e-14, f"{c['name']} dx ({dtype})")
             _close(dg, _exprs(c["dgamma"]), 1e-14, f"{c['name']} dgamma")
+            # the size of the dgamma parity bound: root-sum-square of the summed dy * xhat
+            _close(sg, _exprs(c["dgamma_scale"]), 1e-14, f"{c['name']} dgamma_scale")
 
 
 # ------------------------------------------------------------------------ invariants

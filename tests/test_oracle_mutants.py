@@ -64,6 +64,17 @@ MUTATIONS = [
      "double xhat = (elem(x, dtype, i * N + j) - m) * r[M - 1 - i];"),
     ("dgamma_no_centering", "const double m = mu ? mu[i] : 0.0;", "const double m = 0.0;"),
     ("bf16_decode_shift", "<< 16;", "<< 15;"),
+    # the magnitudes that size the dgamma/dbeta parity bound
+    ("dgamma_scale_no_sqrt", "if (dgamma_scale) dgamma_scale[j] = sqrt(sg2[j - c0]);",
+     "if (dgamma_scale) dgamma_scale[j] = sg2[j - c0];"),
+    ("dbeta_scale_no_sqrt", "if (dbeta_scale) dbeta_scale[j] = sqrt(sb2[j - c0]);",
+     "if (dbeta_scale) dbeta_scale[j] = sb2[j - c0];"),
+    ("dgamma_scale_times_100", "if (dgamma_scale) dgamma_scale[j] = sqrt(sg2[j - c0]);",
+     "if (dgamma_scale) dgamma_scale[j] = 100.0 * sqrt(sg2[j - c0]);"),
+    ("dbeta_scale_times_100", "if (dbeta_scale) dbeta_scale[j] = sqrt(sb2[j - c0]);",
+     "if (dbeta_scale) dbeta_scale[j] = 100.0 * sqrt(sb2[j - c0]);"),
+    ("dgamma_scale_from_dy", "sg2[j - c0] += term * term;", "sg2[j - c0] += d * d;"),
+    ("dbeta_scale_not_squared", "sb2[j - c0] += d * d;", "sb2[j - c0] += d;"),
 ]
 
 
