@@ -91,15 +91,22 @@ typedef enum norm_status {
 
 /* ------------------------------------------------------------------ forward */
 
-/* Bytes of workspace the forward needs for this shape: 0 except for rows long enough to
- * be split over several workgroups, where it holds their per-row partial sums (a few
- * KiB).  A pure function of its arguments: no HIP call; valid on any gfx950 device. */
+/* Bytes of workspace the fastest forward plan for this shape uses: 0 except for rows
+ * long enough to be split over several workgroups, where it holds their per-row partial
+ * sums (a few KiB to a few MiB).  The forward's workspace is optional: a call given a
+ * NULL workspace or fewer bytes than this runs a plan that needs none (a whole row per
+ * workgroup up to 16384 16-byte vectors, else the scalar path), slower for such rows but
+ * with the same results within the stated tolerances.  A pure function of its
+ * arguments: no HIP call; valid on any gfx950 device. */
 size_t norm_fwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype);
 
 /* RMSNorm forward.  x, gamma, y: `dtype`; rstd: float [M], or NULL to not save it.
- * workspace: device memory of at least norm_fwd_workspace_size(M, N, 0, dtype) bytes,
- * 16-byte aligned (may be NULL when that size is 0); its contents on entry do not
- * matter and it must stay alive until the call has completed on `stream`. */
+ * workspace: NULL, or device memory, 16-byte aligned, of workspace_bytes bytes; with at
+ * least norm_fwd_workspace_size(M, N, 0, dtype) bytes the fastest plan runs, else one
+ * that needs no workspace (see there).  Its contents on entry do not matter and it must
+ * stay alive until the call has completed on `stream`.  With the _ex variant forcing
+ * NORM_PATH_CLUSTER the workspace is required (NORM_ERR_NULL_PTR /
+ * NORM_ERR_WORKSPACE_TOO_SMALL otherwise). */
 norm_status_t norm_rms_fwd(const void* x, const void* gamma, void* y, float* rstd,
                            int64_t M, int64_t N, float eps, norm_dtype_t dtype,
                            void* workspace, size_t workspace_bytes, hipStream_t stream);

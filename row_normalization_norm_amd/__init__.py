@@ -116,6 +116,12 @@ def lib() -> ctypes.CDLL:
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
                 f"g.build()'` (hipcc, gfx950)")
+        # torch ships its own HIP runtime under the soname libamdhip64.so.7 but links it
+        # by another name, so the dynamic loader would load a second runtime if this
+        # library (which names the soname) came first: torch's device pointers and
+        # streams would then be foreign to it.  Importing torch first makes this library
+        # bind to torch's runtime.
+        _torch()
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
@@ -206,6 +212,19 @@ def _opt(options):
     return None if options is None else ctypes.byref(options)
 
 
+def _keep_for_stream(ws, device, stream):
+    """A workspace the binding allocated lives in torch's caching allocator, which
+    tracks it on the current stream.  When the call runs on another stream, mark the
+    block as used there too, so that it is not handed to a later allocation before
+    the kernels reading it have finished."""
+    if ws is None or stream is None:
+        return
+    torch = _torch()
+    ptr = _stream(device, stream)
+    if ptr != _stream(device, None):
+        ws.record_stream(torch.cuda.ExternalStream(ptr, device=device))
+
+
 # ------------------------------------------------------------------- entry points
 def norm_fwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, options=None) -> int:
     if options is None:
@@ -217,7 +236,7 @@ def norm_fwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
 _FWD_WS = {}
 
 
-def _fwd_workspace(M, N, ln, dtype, device, workspace, options):
+def _fwd_workspace(M, N, ln, dtype, device, workspace, options, stream):
     """The caller's workspace (the library checks its size), or a new one of the size the
     call needs (None when it needs none)."""
     if workspace is not None:
@@ -231,7 +250,9 @@ def _fwd_workspace(M, N, ln, dtype, device, workspace, options):
         need = norm_fwd_workspace_size(M, N, ln, dtype, options)
     if need == 0:
         return None, 0
-    return _torch().empty(need, dtype=_torch().uint8, device=device), need
+    ws = _torch().empty(need, dtype=_torch().uint8, device=device)
+    _keep_for_stream(ws, device, stream)
+    return ws, need
 
 
 def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stream=None,
@@ -244,7 +265,7 @@ def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stre
     _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options)
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream)
     args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
             _stream(x.device, stream))
     if options is None:
@@ -266,7 +287,7 @@ def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, work
     _need(mean, "mean", M, torch.float32, x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options)
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream)
     args = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, float(eps),
             dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
     if options is None:
@@ -283,13 +304,14 @@ def norm_bwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
                                                 _opt(options)))
 
 
-def _workspace(M, N, ln, dtype, device, workspace, options):
+def _workspace(M, N, ln, dtype, device, workspace, options, stream):
     """The caller's workspace (the library checks its size), or a new one of the size the
     call needs."""
     if workspace is None:
         torch = _torch()
         need = norm_bwd_workspace_size(M, N, ln, dtype, options)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        _keep_for_stream(workspace, device, stream)
     return workspace, workspace.numel() * workspace.element_size()
 
 
@@ -303,7 +325,7 @@ def norm_rms_bwd(dy, x, gamma, rstd, dx, dgamma, workspace=None, stream=None, op
     _need(rstd, "rstd", M, torch.float32, x.device)
     _need(dgamma, "dgamma", N, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _workspace(M, N, False, dt, x.device, workspace, options)
+    ws, ws_bytes = _workspace(M, N, False, dt, x.device, workspace, options, stream)
     args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N, dt,
             _ptr(ws), ws_bytes, _stream(x.device, stream))
     if options is None:
@@ -325,7 +347,7 @@ def norm_ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace=None, str
                     (dbeta, "dbeta", N)):
         _need(t, n, k, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _workspace(M, N, True, dt, x.device, workspace, options)
+    ws, ws_bytes = _workspace(M, N, True, dt, x.device, workspace, options, stream)
     args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
             _ptr(dbeta), M, N, dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
     if options is None:
@@ -361,7 +383,7 @@ def norm_rms_fwd_add(x, residual, gamma, y, sum_out, rstd=None, eps: float = 1e-
     _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options)
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream)
     _check(lib().norm_rms_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(sum_out),
                                   _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
                                   _stream(x.device, stream), _opt(options)), "norm_rms_fwd_add")
@@ -380,7 +402,7 @@ def norm_ln_fwd_add(x, residual, gamma, beta, y, sum_out, mean=None, rstd=None,
     _need(mean, "mean", M, torch.float32, x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options)
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream)
     _check(lib().norm_ln_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
                                  _ptr(sum_out), _ptr(mean), _ptr(rstd), M, N, float(eps), dt,
                                  _ptr(ws), ws_bytes, _stream(x.device, stream), _opt(options)),
@@ -400,7 +422,7 @@ def norm_rms_bwd_add(dy, sum_in, gamma, rstd, dsum, dx, dgamma, workspace=None, 
     _need(rstd, "rstd", M, torch.float32, sum_in.device)
     _need(dgamma, "dgamma", N, torch.float32, sum_in.device)
     dt = _types(sum_in, gamma)
-    ws, ws_bytes = _workspace(M, N, False, dt, sum_in.device, workspace, options)
+    ws, ws_bytes = _workspace(M, N, False, dt, sum_in.device, workspace, options, stream)
     _check(lib().norm_rms_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(rstd), _ptr(dsum),
                                   _ptr(dx), _ptr(dgamma), M, N, dt, _ptr(ws), ws_bytes,
                                   _stream(sum_in.device, stream), _opt(options)),
@@ -420,7 +442,7 @@ def norm_ln_bwd_add(dy, sum_in, gamma, mean, rstd, dsum, dx, dgamma, dbeta, work
                     (dbeta, "dbeta", N)):
         _need(t, n, k, torch.float32, sum_in.device)
     dt = _types(sum_in, gamma)
-    ws, ws_bytes = _workspace(M, N, True, dt, sum_in.device, workspace, options)
+    ws, ws_bytes = _workspace(M, N, True, dt, sum_in.device, workspace, options, stream)
     _check(lib().norm_ln_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(mean), _ptr(rstd),
                                  _ptr(dsum), _ptr(dx), _ptr(dgamma), _ptr(dbeta), M, N, dt,
                                  _ptr(ws), ws_bytes, _stream(sum_in.device, stream),

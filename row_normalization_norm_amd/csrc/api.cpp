@@ -7,6 +7,8 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <mutex>
 
 #include "../../include/rownorm.h"
@@ -135,7 +137,14 @@ norm_status_t check_shape_dtype(int64_t M, int64_t N, norm_dtype_t dtype) {
   return NORM_OK;
 }
 
-norm_status_t hip_status(hipError_t e) { return e == hipSuccess ? NORM_OK : NORM_ERR_HIP; }
+// NORM_OK, or NORM_ERR_HIP for a failed HIP call; with ROWNORM_DEBUG set in the
+// environment the HIP error is also printed to stderr.
+norm_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return NORM_OK;
+  if (std::getenv("ROWNORM_DEBUG"))
+    std::fprintf(stderr, "rownorm: HIP error %d (%s)\n", int(e), hipGetErrorString(e));
+  return NORM_ERR_HIP;
+}
 
 struct EventScope {
   const norm_options_t* opt;
@@ -252,6 +261,15 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   Plan p;
   st = make_plan(false, ln, M, N, dt.x, a16, opt, &p);
   if (st != NORM_OK) return st;
+  // The forward's workspace is optional: only split rows use one (their exchange
+  // words).  Given none, or too little, the call takes a plan that needs none, unless
+  // the split-row path was asked for explicitly.
+  const bool forced_cluster = opt && opt->path == NORM_PATH_CLUSTER;
+  if (p.ws_need > 0 && !forced_cluster &&
+      (!workspace || workspace_bytes_given < p.ws_need)) {
+    st = make_fwd_plan_without_workspace(ln, M, N, dt.x, a16, opt, &p);
+    if (st != NORM_OK) return st;
+  }
   st = check_workspace(p, workspace, workspace_bytes_given);
   if (st != NORM_OK) return st;
   if (M == 0) return NORM_OK;
@@ -281,9 +299,9 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   hipError_t e = hipSuccess;
   if (p.path == NORM_PATH_CLUSTER) {
     e = clear_exchange(p, ws, stream);
-    if (e != hipSuccess) return NORM_ERR_HIP;
+    if (e != hipSuccess) return hip_status(e);
   }
-  if (ev.start() != hipSuccess) return NORM_ERR_HIP;
+  if ((e = ev.start()) != hipSuccess) return hip_status(e);
   switch (p.path) {
     case NORM_PATH_ROWS:
       e = launch_fwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
@@ -296,7 +314,7 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
       e = p.vpl > 0 ? launch_fwd_grows(kind, dt.tc, p.vpl, a, p.grid, stream)
                     : launch_fwd_generic(kind, dt.tc, a, p.grid, stream);
   }
-  if (e != hipSuccess) return NORM_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e);
   return hip_status(ev.stop());
 }
 
@@ -366,13 +384,13 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   hipError_t e = hipSuccess;
   if (mode != NORM_DGAMMA_TWO_STAGE) {
     e = launch_zero(dgamma, db, int32_t(N), stream);
-    if (e != hipSuccess) return NORM_ERR_HIP;
+    if (e != hipSuccess) return hip_status(e);
   }
   if (p.path == NORM_PATH_CLUSTER) {
     e = clear_exchange(p, ws, stream);
-    if (e != hipSuccess) return NORM_ERR_HIP;
+    if (e != hipSuccess) return hip_status(e);
   }
-  if (ev.start() != hipSuccess) return NORM_ERR_HIP;
+  if ((e = ev.start()) != hipSuccess) return hip_status(e);
   if (p.path == NORM_PATH_ROWS) {
     e = launch_bwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
   } else if (p.path == NORM_PATH_CLUSTER) {
@@ -386,8 +404,8 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
     if (e == hipSuccess)
       e = launch_bwd_colslice(kind, dt.tc, vec, a, p.slices, int(p.partial_rows), stream);
   }
-  if (e != hipSuccess) return NORM_ERR_HIP;
-  if (ev.stop() != hipSuccess) return NORM_ERR_HIP;
+  if (e != hipSuccess) return hip_status(e);
+  if ((e = ev.stop()) != hipSuccess) return hip_status(e);
   if (mode == NORM_DGAMMA_TWO_STAGE) {
     e = launch_colreduce(a.part_g, a.part_b, p.partial_rows, int32_t(N), dgamma, db, stream);
   }

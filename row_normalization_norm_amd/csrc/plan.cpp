@@ -435,6 +435,27 @@ norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64
   return NORM_OK;
 }
 
+norm_status_t make_fwd_plan_without_workspace(bool layernorm, int64_t M, int64_t N, int dtype,
+                                              bool aligned16, const norm_options_t* opt,
+                                              Plan* out) {
+  norm_options_t o = {};
+  if (opt) o.grid = opt->grid;
+  Plan p;
+  const int epv = dtype != NORM_DTYPE_F32 ? 8 : 4;
+  const bool vec_ok = aligned16 && (N % epv == 0);
+  const int64_t nvec = vec_ok ? N / epv : 0;
+  p.nvec = int(nvec);
+  if (!(vec_ok && nvec <= kFwdRowsWideMaxVecs && plan_rows(false, layernorm, M, N, nvec, o, false, p))) {
+    p = Plan();
+    p.nvec = int(nvec);
+    plan_generic_fwd(M, N, o, p);
+  }
+  if (M == 0) p.grid = 0;
+  p.ws_need = p.ws_bytes;
+  *out = p;
+  return NORM_OK;
+}
+
 size_t workspace_bytes(bool backward, int64_t M, int64_t N, bool layernorm, int dtype,
                        const norm_options_t* opt) {
   size_t best = 0;

@@ -48,6 +48,13 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
 norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
                                  Plan* out);
 
+// A forward plan that needs no workspace, for a call given none (or too little) where
+// the planned one would split rows over clusters: the widest register-resident row
+// mapping that covers the row, else the scalar path.  The options' grid is kept.
+norm_status_t make_fwd_plan_without_workspace(bool layernorm, int64_t M, int64_t N, int dtype,
+                                              bool aligned16, const norm_options_t* opt,
+                                              Plan* out);
+
 // Workspace bytes a call needs with these options, for either pointer alignment.
 size_t workspace_bytes(bool backward, int64_t M, int64_t N, bool layernorm, int dtype,
                        const norm_options_t* opt);

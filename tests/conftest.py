@@ -37,3 +37,17 @@ def device():
     import row_normalization_norm_amd as rn
     rn.lib()  # raises when librownorm.so is missing: never fall back
     return torch.device("cuda:0")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With PARITY_REPORT=path, write every compared output's worst error as a fraction
+    of its bound (one JSON object per line)."""
+    path = os.environ.get("PARITY_REPORT")
+    if not path or "parity" not in sys.modules:
+        return
+    import json
+    from parity import REPORT
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        for r in REPORT:
+            f.write(json.dumps(r) + "\n")

@@ -5,12 +5,12 @@ Tolerances (the GPU result against the fp64 oracle, per element):
   * fp16 y / dx:   |gpu - ref| <= 2^-10 * max(1, |ref|): the bf16 rule carried over to
                    binary16 (two half-units in the last place of its 11-bit significand)
   * fp32 y:        |gpu - ref| <= 1e-5 * max(1, |ref|)
-  * fp32 dx:       |gpu - ref| <= 1e-5 * max(1, |ref|, rstd*(|g| + |c2| + |xhat*c1|)):
-                   dx is a difference and can cancel (for N = 1, RMSNorm's dx is
-                   rstd*g*eps/(x^2+eps)); the rounding of the fp32 statistics alone is then
-                   amplified, so the bound is relative to the size of the terms the
-                   difference is formed from.  (This scale is a tolerance only; the
-                   expected values are the oracle's.)
+  * fp32 dx:       |gpu - ref| <= 1e-5 * max(1, |ref|) for rows of N >= 2 elements (the
+                   literal rule; measured worst 0.07 of it).  Rows of one element are pure
+                   cancellation (RMSNorm's dx is rstd*g*eps/(x^2+eps), LayerNorm's is 0
+                   exactly), so there the bound is relative to the terms the difference is
+                   formed from: 1e-5 * max(1, |ref|, rstd*(|g| + |c2| + |xhat*c1|)).  (That
+                   scale is a tolerance only; the expected values are the oracle's.)
   * rstd:          |gpu - ref| <= 1e-5 * |ref|
   * mean:          |gpu - ref| <= 1e-5 * RMS(x row)   (the mean of a centred row is ~0,
                    so a purely relative bound would be meaningless there)
@@ -104,23 +104,24 @@ class GpuRun:
         self.dgamma = torch.empty(N, dtype=torch.float32, device=device)
         self.dbeta = torch.empty(N, dtype=torch.float32, device=device) if w.kind == "ln" else None
 
-    def forward(self, options=None):
+    def forward(self, options=None, stream=None):
         w = self.w
         if w.kind == "rms":
-            rn.norm_rms_fwd(self.x, self.gamma, self.y, self.rstd, eps=w.eps, options=options)
+            rn.norm_rms_fwd(self.x, self.gamma, self.y, self.rstd, eps=w.eps, options=options,
+                            stream=stream)
         else:
             rn.norm_ln_fwd(self.x, self.gamma, self.beta, self.y, self.mean, self.rstd, eps=w.eps,
-                           options=options)
+                           options=options, stream=stream)
 
-    def backward(self, options=None, workspace=None, mean=None, rstd=None):
+    def backward(self, options=None, workspace=None, mean=None, rstd=None, stream=None):
         mean = self.mean if mean is None else mean
         rstd = self.rstd if rstd is None else rstd
         if self.w.kind == "rms":
             rn.norm_rms_bwd(self.dy, self.x, self.gamma, rstd, self.dx, self.dgamma,
-                            workspace=workspace, options=options)
+                            workspace=workspace, options=options, stream=stream)
         else:
             rn.norm_ln_bwd(self.dy, self.x, self.gamma, mean, rstd, self.dx, self.dgamma,
-                           self.dbeta, workspace=workspace, options=options)
+                           self.dbeta, workspace=workspace, options=options, stream=stream)
 
     def sync(self):
         import torch
@@ -149,24 +150,31 @@ def out_tol(dtype: str) -> float:
     return {"bf16": TOL_BF16, "f16": TOL_F16}.get(dtype, TOL_F32)
 
 
-def check_forward(run: GpuRun, inputs: dict, rows, orc=None):
+def check_forward(run: GpuRun, inputs: dict, rows, orc=None, note=True):
+    """Compare y and the saved statistics of the given rows; returns each output's worst
+    error as a fraction of its bound."""
     orc = orc or oracle.get()
     w = run.w
     rows = np.asarray(rows, dtype=np.int64)
+    out = {}
     y = rows_to_host64(run.y, rows)
-    rstd = run.rstd.cpu().numpy().astype(np.float64)[rows]
+    rstd = rows_to_host64(run.rstd, rows)
     if w.kind == "rms":
         y_ref, rstd_ref = orc.rms_fwd(inputs["x"], inputs["gamma"], w.eps, rows=rows)
     else:
         y_ref, mean_ref, rstd_ref = orc.ln_fwd(inputs["x"], inputs["gamma"], inputs["beta"], w.eps,
                                               rows=rows)
-        mean = run.mean.cpu().numpy().astype(np.float64)[rows]
+        mean = rows_to_host64(run.mean, rows)
         xr = inputs["x"][rows]
         xr = gen.bf16_to_f32(xr) if w.dtype == "bf16" else xr
         row_rms = np.sqrt(np.mean(xr.astype(np.float64) ** 2, axis=1))
-        _check("mean", mean, mean_ref, TOL_STAT, scale=np.maximum(row_rms, 1e-30))
-    _check("rstd", rstd, rstd_ref, TOL_STAT, scale=np.abs(rstd_ref))
-    _check("y", y, y_ref, out_tol(w.dtype))
+        out["mean"] = _check("mean", mean, mean_ref, TOL_STAT, scale=np.maximum(row_rms, 1e-30))
+    out["rstd"] = _check("rstd", rstd, rstd_ref, TOL_STAT, scale=np.abs(rstd_ref))
+    out["y"] = _check("y", y, y_ref, out_tol(w.dtype))
+    if note:
+        for k, v in out.items():
+            _note(run, k, v, rows=int(rows.size))
+    return out
 
 
 def dx_term_scale(w, inputs, rows, dx_ref, orc):
@@ -187,29 +195,79 @@ def dx_term_scale(w, inputs, rows, dx_ref, orc):
     return np.maximum(1.0, np.maximum(np.abs(dx_ref), terms))
 
 
-def check_backward(run: GpuRun, inputs: dict, rows, orc=None, check_dgamma=True):
+def _ratio(got, ref, bound):
+    """Worst |got - ref| / bound, for reporting only (the checks assert)."""
+    if np.size(got) == 0:
+        return 0.0
+    return float(np.max(np.abs(np.asarray(got) - ref) / np.maximum(bound, 1e-300)))
+
+
+def check_backward(run: GpuRun, inputs: dict, rows, orc=None, check_dgamma=True, note=True):
+    """Compare dx of the given rows and (unless check_dgamma is False) the complete
+    dgamma/dbeta; returns each output's worst error as a fraction of its bound.  For fp32
+    rows of one element it also reports the worst error against the literal
+    1e-5 * max(1, |ref|) rule, which those rows are not held to."""
     orc = orc or oracle.get()
     w = run.w
     rows = np.asarray(rows, dtype=np.int64)
+    out = {}
     dx = rows_to_host64(run.dx, rows)
     if w.kind == "rms":
         dx_ref = orc.rms_bwd_dx(inputs["dy"], inputs["x"], inputs["gamma"], w.eps, rows=rows)
     else:
         dx_ref = orc.ln_bwd_dx(inputs["dy"], inputs["x"], inputs["gamma"], w.eps, rows=rows)
-    if w.dtype == "f32":
-        _check("dx", dx, dx_ref, TOL_F32, scale=dx_term_scale(w, inputs, rows, dx_ref, orc))
+    if w.dtype == "f32" and run.N == 1:
+        out["dx"] = _check("dx", dx, dx_ref, TOL_F32,
+                           scale=dx_term_scale(w, inputs, rows, dx_ref, orc))
+        out["dx_literal_1e-5"] = _ratio(dx, dx_ref, TOL_F32 * np.maximum(1.0, np.abs(dx_ref)))
     else:
-        _check("dx", dx, dx_ref, out_tol(w.dtype))
-    if not check_dgamma:
-        return
-    dg = run.dgamma.cpu().numpy().astype(np.float64)
-    if w.kind == "rms":
-        dg_ref, sg = orc.rms_dgamma(inputs["dy"], inputs["x"], w.eps)
-    else:
-        dg_ref, db_ref, sg, sb = orc.ln_dgamma_dbeta(inputs["dy"], inputs["x"], w.eps)
-        db = run.dbeta.cpu().numpy().astype(np.float64)
-        _check("dbeta", db, db_ref, TOL_DGAMMA, scale=np.maximum(np.abs(db_ref), sb))
-    _check("dgamma", dg, dg_ref, TOL_DGAMMA, scale=np.maximum(np.abs(dg_ref), sg))
+        out["dx"] = _check("dx", dx, dx_ref, out_tol(w.dtype))
+    if check_dgamma:
+        dg = run.dgamma.cpu().numpy().astype(np.float64)
+        if w.kind == "rms":
+            dg_ref, sg = orc.rms_dgamma(inputs["dy"], inputs["x"], w.eps)
+        else:
+            dg_ref, db_ref, sg, sb = orc.ln_dgamma_dbeta(inputs["dy"], inputs["x"], w.eps)
+            db = run.dbeta.cpu().numpy().astype(np.float64)
+            out["dbeta"] = _check("dbeta", db, db_ref, TOL_DGAMMA,
+                                  scale=np.maximum(np.abs(db_ref), sb))
+        out["dgamma"] = _check("dgamma", dg, dg_ref, TOL_DGAMMA,
+                               scale=np.maximum(np.abs(dg_ref), sg))
+    if note:
+        for k, v in out.items():
+            _note(run, k, v, rows=int(rows.size))
+    return out
+
+
+# Worst error of each compared output as a fraction of its bound, and for fp32 dx also
+# against the literal rule 1e-5 * max(1, |ref|) without the cancellation scale; filled
+# by the checks, written out by tests/conftest.py when PARITY_REPORT names a file.
+REPORT = []
+
+
+def _note(run, name, ratio, **extra):
+    REPORT.append(dict(workload=run.w.name, M=int(run.M), N=int(run.N), dtype=run.w.dtype,
+                       output=name, max_err_over_bound=ratio, **extra))
+
+
+def check_all_rows(run: GpuRun, inputs: dict, orc=None, elems_per_chunk: int = 1 << 24):
+    """Every row of y, dx and the statistics, in chunks of rows the oracle evaluates one
+    chunk at a time (so no fp64 copy of a whole large tensor is ever held), then the
+    complete dgamma/dbeta vectors."""
+    orc = orc or oracle.get()
+    step = max(1, elems_per_chunk // run.N)
+    worst = {}
+    for r0 in range(0, run.M, step):
+        rows = np.arange(r0, min(run.M, r0 + step), dtype=np.int64)
+        for k, v in check_forward(run, inputs, rows, orc, note=False).items():
+            worst[k] = max(worst.get(k, 0.0), v)
+        for k, v in check_backward(run, inputs, rows, orc, check_dgamma=False, note=False).items():
+            worst[k] = max(worst.get(k, 0.0), v)
+    for k, v in check_backward(run, inputs, rows[:0], orc, note=False).items():
+        worst[k] = max(worst.get(k, 0.0), v)
+    for k, v in worst.items():
+        _note(run, k, v, rows="all")
+    return worst
 
 
 def full_check(w: gen.Workload, device, rows=None, fwd_options=None, bwd_options=None,

@@ -52,11 +52,18 @@ def test_status_strings():
     assert rn.status_string(99) == "unknown status"
 
 
+CLUSTER = rn.Options(path=rn.NORM_PATH_CLUSTER)
+
+
 def rms_fwd(**kw):
-    a = dict(x=A, gamma=A, y=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16, ws=None, ws_bytes=0)
+    a = dict(x=A, gamma=A, y=A, rstd=A, M=4, N=64, eps=1e-6, dtype=BF16, ws=None, ws_bytes=0,
+             opt=None)
     a.update(kw)
-    return rn.lib().norm_rms_fwd(a["x"], a["gamma"], a["y"], a["rstd"], a["M"], a["N"], a["eps"],
-                                 a["dtype"], a["ws"], a["ws_bytes"], None)
+    args = (a["x"], a["gamma"], a["y"], a["rstd"], a["M"], a["N"], a["eps"], a["dtype"], a["ws"],
+            a["ws_bytes"], None)
+    if a["opt"] is not None:
+        return rn.lib().norm_rms_fwd_ex(*args, ctypes.byref(a["opt"]))
+    return rn.lib().norm_rms_fwd(*args)
 
 
 def ln_fwd(**kw):
@@ -101,9 +108,11 @@ def ln_bwd(**kw):
     (rms_fwd, dict(dtype=F32, y=A + 2), rn.NORM_ERR_MISALIGNED),
     (ln_fwd, dict(beta=None), rn.NORM_ERR_NULL_PTR),
     (ln_fwd, dict(mean=A + 1), rn.NORM_ERR_MISALIGNED),
-    # rows long enough to be split over a cluster of workgroups need a forward workspace
-    (rms_fwd, dict(M=1024, N=262144), rn.NORM_ERR_NULL_PTR),
-    (rms_fwd, dict(M=1024, N=262144, ws=A, ws_bytes=64), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
+    # the split-row forward, when asked for, needs its workspace (without options a
+    # missing or short forward workspace selects a plan that needs none)
+    (rms_fwd, dict(M=1024, N=262144, opt=CLUSTER), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(M=1024, N=262144, ws=A, ws_bytes=64, opt=CLUSTER),
+     rn.NORM_ERR_WORKSPACE_TOO_SMALL),
     (ln_fwd, dict(M=1024, N=262144, ws=A + 8, ws_bytes=1 << 20), rn.NORM_ERR_MISALIGNED),
     (rms_bwd, dict(dy=None), rn.NORM_ERR_NULL_PTR),
     (rms_bwd, dict(rstd=None), rn.NORM_ERR_NULL_PTR),
@@ -322,3 +331,35 @@ def test_type_pairs_plan_like_their_activations():
                         (ref.path, ref.lanes_per_row, ref.vecs_per_lane, ref.grid, ref.cluster_size)
                     size = rn.norm_bwd_workspace_size if bwd else rn.norm_fwd_workspace_size
                     assert size(M, N, ln, code) == size(M, N, ln, BF16)
+
+
+def test_rejected_forced_plans_are_the_unbuilt_ones():
+    """The GPU parity tests force only plans the planner accepts (tests/plan_cases.py);
+    the rest must be exactly the combinations with no compiled kernel."""
+    import plan_cases as pc
+    pairs = [("bf16", None), ("f32", None), ("f16", None), ("bf16", "f32"), ("f16", "f32")]
+    # Row mappings: a 1024-lane backward mapping with more than one vector per lane exists
+    # only with its per-column partials in LDS, which needs >= 16 of them per lane and
+    # 1024 lanes x 4 bytes x that many to fit in 160 KiB.
+    def unbuilt(k, d, dr, lpr, vpl):
+        sums = vpl * pc.epv(d) * (2 if k == "ln" else 1)
+        return dr == "bwd" and lpr == 1024 and vpl > 1 and not (
+            sums >= 16 and 1024 * sums * 4 <= 160 * 1024)
+    rejected = pc.mapping_cases(pairs, accepted=False)
+    expect = [c for c in pc.all_mapping_cases(pairs) if unbuilt(c[0], c[1], c[3], c[4], c[5])]
+    assert sorted(rejected, key=str) == sorted(expect, key=str)
+    assert len(rejected) == 5  # RMSNorm fp32 1024x2; LayerNorm 16-bit 1024x4 (four pairs)
+    # Split rows: a member's slice (N / elements per vector / C vectors) must be covered by
+    # a compiled (threads x vectors) member mapping for the step's row count, with less
+    # than one vector of padding per lane and at most 4 (forward) / 2 (backward) vectors.
+    maps = pc.compiled_cluster_mappings()
+
+    def covered(direction, sv, R):
+        vmax = 4 if direction == "fwd" else 2
+        return any(t * v >= sv and t * v - sv < t for dr, t, v, r in maps
+                   if dr == direction and r == R and v <= vmax)
+    rejected = pc.cluster_cases(pairs, accepted=False)
+    expect = [c for c in pc.all_cluster_cases(pairs)
+              if not all(covered(dr, c[3] // pc.epv(c[1]) // c[4], c[5]) for dr in ("fwd", "bwd"))]
+    assert sorted(rejected, key=str) == sorted(expect, key=str)
+    assert rejected and all(c[3] == 65536 for c in rejected)

@@ -1,15 +1,24 @@
 """GPU parity: the HIP library against the fp64 oracle, element by element.
 
-Small cases compare every row; the full-size workloads compare sampled rows of y and dx
-(the oracle evaluates them one by one) and the complete dgamma/dbeta vectors (the
-oracle sums all rows).  Tolerances are in parity.py.  All calls go through the C ABI.
+Small cases compare every row.  The named workloads at full size, and the N = 65536
+sweep points, compare every row too (the oracle evaluates them a chunk of rows at a
+time); the other sweep points and the other type pairs at full size compare sampled
+rows.  dgamma/dbeta are always compared in full (the oracle sums all rows).
+Tolerances are in parity.py.  All calls go through the C ABI.
+
+Forced mappings and split-row sizes are listed only where the planner accepts them;
+tests/test_abi.py checks on the CPU that exactly the others are rejected.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
 import gen
 import row_normalization_norm_amd as rn
-from parity import GpuRun, check_backward, check_forward, full_check, sample_rows, to_device
+from parity import (GpuRun, check_all_rows, check_backward, check_forward, full_check,
+                    sample_rows, to_device)
+import plan_cases
 
 pytestmark = pytest.mark.gpu
 
@@ -45,10 +54,28 @@ def test_small_shapes(device, kind, dtype, pdtype, N):
     full_check(w, device, rows=np.arange(w.M))
 
 
+def _all_rows(w, device):
+    print(f"all-row parity: {w.name} [{w.M}x{w.N}] {w.dtype}", flush=True)
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    run.forward()
+    run.backward()
+    run.sync()
+    check_all_rows(run, inputs)
+
+
 @pytest.mark.parametrize("name", ["rms1", "ln2", "rms3", "rms4"])
 def test_workloads_full_size(device, name):
-    """The named workloads at full size, in the launch configuration the benchmark times."""
-    full_check(gen.WORKLOADS[name], device, rows=sample_rows(gen.WORKLOADS[name].M, 64))
+    """The named workloads at full size, in the launch configuration the benchmark times,
+    every element of y, dx and the statistics compared."""
+    _all_rows(gen.WORKLOADS[name], device)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_sweep_longest_rows_all_rows(device, kind, dtype):
+    """The sweep's longest rows (N = 65536: split rows) with every element compared."""
+    _all_rows(gen.sweep_workload(kind, dtype, 65536), device)
 
 
 @pytest.mark.parametrize("dtype,pdtype", PAIRS[2:], ids=PAIR_IDS[2:])
@@ -70,39 +97,21 @@ def test_sweep_full_size(device, kind, dtype, N):
     full_check(w, device, rows=sample_rows(w.M, 24))
 
 
-def _mapping_cases():
-    cases = []
-    import re
-    src = open(rn.__file__.replace("__init__.py", "csrc/launch.h")).read()
-    for direction, macro in (("fwd", "RN_FWD_MAPPINGS"), ("bwd", "RN_BWD_MAPPINGS")):
-        body = src[src.index(f"#define {macro}"):]
-        body = body[:body.index("\n\n")]
-        for lpr, vpl in re.findall(r"X\((\d+), (\d+)\)", body):
-            cases.append((direction, int(lpr), int(vpl)))
-    return cases
+MAPPING_CASES = plan_cases.mapping_cases(PAIRS)
 
 
-MAPPINGS = _mapping_cases()
-
-
-@pytest.mark.parametrize("direction,lpr,vpl", MAPPINGS,
-                         ids=[f"{d}-{l}x{v}" for d, l, v in MAPPINGS])
-@pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("kind", ["rms", "ln"])
+@pytest.mark.parametrize("kind,dtype,pdtype,direction,lpr,vpl", MAPPING_CASES,
+                         ids=[f"{k}-{d}{'+' + p if p else ''}-{dr}-{l}x{v}"
+                              for k, d, p, dr, l, v in MAPPING_CASES])
 def test_every_mapping(device, kind, dtype, pdtype, direction, lpr, vpl):
     """Force each compiled (lanes per row, vectors per lane) mapping on a row that leaves
     the last vector slot partly empty, with a ragged final row group."""
-    epv = 4 if dtype == "f32" else 8
-    nvec = lpr * vpl - max(1, lpr // 3) if lpr * vpl > 1 else 1
-    N = nvec * epv
-    M = max(5, min(301, 400_000 // N))
+    N, M = plan_cases.mapping_shape(dtype, lpr, vpl)
     w = small_workload(kind, dtype, N, M=M, x_mean=0.1, pdtype=pdtype)
     opt = rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=lpr, vecs_per_lane=vpl)
-    code = {"f32": rn.NORM_DTYPE_F32, "bf16": rn.NORM_DTYPE_BF16, "f16": rn.NORM_DTYPE_F16}[dtype]
-    try:
-        rn.norm_plan(direction == "bwd", kind == "ln", M, N, code, options=opt)
-    except rn.NormError:
-        pytest.skip("mapping not built for this kind and element width")
+    code = dtype_code(dtype, pdtype)
+    p = rn.norm_plan(direction == "bwd", kind == "ln", M, N, code, options=opt)
+    assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, lpr, vpl)
     inputs = gen.make_inputs(w)
     run = GpuRun(w, inputs, device)
     if direction == "fwd":
@@ -127,29 +136,22 @@ def test_forced_paths(device, kind, dtype, pdtype, N, path):
                bwd_options=rn.Options(path=path))
 
 
-CLUSTER_CASES = [(N, C) for N in (2048, 8192, 65536) for C in (2, 4, 8, 16, 32)
-                 if (N // 8) % C == 0 and (N // 8) // C <= 4096]
+CLUSTER_CASES = plan_cases.cluster_cases(PAIRS)
 
 
-@pytest.mark.parametrize("R", [1, 2])
-@pytest.mark.parametrize("N,C", CLUSTER_CASES, ids=[f"N{n}-C{c}" for n, c in CLUSTER_CASES])
-@pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
-@pytest.mark.parametrize("kind", ["rms", "ln"])
+@pytest.mark.parametrize("kind,dtype,pdtype,N,C,R", CLUSTER_CASES,
+                         ids=[f"{k}-{d}{'+' + p if p else ''}-N{n}-C{c}-R{r}"
+                              for k, d, p, n, c, r in CLUSTER_CASES])
 def test_cluster_path(device, kind, dtype, pdtype, N, C, R):
     """Rows split over C workgroups, forward and backward, with a row count that leaves
     the clusters unevenly loaded."""
-    epv = 4 if dtype == "f32" else 8
-    if (N // epv) % C:
-        pytest.skip("row does not split evenly")
-    M = max(3, min(997, 2_000_000 // N))
+    M = plan_cases.cluster_rows(N)
     w = small_workload(kind, dtype, N, M=M, x_mean=0.3, x_std=1.2, pdtype=pdtype)
     opt = rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=C, cluster_rows=R)
     code = dtype_code(dtype, pdtype)
-    try:
-        rn.norm_plan(False, kind == "ln", M, N, code, options=opt)
-        rn.norm_plan(True, kind == "ln", M, N, code, options=opt)
-    except rn.NormError:
-        pytest.skip("no compiled cluster mapping covers this slice")
+    for bwd in (False, True):
+        assert rn.norm_plan(bwd, kind == "ln", M, N, code, options=opt).path == \
+            rn.NORM_PATH_CLUSTER
     for bwd in (False, True):
         assert rn.norm_cluster_resident(bwd, kind == "ln", M, N, code, opt) == 1, \
             "one cluster must fit the device (otherwise the call silently takes another path)"
@@ -210,9 +212,12 @@ def test_every_cluster_mapping(device, kind, dtype, pdtype, direction, T, V, R):
         check_backward(run, inputs, np.arange(M))
 
 
+# Both kinds, fp32 (plain fmaf / adds) and 16-bit (dot-product) partial sums, one and two
+# rows per exchange step; every case is accepted by the planner in both directions.
 SELF_CASES = [("ln", "bf16", None, 65536, 4, 1), ("rms", "bf16", None, 131072, 8, 1),
-              ("ln", "f32", None, 32768, 4, 2), ("rms", "f16", "f32", 65536, 8, 2),
-              ("ln", "bf16", None, 262144, 8, 1)]
+              ("rms", "f32", None, 32768, 4, 1), ("ln", "f32", None, 65536, 8, 1),
+              ("ln", "f32", None, 32768, 8, 2), ("ln", "bf16", None, 32768, 4, 2),
+              ("rms", "f16", "f32", 65536, 8, 2), ("ln", "bf16", None, 262144, 16, 1)]
 
 
 @pytest.mark.parametrize("fused", [False, True], ids=["plain", "residual"])
@@ -231,11 +236,11 @@ def test_cluster_partials_computed_locally(device, kind, dtype, pdtype, N, C, R,
     for wait in (0, -1):
         opt = rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=C, cluster_rows=R,
                          cluster_wait=wait)
-        try:
-            for bwd in (False, True):
-                rn.norm_plan(bwd, kind == "ln", M, N, code, options=opt)
-        except rn.NormError:
-            pytest.skip("no compiled split-row mapping covers this slice")
+        for bwd in (False, True):
+            p = rn.norm_plan(bwd, kind == "ln", M, N, code, options=opt)
+            assert (p.path, p.cluster_size, p.cluster_rows) == (rn.NORM_PATH_CLUSTER, C, R)
+            # otherwise both runs would take the fallback plan and agree trivially
+            assert rn.norm_cluster_resident(bwd, kind == "ln", M, N, code, opt) == 1
         inputs = gen.make_inputs(w, residual=fused)
         run = GpuRun(w, inputs, device)
         if fused:
@@ -441,6 +446,64 @@ def test_events_and_streams(device):
     assert e0.elapsed_time(e1) > 0
     check_forward(run, inputs, sample_rows(w.M))
     check_backward(run, inputs, sample_rows(w.M))
+
+
+@pytest.mark.parametrize("kind,dtype,M,N", [("rms", "bf16", 64, 262144), ("ln", "bf16", 48, 262144),
+                                             ("rms", "f32", 40, 131072), ("rms", "bf16", 2048, 131072)])
+def test_forward_without_workspace(device, kind, dtype, M, N):
+    """The forward's argument list without a workspace (NULL, 0 bytes) works at every row
+    length: rows that the fastest plan splits over a cluster run a plan that needs none."""
+    import torch
+    code = dtype_code(dtype)
+    assert rn.norm_fwd_workspace_size(M, N, kind == "ln", code) > 0
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.2)
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    stream = torch.cuda.current_stream(device).cuda_stream
+    lib = rn.lib()
+    if kind == "rms":
+        st = lib.norm_rms_fwd(run.x.data_ptr(), run.gamma.data_ptr(), run.y.data_ptr(),
+                              run.rstd.data_ptr(), M, N, w.eps, code, None, 0, stream)
+    else:
+        st = lib.norm_ln_fwd(run.x.data_ptr(), run.gamma.data_ptr(), run.beta.data_ptr(),
+                             run.y.data_ptr(), run.mean.data_ptr(), run.rstd.data_ptr(), M, N,
+                             w.eps, code, None, 0, stream)
+    assert st == rn.NORM_OK, rn.status_string(st)
+    run.sync()
+    check_forward(run, inputs, np.arange(M))
+    # a workspace that is too short is treated the same way
+    y0 = run.y.clone()
+    run.y.zero_()
+    short = torch.empty(64, dtype=torch.uint8, device=device)
+    if kind == "rms":
+        st = lib.norm_rms_fwd(run.x.data_ptr(), run.gamma.data_ptr(), run.y.data_ptr(),
+                              run.rstd.data_ptr(), M, N, w.eps, code, short.data_ptr(), 64, stream)
+        assert st == rn.NORM_OK
+        run.sync()
+        assert torch.equal(run.y.view(torch.int16) if dtype == "bf16" else run.y,
+                           y0.view(torch.int16) if dtype == "bf16" else y0)
+
+
+def test_side_stream_with_binding_workspace(device):
+    """The binding's own workspace stays reserved while a call on a side stream uses it,
+    though torch's caching allocator tracks it on the current stream: allocations made on
+    the current stream in between must not reuse it."""
+    import torch
+    w = small_workload("rms", "bf16", 131072, M=512)
+    inputs = gen.make_inputs(w)
+    run = GpuRun(w, inputs, device)
+    side = torch.cuda.Stream(device)
+    side.wait_stream(torch.cuda.current_stream(device))
+    for _ in range(3):
+        run.forward(stream=side)
+        run.backward(stream=side)
+        # fill fresh blocks on the current stream while the side stream may still run
+        junk = [torch.full((1 << 20,), 7, dtype=torch.uint8, device=device) for _ in range(8)]
+        del junk
+    side.synchronize()
+    run.sync()
+    check_forward(run, inputs, np.arange(w.M))
+    check_backward(run, inputs, np.arange(w.M))
 
 
 @pytest.mark.parametrize("nbytes", [16, 4096 + 16, (1 << 20) + 48])
