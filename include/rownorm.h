@@ -86,7 +86,9 @@ typedef enum norm_status {
   NORM_ERR_WORKSPACE_TOO_SMALL = 5,  /* workspace_bytes < the size the call needs */
   NORM_ERR_HIP = 6,                  /* a HIP runtime call or launch failed */
   NORM_ERR_MISALIGNED = 7,           /* a pointer is not aligned to its element size */
-  NORM_ERR_BAD_OPTION = 8            /* a norm_options_t field is out of range */
+  NORM_ERR_BAD_OPTION = 8,           /* a norm_options_t field is out of range */
+  NORM_ERR_SCRATCH_TOO_SMALL = 9     /* norm_ln_bwd_noalloc: the call needs more scratch
+                                        than the library's static buffer holds */
 } norm_status_t;
 
 /* ------------------------------------------------------------------ forward */
@@ -138,6 +140,23 @@ norm_status_t norm_ln_bwd(const void* dy, const void* x, const void* gamma, cons
                           const float* rstd, void* dx, float* dgamma, float* dbeta, int64_t M,
                           int64_t N, norm_dtype_t dtype, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/* LayerNorm backward that allocates nothing, for callers that cannot call hipMalloc
+ * or take a workspace (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): norm_ln_bwd with the workspace replaced by a static device array
+ * of the library's, 32 MiB per device, held from the first such call on a device until
+ * the process ends.  Arguments, layouts, types, results and errors are those of
+ * norm_ln_bwd.  A shape whose plan needs more scratch than that (the dgamma/dbeta
+ * partial rows, 8 * N bytes per persistent workgroup, plus the split-row exchange
+ * words) returns NORM_ERR_SCRATCH_TOO_SMALL before any HIP call.  Every call on one
+ * device shares that device's array: calls that overlap in time on one device (on
+ * different streams, or from different threads) race and give wrong dgamma/dbeta;
+ * calls ordered on one stream are safe.  It makes no allocation, so it may be captured
+ * into a HIP graph like the other entry points. */
+norm_status_t norm_ln_bwd_noalloc(const void* dy, const void* x, const void* gamma,
+                                  const float* mean, const float* rstd, void* dx, float* dgamma,
+                                  float* dbeta, int64_t M, int64_t N, norm_dtype_t dtype,
+                                  hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* norm_status_string(norm_status_t status);

@@ -36,6 +36,7 @@ NORM_ERR_WORKSPACE_TOO_SMALL = 5
 NORM_ERR_HIP = 6
 NORM_ERR_MISALIGNED = 7
 NORM_ERR_BAD_OPTION = 8
+NORM_ERR_SCRATCH_TOO_SMALL = 9
 # norm_dgamma_mode_t
 NORM_DGAMMA_TWO_STAGE = 0
 NORM_DGAMMA_ATOMIC_ROW = 1
@@ -103,6 +104,7 @@ SIGNATURES = {
     "norm_ln_bwd_add": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P, _SZ, _P,
                                _OPT]),
     "norm_stream_reference": (_INT, [_INT, _P, _P, _P, _I64, _P]),
+    "norm_ln_bwd_noalloc": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _I64, _I64, _INT, _P]),
 }
 
 _lib = None
@@ -354,6 +356,24 @@ def norm_ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace=None, str
         _check(lib().norm_ln_bwd(*args), "norm_ln_bwd")
     else:
         _check(lib().norm_ln_bwd_ex(*args, _opt(options)), "norm_ln_bwd_ex")
+    return dx, dgamma, dbeta
+
+
+def norm_ln_bwd_noalloc(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, stream=None):
+    """norm_ln_bwd on the library's static scratch: no workspace, no allocation (the
+    binding allocates nothing either).  Calls that overlap on one device race."""
+    torch = _torch()
+    M, N = _shape(x)
+    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
+        _need(t, n, k, x.dtype, x.device)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
+    for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
+                    (dbeta, "dbeta", N)):
+        _need(t, n, k, torch.float32, x.device)
+    _check(lib().norm_ln_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd),
+                                     _ptr(dx), _ptr(dgamma), _ptr(dbeta), M, N,
+                                     _types(x, gamma), _stream(x.device, stream)),
+           "norm_ln_bwd_noalloc")
     return dx, dgamma, dbeta
 
 

@@ -230,6 +230,39 @@ hipError_t clear_exchange(const Plan& p, char* ws, hipStream_t s) {
                      int32_t(p.xchg_bytes / 4), s);
 }
 
+// ------------------------------------------------------------- static scratch
+// Device memory for norm_ln_bwd_noalloc, for callers that cannot allocate: the
+// dgamma/dbeta partial rows and, for split rows, the exchange words, which the
+// backward's kernels otherwise take from the caller's workspace.  Every device the
+// library runs on holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, not device memory: only the address scratch_address()
+// obtains from the runtime is ever passed to a kernel.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The current device's copy of `scratch`, looked up once per device.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  static std::atomic<void*> addr[64];
+  static std::mutex mu;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (!p) return hipErrorInvalidSymbol;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 norm_status_t check_workspace(const Plan& p, void* workspace, size_t given) {
   if (p.ws_need == 0) return NORM_OK;
   if (!workspace) return NORM_ERR_NULL_PTR;
@@ -319,11 +352,14 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
 }
 
 // dres: the residual-add entry points' gradient arriving at the sum (may be NULL).
+// use_scratch: the workspace is the library's static scratch array (the entry point
+// that allocates nothing); the workspace arguments are then ignored.
 norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma,
                        const float* mean, const float* rstd, void* dx, float* dgamma,
                        float* dbeta, int64_t M, int64_t N, norm_dtype_t dtype, void* workspace,
                        size_t workspace_bytes_given, hipStream_t stream,
-                       const norm_options_t* opt, const void* dres = nullptr) {
+                       const norm_options_t* opt, const void* dres = nullptr,
+                       bool use_scratch = false) {
   norm_status_t st = check_shape_dtype(M, N, dtype);
   if (st != NORM_OK) return st;
   if (!gamma || !dgamma || (ln && !dbeta)) return NORM_ERR_NULL_PTR;
@@ -340,6 +376,16 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   Plan p;
   st = make_plan(true, ln, M, N, dt.x, a16, opt, &p);
   if (st != NORM_OK) return st;
+  if (use_scratch) {
+    // the last check before the first HIP call
+    if (p.ws_need > kScratchBytes) return NORM_ERR_SCRATCH_TOO_SMALL;
+    workspace = nullptr;
+    workspace_bytes_given = kScratchBytes;
+    if (p.ws_need > 0) {
+      hipError_t e = scratch_address(&workspace);
+      if (e != hipSuccess) return hip_status(e);
+    }
+  }
   st = check_workspace(p, workspace, workspace_bytes_given);
   if (st != NORM_OK) return st;
 
@@ -531,6 +577,16 @@ norm_status_t norm_ln_bwd_ex(const void* dy, const void* x, const void* gamma,
   });
 }
 
+norm_status_t norm_ln_bwd_noalloc(const void* dy, const void* x, const void* gamma,
+                                  const float* mean, const float* rstd, void* dx, float* dgamma,
+                                  float* dbeta, int64_t M, int64_t N, norm_dtype_t dtype,
+                                  hipStream_t stream) {
+  return guarded([&] {
+    return bwd_impl(true, dy, x, gamma, mean, rstd, dx, dgamma, dbeta, M, N, dtype, nullptr, 0,
+                    stream, nullptr, nullptr, true);
+  });
+}
+
 norm_status_t norm_rms_fwd_add(const void* x, const void* residual, const void* gamma, void* y,
                                void* sum, float* rstd, int64_t M, int64_t N, float eps,
                                norm_dtype_t dtype, void* workspace, size_t workspace_bytes,
@@ -635,6 +691,8 @@ const char* norm_status_string(norm_status_t s) {
     case NORM_ERR_HIP: return "HIP runtime error";
     case NORM_ERR_MISALIGNED: return "pointer not aligned to its element size";
     case NORM_ERR_BAD_OPTION: return "bad option";
+    case NORM_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more than the library's 32 MiB static scratch";
   }
   return "unknown status";
 }

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_header_symbols_exported():
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     lib = rn.lib()
     for n in names:
         assert hasattr(lib, n), f"{n} declared in rownorm.h but not exported"
@@ -46,7 +46,7 @@ def test_stream_reference_validation():
 
 
 def test_status_strings():
-    for s in range(0, 9):
+    for s in range(0, 10):
         assert rn.status_string(s)
     assert rn.status_string(0) == "ok"
     assert rn.status_string(99) == "unknown status"
@@ -363,3 +363,26 @@ def test_rejected_forced_plans_are_the_unbuilt_ones():
               if not all(covered(dr, c[3] // pc.epv(c[1]) // c[4], c[5]) for dr in ("fwd", "bwd"))]
     assert sorted(rejected, key=str) == sorted(expect, key=str)
     assert rejected and all(c[3] == 65536 for c in rejected)
+
+
+def test_noalloc_validation():
+    """The entry point that allocates nothing validates like norm_ln_bwd, and rejects a
+    shape whose plan needs more than its 32 MiB static scratch, all before any HIP call."""
+    f = rn.lib().norm_ln_bwd_noalloc
+    ok = dict(dy=A, x=A, g=A, mean=A, rstd=A, dx=A, dg=A, db=A, M=4096, N=4096, dt=BF16)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["dy"], a["x"], a["g"], a["mean"], a["rstd"], a["dx"], a["dg"], a["db"], a["M"],
+                 a["N"], a["dt"], None)
+    assert call(db=None) == rn.NORM_ERR_NULL_PTR
+    assert call(mean=None) == rn.NORM_ERR_NULL_PTR
+    assert call(x=A + 1) == rn.NORM_ERR_MISALIGNED
+    assert call(N=0) == rn.NORM_ERR_BAD_SHAPE
+    assert call(dt=9) == rn.NORM_ERR_BAD_DTYPE
+    # LayerNorm bf16 N = 131072 splits rows: 32 clusters x 131072 x 8 bytes of partial
+    # rows alone is 32 MiB, plus the exchange words
+    assert rn.norm_bwd_workspace_size(2048, 131072, True, BF16) > 32 << 20
+    assert call(M=2048, N=131072) == rn.NORM_ERR_SCRATCH_TOO_SMALL
+    assert rn.norm_bwd_workspace_size(65536, 4096, True, BF16) <= 32 << 20
