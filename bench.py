@@ -52,6 +52,14 @@ def main_bwd_kernel_bytes(kind, M, N, s, ps=None):
     return 3 * M * N * s + N * ps + (4 if kind == "rms" else 8) * M
 
 
+def main_bwd_kernel_name(w, plan):
+    """The backward's main kernel for a ROWS plan: the pipelined one when the grid is
+    persistent (fewer workgroups than row groups), else the plain one."""
+    rows_per_wg = plan.block // plan.lanes_per_row
+    groups = -(-w.M // rows_per_wg)
+    return "bwd_pipe_kernel" if plan.grid < groups else "bwd_rows_kernel"
+
+
 def elem_bytes(dtype):
     return 4 if dtype == "f32" else 2
 
@@ -531,6 +539,7 @@ def summarize(d, workload, warmup, steps, copy_bytes):
     fwd_b, bwd_b = ideal_bytes(wl.kind, wl.M, wl.N, s, ps)
     main_b = main_bwd_kernel_bytes(wl.kind, wl.M, wl.N, s, ps)
     algo = {"fwd_rows_kernel": fwd_b, "bwd_rows_kernel": main_b,
+            "fwd_pipe_kernel": fwd_b, "bwd_pipe_kernel": main_b,
             "fwd_cluster_kernel": fwd_b, "bwd_cluster_kernel": main_b,
             "colreduce_kernel": bwd_b - main_b}
     clines = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | bytes read | bytes written | "
@@ -542,7 +551,7 @@ def summarize(d, workload, warmup, steps, copy_bytes):
             continue
         rb, wb = fetch[k] * 1024 * f_scale, write[k] * 1024 * w_scale
         a = next((v for n, v in algo.items() if k.startswith(n)), None)
-        if k.startswith("bwd_rows_kernel"):
+        if k.startswith("bwd_rows_kernel") or k.startswith("bwd_pipe_kernel"):
             bwd_traffic = rb + wb
         li = lds.get(k, {})
         clines.append(f"| `{k}` | {fetch[k]:.0f} | {write[k]:.0f} | {rb:.4g} | {wb:.4g} | "
@@ -602,7 +611,10 @@ def write_summaries(d, w, warmup=DEFAULT_WARMUP, steps=DEFAULT_STEPS, copy_bytes
                 f"Kernel source hash: `{src_hash}`.\n")
     if w == DEFAULT_WORKLOAD and bwd_traffic:
         with open(COUNTERS_FILE, "w") as f:
-            json.dump({"workload": w, "kernel": "bwd_rows_kernel",
+            import row_normalization_norm_amd as rn
+            wl = workload_by_name(w)
+            plan = rn.norm_plan(True, wl.kind == "ln", wl.M, wl.N, lib_dtype(wl))
+            json.dump({"workload": w, "kernel": main_bwd_kernel_name(wl, plan),
                        "kernel_source_hash": src_hash,
                        "traffic_bytes_per_launch": round(bwd_traffic),
                        "fetch_scale": round(fs, 4), "write_scale": round(ws_, 4),
@@ -720,7 +732,7 @@ def main():
         "bwd_call_GBs": round(bwd_b / (r["bwd_call_ms"] * 1e-3) / 1e9, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": f"bwd_rows_kernel (dx + dgamma/dbeta partials), "
+            "kernel": f"{main_bwd_kernel_name(w, plan)} (dx + dgamma/dbeta partials), "
                       f"{plan.lanes_per_row}x{plan.vecs_per_lane}, grid {plan.grid}",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

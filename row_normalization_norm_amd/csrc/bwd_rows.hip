@@ -368,8 +368,339 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_rows_kernel(const BwdArgs 
   }
 }
 
+// Pipelined backward for persistent grids (several row groups per workgroup) in the
+// two-stage mode.  The same computation as bwd_rows_kernel, with every access to x, dy,
+// dx, the residual gradient, the saved statistics and gamma a raw buffer access through a
+// resource of the row group (ROWS consecutive rows; groups past the last row get an empty
+// one) or of gamma, so that none sits under a branch: rows past M and the padding lanes of
+// the last vector slot read zeros (and so add nothing to the column sums) and drop their
+// stores.  The row loop is unrolled twice over two fixed sets of registers, the next
+// group's loads issued into one while the other is reduced and stored.  The compiler can
+// then count the memory operations in flight and wait only for the loads a step uses; the
+// plain kernel's loop waited for every load and store, its own dx stores included, at the
+// end of each iteration.
+template <bool LN, typename D, typename P, int LPR, int VPL, bool ADD>
+__global__ __launch_bounds__(bwd_block(LPR)) void bwd_pipe_kernel(const BwdArgs a) {
+  using PV = Param<D, P>;
+  constexpr int BLOCK = bwd_block(LPR);
+  constexpr int EPV = D::kPerVec;
+  constexpr int ROWS = BLOCK / LPR;
+  constexpr int WPR = LPR > 64 ? LPR / 64 : 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid % LPR;
+  const int slot = tid / LPR;
+  const int nvec = a.nvec;
+  const uint32_t row_bytes = static_cast<uint32_t>(nvec) * 16u;
+
+  // Byte offset of this lane's vector slot v inside its row group (col_ofs: inside the
+  // row, for gamma).  Only the last slot can hold padding lanes; they get an
+  // out-of-range offset.
+  const bool last_in_row = (VPL - 1) * LPR + lane < nvec;
+  const uint32_t row_ofs = static_cast<uint32_t>(slot) * row_bytes;
+  auto col_ofs = [&](int v) -> uint32_t {
+    return (v == VPL - 1 && !last_in_row) ? kOutOfRange
+                                          : static_cast<uint32_t>(v * LPR + lane) * 16u;
+  };
+  auto ofs = [&](int v) -> uint32_t {
+    return (v == VPL - 1 && !last_in_row) ? kOutOfRange
+                                          : row_ofs + static_cast<uint32_t>(v * LPR + lane) * 16u;
+  };
+  auto group_rows = [&](int64_t grp) -> uint32_t {
+    const int64_t left = a.M - grp * ROWS;
+    return left <= 0 ? 0u : left >= ROWS ? uint32_t(ROWS) : static_cast<uint32_t>(left);
+  };
+  auto group = [&](const void* base, int64_t grp) {
+    return make_rsrc(static_cast<const char*>(base) + grp * ROWS * static_cast<int64_t>(row_bytes),
+                     group_rows(grp) * row_bytes);
+  };
+  auto group_stat = [&](const float* base, int64_t grp) {
+    return make_rsrc(base + grp * ROWS, group_rows(grp) * 4u);
+  };
+  const uint32_t stat_ofs = static_cast<uint32_t>(slot) * 4u;
+
+  // Per-column partial sums: registers, or (LACC) LDS words private to each lane, laid
+  // out [dgamma|dbeta][vector][4-column chunk][lane] so that a wave's 16-byte accesses
+  // are contiguous.
+  constexpr bool LACC = bwd_lds_acc(LN, EPV, LPR, VPL);
+  static_assert(!LACC || ROWS == 1, "LDS partials assume one row per workgroup");
+  constexpr int CH = EPV / 4;
+  constexpr int RV = LACC ? 1 : VPL;
+  float accg[RV][EPV];
+  float accb[LN ? RV : 1][EPV];
+  __shared__ float4 lacc[LACC ? (LN ? 2 : 1) * VPL * CH * LPR : 1];
+  auto lidx = [&](int which, int v, int h) { return ((which * VPL + v) * CH + h) * LPR + lane; };
+  if constexpr (LACC) {
+#pragma unroll
+    for (int w = 0; w < (LN ? 2 : 1); ++w)
+#pragma unroll
+      for (int v = 0; v < VPL; ++v)
+#pragma unroll
+        for (int h = 0; h < CH; ++h) lacc[lidx(w, v, h)] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  } else {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        accg[v][e] = 0.0f;
+        if constexpr (LN) accb[v][e] = 0.0f;
+      }
+    }
+  }
+
+  __shared__ float red[WPR > 1 ? 2 * ROWS * WPR * 2 : 1];
+  int parity = 0;
+
+  // gamma stays in registers across the workgroup's rows when the row is short enough,
+  // for the shortest rows also unpacked to fp32.
+  constexpr bool GREG = VPL <= 2;
+  constexpr bool GUNP = GREG && VPL * EPV <= 16;
+  constexpr bool kDot = !std::is_same<D, F32>::value && PV::kPacked;
+  constexpr int kPB = PV::kPacked ? 16 : 32;
+  const rsrc_t rgam = make_rsrc(a.gamma, static_cast<uint32_t>(nvec) * kPB);
+  PV greg[GREG ? VPL : 1];
+  float gunp[GUNP ? VPL : 1][EPV];
+  if constexpr (GREG) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      greg[v].load_buf(rgam, col_ofs(v));
+      if constexpr (GUNP) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) gunp[v][e] = greg[v].get(e);
+      }
+    }
+  }
+
+  struct Stage {
+    u32x4 x[VPL], d[VPL];
+    u32x4 g2[ADD ? VPL : 1];  // ADD: the gradient arriving at the residual sum
+    float r, mu;
+  };
+  auto load = [&](int64_t grp, Stage& st) {
+    const rsrc_t rx = group(a.x, grp), rd = group(a.dy, grp);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      st.x[v] = buf_ld16(rx, ofs(v));
+      st.d[v] = buf_ld16(rd, ofs(v));
+    }
+    if constexpr (ADD) {
+      const rsrc_t rr = group(a.dres, grp);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) st.g2[v] = buf_ld16(rr, ofs(v));
+    }
+    st.r = buf_ldf(group_stat(a.rstd, grp), stat_ofs);
+    st.mu = LN ? buf_ldf(group_stat(a.mean, grp), stat_ofs) : 0.0f;
+  };
+
+  auto process = [&](int64_t grp, Stage& st) {
+    PV gv[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      if constexpr (GREG) {
+        gv[v] = greg[v];
+      } else {
+        gv[v].load_buf(rgam, col_ofs(v));
+      }
+    }
+    const float r = st.r;
+    const float mu = st.mu;
+
+    // Row sums, and the per-column contributions (which do not need the row sums).
+    // Short rows keep xhat and g in registers for the dx pass; longer ones unpack the
+    // packed words again there, so that only those stay live across the reduction.
+    constexpr bool KEEP = VPL * EPV <= 16;
+    float kxh[KEEP ? VPL : 1][EPV], kg[KEEP ? VPL : 1][EPV];
+    float s1 = 0.0f, s2 = 0.0f;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      if constexpr (LN && kDot) s2 = D::dot(st.d[v], gv[v].v, s2);
+      float xs[EPV], ds[EPV];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        const float xh = (D::get(st.x[v], e) - mu) * r;
+        const float d = D::get(st.d[v], e);
+        const float g = d * (GUNP ? gunp[GUNP ? v : 0][e] : gv[v].get(e));
+        s1 = fmaf(g, xh, s1);
+        if constexpr (LN && !kDot) s2 += g;
+        xs[e] = xh;
+        ds[e] = d;
+        if constexpr (!LACC) {
+          accg[v][e] = fmaf(d, xh, accg[v][e]);
+          if constexpr (LN) accb[v][e] += d;
+        }
+        if constexpr (KEEP) {
+          kxh[v][e] = xh;
+          kg[v][e] = g;
+        }
+      }
+      if constexpr (LACC) {
+#pragma unroll
+        for (int h = 0; h < CH; ++h) {
+          float4 t = lacc[lidx(0, v, h)];
+          t.x = fmaf(ds[4 * h], xs[4 * h], t.x);
+          t.y = fmaf(ds[4 * h + 1], xs[4 * h + 1], t.y);
+          t.z = fmaf(ds[4 * h + 2], xs[4 * h + 2], t.z);
+          t.w = fmaf(ds[4 * h + 3], xs[4 * h + 3], t.w);
+          lacc[lidx(0, v, h)] = t;
+          if constexpr (LN) {
+            float4 u = lacc[lidx(1, v, h)];
+            u.x += ds[4 * h];
+            u.y += ds[4 * h + 1];
+            u.z += ds[4 * h + 2];
+            u.w += ds[4 * h + 3];
+            lacc[lidx(1, v, h)] = u;
+          }
+        }
+      }
+    }
+
+    constexpr int W = LPR < 64 ? LPR : 64;
+    s1 = group_sum<W>(s1);
+    if constexpr (LN) s2 = group_sum<W>(s2);
+    if constexpr (WPR > 1) {
+      const int wave = (tid >> 6) % WPR;
+      float* buf = red + (parity * ROWS + slot) * WPR * 2;
+      if ((tid & 63) == 0) {
+        buf[2 * wave] = s1;
+        buf[2 * wave + 1] = s2;
+      }
+      __syncthreads();
+      s1 = 0.0f;
+      s2 = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WPR; ++w) {
+        s1 += buf[2 * w];
+        if constexpr (LN) s2 += buf[2 * w + 1];
+      }
+      parity ^= 1;
+    }
+    // dx = r * (g - c2 - xhat * c1) = g * r + (xhat * (-r * c1) + (-r * c2)).
+    const float nrc1 = -r * (s1 * a.inv_n);
+    const float nrc2 = LN ? -r * (s2 * a.inv_n) : 0.0f;
+
+    const rsrc_t rdx = group(a.dx, grp);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      float o[EPV];
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        float xh, g;
+        if constexpr (KEEP) {
+          xh = kxh[v][e];
+          g = kg[v][e];
+        } else {
+          xh = (D::get_fresh(st.x[v], e) - mu) * r;
+          g = D::get_fresh(st.d[v], e) * gv[v].get_fresh(e);
+        }
+        o[e] = fmaf(g, r, fmaf(xh, nrc1, nrc2));
+        if constexpr (ADD) o[e] += D::get_fresh(st.g2[v], e);
+      }
+      buf_st16(rdx, ofs(v), D::pack(o));
+    }
+  };
+
+  // Persistent loop over row groups b, b + G, b + 2G, ... in pairs of stages.  Loads for
+  // groups past the last read zeros through an empty resource and are never used (the
+  // kernel is launched with several groups per workgroup).
+  const int64_t G = gridDim.x;
+  int64_t grp = blockIdx.x;
+  {
+    Stage A, B;
+    load(grp, A);
+    while (grp < a.groups) {
+      // The scheduling barriers keep the next group's loads ahead of the work on the
+      // current one (otherwise the compiler moves that work up, and its wait for the
+      // current loads, which is a wait for everything in flight before them, comes
+      // first).
+      load(grp + G, B);
+      __builtin_amdgcn_sched_barrier(0);
+      process(grp, A);
+      grp += G;
+      if (grp >= a.groups) break;
+      load(grp + G, A);
+      __builtin_amdgcn_sched_barrier(0);
+      process(grp, B);
+      grp += G;
+    }
+  }
+
+  // Combine the workgroup's row slots and emit one partial row.
+  float* const out_g = a.part_g + (int64_t)blockIdx.x * a.N;
+  float* const out_b = a.part_b + (int64_t)blockIdx.x * a.N;
+  if constexpr (LACC) {
+    // Each lane reads back only the LDS words it wrote: no barrier is needed.
+#pragma unroll
+    for (int w = 0; w < (LN ? 2 : 1); ++w) {
+      float* const out = w == 0 ? out_g : out_b;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        const int vi = v * LPR + lane;
+        if (vi < nvec) {
+#pragma unroll
+          for (int h = 0; h < CH; ++h)
+            *reinterpret_cast<float4*>(out + vi * EPV + 4 * h) = lacc[lidx(w, v, h)];
+        }
+      }
+    }
+  } else if constexpr (ROWS == 1) {
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) {
+      const int vi = v * LPR + lane;
+      if (vi < nvec) {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const int col = vi * EPV + e;
+          out_g[col] = accg[v][e];
+          if constexpr (LN) out_b[col] = accb[v][e];
+        }
+      }
+    }
+  } else {
+    // cbuf holds one vector column block of every slot: element e of lane l of a slot at
+    // l*(EPV+1) + e.  The pad word keeps the lanes' stores, EPV words apart otherwise, on
+    // distinct LDS banks.
+    constexpr int SPAN = LPR * EPV;
+    constexpr int PSPAN = LPR * (EPV + 1);
+    __shared__ float cbuf[ROWS * PSPAN];
+#pragma unroll
+    for (int pass = 0; pass < (LN ? 2 : 1); ++pass) {
+      float* const out = pass == 0 ? out_g : out_b;
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          cbuf[slot * PSPAN + lane * (EPV + 1) + e] = pass == 0 ? accg[v][e] : accb[LN ? v : 0][e];
+        }
+        __syncthreads();
+        for (int c = tid; c < SPAN; c += BLOCK) {
+          float sum = 0.0f;
+#pragma unroll 4
+          for (int k = 0; k < ROWS; ++k) sum += cbuf[k * PSPAN + (c / EPV) * (EPV + 1) + c % EPV];
+          const int col = v * SPAN + c;
+          if (col < a.N) out[col] = sum;
+        }
+      }
+    }
+  }
+}
+
 template <bool LN, typename D, typename P, int LPR, int VPL>
 hipError_t launch_one(const BwdArgs& a, int grid, hipStream_t s) {
+  // Persistent grids in the two-stage mode take the pipelined kernel, except the
+  // 1024-lane mappings of 4 vectors, which have no registers for a second stage.
+  if constexpr (!(LPR == 1024 && VPL > 2)) {
+    if (a.mode == kTwoStage && grid < a.groups) {
+      if (a.dres) {
+        hipLaunchKernelGGL((bwd_pipe_kernel<LN, D, P, LPR, VPL, true>), dim3(grid),
+                           dim3(bwd_block(LPR)), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((bwd_pipe_kernel<LN, D, P, LPR, VPL, false>), dim3(grid),
+                           dim3(bwd_block(LPR)), 0, s, a);
+      }
+      return hipGetLastError();
+    }
+  }
   if (a.dres) {
     hipLaunchKernelGGL((bwd_rows_kernel<LN, D, P, LPR, VPL, true>), dim3(grid),
                        dim3(bwd_block(LPR)), 0, s, a);

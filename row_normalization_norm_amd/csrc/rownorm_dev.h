@@ -283,6 +283,17 @@ __device__ inline void buf_st16(rsrc_t r, uint32_t byte_ofs, const u32x4& v) {
 __device__ inline float buf_ldf(rsrc_t r, uint32_t byte_ofs) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, byte_ofs, 0, 0));
 }
+__device__ inline void buf_stf(rsrc_t r, uint32_t byte_ofs, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, byte_ofs, 0, 0);
+}
+// Cached (temporal) 16-byte load, for data every workgroup reads (gamma, beta).
+__device__ inline u32x4 buf_ld16_cached(rsrc_t r, uint32_t byte_ofs) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_ofs, 0, 0);
+}
+// A byte offset that no buffer the kernels address reaches (every resource they build
+// is smaller than 1 GiB), so an access made with it reads zero or is dropped; twice it,
+// the offset of the second half of a pair of vectors, still is out of range.
+constexpr uint32_t kOutOfRange = 0x40000000u;
 
 __device__ inline u32x4 zero16() {
   u32x4 z = {0u, 0u, 0u, 0u};
@@ -301,6 +312,9 @@ struct Param<D, P, true> {
   static constexpr bool kPacked = true;  // the same packing as the activations
   u32x4 v;
   __device__ inline void load(const void* base, int64_t vi) { v = ld16(base, vi); }
+  // From a buffer resource of the parameters, at the byte offset of the activation
+  // vector they go with (kOutOfRange: zeros).
+  __device__ inline void load_buf(rsrc_t r, uint32_t act_ofs) { v = buf_ld16_cached(r, act_ofs); }
   __device__ inline void clear() { v = zero16(); }
   __device__ inline float get(int e) const { return D::get(v, e); }
   __device__ inline float get_fresh(int e) const { return D::get_fresh(v, e); }
@@ -315,6 +329,11 @@ struct Param<D, P, false> {
   __device__ inline void load(const void* base, int64_t vi) {
     v[0] = ld16(base, 2 * vi);
     v[1] = ld16(base, 2 * vi + 1);
+  }
+  // fp32 parameters take twice the activations' bytes: byte offset 2 * act_ofs.
+  __device__ inline void load_buf(rsrc_t r, uint32_t act_ofs) {
+    v[0] = buf_ld16_cached(r, 2u * act_ofs);
+    v[1] = buf_ld16_cached(r, 2u * act_ofs + 16u);
   }
   __device__ inline void clear() {
     v[0] = zero16();

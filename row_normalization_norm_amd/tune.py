@@ -59,7 +59,7 @@ def _time(fn, iters=20, warm=3):
     return e0.elapsed_time(e1) / iters
 
 
-def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 1024, -1), grids_b=(0, 256, 512), cluster=True,
+def tune_shape(kind, dtype, M, N, grids_f=(0, 256, 512, 1024, -1), grids_b=(0, 256, 512, 1024), cluster=True,
                dirs=("fwd", "bwd")):
     """Time every candidate for one shape; returns a list of result dicts.  A forward grid
     of -1 stands for one row group per workgroup (the grid recorded is that count)."""

@@ -104,6 +104,17 @@ def test_fused_residual(device, kind, dtype, pdtype, N, with_dsum):
     _check_all(*_run(device, kind, dtype, pdtype, M, N, with_dsum))
 
 
+@pytest.mark.parametrize("N", [384, 4096])
+@pytest.mark.parametrize("dtype,pdtype", [("bf16", None), ("f32", None), ("f16", "f32")],
+                         ids=["bf16", "f32", "f16+f32"])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_fused_residual_persistent(device, kind, dtype, pdtype, N):
+    """The residual add and gradient in the pipelined kernels (a persistent grid of 3
+    workgroups, each taking many row groups)."""
+    opt = rn.Options(grid=3)
+    _check_all(*_run(device, kind, dtype, pdtype, 333, N, True, opt, opt))
+
+
 @pytest.mark.parametrize("path", [rn.NORM_PATH_SPLIT, rn.NORM_PATH_GENERIC, rn.NORM_PATH_CLUSTER])
 @pytest.mark.parametrize("dtype,pdtype", [("bf16", None), ("f32", None), ("f16", "f32")],
                          ids=["bf16", "f32", "f16+f32"])
