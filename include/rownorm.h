@@ -208,6 +208,12 @@ typedef struct norm_options {
   int cluster_wait;    /* CLUSTER path: polls of another member's partial sums before
                           computing them locally; 0 = default, -1 = never wait (every
                           member computes every partial itself: for tests) */
+  int pipeline;        /* ROWS path with a persistent grid (fewer workgroups than row
+                          groups): 0 = planner, 1 = the plain kernel, 2 = the pipelined
+                          one (two register stages, the next row group's loads in flight
+                          while the current one is reduced and stored).  Ignored when every
+                          workgroup takes at most one row group (the plain kernel runs);
+                          the backward's pipelined kernel is two-stage mode only */
 } norm_options_t;
 
 /* What the planner chose for a call (filled by norm_plan). */
@@ -221,6 +227,8 @@ typedef struct norm_plan_info {
   int cluster_size;      /* CLUSTER path: workgroups per row (else 0) */
   int cluster_rows;      /* CLUSTER path: rows per exchange step (else 0) */
   size_t workspace_bytes;
+  int pipelined;         /* ROWS path: 1 if the pipelined kernel runs (see
+                            norm_options_t.pipeline), else 0 */
 } norm_plan_info_t;
 
 /* Fill *info for a forward (is_backward = 0) or backward call with these arguments.

@@ -61,7 +61,8 @@ class Options(ctypes.Structure):
                 ("vecs_per_lane", ctypes.c_int), ("dgamma_mode", ctypes.c_int),
                 ("grid", ctypes.c_int), ("cluster_size", ctypes.c_int),
                 ("cluster_rows", ctypes.c_int), ("ev_start", ctypes.c_void_p),
-                ("ev_stop", ctypes.c_void_p), ("cluster_wait", ctypes.c_int)]
+                ("ev_stop", ctypes.c_void_p), ("cluster_wait", ctypes.c_int),
+                ("pipeline", ctypes.c_int)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -70,7 +71,7 @@ class PlanInfo(ctypes.Structure):
                 ("vecs_per_lane", ctypes.c_int), ("block", ctypes.c_int),
                 ("grid", ctypes.c_int), ("partial_rows", ctypes.c_int),
                 ("cluster_size", ctypes.c_int), ("cluster_rows", ctypes.c_int),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("pipelined", ctypes.c_int)]
 
 
 _P = ctypes.c_void_p

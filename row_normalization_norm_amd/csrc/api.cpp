@@ -19,8 +19,8 @@ namespace rownorm {
 
 // Per-(kind, type pair) launchers, one translation unit each (TypeCombo in launch.h).
 #define RN_DECL_TU(K, T)                                                                  \
-  hipError_t launch_fwd_rows_k##K##_t##T(int, int, const FwdArgs&, int, hipStream_t);      \
-  hipError_t launch_bwd_rows_k##K##_t##T(int, int, const BwdArgs&, int, hipStream_t);      \
+  hipError_t launch_fwd_rows_k##K##_t##T(int, int, const FwdArgs&, int, bool, hipStream_t); \
+  hipError_t launch_bwd_rows_k##K##_t##T(int, int, const BwdArgs&, int, bool, hipStream_t); \
   hipError_t launch_fwd_cluster_k##K##_t##T(int, int, int, const FwdArgs&, const ClusterArgs&, \
                                             int, hipStream_t);                             \
   hipError_t launch_bwd_cluster_k##K##_t##T(int, int, int, const BwdArgs&, const ClusterArgs&, \
@@ -41,8 +41,8 @@ RN_DECL_TU(1, 0) RN_DECL_TU(1, 1) RN_DECL_TU(1, 2) RN_DECL_TU(1, 3) RN_DECL_TU(1
   }
 
 namespace {
-using FwdRowsFn = hipError_t (*)(int, int, const FwdArgs&, int, hipStream_t);
-using BwdRowsFn = hipError_t (*)(int, int, const BwdArgs&, int, hipStream_t);
+using FwdRowsFn = hipError_t (*)(int, int, const FwdArgs&, int, bool, hipStream_t);
+using BwdRowsFn = hipError_t (*)(int, int, const BwdArgs&, int, bool, hipStream_t);
 using FwdClusterFn = hipError_t (*)(int, int, int, const FwdArgs&, const ClusterArgs&, int,
                                     hipStream_t);
 using BwdClusterFn = hipError_t (*)(int, int, int, const BwdArgs&, const ClusterArgs&, int,
@@ -62,8 +62,8 @@ const OccFn kBwdOcc[2][kNumTypeCombos] = RN_TABLE(occupancy_bwd_cluster);
 #undef RN_TABLE
 
 hipError_t launch_fwd_rows(int kind, int tc, int lpr, int vpl, const FwdArgs& a, int grid,
-                           hipStream_t s) {
-  return kFwdRows[kind][tc](lpr, vpl, a, grid, s);
+                           bool pipe, hipStream_t s) {
+  return kFwdRows[kind][tc](lpr, vpl, a, grid, pipe, s);
 }
 hipError_t launch_fwd_grows(int kind, int tc, int epl, const FwdArgs& a, int grid,
                             hipStream_t s) {
@@ -74,8 +74,8 @@ hipError_t launch_bwd_grows(int kind, int tc, int epl, const BwdArgs& a, int gri
   return kBwdGrows[kind][tc](epl, a, grid, s);
 }
 hipError_t launch_bwd_rows(int kind, int tc, int lpr, int vpl, const BwdArgs& a, int grid,
-                           hipStream_t s) {
-  return kBwdRows[kind][tc](lpr, vpl, a, grid, s);
+                           bool pipe, hipStream_t s) {
+  return kBwdRows[kind][tc](lpr, vpl, a, grid, pipe, s);
 }
 hipError_t launch_fwd_cluster(int kind, int tc, int t, int vpl, int rows, const FwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s) {
@@ -337,7 +337,7 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   if ((e = ev.start()) != hipSuccess) return hip_status(e);
   switch (p.path) {
     case NORM_PATH_ROWS:
-      e = launch_fwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
+      e = launch_fwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, p.pipelined, stream);
       break;
     case NORM_PATH_CLUSTER:
       e = launch_fwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws, opt),
@@ -438,7 +438,7 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   }
   if ((e = ev.start()) != hipSuccess) return hip_status(e);
   if (p.path == NORM_PATH_ROWS) {
-    e = launch_bwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, stream);
+    e = launch_bwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, p.pipelined, stream);
   } else if (p.path == NORM_PATH_CLUSTER) {
     e = launch_bwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws, opt),
                            p.grid, stream);
@@ -651,6 +651,7 @@ norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
   info->cluster_size = p.cluster;
   info->cluster_rows = p.rows_per_step;
   info->workspace_bytes = p.ws_need;
+  info->pipelined = p.pipelined ? 1 : 0;
   return NORM_OK;
 }
 

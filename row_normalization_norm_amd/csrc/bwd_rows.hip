@@ -686,11 +686,11 @@ __global__ __launch_bounds__(bwd_block(LPR)) void bwd_pipe_kernel(const BwdArgs 
 }
 
 template <bool LN, typename D, typename P, int LPR, int VPL>
-hipError_t launch_one(const BwdArgs& a, int grid, hipStream_t s) {
-  // Persistent grids in the two-stage mode take the pipelined kernel, except the
-  // 1024-lane mappings of 4 vectors, which have no registers for a second stage.
+hipError_t launch_one(const BwdArgs& a, int grid, bool pipe, hipStream_t s) {
+  // The pipelined kernel when asked for on a persistent grid in the two-stage mode (the
+  // 1024-lane mappings of 4 vectors have no registers for a second stage).
   if constexpr (!(LPR == 1024 && VPL > 2)) {
-    if (a.mode == kTwoStage && grid < a.groups) {
+    if (pipe && a.mode == kTwoStage && grid < a.groups) {
       if (a.dres) {
         hipLaunchKernelGGL((bwd_pipe_kernel<LN, D, P, LPR, VPL, true>), dim3(grid),
                            dim3(bwd_block(LPR)), 0, s, a);
@@ -717,13 +717,13 @@ hipError_t launch_one(const BwdArgs& a, int grid, hipStream_t s) {
 #define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
 #define RN_LAUNCHER RN_CAT(launch_bwd_rows_k, RN_KIND, _t, RN_TC)
 
-hipError_t RN_LAUNCHER(int lpr, int vpl, const BwdArgs& a, int grid, hipStream_t s) {
+hipError_t RN_LAUNCHER(int lpr, int vpl, const BwdArgs& a, int grid, bool pipe, hipStream_t s) {
   constexpr bool kLN = RN_KIND == 1;
   using D = Types<RN_TC>::D;
   using P = Types<RN_TC>::P;
 #define RN_CASE(L, V)                                                \
   if constexpr (bwd_mapping_built(kLN, D::kPerVec, L, V)) {          \
-    if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, s); \
+    if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, pipe, s); \
   }
   RN_BWD_MAPPINGS(RN_CASE)
 #undef RN_CASE

@@ -440,9 +440,9 @@ __global__ __launch_bounds__(fwd_block(LPR)) void fwd_pipe_kernel(const FwdArgs 
 }
 
 template <bool LN, typename D, typename P, int LPR, int VPL>
-hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t s) {
+hipError_t launch_one(const FwdArgs& a, int grid, bool pipe, hipStream_t s) {
   if constexpr (VPL <= 8) {
-    if (grid < a.groups) {
+    if (pipe && grid < a.groups) {
       if (a.res) {
         hipLaunchKernelGGL((fwd_pipe_kernel<LN, D, P, LPR, VPL, true, 2>), dim3(grid),
                            dim3(fwd_block(LPR)), 0, s, a);
@@ -469,12 +469,12 @@ hipError_t launch_one(const FwdArgs& a, int grid, hipStream_t s) {
 #define RN_CAT(a, b, c, d) RN_CAT_(a, b, c, d)
 #define RN_LAUNCHER RN_CAT(launch_fwd_rows_k, RN_KIND, _t, RN_TC)
 
-hipError_t RN_LAUNCHER(int lpr, int vpl, const FwdArgs& a, int grid, hipStream_t s) {
+hipError_t RN_LAUNCHER(int lpr, int vpl, const FwdArgs& a, int grid, bool pipe, hipStream_t s) {
   constexpr bool kLN = RN_KIND == 1;
   using D = Types<RN_TC>::D;
   using P = Types<RN_TC>::P;
 #define RN_CASE(L, V) \
-  if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, s);
+  if (lpr == L && vpl == V) return launch_one<kLN, D, P, L, V>(a, grid, pipe, s);
   RN_FWD_MAPPINGS(RN_CASE)
 #undef RN_CASE
   return hipErrorInvalidValue;

@@ -170,10 +170,11 @@ struct ClusterArgs {
 // ------------------------------------------------------------------ launchers
 // kind: 0 = RMSNorm, 1 = LayerNorm.  tc: the activation/parameter type pair
 // (TypeCombo).  Each returns hipErrorInvalidValue when the mapping is not compiled.
+// pipe: the pipelined kernel when the grid is persistent (grid < row groups).
 hipError_t launch_fwd_rows(int kind, int tc, int lpr, int vpl, const FwdArgs& a, int grid,
-                           hipStream_t s);
+                           bool pipe, hipStream_t s);
 hipError_t launch_bwd_rows(int kind, int tc, int lpr, int vpl, const BwdArgs& a, int grid,
-                           hipStream_t s);
+                           bool pipe, hipStream_t s);
 // SPLIT path (16-byte vectors): per-row reduction, then the column-sliced pass on a
 // (slices, row_blocks) grid.
 hipError_t launch_bwd_rowdot(int kind, int tc, bool vec, const BwdArgs& a, int grid,

@@ -145,6 +145,17 @@ bool choose_mapping_n(const Mapping* list, int n, int64_t units, int target, int
   return found;
 }
 
+// Whether a ROWS plan runs the pipelined kernel: only on a persistent grid (a workgroup
+// takes several row groups); as the options say, else (no table entry) for rows of 128
+// vectors and more, where it measured faster on MI355X than the plain kernel (shorter
+// rows mostly stream better through the plain one).
+constexpr int64_t kPipelineMinVecs = 128;
+bool use_pipeline(const norm_options_t& o, bool persistent, int64_t nvec) {
+  if (!persistent) return false;
+  if (o.pipeline) return o.pipeline == 2;
+  return nvec >= kPipelineMinVecs;
+}
+
 bool plan_rows(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec,
                const norm_options_t& o, bool atomic, Plan& p) {
   Mapping m{0, 0};
@@ -171,6 +182,7 @@ bool plan_rows(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec
     if (o.grid) grid = o.grid < p.groups ? o.grid : p.groups;
     if (grid < 1) grid = 1;
     p.grid = int(grid);
+    p.pipelined = use_pipeline(o, grid < p.groups, nvec);
   } else {
     p.block = bwd_block(m.lpr);
     p.groups = ceil_div(M, p.block / m.lpr);
@@ -181,6 +193,9 @@ bool plan_rows(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec
     if (o.grid) grid = o.grid < p.groups ? o.grid : p.groups;
     if (grid < 1) grid = 1;
     p.grid = int(grid);
+    // the pipelined backward: two-stage mode, and registers for a second stage
+    p.pipelined = !atomic && !(m.lpr == 1024 && m.vpl > 2) &&
+                  use_pipeline(o, grid < p.groups, nvec);
     if (!atomic) {
       p.partial_rows = grid;
       p.off_part_g = 0;
@@ -326,7 +341,8 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
   if (o.path < NORM_PATH_AUTO || o.path > NORM_PATH_CLUSTER || o.lanes_per_row < 0 ||
       o.vecs_per_lane < 0 || o.grid < 0 || o.cluster_size < 0 || o.cluster_size > kMaxCluster ||
       o.cluster_rows < 0 || o.cluster_rows > 2 ||
-      o.dgamma_mode < NORM_DGAMMA_TWO_STAGE || o.dgamma_mode > NORM_DGAMMA_ATOMIC_WG)
+      o.dgamma_mode < NORM_DGAMMA_TWO_STAGE || o.dgamma_mode > NORM_DGAMMA_ATOMIC_WG ||
+      o.pipeline < 0 || o.pipeline > 2)
     return NORM_ERR_BAD_OPTION;
   const bool atomic = backward && o.dgamma_mode != NORM_DGAMMA_TWO_STAGE;
 
@@ -347,6 +363,7 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
         ot.lanes_per_row = t->lanes;
         ot.vecs_per_lane = t->vecs;
         if (!ot.grid) ot.grid = t->grid;
+        if (!ot.pipeline) ot.pipeline = t->pipelined ? 2 : 1;
         if (t->path == NORM_PATH_CLUSTER) {
           ot.cluster_size = t->cluster;
           ot.cluster_rows = t->rows;
@@ -405,6 +422,7 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
       (o.lanes_per_row || o.vecs_per_lane))
     return NORM_ERR_BAD_OPTION;
   if (p.path != NORM_PATH_CLUSTER && (o.cluster_size || o.cluster_rows)) return NORM_ERR_BAD_OPTION;
+  if (p.path != NORM_PATH_ROWS) p.pipelined = false;
   if (atomic && p.path != NORM_PATH_ROWS) return NORM_ERR_BAD_OPTION;
 
   p.ws_need = p.ws_bytes;

@@ -31,6 +31,7 @@ struct Plan {
   int nclusters = 0;          // CLUSTER: clusters
   int slice_vecs = 0;         // CLUSTER: vectors per member slice
   int rows_per_step = 0;      // CLUSTER: rows one reduction and one exchange serve
+  bool pipelined = false;     // ROWS: the pipelined kernel (persistent grids only)
   size_t ws_bytes = 0;        // bytes this plan uses
   size_t ws_need = 0;         // bytes the call requires (covers the fallback plan too)
   size_t off_part_g = 0, off_part_b = 0, off_rowc = 0;  // byte offsets into the workspace

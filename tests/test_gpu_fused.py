@@ -104,14 +104,15 @@ def test_fused_residual(device, kind, dtype, pdtype, N, with_dsum):
     _check_all(*_run(device, kind, dtype, pdtype, M, N, with_dsum))
 
 
+@pytest.mark.parametrize("pipeline", [1, 2], ids=["plain", "pipelined"])
 @pytest.mark.parametrize("N", [384, 4096])
 @pytest.mark.parametrize("dtype,pdtype", [("bf16", None), ("f32", None), ("f16", "f32")],
                          ids=["bf16", "f32", "f16+f32"])
 @pytest.mark.parametrize("kind", ["rms", "ln"])
-def test_fused_residual_persistent(device, kind, dtype, pdtype, N):
-    """The residual add and gradient in the pipelined kernels (a persistent grid of 3
-    workgroups, each taking many row groups)."""
-    opt = rn.Options(grid=3)
+def test_fused_residual_persistent(device, kind, dtype, pdtype, N, pipeline):
+    """The residual add and gradient on a persistent grid of 3 workgroups (each taking
+    many row groups), in the plain and the pipelined kernels."""
+    opt = rn.Options(grid=3, pipeline=pipeline)
     _check_all(*_run(device, kind, dtype, pdtype, 333, N, True, opt, opt))
 
 

@@ -100,16 +100,16 @@ def test_sweep_full_size(device, kind, dtype, N):
 MAPPING_CASES = plan_cases.mapping_cases(PAIRS)
 
 
-@pytest.mark.parametrize("persistent", [False, True], ids=["one-pass", "persistent"])
+@pytest.mark.parametrize("pipeline", [0, 1, 2], ids=["one-pass", "persistent", "pipelined"])
 @pytest.mark.parametrize("kind,dtype,pdtype,direction,lpr,vpl", MAPPING_CASES,
                          ids=[f"{k}-{d}{'+' + p if p else ''}-{dr}-{l}x{v}"
                               for k, d, p, dr, l, v in MAPPING_CASES])
-def test_every_mapping(device, kind, dtype, pdtype, direction, lpr, vpl, persistent):
+def test_every_mapping(device, kind, dtype, pdtype, direction, lpr, vpl, pipeline):
     """Force each compiled (lanes per row, vectors per lane) mapping on a row that leaves
     the last vector slot partly empty, with a ragged final row group: with the planner's
     grid (one row group per workgroup at these sizes), and with a persistent grid of a
-    third of the row groups (each workgroup takes several, and the pipelined kernels
-    run, with uneven counts per workgroup)."""
+    third of the row groups (each workgroup takes several, unevenly) in the plain and in
+    the pipelined kernel."""
     N, M = plan_cases.mapping_shape(dtype, lpr, vpl)
     w = small_workload(kind, dtype, N, M=M, x_mean=0.1, pdtype=pdtype)
     opt = rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=lpr, vecs_per_lane=vpl)
@@ -117,11 +117,17 @@ def test_every_mapping(device, kind, dtype, pdtype, direction, lpr, vpl, persist
     p = rn.norm_plan(direction == "bwd", kind == "ln", M, N, code, options=opt)
     assert (p.path, p.lanes_per_row, p.vecs_per_lane) == (rn.NORM_PATH_ROWS, lpr, vpl)
     groups = -(-M // (p.block // lpr))
-    if persistent:
-        if groups < 2:
-            pytest.skip("one row group: no persistent grid")
-        opt.grid = max(1, groups // 3)
-        assert rn.norm_plan(direction == "bwd", kind == "ln", M, N, code, options=opt).grid < groups
+    if pipeline:
+        assert groups >= 3
+        opt.grid = groups // 3
+        opt.pipeline = pipeline
+        q = rn.norm_plan(direction == "bwd", kind == "ln", M, N, code, options=opt)
+        assert q.grid < groups
+        if pipeline == 2 and not q.pipelined:
+            # 1024 lanes x 4 vectors (backward): no registers for a second stage
+            assert direction == "bwd" and lpr == 1024 and vpl > 2
+        else:
+            assert q.pipelined == (pipeline == 2)
     inputs = gen.make_inputs(w)
     run = GpuRun(w, inputs, device)
     if direction == "fwd":

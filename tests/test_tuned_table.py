@@ -1,6 +1,7 @@
 """The planner's measured table (csrc/tuned.h) is what the planner actually uses: at each
 entry's own row length (M = 2^27 / N rows, the shape it was measured at) the plan has the
-entry's path, mapping and, where the entry fixes one, its grid.  An entry that stopped
+entry's path, mapping, kernel (plain or pipelined) and, where the entry fixes one, its
+grid.  An entry that stopped
 fitting (a mapping no longer built, a cluster that no longer fits the workspace rules)
 would otherwise fall through to the rules without notice.  No GPU is needed."""
 import os
@@ -11,7 +12,8 @@ import pytest
 import row_normalization_norm_amd as rn
 
 TUNED = os.path.join(os.path.dirname(rn.__file__), "csrc", "tuned.h")
-ENTRY = re.compile(r"^\s*\{(-?\d+), (-?\d+), (-?\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\},")
+ENTRY = re.compile(r"^\s*\{(-?\d+), (-?\d+), (-?\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), "
+                   r"(\d+)\},")
 
 
 def entries():
@@ -33,7 +35,7 @@ def test_table_parses():
 
 @pytest.mark.parametrize("t", entries(), ids=lambda t: "bwd%d_ln%d_b16%d_nvec%d" % t[:4])
 def test_entry_is_the_plan_at_its_shape(t):
-    bwd, ln, b16, nvec, path, lanes, vecs, grid, cluster, rows = t
+    bwd, ln, b16, nvec, path, lanes, vecs, grid, cluster, rows, pipelined = t
     dt = rn.NORM_DTYPE_BF16 if b16 else rn.NORM_DTYPE_F32
     N = nvec * (8 if b16 else 4)
     M = max(1, (1 << 27) // N)
@@ -44,3 +46,4 @@ def test_entry_is_the_plan_at_its_shape(t):
     if grid:
         # an explicit grid is kept, or clamped to the row groups there are
         assert 0 < p.grid <= grid
+    assert p.pipelined == pipelined
