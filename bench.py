@@ -53,11 +53,13 @@ def main_bwd_kernel_bytes(kind, M, N, s, ps=None):
 
 
 def main_bwd_kernel_name(w, plan):
-    """The backward's main kernel for a ROWS plan: the pipelined one when the grid is
-    persistent (fewer workgroups than row groups), else the plain one."""
-    rows_per_wg = plan.block // plan.lanes_per_row
-    groups = -(-w.M // rows_per_wg)
-    return "bwd_pipe_kernel" if plan.grid < groups else "bwd_rows_kernel"
+    """The backward's main kernel for the planned call."""
+    import row_normalization_norm_amd as rn
+    if plan.path == rn.NORM_PATH_CLUSTER:
+        return "bwd_cluster_kernel"
+    if plan.path == rn.NORM_PATH_ROWS:
+        return "bwd_pipe_kernel" if plan.pipelined else "bwd_rows_kernel"
+    return "bwd_grows_kernel" if plan.vecs_per_lane else "colslice_kernel"
 
 
 def elem_bytes(dtype):
