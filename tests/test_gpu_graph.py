@@ -4,8 +4,8 @@ Each case runs forward + backward eagerly for the reference outputs, captures th
 calls into a graph, then replays it several times with unrelated eager work and
 synchronisations between the replays (the outputs are cleared by fill kernels before
 each replay), and requires every replay to reproduce the eager outputs bit for bit.
-The cases cover every kernel family, the split-row one (with its exchange-slot fill
-kernel) included.
+The cases cover every kernel family, the pipelined row kernels and the split-row one
+(with its exchange-slot fill kernel) included.
 """
 import numpy as np
 import pytest
@@ -20,6 +20,8 @@ CASES = [
     # kind, dtype, M, N, fused
     ("rms", "bf16", 4096, 1024, False),    # the small benchmark shape (row-resident path)
     ("ln", "bf16", 1000, 4096, False),
+    ("ln", "bf16", 8192, 4096, False),     # pipelined forward and backward (persistent grids)
+    ("rms", "bf16", 16384, 1024, False),   # pipelined backward, one-group forward
     ("ln", "f32", 96, 65536, False),       # backward on the split-row path
     ("ln", "bf16", 16, 131072, False),     # a whole row per workgroup forward
     ("rms", "bf16", 8, 262144, False),     # forward and backward on the split-row path
