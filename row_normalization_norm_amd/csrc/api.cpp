@@ -322,6 +322,8 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   a.groups = p.groups;
   a.res = fused ? res : nullptr;
   a.sum = fused ? sum : nullptr;
+  a.static_end = p.groups;
+  a.persistent = 0;
 
   const int kind = ln ? 1 : 0;
   EventScope ev{opt, stream};

@@ -131,6 +131,11 @@ struct FwdArgs {
   // s = x + res rounded to the activation type, and s is written to `sum`.
   const void* res;
   void* sum;
+  // Pipelined kernel only: workgroups below `persistent` take row groups b, b +
+  // persistent, ... below `static_end`; each workgroup above takes one of the groups
+  // from static_end on (persistent = 0: every workgroup strides over all the groups).
+  int64_t static_end;
+  int32_t persistent;
 };
 
 struct BwdArgs {
