@@ -32,6 +32,11 @@ HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "ln2"
 DEFAULT_STEPS = 50
 DEFAULT_WARMUP = 100
+# The untimed warm-up lasts at least this long.  Measured on MI355X (LayerNorm [65536,
+# 4096] bf16, fresh process, 20 timed steps): after 5 warm-up steps the step runs at
+# 5.5 TB/s, after 0.3 s of steps at 6.2 TB/s, the steady state; 0.3 s of another kernel
+# before the 5 steps does not help.  The timed region is the same K steps either way.
+DEFAULT_WARMUP_S = 0.3
 MALL_BYTES = 256 << 20
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_bwd_rows_ln2.json")
 
@@ -211,7 +216,7 @@ def run_gpu(w, steps, warmup, device, fused=False, warmup_s=0.0):
     b = Bench(w, device, fused)
     # `warmup` steps, continued (when warmup_s is set) until that much wall time has gone
     # by: on MI355X the first tens of milliseconds of sustained traffic run slower than
-    # the steady state (a short step's first 50 timed steps up to 13 % slower)
+    # the steady state (DEFAULT_WARMUP_S)
     t0 = time.perf_counter()
     k = 0
     while k < warmup or time.perf_counter() - t0 < warmup_s:
@@ -248,7 +253,8 @@ def run_gpu(w, steps, warmup, device, fused=False, warmup_s=0.0):
     bwd_ms = sum(bev[2 * i].elapsed_time(bev[2 * i + 1]) for i in range(steps)) / steps
     call_ms = sum(cev[2 * i].elapsed_time(cev[2 * i + 1]) for i in range(steps)) / steps
     return dict(ms_per_step=total_ms / steps, fwd_kernel_ms=fwd_ms, bwd_main_kernel_ms=bwd_ms,
-                bwd_call_ms=call_ms, wall_s=wall, sets=b.sets, setup_s=b.setup_s)
+                bwd_call_ms=call_ms, wall_s=wall, sets=b.sets, setup_s=b.setup_s,
+                warmup_steps=warmup)
 
 
 def workload_by_name(name):
@@ -575,24 +581,39 @@ def summarize(d, workload, warmup, steps, copy_bytes):
 PROFILE_STEPS = (
     "cd /tmp && export TMPDIR=/tmp; R=/root/repo; D=${{PROF_OUT:-$R/prof_out}}; mkdir -p $D",
     "rocprofv3 --kernel-trace --stats --output-format csv -d $D/trace -o {w} -- "
-    "python3 $R/bench.py --workload {w} --no-cpu",
+    "python3 $R/bench.py --workload {w} --no-cpu > $D/trace_{w}.log",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE -o {w} -- "
-    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu > $D/FETCH_SIZE_{w}.log",
+    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --warmup-time 0 --no-cpu > $D/FETCH_SIZE_{w}.log",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $D/WRITE_SIZE -o {w} -- "
-    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu",
+    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --warmup-time 0 --no-cpu",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $D/FETCH_SIZE_copy -o copy -- "
     "python3 $R/bench.py --copy-probe {c} --steps 3",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $D/WRITE_SIZE_copy -o copy -- "
     "python3 $R/bench.py --copy-probe {c} --steps 3",
     "rocprofv3 --pmc SQ_LDS_BANK_CONFLICT SQ_INSTS_LDS --output-format csv -d $D/LDS -o {w} -- "
-    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --no-cpu",
+    "python3 $R/bench.py --workload {w} --steps 3 --warmup 1 --warmup-time 0 --no-cpu",
     "python3 $R/bench.py --summarize $D --workload {w}",
 )
+
+
+def traced_run_counts(d, w, warmup, steps):
+    """The warm-up and timed step counts of the traced run, from the JSON line it printed
+    (trace_<w>.log beside the trace directory; the warm-up runs for a minimum time, so
+    its step count varies), else the defaults."""
+    log = os.path.join(d, f"trace_{w}.log")
+    if os.path.exists(log):
+        with open(log) as f:
+            for line in f:
+                if line.startswith("{") and '"warmup_steps_run"' in line:
+                    j = json.loads(line)
+                    return j["warmup_steps_run"], j["steps"]
+    return warmup, steps
 
 
 def write_summaries(d, w, warmup=DEFAULT_WARMUP, steps=DEFAULT_STEPS, copy_bytes=1 << 30):
     """--summarize: write profiles/<w>_kernel_trace.md, profiles/<w>_hbm_counters.md and
     (for the benchmark's own workload) the counter file bench.py reports traffic from."""
+    warmup, steps = traced_run_counts(d, w, warmup, steps)
     tt, tavg, ct, fs, ws_, bwd_traffic, src_hash = summarize(d, w, warmup, steps, copy_bytes)
     cmds = "\n".join(c.format(w=w, c=copy_bytes) for c in PROFILE_STEPS)
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
@@ -642,6 +663,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=DEFAULT_STEPS)
     ap.add_argument("--warmup", type=int, default=DEFAULT_WARMUP)
+    ap.add_argument("--warmup-time", type=float, default=DEFAULT_WARMUP_S, metavar="SECONDS",
+                    help="after the --warmup steps, keep stepping (untimed) until this much "
+                         "wall time has gone by (0: exactly --warmup steps)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-only", action="store_true",
@@ -707,7 +731,7 @@ def main():
     w = workload_by_name(args.workload)
     s, ps = elem_bytes(w.dtype), elem_bytes(w.param_dtype)
     fwd_b, bwd_b = ideal_bytes(w.kind, w.M, w.N, s, ps)
-    r = run_gpu(w, args.steps, args.warmup, device)
+    r = run_gpu(w, args.steps, args.warmup, device, warmup_s=args.warmup_time)
     value = (fwd_b + bwd_b) / (r["ms_per_step"] * 1e-3) / 1e9
 
     main_bytes = main_bwd_kernel_bytes(w.kind, w.M, w.N, s, ps)
@@ -720,6 +744,8 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_steps_run": r["warmup_steps"],
+        "warmup_min_s": args.warmup_time,
         "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
