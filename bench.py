@@ -34,8 +34,8 @@ DEFAULT_STEPS = 50
 DEFAULT_WARMUP = 100
 # The untimed warm-up lasts at least this long.  Measured on MI355X (LayerNorm [65536,
 # 4096] bf16, fresh process, 20 timed steps): after 5 warm-up steps the step runs at
-# 5.5 TB/s, after 0.3 s of steps at 6.2 TB/s, the steady state; 0.3 s of another kernel
-# before the 5 steps does not help.  The timed region is the same K steps either way.
+# 5.5 TB/s, after 0.3 s of steps at 6.2 TB/s, the steady state.  The timed region is the
+# same K steps either way.
 DEFAULT_WARMUP_S = 0.3
 MALL_BYTES = 256 << 20
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters_bwd_rows_ln2.json")
