@@ -5,11 +5,13 @@
 // and enqueue the kernels on the caller's stream; nothing here synchronises,
 // allocates device memory, or keeps a pointer past the call.
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
+#include <random>
 
 #include "../../include/rownorm.h"
 #include "launch.h"
@@ -211,8 +213,19 @@ bool fit_cluster(bool backward, int kind, int tc, bool add, Plan& p) {
 
 namespace {
 
-ClusterArgs cluster_args(const Plan& p, char* ws, const norm_options_t* opt) {
+// The SplitMix64 output function (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014), a bijection that spreads the epochs, which count up, over
+// all 64 bits of the kernels' tag base.
+uint64_t tag_base(uint64_t epoch) {
+  uint64_t z = epoch;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+ClusterArgs cluster_args(const Plan& p, char* ws, const norm_options_t* opt, uint64_t epoch) {
   ClusterArgs c;
+  c.tag_base = tag_base(epoch);
   c.C = p.cluster;
   c.nclusters = p.nclusters;
   c.slice_vecs = p.slice_vecs;
@@ -228,6 +241,38 @@ ClusterArgs cluster_args(const Plan& p, char* ws, const norm_options_t* opt) {
 hipError_t clear_exchange(const Plan& p, char* ws, hipStream_t s) {
   return launch_zero(reinterpret_cast<float*>(ws + p.off_xchg), nullptr,
                      int32_t(p.xchg_bytes / 4), s);
+}
+
+// Epochs of split-row launches: odd (0 is the epoch of captured calls), distinct within
+// the process, and starting from a random point so that words another process left in
+// reused memory do not share them.
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> counter{[] {
+    uint64_t seed = static_cast<uint64_t>(
+        std::chrono::steady_clock::now().time_since_epoch().count());
+    try {
+      std::random_device rd;
+      seed ^= (static_cast<uint64_t>(rd()) << 32) ^ rd();
+    } catch (...) {
+    }
+    return seed;
+  }()};
+  return (counter.fetch_add(1, std::memory_order_relaxed) << 1) | 1u;
+}
+
+// The exchange of one split-row launch.  A call outside graph capture gets a fresh
+// epoch, which the tags of its words carry, so the words earlier calls left in the
+// workspace (and whatever else it holds) do not match and nothing needs clearing.  A
+// captured call would replay one epoch, so it takes epoch 0 and zeroes the slots with a
+// fill kernel that is captured with it.
+hipError_t prepare_exchange(const Plan& p, char* ws, hipStream_t s, uint64_t* epoch) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) {
+    *epoch = 0;
+    return clear_exchange(p, ws, s);
+  }
+  *epoch = next_epoch();
+  return hipSuccess;
 }
 
 // ------------------------------------------------------------- static scratch
@@ -332,8 +377,9 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
     make_fallback_plan(false, ln, M, N, dt.x, &p);
   }
   hipError_t e = hipSuccess;
+  uint64_t epoch = 0;
   if (p.path == NORM_PATH_CLUSTER) {
-    e = clear_exchange(p, ws, stream);
+    e = prepare_exchange(p, ws, stream, &epoch);
     if (e != hipSuccess) return hip_status(e);
   }
   if ((e = ev.start()) != hipSuccess) return hip_status(e);
@@ -342,7 +388,8 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
       e = launch_fwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, p.pipelined, stream);
       break;
     case NORM_PATH_CLUSTER:
-      e = launch_fwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws, opt),
+      e = launch_fwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a,
+                             cluster_args(p, ws, opt, epoch),
                              p.grid, stream);
       break;
     default:
@@ -434,16 +481,17 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
     e = launch_zero(dgamma, db, int32_t(N), stream);
     if (e != hipSuccess) return hip_status(e);
   }
+  uint64_t epoch = 0;
   if (p.path == NORM_PATH_CLUSTER) {
-    e = clear_exchange(p, ws, stream);
+    e = prepare_exchange(p, ws, stream, &epoch);
     if (e != hipSuccess) return hip_status(e);
   }
   if ((e = ev.start()) != hipSuccess) return hip_status(e);
   if (p.path == NORM_PATH_ROWS) {
     e = launch_bwd_rows(kind, dt.tc, p.lpr, p.vpl, a, p.grid, p.pipelined, stream);
   } else if (p.path == NORM_PATH_CLUSTER) {
-    e = launch_bwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a, cluster_args(p, ws, opt),
-                           p.grid, stream);
+    e = launch_bwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a,
+                           cluster_args(p, ws, opt, epoch), p.grid, stream);
   } else if (!two_pass) {
     e = launch_bwd_grows(kind, dt.tc, p.vpl, a, p.grid, stream);
   } else {

@@ -11,12 +11,20 @@
 // member order (identical, deterministic bits in every member).  HBM sees every element
 // once, as in the register-resident kernels.
 //
-// Exchange: every row has its own slots, one per member, of 64-bit words each holding a
-// 32-bit tag (derived from the row index, never 0) and a 32-bit float.  A member writes
-// its words with relaxed agent-scope atomic stores and readers spin on agent-scope
-// atomic loads until the tag matches, so every word validates itself and no ordering
-// between different words is needed.  The slots are zeroed by a fill kernel before each
-// launch and each is written once per launch.
+// Exchange: every step of rows has its own slots, one 64-bit word per member and value
+// (at least two per member), each holding a 32-bit float beside one half of a 64-bit tag
+// (the high half in even words, the low half in odd ones).  The tag derives from the
+// call's tag base and the step.  A member writes its words with relaxed agent-scope
+// atomic stores and readers spin on agent-scope atomic loads until all of a member's
+// words carry the step's tag, so the words validate themselves (a reader that sees some
+// of them before the others just polls again) and no ordering between words is needed.
+// Each slot is written once per launch.  Every call outside graph capture has its own
+// tag base (a hash of a per-process epoch that counts up from a random start), so words
+// left by earlier calls, or any other contents of the workspace, match a step's tag with
+// a probability of 2^-62 per read, and the slots are not cleared between calls.  Calls
+// captured into a graph would replay one tag base, so for them a fill kernel captured
+// with the call zeroes the slots first (a zero word never matches: each tag half has its
+// top bit set).
 //
 // The kernels are launched like any other (a cooperative launch costs about 25 us of
 // idle device time around every call on this platform), with a grid the device can hold
@@ -46,27 +54,41 @@
 namespace rownorm {
 namespace {
 
-__device__ inline uint32_t row_tag(int64_t row) {
-  return static_cast<uint32_t>((row + 1) & 0x7FFFFFFF) | 0x80000000u;
+// Tag of a step's words: the call's 64-bit tag base (a hash of its epoch, made on the
+// host) plus (step + 1) times an odd constant, with the top bit of each 32-bit half set
+// so that a zero word never matches.  Two calls' tags for the same step differ unless
+// their bases do; a word of another call and step matches only if the difference of the
+// bases equals a multiple of the constant that the steps fix, a chance of 2^-62.
+struct Tag {
+  uint32_t hi, lo;
+};
+__device__ inline Tag step_tag(uint64_t base, int64_t step) {
+  const uint64_t h = base + (static_cast<uint64_t>(step) + 1) * 0x9E3779B97F4A7C15ull;
+  return Tag{static_cast<uint32_t>(h >> 32) | 0x80000000u, static_cast<uint32_t>(h) | 0x80000000u};
 }
 
-__device__ inline void publish(unsigned long long* slot, uint32_t tag, float v) {
-  const unsigned long long w = (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
-  __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Words a member writes per step for K values: one per value, at least two, so that the
+// step's words together carry both halves of its tag.
+template <int K>
+constexpr int kWords = K < 2 ? 2 : K;
+
+// Word j of a member's step: [tag half | value], the high half of the tag in even words
+// and the low half in odd ones; with one value, the second word repeats it.
+template <int K>
+__device__ inline unsigned long long step_word(Tag tag, int j, const float (&v)[K]) {
+  const uint32_t half = (j & 1) ? tag.lo : tag.hi;
+  return (static_cast<unsigned long long>(half) << 32) | __float_as_uint(v[j < K ? j : 0]);
 }
 
-// Poll the slot until it carries `tag`, at most `limit` times; the value on success.
-__device__ inline bool poll_for(unsigned long long* slot, uint32_t tag, uint32_t limit,
-                                float* out) {
-  for (uint32_t n = 0; n < limit; ++n) {
-    const unsigned long long w = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (static_cast<uint32_t>(w >> 32) == tag) {
-      *out = __uint_as_float(static_cast<uint32_t>(w));
-      return true;
-    }
-    __builtin_amdgcn_s_sleep(2);
-  }
-  return false;
+// Whether a member's words of a step carry the step's tag (and, with one value, agree).
+template <int K>
+__device__ inline bool words_match(const unsigned long long (&w)[kWords<K>], Tag tag) {
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < kWords<K>; ++j)
+    ok = ok && static_cast<uint32_t>(w[j] >> 32) == ((j & 1) ? tag.lo : tag.hi);
+  if constexpr (K == 1) ok = ok && static_cast<uint32_t>(w[0]) == static_cast<uint32_t>(w[1]);
+  return ok;
 }
 
 // Sum of K values over the workgroup at once (one barrier), identical in every thread.
@@ -95,14 +117,19 @@ __device__ inline void block_sum_n(float (&v)[K], float* red, int& parity) {
 
 // A cluster works in steps of R consecutive rows: step t covers rows t*R .. t*R+R-1, and
 // cluster cl takes steps cl, cl + nclusters, ...  One reduction and one exchange serve
-// all R rows of a step.  Every step has its own exchange slots: [member][K] 64-bit words.
+// all R rows of a step.  Every step has its own exchange slots: [member][kWords<K>]
+// 64-bit words.
 template <int K>
 __device__ inline void publish_step(const ClusterArgs& c, int member, int step,
                                     const float (&mine)[K]) {
   if (threadIdx.x == 0) {
-    unsigned long long* base = c.xchg + static_cast<int64_t>(step) * c.C * K;
+    constexpr int W = kWords<K>;
+    unsigned long long* base = c.xchg + static_cast<int64_t>(step) * c.C * W + member * W;
+    const Tag tag = step_tag(c.tag_base, step);
 #pragma unroll
-    for (int j = 0; j < K; ++j) publish(base + member * K + j, row_tag(step), mine[j]);
+    for (int j = 0; j < W; ++j)
+      __hip_atomic_store(base + j, step_word<K>(tag, j, mine), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -111,48 +138,53 @@ __device__ inline void publish_step(const ClusterArgs& c, int member, int step,
 // spilled) across the step loop, and the address is formed only where it is used.
 template <int K>
 __device__ inline unsigned long long* slot_ptr(const ClusterArgs& c, int step, uint32_t m, int j) {
-  uint32_t ofs = (m * K + j) * 8u;
+  constexpr int W = kWords<K>;
+  uint32_t ofs = (m * W + j) * 8u;
   asm volatile("" : "+v"(ofs));
-  char* base = reinterpret_cast<char*>(c.xchg + static_cast<int64_t>(step) * c.C * K);
+  char* base = reinterpret_cast<char*>(c.xchg + static_cast<int64_t>(step) * c.C * W);
   return reinterpret_cast<unsigned long long*>(base + ofs);
 }
 
-// Thread m < C reads member m's K words of `step` ahead of the gather, so the round trip
-// of the first poll overlaps other work instead of stalling the whole workgroup.
+template <int K>
+__device__ inline void load_words(const ClusterArgs& c, int step, unsigned long long (&w)[kWords<K>]) {
+#pragma unroll
+  for (int j = 0; j < kWords<K>; ++j)
+    w[j] = __hip_atomic_load(slot_ptr<K>(c, step, threadIdx.x, j), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Thread m < C reads member m's words of `step` ahead of the gather, so the round trip of
+// the first poll overlaps other work instead of stalling the whole workgroup.
 template <int K>
 __device__ inline void prefetch_step(const ClusterArgs& c, int step,
-                                     unsigned long long (&pre)[K]) {
-  if (threadIdx.x < c.C) {
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-      pre[j] = __hip_atomic_load(slot_ptr<K>(c, step, threadIdx.x, j), __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
-  }
+                                     unsigned long long (&pre)[kWords<K>]) {
+  if (threadIdx.x < c.C) load_words<K>(c, step, pre);
 }
 
 // Every member's K partials of `step` into xin[member * K + j] (thread m < C handles member
-// m).  A prefetched word that already carries the step's tag is used as is; otherwise the
-// thread polls, at most `limit` times.  xok[m] records whether member m's words arrived.
-// The results are visible to the workgroup after its next barrier.
+// m).  Prefetched words that already carry the step's tag are used as they are; otherwise
+// the thread polls, at most `limit` times, until all of the member's words do (a reader
+// that sees some of them before the others just polls again).  xok[m] records whether
+// member m's words arrived.  The results are visible to the workgroup after its next
+// barrier.
 template <int K>
 __device__ inline void resolve_step(const ClusterArgs& c, int step,
-                                    const unsigned long long (&pre)[K], float* xin, int* xok,
-                                    uint32_t limit) {
+                                    const unsigned long long (&pre)[kWords<K>], float* xin,
+                                    int* xok, uint32_t limit) {
   if (threadIdx.x < c.C) {
-    const uint32_t tag = row_tag(step);
-    bool ok = limit != 0;
+    const Tag tag = step_tag(c.tag_base, step);
+    unsigned long long w[kWords<K>];
 #pragma unroll
-    for (int j = 0; j < K; ++j) {
-      float v = 0.0f;
-      if (ok) {
-        if (static_cast<uint32_t>(pre[j] >> 32) == tag) {
-          v = __uint_as_float(static_cast<uint32_t>(pre[j]));
-        } else {
-          ok = poll_for(slot_ptr<K>(c, step, threadIdx.x, j), tag, limit, &v);
-        }
-      }
-      xin[threadIdx.x * K + j] = v;
+    for (int j = 0; j < kWords<K>; ++j) w[j] = pre[j];
+    bool ok = limit != 0 && words_match<K>(w, tag);
+    for (uint32_t n = 0; limit != 0 && !ok && n < limit; ++n) {
+      __builtin_amdgcn_s_sleep(2);
+      load_words<K>(c, step, w);
+      ok = words_match<K>(w, tag);
     }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+      xin[threadIdx.x * K + j] = ok ? __uint_as_float(static_cast<uint32_t>(w[j])) : 0.0f;
     xok[threadIdx.x] = ok ? 1 : 0;
   }
 }
@@ -171,8 +203,8 @@ __device__ inline unsigned missing_members(const ClusterArgs& c, const int* xok)
 // read them.
 template <int K>
 __device__ inline unsigned gather_step(const ClusterArgs& c, int step,
-                                       const unsigned long long (&pre)[K], float* xin, int* xok,
-                                       uint32_t limit) {
+                                       const unsigned long long (&pre)[kWords<K>], float* xin,
+                                       int* xok, uint32_t limit) {
   resolve_step<K>(c, step, pre, xin, xok, limit);
   __syncthreads();
   return missing_members(c, xok);
@@ -544,7 +576,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
     constexpr int k1 = (k0 + 1) % S, k2 = (k0 + 2) % S;
     if (st >= nsteps) return false;
     const int s1 = st + c.nclusters, s2 = st + 2 * c.nclusters;
-    unsigned long long pre[K];
+    unsigned long long pre[kWords<K>];
     prefetch_step<K>(c, st, pre);
     if constexpr (kLoadFirst) load(s2, sg[k2]);
     {
@@ -581,7 +613,7 @@ __global__ __launch_bounds__(T) void fwd_cluster_kernel(const FwdArgs a, const C
         partial(sb, mine);
         publish_step<K>(c, member, st, mine);
       }
-      unsigned long long pre[K];
+      unsigned long long pre[kWords<K>];
       prefetch_step<K>(c, st, pre);
       float* xs = xin[xp];
       int* xk = xok[xp];
@@ -809,7 +841,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
     constexpr int kp = (k0 + S - 2) % S, kl = (k0 + S - 1) % S;
     if (st >= nsteps) return false;
     const int sp = st + (S - 2) * c.nclusters, sl = st + (S - 1) * c.nclusters;
-    unsigned long long pre[K];
+    unsigned long long pre[kWords<K>];
     prefetch_step<K>(c, st, pre);
     if constexpr (kLoadFirst) load(sl, b[kl]);
     float mine[K];
@@ -843,7 +875,7 @@ __global__ __launch_bounds__(T) void bwd_cluster_kernel(const BwdArgs a, const C
         partial(sb, mine);
         publish_step<K>(c, member, st, mine);
       }
-      unsigned long long pre[K];
+      unsigned long long pre[kWords<K>];
       prefetch_step<K>(c, st, pre);
       float* xs = xin[xp];
       int* xk = xok[xp];

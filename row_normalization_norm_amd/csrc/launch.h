@@ -169,7 +169,8 @@ struct ClusterArgs {
   int32_t slice_vecs;        // 16-byte vectors of a row each member owns (nvec / C)
   int32_t rows_per_step;     // R: rows one reduction and one exchange serve
   uint32_t spin_limit;       // polls before computing a missing partial locally; 0: never poll
-  unsigned long long* xchg;  // [steps][C][2R] tagged partial sums, zeroed before each launch
+  unsigned long long* xchg;  // [steps][C][max(2, K)] tagged partial sums
+  uint64_t tag_base;         // the call's tag base: its exchange words' tags derive from it
 };
 
 // ------------------------------------------------------------------ launchers

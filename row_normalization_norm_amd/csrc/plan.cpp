@@ -252,7 +252,8 @@ bool plan_cluster(bool backward, bool layernorm, int64_t M, int64_t N, int64_t n
   p.nclusters = int(ncl);
   p.grid = int(ncl * C);
   p.off_xchg = 0;
-  // every step of rows has its own exchange slots: 2 values per row and member
+  // every step of rows has its own exchange slots: two 64-bit words per row and member
+  // (a word per value, at least two per step)
   p.xchg_bytes = align256(size_t(M + rows) * C * 2 * 8);
   size_t end = p.xchg_bytes;
   if (backward) {
