@@ -33,8 +33,8 @@ constexpr bool tc_is16(int tc) { return tc != kTcF32; }  // 16-bit activations
   X(128, 1) X(128, 2) X(128, 3) X(128, 4) X(128, 6) X(128, 8)                          \
   X(256, 1) X(256, 2) X(256, 3) X(256, 4) X(256, 6) X(256, 8)                          \
   X(512, 1) X(512, 2) X(512, 3) X(512, 4) X(512, 6) X(512, 8)                          \
-  X(1024, 1) X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 6) X(1024, 8)                    \
-  X(512, 16) X(1024, 12) X(1024, 16)
+  X(1024, 1) X(1024, 2) X(1024, 3) X(1024, 4) X(1024, 5) X(1024, 6) X(1024, 7)         \
+  X(1024, 8) X(512, 16) X(1024, 12) X(1024, 16)
 
 // The backward keeps x, dy and per-column fp32 partials of dgamma (and dbeta) in
 // registers.  Wide one-row workgroups keep the partials in LDS instead (bwd_lds_acc);

@@ -383,9 +383,13 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
         } else {
           plan_generic_fwd(M, N, o, p);
         }
-      } else if (atomic ||
-                 nvec <= (backward ? kBwdRowsMaxVecs : kFwdRowsMaxVecs)) {
+      } else if (atomic || (backward && nvec <= kBwdRowsMaxVecs)) {
         ok = plan_rows(backward, layernorm, M, N, nvec, o, atomic, p);
+      } else if (!backward && nvec <= kFwdRowsMaxVecs &&
+                 plan_rows(false, layernorm, M, N, nvec, o, false, p)) {
+        // one workgroup holds the row
+      } else if (!backward && nvec <= kFwdRowsMaxVecs && (o.lanes_per_row || o.vecs_per_lane)) {
+        ok = false;  // the mapping asked for does not cover the row
       } else if (backward && nvec <= kBwdRowsLdsMaxVecs && !o.lanes_per_row &&
                  !o.vecs_per_lane && plan_rows(true, layernorm, M, N, nvec, o, false, p)) {
         // a 1024-lane mapping with LDS partials covers the row

@@ -54,6 +54,23 @@ def test_small_shapes(device, kind, dtype, pdtype, N):
     full_check(w, device, rows=np.arange(w.M))
 
 
+# Row lengths between the one-workgroup mappings' lengths (their forward used to be
+# refused): 16-byte vectors 4097, 5000, 6500 and 7000, one-workgroup and split-row plans.
+BETWEEN = [("rms", "bf16", 8 * 4097), ("ln", "bf16", 8 * 5000), ("ln", "bf16", 8 * 7000),
+           ("rms", "f32", 4 * 6500), ("ln", "f32", 4 * 4097)]
+
+
+@pytest.mark.parametrize("kind,dtype,N", BETWEEN, ids=[f"{k}-{d}-N{n}" for k, d, n in BETWEEN])
+def test_row_lengths_between_mappings(device, kind, dtype, N):
+    w = small_workload(kind, dtype, N, M=37, x_mean=0.2)
+    code = dtype_code(dtype)
+    p = rn.norm_plan(False, kind == "ln", w.M, N, code)
+    assert p.path in (rn.NORM_PATH_ROWS, rn.NORM_PATH_CLUSTER)
+    print(f"between mappings: {w.name} forward path {p.path} {p.lanes_per_row}x{p.vecs_per_lane}",
+          flush=True)
+    full_check(w, device, rows=np.arange(w.M))
+
+
 def _all_rows(w, device):
     print(f"all-row parity: {w.name} [{w.M}x{w.N}] {w.dtype}", flush=True)
     inputs = gen.make_inputs(w)
