@@ -1,0 +1,48 @@
+"""Parity at row lengths drawn at random (seeded): whatever path and mapping the planner
+picks for an arbitrary N — aligned or not, between the compiled mappings' lengths, short,
+long — must match the oracle on every row, forward and backward.  Sizes are kept to a
+few million elements so the oracle finishes in seconds."""
+import numpy as np
+import pytest
+
+import row_normalization_norm_amd as rn
+from parity import full_check
+from test_gpu_parity import PAIRS, small_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases():
+    rng = np.random.default_rng(20261203)
+    out = []
+    for i in range(48):
+        kind = ("rms", "ln")[i % 2]
+        dtype, pdtype = PAIRS[int(rng.integers(len(PAIRS)))]
+        # log-uniform row length up to 2^18, every other one rounded to whole 16-byte
+        # vectors of bf16 (the common case) and the rest as drawn
+        N = int(np.exp(rng.uniform(0.0, np.log(1 << 18))))
+        if i % 4 in (0, 1):
+            N = max(8, N // 8 * 8)
+        M = int(max(1, min(257, 3_000_000 // N)))
+        M = int(rng.integers(1, M + 1))
+        out.append((kind, dtype, pdtype, M, N))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("kind,dtype,pdtype,M,N", CASES,
+                         ids=[f"{k}-{d}{'+' + p if p else ''}-{m}x{n}" for k, d, p, m, n in CASES])
+def test_random_shape(device, kind, dtype, pdtype, M, N):
+    w = small_workload(kind, dtype, N, M=M, x_mean=0.3, pdtype=pdtype)
+    code = rn.dtype_mixed(_code(dtype), _code(pdtype)) if pdtype else _code(dtype)
+    pf = rn.norm_plan(False, kind == "ln", M, N, code)
+    pb = rn.norm_plan(True, kind == "ln", M, N, code)
+    print(f"random shape: {w.name} fwd path {pf.path} {pf.lanes_per_row}x{pf.vecs_per_lane}, "
+          f"bwd path {pb.path} {pb.lanes_per_row}x{pb.vecs_per_lane}", flush=True)
+    full_check(w, device, rows=np.arange(M))
+
+
+def _code(d):
+    return {"bf16": rn.NORM_DTYPE_BF16, "f32": rn.NORM_DTYPE_F32, "f16": rn.NORM_DTYPE_F16}[d]
