@@ -239,18 +239,21 @@ def norm_fwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
 _FWD_WS = {}
 
 
-def _fwd_workspace(M, N, ln, dtype, device, workspace, options, stream):
+def _aligned16(*tensors):
+    return all(t is None or t.data_ptr() % 16 == 0 for t in tensors)
+
+
+def _fwd_workspace(M, N, ln, dtype, device, workspace, options, stream, aligned):
     """The caller's workspace (the library checks its size), or a new one of the size the
-    call needs (None when it needs none)."""
+    call needs with its pointers' alignment (None when it needs none)."""
     if workspace is not None:
         return workspace, workspace.numel() * workspace.element_size()
-    if options is None:
-        key = (M, N, ln, dtype)
-        need = _FWD_WS.get(key)
-        if need is None:
-            need = _FWD_WS.setdefault(key, norm_fwd_workspace_size(M, N, ln, dtype))
-    else:
-        need = norm_fwd_workspace_size(M, N, ln, dtype, options)
+    key = (M, N, ln, dtype, aligned)
+    need = _FWD_WS.get(key) if options is None else None
+    if need is None:
+        need = int(norm_plan(False, ln, M, N, dtype, aligned, options).workspace_bytes)
+        if options is None:
+            _FWD_WS[key] = need
     if need == 0:
         return None, 0
     ws = _torch().empty(need, dtype=_torch().uint8, device=device)
@@ -268,7 +271,8 @@ def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stre
     _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream)
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream,
+                                  _aligned16(x, gamma, y))
     args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
             _stream(x.device, stream))
     if options is None:
@@ -290,7 +294,8 @@ def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, work
     _need(mean, "mean", M, torch.float32, x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream)
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream,
+                                  _aligned16(x, gamma, beta, y))
     args = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, float(eps),
             dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
     if options is None:
@@ -404,7 +409,8 @@ def norm_rms_fwd_add(x, residual, gamma, y, sum_out, rstd=None, eps: float = 1e-
     _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream)
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream,
+                                  _aligned16(x, residual, gamma, y, sum_out))
     _check(lib().norm_rms_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(sum_out),
                                   _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
                                   _stream(x.device, stream), _opt(options)), "norm_rms_fwd_add")
@@ -423,7 +429,8 @@ def norm_ln_fwd_add(x, residual, gamma, beta, y, sum_out, mean=None, rstd=None,
     _need(mean, "mean", M, torch.float32, x.device)
     _need(rstd, "rstd", M, torch.float32, x.device)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream)
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream,
+                                  _aligned16(x, residual, gamma, beta, y, sum_out))
     _check(lib().norm_ln_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
                                  _ptr(sum_out), _ptr(mean), _ptr(rstd), M, N, float(eps), dt,
                                  _ptr(ws), ws_bytes, _stream(x.device, stream), _opt(options)),

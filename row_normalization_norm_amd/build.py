@@ -33,6 +33,7 @@ def _units():
                               os.path.join(BUILD_DIR, f"{name}_k{k}_t{tc}.o"),
                               [f"-DRN_KIND={k}", f"-DRN_TC={tc}"]))
     units.append((os.path.join(CSRC, "aux_kernels.hip"), os.path.join(BUILD_DIR, "aux.o"), []))
+    units.append((os.path.join(CSRC, "split_rows.hip"), os.path.join(BUILD_DIR, "split.o"), []))
     units.append((os.path.join(CSRC, "plan.cpp"), os.path.join(BUILD_DIR, "plan.o"), ["-x", "hip"]))
     units.append((os.path.join(CSRC, "api.cpp"), os.path.join(BUILD_DIR, "api.o"), ["-x", "hip"]))
     return units

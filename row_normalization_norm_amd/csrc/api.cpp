@@ -339,11 +339,11 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   Plan p;
   st = make_plan(false, ln, M, N, dt.x, a16, opt, &p);
   if (st != NORM_OK) return st;
-  // The forward's workspace is optional: only split rows use one (their exchange
-  // words).  Given none, or too little, the call takes a plan that needs none, unless
-  // the split-row path was asked for explicitly.
-  const bool forced_cluster = opt && opt->path == NORM_PATH_CLUSTER;
-  if (p.ws_need > 0 && !forced_cluster &&
+  // The forward's workspace is optional: only split rows (their exchange words) and the
+  // sliced passes (their per-row tables) use one.  Given none, or too little, the call
+  // takes a plan that needs none, unless one of those paths was asked for explicitly.
+  const bool forced_ws = opt && (opt->path == NORM_PATH_CLUSTER || opt->path == NORM_PATH_SPLIT);
+  if (p.ws_need > 0 && !forced_ws &&
       (!workspace || workspace_bytes_given < p.ws_need)) {
     st = make_fwd_plan_without_workspace(ln, M, N, dt.x, a16, opt, &p);
     if (st != NORM_OK) return st;
@@ -369,6 +369,10 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
   a.sum = fused ? sum : nullptr;
   a.static_end = p.groups;
   a.persistent = 0;
+  a.rowp = nullptr;
+  a.rowtab = nullptr;
+  a.rows_per_block = 0;
+  a.slices = 0;
 
   const int kind = ln ? 1 : 0;
   EventScope ev{opt, stream};
@@ -391,6 +395,13 @@ norm_status_t fwd_impl(bool ln, const void* x, const void* gamma, const void* be
       e = launch_fwd_cluster(kind, dt.tc, p.lpr, p.vpl, p.rows_per_step, a,
                              cluster_args(p, ws, opt, epoch),
                              p.grid, stream);
+      break;
+    case NORM_PATH_SPLIT:
+      a.rowtab = reinterpret_cast<float*>(ws + p.off_rowc);
+      a.rowp = reinterpret_cast<float*>(ws + p.off_rowp);
+      a.rows_per_block = p.rows_per_block;
+      a.slices = p.slices;
+      e = launch_fwd_split(kind, dt.tc, p.vec, a, p.slices, int(p.row_blocks), p.grid, stream);
       break;
     default:
       e = p.vpl > 0 ? launch_fwd_grows(kind, dt.tc, p.vpl, a, p.grid, stream)
@@ -466,13 +477,15 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   const bool two_pass =
       p.path == NORM_PATH_SPLIT || (p.path == NORM_PATH_GENERIC && p.vpl == 0);
   a.rowc = two_pass ? reinterpret_cast<float*>(ws + p.off_rowc) : nullptr;
+  a.rowp = two_pass ? reinterpret_cast<float*>(ws + p.off_rowp) : nullptr;
+  a.slices = two_pass ? p.slices : 0;
   a.M = M;
   a.N = int32_t(N);
   a.nvec = p.nvec;
   a.inv_n = 1.0f / float(N);
   a.mode = mode;
   a.groups = p.groups;
-  a.rows_per_block = p.rows_per_block;
+  a.rows_per_block = p.col_rows_per_block;
   a.dres = dres;
 
   EventScope ev{opt, stream};
@@ -495,10 +508,8 @@ norm_status_t bwd_impl(bool ln, const void* dy, const void* x, const void* gamma
   } else if (!two_pass) {
     e = launch_bwd_grows(kind, dt.tc, p.vpl, a, p.grid, stream);
   } else {
-    const bool vec = p.path == NORM_PATH_SPLIT;
-    e = launch_bwd_rowdot(kind, dt.tc, vec, a, p.grid, stream);
-    if (e == hipSuccess)
-      e = launch_bwd_colslice(kind, dt.tc, vec, a, p.slices, int(p.partial_rows), stream);
+    e = launch_bwd_split(kind, dt.tc, p.vec, a, p.slices, int(p.row_blocks), p.rows_per_block,
+                         int(p.partial_rows), p.col_rows_per_block, p.grid, stream);
   }
   if (e != hipSuccess) return hip_status(e);
   if ((e = ev.stop()) != hipSuccess) return hip_status(e);
@@ -694,9 +705,8 @@ norm_status_t norm_plan(int is_backward, int is_layernorm, int64_t M, int64_t N,
   info->lanes_per_row = p.lpr;
   info->vecs_per_lane = p.vpl;
   info->block = p.block;
-  info->grid = (p.path == NORM_PATH_ROWS || p.path == NORM_PATH_CLUSTER || !is_backward)
-                   ? p.grid
-                   : int(p.slices * p.partial_rows);
+  // the sliced passes report their (slice, row block) grid
+  info->grid = p.slices ? int(p.slices * p.row_blocks) : p.grid;
   info->partial_rows = int(p.partial_rows);
   info->cluster_size = p.cluster;
   info->cluster_rows = p.rows_per_step;

@@ -1,20 +1,13 @@
-// The kernels outside the register-resident row mapping:
+// The kernels outside the register-resident row mapping and the sliced passes
+// (split_rows.hip):
 //
-//  * rowdot   -- per-row reduction pass of the SPLIT and GENERIC backward:
-//                c1 = mean(g * xhat), c2 = mean(g) with g = dy * gamma, written to a
-//                [M, 2] table.  One workgroup per row, looping over the row.
-//  * colslice -- column-sliced pass of the SPLIT and GENERIC backward: a workgroup owns
-//                a slice of columns and a block of rows, writes dx = rstd*(g - c2 -
-//                xhat*c1) from the table, keeps per-column dgamma/dbeta sums in
-//                registers and writes them as one partial row.  It never needs a row
-//                reduction, so a row of any length is handled without cross-workgroup
-//                communication (the price is a second read of x and dy).
 //  * colreduce -- stage 2 of the two-stage dgamma/dbeta reduction: out[j] = sum over p of
 //                part[p, j], in a fixed order (deterministic, no atomics; "Fused RMSNorm",
 //                aryanashta.me, "What didn't work" and "Next").
 //  * zero     -- clears dgamma/dbeta before the atomic comparison variants add into them.
-//  * fwd_generic -- scalar forward for any N and alignment: a workgroup per row, one pass
-//                for the sums and a second (cache-resident) pass to normalize.
+//  * fwd_generic -- scalar forward for any N and alignment, for a call given no
+//                workspace: a workgroup per row, one pass for the sums and a second
+//                (cache-resident) pass to normalize.
 //
 // Formulas as in the forward and backward row kernels ("Fused RMSNorm", "What it is";
 // "SOTA normalization performance with torch.compile", "How Did Torch.compile Catch
@@ -51,168 +44,13 @@ __device__ inline void block_sum2(float& a, float& b, float* red, int& parity) {
   parity ^= 1;
 }
 
-// ----------------------------------------------------------------------- rowdot
-template <bool LN, typename D, typename P, bool VEC>
-__global__ __launch_bounds__(kRowBlock) void rowdot_kernel(const BwdArgs a) {
-  constexpr int EPV = D::kPerVec;
-  __shared__ float red[2 * kRowWaves * 2];
-  int parity = 0;
-  const int tid = threadIdx.x;
-  for (int64_t row = blockIdx.x; row < a.M; row += gridDim.x) {
-    const float r = a.rstd[row];
-    const float mu = LN ? a.mean[row] : 0.0f;
-    float s1 = 0.0f, s2 = 0.0f;
-    if constexpr (VEC) {
-      const int64_t vbase = row * a.nvec;
-#pragma unroll 4
-      for (int vi = tid; vi < a.nvec; vi += kRowBlock) {
-        const u32x4 xv = ld16(a.x, vbase + vi);
-        const u32x4 dv = ld16(a.dy, vbase + vi);
-        Param<D, P> gv;
-        gv.load(a.gamma, vi);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          const float xh = (D::get(xv, e) - mu) * r;
-          const float g = D::get(dv, e) * gv.get(e);
-          s1 = fmaf(g, xh, s1);
-          if constexpr (LN) s2 += g;
-        }
-      }
-    } else {
-      const int64_t base = row * a.N;
-#pragma unroll 4
-      for (int j = tid; j < a.N; j += kRowBlock) {
-        const float xh = (D::scalar(a.x, base + j) - mu) * r;
-        const float g = D::scalar(a.dy, base + j) * P::scalar(a.gamma, j);
-        s1 = fmaf(g, xh, s1);
-        if constexpr (LN) s2 += g;
-      }
-    }
-    block_sum2(s1, s2, red, parity);
-    if (tid == 0) {
-      a.rowc[2 * row] = s1 * a.inv_n;
-      a.rowc[2 * row + 1] = LN ? s2 * a.inv_n : 0.0f;
-    }
-  }
-}
-
-// --------------------------------------------------------------------- colslice
-template <bool LN, typename D, typename P, bool VEC>
-__global__ __launch_bounds__(kSliceBlock) void colslice_kernel(const BwdArgs a) {
-  constexpr int EPV = VEC ? D::kPerVec : 1;
-  constexpr int V = VEC ? kSliceVecs : 1;
-  const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.y * a.rows_per_block;
-  const int64_t r1 = r0 + a.rows_per_block < a.M ? r0 + a.rows_per_block : a.M;
-
-  // Vector (or column) indices this lane owns.
-  int idx[V];
-  bool own[V];
-  const int limit = VEC ? a.nvec : a.N;
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    idx[v] = (blockIdx.x * V + v) * kSliceBlock + tid;
-    own[v] = idx[v] < limit;
-  }
-
-  float gam[V][EPV];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    if constexpr (VEC) {
-      Param<D, P> gv;
-      if (own[v]) {
-        gv.load(a.gamma, idx[v]);
-      } else {
-        gv.clear();
-      }
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) gam[v][e] = gv.get(e);
-    } else {
-      gam[v][0] = own[v] ? P::scalar(a.gamma, idx[v]) : 0.0f;
-    }
-  }
-
-  float accg[V][EPV], accb[LN ? V : 1][EPV];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      accg[v][e] = 0.0f;
-      if constexpr (LN) accb[v][e] = 0.0f;
-    }
-  }
-
-#pragma unroll 2
-  for (int64_t row = r0; row < r1; ++row) {
-    const float r = a.rstd[row];
-    const float mu = LN ? a.mean[row] : 0.0f;
-    const float c1 = a.rowc[2 * row];
-    const float c2 = a.rowc[2 * row + 1];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      if (!own[v]) continue;
-      float xs[EPV], ds[EPV];
-      if constexpr (VEC) {
-        const int64_t vi = row * a.nvec + idx[v];
-        const u32x4 xv = ld16_stream(a.x, vi);
-        const u32x4 dv = ld16_stream(a.dy, vi);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-          xs[e] = D::get(xv, e);
-          ds[e] = D::get(dv, e);
-        }
-      } else {
-        const int64_t i = row * a.N + idx[v];
-        xs[0] = D::scalar(a.x, i);
-        ds[0] = D::scalar(a.dy, i);
-      }
-      float o[VEC ? D::kPerVec : 1];
-#pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const float xh = (xs[e] - mu) * r;
-        const float g = ds[e] * gam[v][e];
-        o[e] = r * fmaf(-xh, c1, g - c2);
-        accg[v][e] = fmaf(ds[e], xh, accg[v][e]);
-        if constexpr (LN) accb[v][e] += ds[e];
-      }
-      if (a.dres) {  // gradient arriving at a fused residual sum
-        if constexpr (VEC) {
-          const u32x4 gv = ld16_stream(a.dres, row * a.nvec + idx[v]);
-#pragma unroll
-          for (int e = 0; e < EPV; ++e) o[e] += D::get(gv, e);
-        } else {
-          o[0] += D::scalar(a.dres, row * a.N + idx[v]);
-        }
-      }
-      if constexpr (VEC) {
-        st16_stream(a.dx, row * a.nvec + idx[v], D::pack(o));
-      } else {
-        D::put_scalar(a.dx, row * a.N + idx[v], o[0]);
-      }
-    }
-  }
-
-  float* const out_g = a.part_g + (int64_t)blockIdx.y * a.N;
-  float* const out_b = a.part_b + (int64_t)blockIdx.y * a.N;
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    if (!own[v]) continue;
-#pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      const int64_t col = (int64_t)idx[v] * EPV + e;
-      out_g[col] = accg[v][e];
-      if constexpr (LN) out_b[col] = accb[v][e];
-    }
-  }
-}
-
 // -------------------------------------------------------------------- colreduce
-template <bool VEC4>
+// S splits of the P rows x L = 256 / S lanes along N (4 columns each with 16-byte loads).
+template <bool VEC4, int S>
 __global__ __launch_bounds__(kColRedThreads) void colreduce_kernel(
     const float* __restrict__ part_g, const float* __restrict__ part_b, int64_t P, int32_t N,
     float* __restrict__ dgamma, float* __restrict__ dbeta) {
-  constexpr int L = colred_lanes(VEC4);
-  constexpr int S = kColRedThreads / L;
+  constexpr int L = kColRedThreads / S;
   constexpr int W = VEC4 ? 4 : 1;
   const float* src = blockIdx.y ? part_b : part_g;
   float* dst = blockIdx.y ? dbeta : dgamma;
@@ -242,8 +80,8 @@ __global__ __launch_bounds__(kColRedThreads) void colreduce_kernel(
 #pragma unroll
   for (int k = 0; k < W; ++k) buf[ty][tx * W + k] = s[k];
   __syncthreads();
-  if (threadIdx.x < L * W) {
-    const int c = threadIdx.x;
+  // L * W columns per workgroup: up to four per thread when there is a single split
+  for (int c = threadIdx.x; c < L * W; c += kColRedThreads) {
     const int64_t out = (int64_t)blockIdx.x * L * W + c;
     float t = 0.0f;
 #pragma unroll
@@ -279,12 +117,12 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
     if constexpr (LN) {
       float s = 0.0f, unused = 0.0f;
 #pragma unroll 4
-      for (int j = tid; j < a.N; j += kRowBlock) s += elem(base + j);
+      for (int64_t j = tid; j < a.N; j += kRowBlock) s += elem(base + j);
       block_sum2(s, unused, red, parity);
       mu = s * a.inv_n;
       float ss = 0.0f;
 #pragma unroll 4
-      for (int j = tid; j < a.N; j += kRowBlock) {
+      for (int64_t j = tid; j < a.N; j += kRowBlock) {
         const float d = elem(base + j) - mu;
         ss = fmaf(d, d, ss);
       }
@@ -293,7 +131,7 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
     } else {
       float ss = 0.0f, unused = 0.0f;
 #pragma unroll 4
-      for (int j = tid; j < a.N; j += kRowBlock) {
+      for (int64_t j = tid; j < a.N; j += kRowBlock) {
         const float f = elem(base + j);
         ss = fmaf(f, f, ss);
       }
@@ -308,7 +146,7 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
       }
     }
 #pragma unroll 4
-    for (int j = tid; j < a.N; j += kRowBlock) {
+    for (int64_t j = tid; j < a.N; j += kRowBlock) {
       const float f = elem(base + j);
       if (a.res) D::put_scalar(a.sum, base + j, f);
       const float gm = P::scalar(a.gamma, j);
@@ -337,40 +175,6 @@ __global__ __launch_bounds__(kRowBlock) void fwd_generic_kernel(const FwdArgs a)
     if (tc == kTcF16F32) { if (ln_) CALL(true, F16, F32) else CALL(false, F16, F32) }    \
   } while (0)
 
-hipError_t launch_bwd_rowdot(int kind, int tc, bool vec, const BwdArgs& a, int grid,
-                             hipStream_t s) {
-#define RN_CALL(LN, D, P)                                                                    \
-  {                                                                                         \
-    if (vec) {                                                                              \
-      hipLaunchKernelGGL((rowdot_kernel<LN, D, P, true>), dim3(grid), dim3(kRowBlock), 0, s, a); \
-    } else {                                                                                \
-      hipLaunchKernelGGL((rowdot_kernel<LN, D, P, false>), dim3(grid), dim3(kRowBlock), 0, s,  \
-                         a);                                                                \
-    }                                                                                       \
-    return hipGetLastError();                                                               \
-  }
-  RN_DISPATCH_KT(kind, tc, RN_CALL);
-#undef RN_CALL
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_bwd_colslice(int kind, int tc, bool vec, const BwdArgs& a, int slices,
-                               int row_blocks, hipStream_t s) {
-  const dim3 grid(slices, row_blocks);
-#define RN_CALL(LN, D, P)                                                                        \
-  {                                                                                             \
-    if (vec) {                                                                                  \
-      hipLaunchKernelGGL((colslice_kernel<LN, D, P, true>), grid, dim3(kSliceBlock), 0, s, a);   \
-    } else {                                                                                    \
-      hipLaunchKernelGGL((colslice_kernel<LN, D, P, false>), grid, dim3(kSliceBlock), 0, s, a);  \
-    }                                                                                           \
-    return hipGetLastError();                                                                   \
-  }
-  RN_DISPATCH_KT(kind, tc, RN_CALL);
-#undef RN_CALL
-  return hipErrorInvalidValue;
-}
-
 hipError_t launch_fwd_generic(int kind, int tc, const FwdArgs& a, int grid, hipStream_t s) {
 #define RN_CALL(LN, D, P)                                                                    \
   {                                                                                         \
@@ -388,16 +192,24 @@ hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P,
                     (part_b == nullptr || (reinterpret_cast<uintptr_t>(part_b) & 15) == 0) &&
                     ((reinterpret_cast<uintptr_t>(dgamma) & 15) == 0) &&
                     (dbeta == nullptr || (reinterpret_cast<uintptr_t>(dbeta) & 15) == 0);
-  const int per_block = colred_lanes(vec4) * (vec4 ? 4 : 1);
+  // As many splits of the P rows as there are rows, up to the most (a few partial rows
+  // then leave no lanes idle); the rest of the 256 threads go along N.
+  const int smax = colred_max_splits(vec4);
+  int splits = 1;
+  while (splits < smax && splits < P) splits *= 2;
+  const int per_block = (kColRedThreads / splits) * (vec4 ? 4 : 1);
   const dim3 grid((N + per_block - 1) / per_block, part_b ? 2 : 1);
-  if (vec4) {
-    hipLaunchKernelGGL((colreduce_kernel<true>), grid, dim3(kColRedThreads), 0, s, part_g, part_b,
-                       P, N, dgamma, dbeta);
-  } else {
-    hipLaunchKernelGGL((colreduce_kernel<false>), grid, dim3(kColRedThreads), 0, s, part_g, part_b,
-                       P, N, dgamma, dbeta);
+#define RN_COLRED(V, S)                                                                     \
+  if (vec4 == V && splits == S) {                                                           \
+    hipLaunchKernelGGL((colreduce_kernel<V, S>), grid, dim3(kColRedThreads), 0, s, part_g,  \
+                       part_b, P, N, dgamma, dbeta);                                        \
+    return hipGetLastError();                                                               \
   }
-  return hipGetLastError();
+  RN_COLRED(true, 1) RN_COLRED(true, 2) RN_COLRED(true, 4) RN_COLRED(true, 8)
+  RN_COLRED(true, 16) RN_COLRED(true, 32)
+  RN_COLRED(false, 1) RN_COLRED(false, 2) RN_COLRED(false, 4) RN_COLRED(false, 8)
+#undef RN_COLRED
+  return hipErrorInvalidValue;
 }
 
 // Streaming reference (a measurement aid, not on the normalization path): each workgroup

@@ -100,16 +100,24 @@ constexpr int grows_epl(int64_t n) {
 constexpr int fwd_block(int lpr) { return lpr >= 256 ? lpr : 256; }
 constexpr int bwd_block(int lpr) { return lpr >= 512 ? lpr : 512; }
 
-// Column-sliced backward pass (SPLIT path): threads and vectors per lane.
+// Sliced passes over rows too long for a workgroup or a cluster (split_rows.hip): a
+// slice is kSliceBlock lanes x kSliceVecs 16-byte vectors, or x kSliceElems elements
+// for rows that are not whole vectors.
 constexpr int kSliceBlock = 256;
 constexpr int kSliceVecs = 2;
-// Row-reduction pass (SPLIT and GENERIC backward) and the scalar forward.
+constexpr int kSliceElems = 8;
+constexpr int slice_units(bool vec) { return kSliceBlock * (vec ? kSliceVecs : kSliceElems); }
+// Per-row merge of the slices' terms: one wavefront per row.
+constexpr int kMergeBlock = 256;
+// The looping scalar forward (no workspace).
 constexpr int kRowBlock = 256;
 // Column reduce of the partial rows: 256 threads = lanes along N x splits of the P rows.
-// The 16-byte path gives each workgroup 8 lanes x 4 columns (128-byte row segments), so
-// a 4096-column LayerNorm spreads over 256 workgroups; the scalar path 32 lanes x 1.
+// With many partial rows the 16-byte path gives each workgroup 8 lanes x 4 columns
+// (128-byte row segments, 32 splits), so a 4096-column LayerNorm spreads over 256
+// workgroups; the scalar path 32 lanes x 1 (8 splits).  Fewer partial rows than that
+// take as many splits as rows.
 constexpr int kColRedThreads = 256;
-constexpr int colred_lanes(bool vec4) { return vec4 ? 8 : 32; }
+constexpr int colred_max_splits(bool vec4) { return vec4 ? 32 : 8; }
 
 enum DgammaMode { kTwoStage = 0, kAtomicRow = 1, kAtomicWg = 2 };
 
@@ -136,6 +144,12 @@ struct FwdArgs {
   // from static_end on (persistent = 0: every workgroup strides over all the groups).
   int64_t static_end;
   int32_t persistent;
+  // SPLIT path: per-(row, slice) statistics [M, slices, 2], the merged per-row (mean,
+  // rstd) [M, 2], and the (slice, row block) grid's rows per block.
+  float* rowp;
+  float* rowtab;
+  int64_t rows_per_block;
+  int32_t slices;
 };
 
 struct BwdArgs {
@@ -150,16 +164,33 @@ struct BwdArgs {
   float* dgamma;   // final outputs (atomic modes add into them)
   float* dbeta;
   float* rowc;     // SPLIT / GENERIC: [M, 2] per-row (c1, c2)
+  float* rowp;     // SPLIT / GENERIC: [M, slices, 2] per-(row, slice) sums of g*xhat, g
   int64_t M;
   int32_t N;
   int32_t nvec;
   float inv_n;
   int32_t mode;    // DgammaMode
   int64_t groups;
-  int64_t rows_per_block;  // SPLIT / GENERIC column pass: rows per row block
+  int64_t rows_per_block;  // SPLIT / GENERIC sliced passes: rows per row block of the pass
+  int32_t slices;          // SPLIT / GENERIC sliced passes: column slices
   // Gradient arriving at the residual sum from later uses (NULL when not fused): it is
   // added to dx, the gradient of both addends.
   const void* dres;
+};
+
+// Per-row merge of the sliced passes' terms (rowp [M, slices, 2]) into out [M, 2]:
+// forward (mean, rstd), also stored to mean / rstd when not NULL; backward (c1, c2).
+struct MergeArgs {
+  const float* rowp;
+  float* out;
+  float* mean;
+  float* rstd;
+  int64_t M;
+  int32_t N;
+  int32_t slices;
+  int32_t slice_elems;  // elements of a full slice (the last one may hold fewer)
+  float inv_n;
+  float eps;
 };
 
 struct ClusterArgs {
@@ -181,12 +212,16 @@ hipError_t launch_fwd_rows(int kind, int tc, int lpr, int vpl, const FwdArgs& a,
                            bool pipe, hipStream_t s);
 hipError_t launch_bwd_rows(int kind, int tc, int lpr, int vpl, const BwdArgs& a, int grid,
                            bool pipe, hipStream_t s);
-// SPLIT path (16-byte vectors): per-row reduction, then the column-sliced pass on a
-// (slices, row_blocks) grid.
-hipError_t launch_bwd_rowdot(int kind, int tc, bool vec, const BwdArgs& a, int grid,
-                             hipStream_t s);
-hipError_t launch_bwd_colslice(int kind, int tc, bool vec, const BwdArgs& a, int slices,
-                               int row_blocks, hipStream_t s);
+// Sliced passes (vec: 16-byte vectors, else elements) on (slices, row blocks) grids,
+// with the per-row merge on merge_grid workgroups between them.  Forward: statistics,
+// merge, normalize, all on row_blocks blocks of a.rows_per_block rows.  Backward: row
+// sums (row_blocks blocks of rows_per_block rows), merge, then dx and the partial rows
+// (col_blocks blocks of col_rows rows, one partial row each).
+hipError_t launch_fwd_split(int kind, int tc, bool vec, const FwdArgs& a, int slices,
+                            int row_blocks, int merge_grid, hipStream_t s);
+hipError_t launch_bwd_split(int kind, int tc, bool vec, const BwdArgs& a, int slices,
+                            int row_blocks, int64_t rows_per_block, int col_blocks,
+                            int64_t col_rows, int merge_grid, hipStream_t s);
 // Split-row kernels and their occupancy (workgroups per CU).
 hipError_t launch_fwd_cluster(int kind, int tc, int t, int vpl, int rows, const FwdArgs& a,
                               const ClusterArgs& c, int grid, hipStream_t s);
@@ -195,10 +230,10 @@ hipError_t launch_bwd_cluster(int kind, int tc, int t, int vpl, int rows, const 
 // add: the variant with the fused residual add (forward) or residual gradient (backward).
 int occupancy_fwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add);
 int occupancy_bwd_cluster(int kind, int tc, int t, int vpl, int rows, bool add);
-// GENERIC forward (scalar loads): looping kernel for any N, register-resident kernel
-// (epl elements per lane, RN_GROWS_EPL) for N up to kGrowsFwdMaxElems; and the
-// register-resident GENERIC backward (one partial row per workgroup, like the ROWS path)
-// for N up to kGrowsBwdMaxElems.
+// GENERIC forward (scalar loads): looping kernel for any N (the plan of a call given no
+// workspace), register-resident kernel (epl elements per lane, RN_GROWS_EPL) for N up
+// to kGrowsFwdMaxElems; and the register-resident GENERIC backward (one partial row per
+// workgroup, like the ROWS path) for N up to kGrowsBwdMaxElems.
 hipError_t launch_fwd_generic(int kind, int tc, const FwdArgs& a, int grid, hipStream_t s);
 hipError_t launch_fwd_grows(int kind, int tc, int epl, const FwdArgs& a, int grid, hipStream_t s);
 hipError_t launch_bwd_grows(int kind, int tc, int epl, const BwdArgs& a, int grid, hipStream_t s);

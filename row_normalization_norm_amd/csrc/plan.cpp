@@ -67,8 +67,19 @@ constexpr int kClusterBwdMaxVpl = 2;
 constexpr int kClusterFwdRows = 1;
 constexpr int kClusterBwdRowsBf16 = 2;
 constexpr int kClusterBwdRowsF32 = 1;
+// Sliced passes.  The forward's passes and the backward's first pass aim at
+// kSliceTargetBlocks workgroups with at least kSliceMinRows rows each (the per-workgroup
+// set-up, gamma and beta, then serves several rows).  The backward's column pass writes
+// a partial row per row block: it aims at kSplitTargetBlocks, up to kSplitMaxRowBlocks
+// row blocks, or more when a block would otherwise hold over kSplitMaxBlockRows rows.
+// Measured on MI355X over rows of 4 100 to 4 194 304 elements and 1 to 65 536 rows.
+constexpr int kSliceTargetBlocks = 8192;
+constexpr int kSliceMinRows = 4;
 constexpr int kSplitTargetBlocks = 2048;
 constexpr int kSplitMaxRowBlocks = 256;
+constexpr int kSplitMaxBlockRows = 32;
+constexpr int kMaxGridY = 65535;  // the grid's y limit
+// the per-row merge's and the looping scalar forward's grid
 constexpr int kRowPassMaxGrid = 2048;
 // Register-resident scalar backward: workgroups (and partial rows); its element loads
 // need many waves in flight.
@@ -267,29 +278,53 @@ bool plan_cluster(bool backward, bool layernorm, int64_t M, int64_t N, int64_t n
   return true;
 }
 
-void plan_split(bool layernorm, int64_t M, int64_t N, int64_t nvec, bool vec,
+// Sliced passes on a (slices, row blocks) grid for rows too long for a workgroup or a
+// cluster, and for long rows that are not whole vectors: the forward (SPLIT) and the
+// backward (SPLIT for 16-byte vectors, else GENERIC with vpl = 0).  The options' grid
+// sets the row blocks of every pass.  Workspace: the per-row table [M, 2], the
+// per-(row, slice) terms [M, slices, 2], then the backward's partial rows.
+int64_t split_row_blocks(int64_t M, int64_t want, const norm_options_t& o) {
+  int64_t rb = o.grid ? o.grid : want;
+  if (rb > kMaxGridY) rb = kMaxGridY;
+  if (rb > M) rb = M;
+  if (rb < 1) rb = M > 0 ? 1 : 0;
+  return rb;
+}
+
+void plan_split(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec, bool vec,
                 const norm_options_t& o, Plan& p) {
-  p.path = vec ? NORM_PATH_SPLIT : NORM_PATH_GENERIC;
+  p.path = (vec || !backward) ? NORM_PATH_SPLIT : NORM_PATH_GENERIC;
+  p.vec = vec;
   p.block = kSliceBlock;
-  p.grid = int(M < kRowPassMaxGrid ? M : kRowPassMaxGrid);
-  const int64_t slice_width = vec ? int64_t(kSliceBlock) * kSliceVecs : int64_t(kSliceBlock);
-  p.slices = int(ceil_div(vec ? nvec : N, slice_width));
-  int64_t row_blocks = ceil_div(kSplitTargetBlocks, p.slices);
-  if (row_blocks > kSplitMaxRowBlocks) row_blocks = kSplitMaxRowBlocks;
-  if (o.grid) row_blocks = o.grid;
-  if (row_blocks > M) row_blocks = M;
-  if (row_blocks < 1) row_blocks = M > 0 ? 1 : 0;
-  p.rows_per_block = row_blocks ? ceil_div(M, row_blocks) : 0;
-  p.partial_rows = p.rows_per_block ? ceil_div(M, p.rows_per_block) : 0;
+  const int64_t merge_blocks = ceil_div(M, kMergeBlock / 64);
+  p.grid = int(merge_blocks < kRowPassMaxGrid ? merge_blocks : kRowPassMaxGrid);
+  p.slices = int(ceil_div(vec ? nvec : N, slice_units(vec)));
+  int64_t want = ceil_div(kSliceTargetBlocks, p.slices);
+  if (want > ceil_div(M, kSliceMinRows)) want = ceil_div(M, kSliceMinRows);
+  const int64_t rb = split_row_blocks(M, want, o);
+  p.rows_per_block = rb ? ceil_div(M, rb) : 0;
+  p.row_blocks = p.rows_per_block ? ceil_div(M, p.rows_per_block) : 0;
   p.off_rowc = 0;
-  p.off_part_g = align256(size_t(M) * 2 * 4);
-  const size_t part = align256(size_t(p.partial_rows) * size_t(N) * 4);
-  p.off_part_b = p.off_part_g + part;
-  p.ws_bytes = layernorm ? p.off_part_b + part : p.off_part_b;
+  p.off_rowp = align256(size_t(M) * 2 * 4);
+  size_t end = p.off_rowp + align256(size_t(M) * size_t(p.slices) * 2 * 4);
+  if (backward) {
+    int64_t cwant = ceil_div(kSplitTargetBlocks, p.slices);
+    int64_t cmax = ceil_div(M, kSplitMaxBlockRows);
+    if (cmax < kSplitMaxRowBlocks) cmax = kSplitMaxRowBlocks;
+    if (cwant > cmax) cwant = cmax;
+    const int64_t cb = split_row_blocks(M, cwant, o);
+    p.col_rows_per_block = cb ? ceil_div(M, cb) : 0;
+    p.partial_rows = p.col_rows_per_block ? ceil_div(M, p.col_rows_per_block) : 0;
+    const size_t part = align256(size_t(p.partial_rows) * size_t(N) * 4);
+    p.off_part_g = end;
+    p.off_part_b = end + part;
+    end += layernorm ? 2 * part : part;
+  }
+  p.ws_bytes = end;
 }
 
 // GENERIC forward: the register-resident scalar kernel (vpl = elements per lane) for rows
-// up to kGrowsFwdMaxElems, else the looping kernel (vpl = 0).
+// up to kGrowsFwdMaxElems, else the looping kernel (vpl = 0), which needs no workspace.
 void plan_generic_fwd(int64_t M, int64_t N, const norm_options_t& o, Plan& p) {
   p.path = NORM_PATH_GENERIC;
   p.block = kRowBlock;
@@ -305,7 +340,7 @@ void plan_generic_bwd(bool layernorm, int64_t M, int64_t N, int64_t nvec, bool a
                       const norm_options_t& o, Plan& p) {
   const int epl = N <= kGrowsBwdMaxElems ? grows_epl(N) : 0;
   if (!epl) {
-    plan_split(layernorm, M, N, nvec, false, o, p);
+    plan_split(true, layernorm, M, N, nvec, false, o, p);
     return;
   }
   p.path = NORM_PATH_GENERIC;
@@ -380,8 +415,10 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
       if (!vec_ok) {
         if (backward) {
           plan_generic_bwd(layernorm, M, N, nvec, atomic, o, p);
-        } else {
+        } else if (N <= kGrowsFwdMaxElems) {
           plan_generic_fwd(M, N, o, p);
+        } else {
+          plan_split(false, layernorm, M, N, nvec, false, o, p);
         }
       } else if (atomic || (backward && nvec <= kBwdRowsMaxVecs)) {
         ok = plan_rows(backward, layernorm, M, N, nvec, o, atomic, p);
@@ -397,10 +434,10 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
                  !o.vecs_per_lane && plan_rows(false, layernorm, M, N, nvec, o, false, p)) {
         // a 12- or 16-vector mapping covers the row
       } else if (!plan_cluster(backward, layernorm, M, N, nvec, dtype, o, p)) {
-        if (backward) {
-          plan_split(layernorm, M, N, nvec, true, o, p);
-        } else if (!plan_rows(false, layernorm, M, N, nvec, o, false, p)) {
-          plan_generic_fwd(M, N, o, p);
+        if (backward || !plan_rows(false, layernorm, M, N, nvec, o, false, p)) {
+          p = Plan();
+          p.nvec = int(nvec);
+          plan_split(backward, layernorm, M, N, nvec, true, o, p);
         }
       }
       break;
@@ -411,8 +448,9 @@ norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int
       ok = vec_ok && !atomic && plan_cluster(backward, layernorm, M, N, nvec, dtype, o, p);
       break;
     case NORM_PATH_SPLIT:
-      ok = vec_ok && backward;
-      if (ok) plan_split(layernorm, M, N, nvec, true, o, p);
+      // the backward's sliced passes over elements are its GENERIC plan
+      ok = vec_ok || !backward;
+      if (ok) plan_split(backward, layernorm, M, N, nvec, vec_ok, o, p);
       break;
     case NORM_PATH_GENERIC:
       if (backward) {
@@ -447,11 +485,7 @@ norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64
   Plan p;
   const int epv = dtype != NORM_DTYPE_F32 ? 8 : 4;
   p.nvec = int(N / epv);
-  if (backward) {
-    plan_split(layernorm, M, N, p.nvec, true, o, p);
-  } else {
-    plan_generic_fwd(M, N, o, p);
-  }
+  plan_split(backward, layernorm, M, N, p.nvec, true, o, p);
   if (M == 0) p.grid = 0;
   p.ws_need = p.ws_bytes;
   *out = p;

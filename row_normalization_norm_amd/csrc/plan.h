@@ -22,10 +22,14 @@ struct Plan {
                               // CLUSTER: threads per member workgroup / vectors per lane.
   int block = 0;              // threads per workgroup of the main kernel
   int64_t groups = 0;         // ROWS: row groups
-  int grid = 0;               // ROWS / CLUSTER: main grid; SPLIT/GENERIC bwd: row-pass grid
+  int grid = 0;               // ROWS / CLUSTER: main grid; sliced passes: merge grid
   int64_t partial_rows = 0;   // P: rows of dgamma/dbeta partials (two-stage backward)
-  int slices = 0;             // SPLIT/GENERIC bwd: column slices of the column pass
-  int64_t rows_per_block = 0; // SPLIT/GENERIC bwd: rows per row block of the column pass
+  int slices = 0;             // sliced passes: column slices (0: not a sliced plan)
+  int64_t row_blocks = 0;     // sliced passes: row blocks of the forward's passes and the
+  int64_t rows_per_block = 0; //   backward's first pass, and their rows per block
+  int64_t col_rows_per_block = 0;  // backward column pass: rows per row block (its row
+                                   // blocks are the partial rows)
+  bool vec = false;           // sliced passes: 16-byte vectors (else elements)
   int nvec = 0;               // N / elements per 16-byte vector (vector paths)
   int cluster = 0;            // CLUSTER: workgroups per row
   int nclusters = 0;          // CLUSTER: clusters
@@ -34,7 +38,9 @@ struct Plan {
   bool pipelined = false;     // ROWS: the pipelined kernel (persistent grids only)
   size_t ws_bytes = 0;        // bytes this plan uses
   size_t ws_need = 0;         // bytes the call requires (covers the fallback plan too)
-  size_t off_part_g = 0, off_part_b = 0, off_rowc = 0;  // byte offsets into the workspace
+  // byte offsets into the workspace: partial rows, the sliced passes' per-row table
+  // (backward c1/c2, forward mean/rstd) and per-(row, slice) terms
+  size_t off_part_g = 0, off_part_b = 0, off_rowc = 0, off_rowp = 0;
   size_t off_xchg = 0, xchg_bytes = 0;
 };
 
@@ -44,14 +50,15 @@ struct Plan {
 norm_status_t make_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
                         bool aligned16, const norm_options_t* opt, Plan* out);
 
-// The SPLIT (bwd) or GENERIC (fwd) plan a CLUSTER plan falls back to when the device
-// cannot hold one cluster's workgroups at once.
+// The sliced (SPLIT) plan a CLUSTER plan falls back to when the device cannot hold one
+// cluster's workgroups at once.
 norm_status_t make_fallback_plan(bool backward, bool layernorm, int64_t M, int64_t N, int dtype,
                                  Plan* out);
 
 // A forward plan that needs no workspace, for a call given none (or too little) where
-// the planned one would split rows over clusters: the widest register-resident row
-// mapping that covers the row, else the scalar path.  The options' grid is kept.
+// the planned one needs one (rows split over clusters, or the sliced passes): the widest
+// register-resident row mapping that covers the row, else the scalar path.  The options'
+// grid is kept.
 norm_status_t make_fwd_plan_without_workspace(bool layernorm, int64_t M, int64_t N, int dtype,
                                               bool aligned16, const norm_options_t* opt,
                                               Plan* out);

@@ -53,6 +53,7 @@ def test_status_strings():
 
 
 CLUSTER = rn.Options(path=rn.NORM_PATH_CLUSTER)
+SPLIT = rn.Options(path=rn.NORM_PATH_SPLIT)
 
 
 def rms_fwd(**kw):
@@ -111,6 +112,8 @@ def ln_bwd(**kw):
     # the split-row forward, when asked for, needs its workspace (without options a
     # missing or short forward workspace selects a plan that needs none)
     (rms_fwd, dict(M=1024, N=262144, opt=CLUSTER), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(M=4, N=4096, opt=SPLIT), rn.NORM_ERR_NULL_PTR),
+    (rms_fwd, dict(M=4, N=5001, ws=A, ws_bytes=64, opt=SPLIT), rn.NORM_ERR_WORKSPACE_TOO_SMALL),
     (rms_fwd, dict(M=1024, N=262144, ws=A, ws_bytes=64, opt=CLUSTER),
      rn.NORM_ERR_WORKSPACE_TOO_SMALL),
     (ln_fwd, dict(M=1024, N=262144, ws=A + 8, ws_bytes=1 << 20), rn.NORM_ERR_MISALIGNED),
@@ -172,7 +175,6 @@ def test_bad_options_rejected():
     bad = [rn.Options(path=9), rn.Options(lanes_per_row=-1),
            rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=48, vecs_per_lane=1),
            rn.Options(path=rn.NORM_PATH_ROWS, lanes_per_row=8, vecs_per_lane=1),  # cannot cover N
-           rn.Options(path=rn.NORM_PATH_SPLIT),  # forward has no SPLIT path
            rn.Options(dgamma_mode=5),
            rn.Options(cluster_size=64),  # above the largest cluster
            rn.Options(path=rn.NORM_PATH_CLUSTER, cluster_size=3)]  # not a power of two
@@ -215,10 +217,23 @@ def test_plan_shape_classes():
     # the two-pass column-sliced backward remains available
     p = rn.norm_plan(True, False, 2048, 131072, BF16, options=rn.Options(path=rn.NORM_PATH_SPLIT))
     assert p.path == rn.NORM_PATH_SPLIT and p.partial_rows >= 1
-    # misaligned pointers or N not a multiple of the vector fall back to the scalar path
-    assert rn.norm_plan(False, True, 100, 4096, BF16, aligned16=False).path == rn.NORM_PATH_GENERIC
-    assert rn.norm_plan(False, True, 100, 4095, BF16).path == rn.NORM_PATH_GENERIC
+    # misaligned pointers or N not a multiple of the vector fall back to element loads:
+    # the register-resident scalar kernels for short rows, the sliced passes beyond
+    assert rn.norm_plan(False, True, 100, 3000, BF16, aligned16=False).path == rn.NORM_PATH_GENERIC
+    assert rn.norm_plan(False, True, 100, 3071, BF16).path == rn.NORM_PATH_GENERIC
     assert rn.norm_plan(True, True, 100, 7, F32).path == rn.NORM_PATH_GENERIC
+    for N, aligned in ((4096, False), (4095, True), (1 << 22, False)):
+        p = rn.norm_plan(False, True, 100, N, BF16, aligned16=aligned)
+        slices = -(-N // 2048)  # 256 lanes x 8 elements per slice
+        # about 8192 workgroups in all, each with 4 rows or more
+        row_blocks = min(-(-8192 // slices), -(-100 // 4))
+        assert p.path == rn.NORM_PATH_SPLIT and p.grid == slices * row_blocks, (N, p.grid)
+        assert p.workspace_bytes > 0
+    # long rows past the reach of a cluster take the sliced passes in both directions,
+    # spread over many workgroups even for a single row
+    for bwd in (False, True):
+        p = rn.norm_plan(bwd, False, 1, 1 << 22, BF16)
+        assert p.path == rn.NORM_PATH_SPLIT and p.grid == (1 << 22) // 4096, (bwd, p.grid)
     # every plan's lanes x vectors covers the row with less than one vector slot of padding
     for N in (256, 384, 512, 768, 1024, 2048, 4096, 8192, 16384, 65536):
         for dt, epv in ((BF16, 8), (F32, 4)):
@@ -320,7 +335,11 @@ def test_lds_partial_mappings():
     assert rn.norm_plan(True, False, 4096, 3500 * 8, BF16).path == rows
     assert rn.norm_plan(True, True, 4096, 3500 * 8, BF16).path == rn.NORM_PATH_CLUSTER
     assert rn.norm_plan(True, False, 4096, 2500 * 8, BF16).path == rn.NORM_PATH_CLUSTER
-    assert rn.norm_fwd_workspace_size(65536, 4096, True, BF16) == 0
+    # the aligned forward of 4096 bf16 columns needs no workspace; the size query covers
+    # misaligned pointers too, whose plan (element loads, the sliced passes) needs one
+    assert rn.norm_plan(False, True, 65536, 4096, BF16).workspace_bytes == 0
+    assert rn.norm_fwd_workspace_size(65536, 4096, True, BF16) == \
+        rn.norm_plan(False, True, 65536, 4096, BF16, aligned16=False).workspace_bytes > 0
 
 
 def test_type_pairs_plan_like_their_activations():
@@ -390,4 +409,6 @@ def test_noalloc_validation():
     # rows alone is 32 MiB, plus the exchange words
     assert rn.norm_bwd_workspace_size(2048, 131072, True, BF16) > 32 << 20
     assert call(M=2048, N=131072) == rn.NORM_ERR_SCRATCH_TOO_SMALL
-    assert rn.norm_bwd_workspace_size(65536, 4096, True, BF16) <= 32 << 20
+    # the benchmark's LayerNorm [65536, 4096] fits (its 16-byte-aligned plan: 8 MiB of
+    # partial rows; the size query also covers misaligned pointers, which need more)
+    assert rn.norm_plan(True, True, 65536, 4096, BF16).workspace_bytes <= 32 << 20

@@ -96,7 +96,7 @@ def _check_all(w, inp, res, dsum, out):
 
 
 @pytest.mark.parametrize("with_dsum", [False, True], ids=["no-dsum", "dsum"])
-@pytest.mark.parametrize("N", [64, 384, 1000, 4096, 16384, 65536])
+@pytest.mark.parametrize("N", [64, 384, 1000, 4096, 5003, 16384, 65536])
 @pytest.mark.parametrize("dtype,pdtype", PAIRS, ids=PAIR_IDS)
 @pytest.mark.parametrize("kind", ["rms", "ln"])
 def test_fused_residual(device, kind, dtype, pdtype, N, with_dsum):
@@ -124,10 +124,18 @@ def test_fused_residual_every_path(device, kind, dtype, pdtype, path):
     """The residual add and the residual gradient on the split-row, split and scalar paths."""
     N = 8192
     M = 97
-    fwd_opt = rn.Options(path=path) if path != rn.NORM_PATH_SPLIT else None
+    fwd_opt = rn.Options(path=path)
     if path == rn.NORM_PATH_CLUSTER:
         fwd_opt = rn.Options(path=path, cluster_size=4)
         bwd_opt = rn.Options(path=path, cluster_size=4)
     else:
         bwd_opt = rn.Options(path=path)
     _check_all(*_run(device, kind, dtype, pdtype, M, N, True, fwd_opt, bwd_opt))
+
+
+@pytest.mark.parametrize("kind,dtype,M,N", [("rms", "bf16", 2, (1 << 21) + 8),
+                                             ("ln", "f16", 1, (1 << 21) + 5)])
+def test_fused_residual_beyond_a_cluster(device, kind, dtype, M, N):
+    """The residual add and gradient on the sliced passes, at rows no cluster holds: the
+    statistics pass writes the sum, the normalize pass reads it back."""
+    _check_all(*_run(device, kind, dtype, None, M, N, True))

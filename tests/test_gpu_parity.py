@@ -164,8 +164,7 @@ def test_every_mapping(device, kind, dtype, pdtype, direction, lpr, vpl, pipelin
 @pytest.mark.parametrize("N", [256, 384, 4096, 12288])
 def test_forced_paths(device, kind, dtype, pdtype, N, path):
     w = small_workload(kind, dtype, N, M=517, pdtype=pdtype)
-    fwd_opt = rn.Options(path=rn.NORM_PATH_GENERIC) if path == rn.NORM_PATH_GENERIC else None
-    full_check(w, device, rows=np.arange(w.M), fwd_options=fwd_opt,
+    full_check(w, device, rows=np.arange(w.M), fwd_options=rn.Options(path=path),
                bwd_options=rn.Options(path=path))
 
 
@@ -482,10 +481,13 @@ def test_events_and_streams(device):
 
 
 @pytest.mark.parametrize("kind,dtype,M,N", [("rms", "bf16", 64, 262144), ("ln", "bf16", 48, 262144),
-                                             ("rms", "f32", 40, 131072), ("rms", "bf16", 2048, 131072)])
+                                             ("rms", "f32", 40, 131072), ("rms", "bf16", 2048, 131072),
+                                             ("ln", "bf16", 2, (1 << 21) + 8),
+                                             ("rms", "f32", 3, 100003)])
 def test_forward_without_workspace(device, kind, dtype, M, N):
     """The forward's argument list without a workspace (NULL, 0 bytes) works at every row
-    length: rows that the fastest plan splits over a cluster run a plan that needs none."""
+    length: rows that the fastest plan splits over a cluster, or over the sliced passes,
+    run a plan that needs none."""
     import torch
     code = dtype_code(dtype)
     assert rn.norm_fwd_workspace_size(M, N, kind == "ln", code) > 0
