@@ -164,50 +164,71 @@ def _pdtype(x, gamma):
     return x.dtype if gamma is None else gamma.dtype
 
 
+_TYPES = {}
+
+
 def _types(x, gamma):
     """The library's dtype code for activations like x and parameters like gamma."""
+    key = (x.dtype, None if gamma is None else gamma.dtype)
+    code = _TYPES.get(key)
+    if code is not None:
+        return code
     act = _dtype_code(x)
     par = act if gamma is None else _dtype_code(gamma)
     if par == act:
-        return act
-    if par == NORM_DTYPE_F32 and act in (NORM_DTYPE_BF16, NORM_DTYPE_F16):
-        return dtype_mixed(act, par)
-    raise TypeError(f"gamma/beta of {gamma.dtype} with activations of {x.dtype}: use the "
-                    f"activations' type or float32")
+        code = act
+    elif par == NORM_DTYPE_F32 and act in (NORM_DTYPE_BF16, NORM_DTYPE_F16):
+        code = dtype_mixed(act, par)
+    else:
+        raise TypeError(f"gamma/beta of {gamma.dtype} with activations of {x.dtype}: use "
+                        f"the activations' type or float32")
+    _TYPES[key] = code
+    return code
 
 
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
-def _need(t, name, numel, dtype, device):
+def _need(t, name, numel, dtype, dev):
+    """t (unless None) is a contiguous tensor of numel elements of dtype on GPU dev (an
+    index).  One combined test on the common path: these checks run on every call."""
     if t is None:
         return
-    if t.device != device:
-        raise ValueError(f"{name} must be on {device}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.numel() != numel:
+    if t.dtype is not dtype or t.numel() != numel or t.get_device() != dev or \
+            not t.is_contiguous():
+        if t.get_device() != dev:
+            raise ValueError(f"{name} must be on cuda:{dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
         raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
 
 
 def _shape(x):
+    """(M, N, device index) of the activations x."""
     if x.dim() != 2:
         raise ValueError("x must be 2-D [M, N] (reshape leading dimensions into M)")
-    if not x.is_cuda:
+    dev = x.get_device()
+    if dev < 0 or not x.is_cuda:
         raise ValueError("x must be a GPU tensor")
-    return int(x.shape[0]), int(x.shape[1])
+    M, N = x.shape
+    return M, N, dev
 
 
-def _stream(device, stream):
-    torch = _torch()
+_RAW_STREAM = None
+
+
+def _stream(dev, stream):
+    """The raw HIP stream: the given one, else torch's current stream on GPU dev."""
+    global _RAW_STREAM
     if stream is None:
-        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
-        if raw is not None:
-            return raw(device.index if device.index is not None else torch.cuda.current_device())
-        return torch.cuda.current_stream(device).cuda_stream
+        if _RAW_STREAM is None:
+            torch = _torch()
+            _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or \
+                (lambda d: torch.cuda.current_stream(d).cuda_stream)
+        return _RAW_STREAM(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
@@ -215,7 +236,7 @@ def _opt(options):
     return None if options is None else ctypes.byref(options)
 
 
-def _keep_for_stream(ws, device, stream):
+def _keep_for_stream(ws, dev, stream):
     """A workspace the binding allocated lives in torch's caching allocator, which
     tracks it on the current stream.  When the call runs on another stream, mark the
     block as used there too, so that it is not handed to a later allocation before
@@ -223,9 +244,9 @@ def _keep_for_stream(ws, device, stream):
     if ws is None or stream is None:
         return
     torch = _torch()
-    ptr = _stream(device, stream)
-    if ptr != _stream(device, None):
-        ws.record_stream(torch.cuda.ExternalStream(ptr, device=device))
+    ptr = _stream(dev, stream)
+    if ptr != _stream(dev, None):
+        ws.record_stream(torch.cuda.ExternalStream(ptr, device=dev))
 
 
 # ------------------------------------------------------------------- entry points
@@ -240,10 +261,14 @@ _FWD_WS = {}
 
 
 def _aligned16(*tensors):
-    return all(t is None or t.data_ptr() % 16 == 0 for t in tensors)
+    bits = 0
+    for t in tensors:
+        if t is not None:
+            bits |= t.data_ptr()
+    return bits & 15 == 0
 
 
-def _fwd_workspace(M, N, ln, dtype, device, workspace, options, stream, aligned):
+def _fwd_workspace(M, N, ln, dtype, dev, workspace, options, stream, aligned):
     """The caller's workspace (the library checks its size), or a new one of the size the
     call needs with its pointers' alignment (None when it needs none)."""
     if workspace is not None:
@@ -256,8 +281,8 @@ def _fwd_workspace(M, N, ln, dtype, device, workspace, options, stream, aligned)
             _FWD_WS[key] = need
     if need == 0:
         return None, 0
-    ws = _torch().empty(need, dtype=_torch().uint8, device=device)
-    _keep_for_stream(ws, device, stream)
+    ws = _torch().empty(need, dtype=_torch().uint8, device=dev)
+    _keep_for_stream(ws, dev, stream)
     return ws, need
 
 
@@ -265,16 +290,16 @@ def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stre
                  options=None):
     """y = x * rstd * gamma with rstd = 1/sqrt(mean(x^2) + eps) per row; rstd saved if given."""
     torch = _torch()
-    M, N = _shape(x)
-    _need(x, "x", M * N, x.dtype, x.device)
-    _need(y, "y", M * N, x.dtype, x.device)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
-    _need(rstd, "rstd", M, torch.float32, x.device)
+    M, N, dev = _shape(x)
+    _need(x, "x", M * N, x.dtype, dev)
+    _need(y, "y", M * N, x.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
+    _need(rstd, "rstd", M, torch.float32, dev)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream,
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, dev, workspace, options, stream,
                                   _aligned16(x, gamma, y))
     args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
-            _stream(x.device, stream))
+            _stream(dev, stream))
     if options is None:
         _check(lib().norm_rms_fwd(*args), "norm_rms_fwd")
     else:
@@ -286,18 +311,18 @@ def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, work
                 stream=None, options=None):
     """y = (x - mean) * rstd * gamma + beta per row; mean and rstd saved if given."""
     torch = _torch()
-    M, N = _shape(x)
-    _need(x, "x", M * N, x.dtype, x.device)
-    _need(y, "y", M * N, x.dtype, x.device)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
-    _need(beta, "beta", N, _pdtype(x, gamma), x.device)
-    _need(mean, "mean", M, torch.float32, x.device)
-    _need(rstd, "rstd", M, torch.float32, x.device)
+    M, N, dev = _shape(x)
+    _need(x, "x", M * N, x.dtype, dev)
+    _need(y, "y", M * N, x.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
+    _need(beta, "beta", N, _pdtype(x, gamma), dev)
+    _need(mean, "mean", M, torch.float32, dev)
+    _need(rstd, "rstd", M, torch.float32, dev)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream,
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, dev, workspace, options, stream,
                                   _aligned16(x, gamma, beta, y))
     args = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, float(eps),
-            dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
+            dt, _ptr(ws), ws_bytes, _stream(dev, stream))
     if options is None:
         _check(lib().norm_ln_fwd(*args), "norm_ln_fwd")
     else:
@@ -312,30 +337,30 @@ def norm_bwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
                                                 _opt(options)))
 
 
-def _workspace(M, N, ln, dtype, device, workspace, options, stream):
+def _workspace(M, N, ln, dtype, dev, workspace, options, stream):
     """The caller's workspace (the library checks its size), or a new one of the size the
     call needs."""
     if workspace is None:
         torch = _torch()
         need = norm_bwd_workspace_size(M, N, ln, dtype, options)
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
-        _keep_for_stream(workspace, device, stream)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        _keep_for_stream(workspace, dev, stream)
     return workspace, workspace.numel() * workspace.element_size()
 
 
 def norm_rms_bwd(dy, x, gamma, rstd, dx, dgamma, workspace=None, stream=None, options=None):
     """dx and dgamma (overwritten) of RMSNorm from the forward's saved rstd."""
     torch = _torch()
-    M, N = _shape(x)
+    M, N, dev = _shape(x)
     for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
-        _need(t, n, k, x.dtype, x.device)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
-    _need(rstd, "rstd", M, torch.float32, x.device)
-    _need(dgamma, "dgamma", N, torch.float32, x.device)
+        _need(t, n, k, x.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
+    _need(rstd, "rstd", M, torch.float32, dev)
+    _need(dgamma, "dgamma", N, torch.float32, dev)
     dt = _types(x, gamma)
-    ws, ws_bytes = _workspace(M, N, False, dt, x.device, workspace, options, stream)
+    ws, ws_bytes = _workspace(M, N, False, dt, dev, workspace, options, stream)
     args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N, dt,
-            _ptr(ws), ws_bytes, _stream(x.device, stream))
+            _ptr(ws), ws_bytes, _stream(dev, stream))
     if options is None:
         _check(lib().norm_rms_bwd(*args), "norm_rms_bwd")
     else:
@@ -347,17 +372,17 @@ def norm_ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace=None, str
                 options=None):
     """dx, dgamma and dbeta (overwritten) of LayerNorm from the saved mean and rstd."""
     torch = _torch()
-    M, N = _shape(x)
+    M, N, dev = _shape(x)
     for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
-        _need(t, n, k, x.dtype, x.device)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
+        _need(t, n, k, x.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
     for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
                     (dbeta, "dbeta", N)):
-        _need(t, n, k, torch.float32, x.device)
+        _need(t, n, k, torch.float32, dev)
     dt = _types(x, gamma)
-    ws, ws_bytes = _workspace(M, N, True, dt, x.device, workspace, options, stream)
+    ws, ws_bytes = _workspace(M, N, True, dt, dev, workspace, options, stream)
     args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
-            _ptr(dbeta), M, N, dt, _ptr(ws), ws_bytes, _stream(x.device, stream))
+            _ptr(dbeta), M, N, dt, _ptr(ws), ws_bytes, _stream(dev, stream))
     if options is None:
         _check(lib().norm_ln_bwd(*args), "norm_ln_bwd")
     else:
@@ -369,16 +394,16 @@ def norm_ln_bwd_noalloc(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, stream=None
     """norm_ln_bwd on the library's static scratch: no workspace, no allocation (the
     binding allocates nothing either).  Calls that overlap on one device race."""
     torch = _torch()
-    M, N = _shape(x)
+    M, N, dev = _shape(x)
     for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
-        _need(t, n, k, x.dtype, x.device)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
+        _need(t, n, k, x.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
     for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
                     (dbeta, "dbeta", N)):
-        _need(t, n, k, torch.float32, x.device)
+        _need(t, n, k, torch.float32, dev)
     _check(lib().norm_ln_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd),
                                      _ptr(dx), _ptr(dgamma), _ptr(dbeta), M, N,
-                                     _types(x, gamma), _stream(x.device, stream)),
+                                     _types(x, gamma), _stream(dev, stream)),
            "norm_ln_bwd_noalloc")
     return dx, dgamma, dbeta
 
@@ -403,17 +428,17 @@ def norm_rms_fwd_add(x, residual, gamma, y, sum_out, rstd=None, eps: float = 1e-
                      workspace=None, stream=None, options=None):
     """sum_out = x + residual (rounded to x's type); y = RMSNorm(sum_out)."""
     torch = _torch()
-    M, N = _shape(x)
+    M, N, dev = _shape(x)
     for t, n in ((x, "x"), (residual, "residual"), (y, "y"), (sum_out, "sum_out")):
-        _need(t, n, M * N, x.dtype, x.device)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
-    _need(rstd, "rstd", M, torch.float32, x.device)
+        _need(t, n, M * N, x.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
+    _need(rstd, "rstd", M, torch.float32, dev)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, x.device, workspace, options, stream,
+    ws, ws_bytes = _fwd_workspace(M, N, False, dt, dev, workspace, options, stream,
                                   _aligned16(x, residual, gamma, y, sum_out))
     _check(lib().norm_rms_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(sum_out),
                                   _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
-                                  _stream(x.device, stream), _opt(options)), "norm_rms_fwd_add")
+                                  _stream(dev, stream), _opt(options)), "norm_rms_fwd_add")
     return y, sum_out
 
 
@@ -421,19 +446,19 @@ def norm_ln_fwd_add(x, residual, gamma, beta, y, sum_out, mean=None, rstd=None,
                     eps: float = 1e-5, workspace=None, stream=None, options=None):
     """sum_out = x + residual (rounded to x's type); y = LayerNorm(sum_out)."""
     torch = _torch()
-    M, N = _shape(x)
+    M, N, dev = _shape(x)
     for t, n in ((x, "x"), (residual, "residual"), (y, "y"), (sum_out, "sum_out")):
-        _need(t, n, M * N, x.dtype, x.device)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), x.device)
-    _need(beta, "beta", N, _pdtype(x, gamma), x.device)
-    _need(mean, "mean", M, torch.float32, x.device)
-    _need(rstd, "rstd", M, torch.float32, x.device)
+        _need(t, n, M * N, x.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
+    _need(beta, "beta", N, _pdtype(x, gamma), dev)
+    _need(mean, "mean", M, torch.float32, dev)
+    _need(rstd, "rstd", M, torch.float32, dev)
     dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, x.device, workspace, options, stream,
+    ws, ws_bytes = _fwd_workspace(M, N, True, dt, dev, workspace, options, stream,
                                   _aligned16(x, residual, gamma, beta, y, sum_out))
     _check(lib().norm_ln_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
                                  _ptr(sum_out), _ptr(mean), _ptr(rstd), M, N, float(eps), dt,
-                                 _ptr(ws), ws_bytes, _stream(x.device, stream), _opt(options)),
+                                 _ptr(ws), ws_bytes, _stream(dev, stream), _opt(options)),
            "norm_ln_fwd_add")
     return y, sum_out
 
@@ -443,17 +468,17 @@ def norm_rms_bwd_add(dy, sum_in, gamma, rstd, dsum, dx, dgamma, workspace=None, 
     """dx = RMSNorm backward at sum_in (+ dsum, the gradient arriving at the sum, if given);
     dgamma overwritten."""
     torch = _torch()
-    M, N = _shape(sum_in)
+    M, N, dev = _shape(sum_in)
     for t, n in ((dy, "dy"), (sum_in, "sum_in"), (dsum, "dsum"), (dx, "dx")):
-        _need(t, n, M * N, sum_in.dtype, sum_in.device)
-    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), sum_in.device)
-    _need(rstd, "rstd", M, torch.float32, sum_in.device)
-    _need(dgamma, "dgamma", N, torch.float32, sum_in.device)
+        _need(t, n, M * N, sum_in.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), dev)
+    _need(rstd, "rstd", M, torch.float32, dev)
+    _need(dgamma, "dgamma", N, torch.float32, dev)
     dt = _types(sum_in, gamma)
-    ws, ws_bytes = _workspace(M, N, False, dt, sum_in.device, workspace, options, stream)
+    ws, ws_bytes = _workspace(M, N, False, dt, dev, workspace, options, stream)
     _check(lib().norm_rms_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(rstd), _ptr(dsum),
                                   _ptr(dx), _ptr(dgamma), M, N, dt, _ptr(ws), ws_bytes,
-                                  _stream(sum_in.device, stream), _opt(options)),
+                                  _stream(dev, stream), _opt(options)),
            "norm_rms_bwd_add")
     return dx, dgamma
 
@@ -462,18 +487,18 @@ def norm_ln_bwd_add(dy, sum_in, gamma, mean, rstd, dsum, dx, dgamma, dbeta, work
                     stream=None, options=None):
     """dx = LayerNorm backward at sum_in (+ dsum if given); dgamma, dbeta overwritten."""
     torch = _torch()
-    M, N = _shape(sum_in)
+    M, N, dev = _shape(sum_in)
     for t, n in ((dy, "dy"), (sum_in, "sum_in"), (dsum, "dsum"), (dx, "dx")):
-        _need(t, n, M * N, sum_in.dtype, sum_in.device)
-    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), sum_in.device)
+        _need(t, n, M * N, sum_in.dtype, dev)
+    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), dev)
     for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
                     (dbeta, "dbeta", N)):
-        _need(t, n, k, torch.float32, sum_in.device)
+        _need(t, n, k, torch.float32, dev)
     dt = _types(sum_in, gamma)
-    ws, ws_bytes = _workspace(M, N, True, dt, sum_in.device, workspace, options, stream)
+    ws, ws_bytes = _workspace(M, N, True, dt, dev, workspace, options, stream)
     _check(lib().norm_ln_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(mean), _ptr(rstd),
                                  _ptr(dsum), _ptr(dx), _ptr(dgamma), _ptr(dbeta), M, N, dt,
-                                 _ptr(ws), ws_bytes, _stream(sum_in.device, stream),
+                                 _ptr(ws), ws_bytes, _stream(dev, stream),
                                  _opt(options)), "norm_ln_bwd_add")
     return dx, dgamma, dbeta
 
@@ -493,5 +518,5 @@ def norm_stream_reference(kind: int, a, b, dst, stream=None):
             raise ValueError(f"{n} must be contiguous and at least as large as dst")
     _check(lib().norm_stream_reference(int(kind), a.data_ptr(),
                                        b.data_ptr() if b is not None else None, dst.data_ptr(),
-                                       nbytes // 16, _stream(dst.device, stream)),
+                                       nbytes // 16, _stream(dst.get_device(), stream)),
            "norm_stream_reference")
