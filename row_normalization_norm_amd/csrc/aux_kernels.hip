@@ -198,7 +198,8 @@ hipError_t launch_colreduce(const float* part_g, const float* part_b, int64_t P,
   int splits = 1;
   while (splits < smax && splits < P) splits *= 2;
   const int per_block = (kColRedThreads / splits) * (vec4 ? 4 : 1);
-  const dim3 grid((N + per_block - 1) / per_block, part_b ? 2 : 1);
+  const dim3 grid(static_cast<uint32_t>((static_cast<int64_t>(N) + per_block - 1) / per_block),
+                  part_b ? 2 : 1);
 #define RN_COLRED(V, S)                                                                     \
   if (vec4 == V && splits == S) {                                                           \
     hipLaunchKernelGGL((colreduce_kernel<V, S>), grid, dim3(kColRedThreads), 0, s, part_g,  \
@@ -258,10 +259,10 @@ hipError_t launch_stream_reference(bool two_reads, const void* a, const void* b,
 }
 
 hipError_t launch_zero(float* a, float* b, int32_t N, hipStream_t s) {
-  int grid = (N + 255) / 256;
+  int64_t grid = (static_cast<int64_t>(N) + 255) / 256;
   if (grid > 1024) grid = 1024;
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, a, b, N);
+  hipLaunchKernelGGL(zero_kernel, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s, a, b, N);
   return hipGetLastError();
 }
 
