@@ -29,3 +29,33 @@ def test_every_row_length_has_a_plan(dtype, code, epv, kind, backward):
                 # one workgroup or a cluster holds the row in 16-byte vectors
                 assert p.path in (rn.NORM_PATH_ROWS, rn.NORM_PATH_CLUSTER), (N, M, p.path)
     assert not failures, failures[:10]
+
+
+@pytest.mark.parametrize("backward", [False, True], ids=["fwd", "bwd"])
+def test_sliced_plan_geometry(backward):
+    """The sliced passes' plan at row lengths past a cluster and at long rows of elements:
+    the grid covers every (slice, row) once within the grid's y limit, and the workspace
+    holds the per-row table, the per-(row, slice) terms and (backward) the partial rows."""
+    import random
+    rnd = random.Random(7)
+    shapes = [(1, (1 << 31) - 1), (3, (1 << 22) + 8), (65536, 4100), (70000, 5001), (1, 3073),
+              (2, (1 << 20) + 8), (1 << 20, 4099)]
+    shapes += [(rnd.randint(1, 1 << 18), rnd.randint(3073, 1 << 23)) for _ in range(200)]
+    for M, N in shapes:
+        for code, size, epv in ((rn.NORM_DTYPE_BF16, 2, 8), (rn.NORM_DTYPE_F32, 4, 4)):
+            for ln in (False, True):
+                for aligned in (False, True):
+                    p = rn.norm_plan(backward, ln, M, N, code, aligned16=aligned)
+                    vec = aligned and N % epv == 0
+                    if p.path not in (rn.NORM_PATH_SPLIT, rn.NORM_PATH_GENERIC) or p.block != 256:
+                        continue  # a row, cluster or register-resident scalar plan
+                    units = N // epv if vec else N
+                    slices = -(-units // (512 if vec else 2048))
+                    assert p.grid % slices == 0, (M, N, p.grid, slices)
+                    row_blocks = p.grid // slices
+                    assert 1 <= row_blocks <= min(M, 65535)
+                    need = 8 * M + 8 * M * slices
+                    if backward:
+                        assert 1 <= p.partial_rows <= min(M, 65535)
+                        need += 4 * p.partial_rows * N * (2 if ln else 1)
+                    assert p.workspace_bytes >= need, (M, N, p.workspace_bytes, need)
