@@ -4,8 +4,8 @@ Each case runs forward + backward eagerly for the reference outputs, captures th
 calls into a graph, then replays it several times with unrelated eager work and
 synchronisations between the replays (the outputs are cleared by fill kernels before
 each replay), and requires every replay to reproduce the eager outputs bit for bit.
-The cases cover every kernel family, the pipelined row kernels and the split-row one
-(with its exchange-slot fill kernel) included.
+The cases cover every kernel family, the pipelined row kernels, the split-row one (with
+its exchange-slot fill kernel) and the sliced passes included.
 """
 import numpy as np
 import pytest
@@ -26,6 +26,8 @@ CASES = [
     ("ln", "bf16", 16, 131072, False),     # a whole row per workgroup forward
     ("rms", "bf16", 8, 262144, False),     # forward and backward on the split-row path
     ("ln", "bf16", 333, 1000, False),      # N not a multiple of 8: scalar and split paths
+    ("rms", "bf16", 2, (1 << 21) + 8, False),  # rows past a cluster: the sliced passes
+    ("ln", "bf16", 40, 5003, True),         # long rows of elements: sliced, residual add
     ("ln", "bf16", 512, 4096, True),       # residual-add entry points
     ("rms", "f32", 700, 12288, True),
 ]

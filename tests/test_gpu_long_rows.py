@@ -104,3 +104,55 @@ def test_sliced_passes_are_deterministic(device):
         assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a,
                            b.view(torch.int16) if b.dtype == torch.bfloat16 else b)
     check_all_rows(run, inputs)
+
+
+@pytest.mark.parametrize("N", [5000, 5003])
+def test_sliced_degenerate_rows_and_nan(device, N):
+    """On the sliced passes: RMSNorm of a zero row is 0, LayerNorm of a constant row is
+    beta, and a NaN reaches its own row's outputs only."""
+    import torch
+    eps = 1e-5
+    M = 5
+    x = torch.randn(M, N, device=device).to(torch.bfloat16)
+    x[0] = 0.0
+    x[1] = 2.5
+    x[3, N // 2] = float("nan")
+    g = torch.full((N,), 1.5, dtype=torch.bfloat16, device=device)
+    b = (torch.arange(N, device=device) % 7 * 0.125).to(torch.bfloat16)
+    y = torch.empty_like(x)
+    rstd = torch.empty(M, device=device)
+    mean = torch.empty(M, device=device)
+    rn.norm_rms_fwd(x, g, y, rstd, eps=eps, options=SPLIT)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y[0]).item() == 0
+    assert abs(rstd[0].item() - eps ** -0.5) <= 1e-5 * eps ** -0.5
+    assert torch.isnan(y[3].float()).all()
+    others = torch.tensor([0, 1, 2, 4], device=device)
+    assert not torch.isnan(y[others].float()).any()
+    rn.norm_ln_fwd(x, g, b, y, mean, rstd, eps=eps, options=SPLIT)
+    torch.cuda.synchronize()
+    assert torch.equal(y[0].float(), b.float()), "a zero row gives beta"
+    # a constant 2.5: its mean is 2.5 only up to the rounding of sum * (1/N) when 1/N is
+    # not a power of two, so beta within the bf16 bound
+    assert torch.all((y[1].float() - b.float()).abs() <= 2.0 ** -7), "a constant row gives beta"
+    assert torch.isnan(y[3].float()).all()
+    assert not torch.isnan(y[others].float()).any()
+
+
+def test_sliced_empty_batch(device):
+    """No rows at a length the sliced passes would take: nothing is written but the
+    column sums, which are zero."""
+    import torch
+    N = (1 << 21) + 8
+    x = torch.empty(0, N, dtype=torch.bfloat16, device=device)
+    g = torch.ones(N, dtype=torch.bfloat16, device=device)
+    b = torch.zeros(N, dtype=torch.bfloat16, device=device)
+    y = torch.empty_like(x)
+    mean = torch.empty(0, device=device)
+    rstd = torch.empty(0, device=device)
+    dg = torch.full((N,), 7.0, device=device)
+    db = torch.full((N,), 7.0, device=device)
+    rn.norm_ln_fwd(x, g, b, y, mean, rstd)
+    rn.norm_ln_bwd(x, x, g, mean, rstd, torch.empty_like(x), dg, db)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dg).item() == 0 and torch.count_nonzero(db).item() == 0
