@@ -93,13 +93,17 @@ typedef enum norm_status {
 
 /* ------------------------------------------------------------------ forward */
 
-/* Bytes of workspace the fastest forward plan for this shape uses: 0 except for rows
- * long enough to be split over several workgroups, where it holds their per-row partial
- * sums (a few KiB to a few MiB).  The forward's workspace is optional: a call given a
- * NULL workspace or fewer bytes than this runs a plan that needs none (a whole row per
- * workgroup up to 16384 16-byte vectors, else the scalar path), slower for such rows but
- * with the same results within the stated tolerances.  A pure function of its
- * arguments: no HIP call; valid on any gfx950 device. */
+/* Bytes of workspace the fastest forward plan for this shape uses, for either pointer
+ * alignment: 0 except for rows long enough to be split over several workgroups, where
+ * it holds their per-row partial sums (a few KiB to a few MiB), and for long rows that
+ * are not whole 16-byte vectors or run past 2^17 of them (the sliced passes: 16 bytes
+ * per row and slice of 2048 to 4096 elements, plus 8 per row).  The forward's workspace
+ * is optional: a call given a NULL workspace or fewer bytes than its plan needs runs a
+ * plan that needs none (a whole row per workgroup up to 16384 16-byte vectors, else one
+ * workgroup looping over each row with element loads), slower for such rows, much
+ * slower for a few very long rows, but with the same results within the stated
+ * tolerances.  A pure function of its arguments: no HIP call; valid on any gfx950
+ * device. */
 size_t norm_fwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtype_t dtype);
 
 /* RMSNorm forward.  x, gamma, y: `dtype`; rstd: float [M], or NULL to not save it.
@@ -107,7 +111,7 @@ size_t norm_fwd_workspace_size(int64_t M, int64_t N, int is_layernorm, norm_dtyp
  * least norm_fwd_workspace_size(M, N, 0, dtype) bytes the fastest plan runs, else one
  * that needs no workspace (see there).  Its contents on entry do not matter and it must
  * stay alive until the call has completed on `stream`.  With the _ex variant forcing
- * NORM_PATH_CLUSTER the workspace is required (NORM_ERR_NULL_PTR /
+ * NORM_PATH_CLUSTER or NORM_PATH_SPLIT the workspace is required (NORM_ERR_NULL_PTR /
  * NORM_ERR_WORKSPACE_TOO_SMALL otherwise). */
 norm_status_t norm_rms_fwd(const void* x, const void* gamma, void* y, float* rstd,
                            int64_t M, int64_t N, float eps, norm_dtype_t dtype,
@@ -179,10 +183,14 @@ typedef enum norm_dgamma_mode {
 typedef enum norm_path {
   NORM_PATH_AUTO = 0,      /* the planner's choice */
   NORM_PATH_ROWS = 1,      /* register-resident rows: lanes_per_row lanes hold one row */
-  NORM_PATH_SPLIT = 2,     /* backward for rows too long to keep per-column partials in
-                              registers: a per-row reduction pass, then a
-                              column-sliced pass for dx and the partials */
-  NORM_PATH_GENERIC = 3,   /* scalar loads, any N and alignment */
+  NORM_PATH_SPLIT = 2,     /* the sliced passes: each row cut into column slices, every
+                              pass on a (slice, row block) grid, a per-row merge between
+                              them.  Forward: statistics, merge, normalize (x read
+                              twice).  Backward (16-byte vectors): row sums, merge, then
+                              dx and the partials (x and dy read twice).  Needs a
+                              workspace in both directions */
+  NORM_PATH_GENERIC = 3,   /* element loads, any N and alignment (the backward's long
+                              rows take the sliced passes over elements) */
   NORM_PATH_CLUSTER = 4    /* long rows split over a cluster of workgroups, each owning
                               a column slice and exchanging per-row partial sums through
                               the workspace (a member that waits too long for another's
