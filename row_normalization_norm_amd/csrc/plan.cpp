@@ -278,11 +278,8 @@ bool plan_cluster(bool backward, bool layernorm, int64_t M, int64_t N, int64_t n
   return true;
 }
 
-// Sliced passes on a (slices, row blocks) grid for rows too long for a workgroup or a
-// cluster, and for long rows that are not whole vectors: the forward (SPLIT) and the
-// backward (SPLIT for 16-byte vectors, else GENERIC with vpl = 0).  The options' grid
-// sets the row blocks of every pass.  Workspace: the per-row table [M, 2], the
-// per-(row, slice) terms [M, slices, 2], then the backward's partial rows.
+// Row blocks of a sliced pass: the options' grid if set, else `want`, within [1, M] and
+// the grid's y limit.
 int64_t split_row_blocks(int64_t M, int64_t want, const norm_options_t& o) {
   int64_t rb = o.grid ? o.grid : want;
   if (rb > kMaxGridY) rb = kMaxGridY;
@@ -291,6 +288,11 @@ int64_t split_row_blocks(int64_t M, int64_t want, const norm_options_t& o) {
   return rb;
 }
 
+// Sliced passes on a (slices, row blocks) grid for rows too long for a workgroup or a
+// cluster, and for long rows that are not whole vectors: the forward (SPLIT) and the
+// backward (SPLIT for 16-byte vectors, else GENERIC with vpl = 0).  Workspace: the
+// per-row table [M, 2], the per-(row, slice) terms [M, slices, 2], then the backward's
+// partial rows (one per row block of its column pass).
 void plan_split(bool backward, bool layernorm, int64_t M, int64_t N, int64_t nvec, bool vec,
                 const norm_options_t& o, Plan& p) {
   p.path = (vec || !backward) ? NORM_PATH_SPLIT : NORM_PATH_GENERIC;
