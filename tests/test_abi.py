@@ -412,3 +412,14 @@ def test_noalloc_validation():
     # the benchmark's LayerNorm [65536, 4096] fits (its 16-byte-aligned plan: 8 MiB of
     # partial rows; the size query also covers misaligned pointers, which need more)
     assert rn.norm_plan(True, True, 65536, 4096, BF16).workspace_bytes <= 32 << 20
+
+
+def test_binding_rejects_host_tensors():
+    """The binding's first check, made before any GPU call: activations must live on a GPU."""
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.ones(64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        rn.norm_rms_fwd(x, g, torch.empty_like(x))
+    with pytest.raises(ValueError, match="2-D"):
+        rn.norm_rms_fwd(x.view(-1), g, x.view(-1))
