@@ -675,6 +675,10 @@ def main():
     ap.add_argument("--all", metavar="JSON", help="also time every workload, write a table")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only time a plain device copy of BYTES and print it")
+    ap.add_argument("--stream-reference", type=int, metavar="BYTES",
+                    help="only time the streaming reference kernel (copy, then two reads "
+                         "and one write) over BYTES per stream, --steps launches per "
+                         "rotating buffer set, and print it")
     ap.add_argument("--dgamma-compare", metavar="JSON",
                     help="only time the backward with the two-stage and the atomic dgamma "
                          "reductions on rms1, ln2, rms3 and sweep points up to N=8192, "
@@ -710,6 +714,17 @@ def main():
     device = torch.device("cuda:0")
     if args.copy_probe:
         print(json.dumps(copy_probe(args.copy_probe, args.steps, device)), flush=True)
+        return
+
+    if args.stream_reference:
+        nb = args.stream_reference
+        out = {"bytes_per_stream": nb}
+        for key, two in (("copy", False), ("two_reads_one_write", True)):
+            ms = stream_reference_ms(nb, device, two_reads=two, reps=args.steps)
+            moved = (3 if two else 2) * ((nb + 15) // 16 * 16)
+            out[key] = {"us_per_launch": round(ms * 1e3, 3),
+                        "GBs": round(moved / (ms * 1e-3) / 1e9, 1)}
+        print(json.dumps(out), flush=True)
         return
 
     if args.dgamma_compare:
