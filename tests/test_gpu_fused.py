@@ -12,8 +12,8 @@ import pytest
 import gen
 import oracle
 import row_normalization_norm_amd as rn
-from parity import (TOL_DGAMMA, TOL_F32, TOL_STAT, _check, dx_term_scale, out_tol,
-                    rows_to_host64, to_device, to_host64)
+from parity import (TOL_DGAMMA, TOL_F32, TOL_STAT, _check, dgamma_scale, fp32_dx_scale,
+                    out_tol, rows_to_host64, to_device, to_host64)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,21 +78,20 @@ def _check_all(w, inp, res, dsum, out):
         dg_ref, db_ref, sg, sb = orc.ln_dgamma_dbeta(inp["dy"], s_bits, w.eps)
         _check("dbeta", out["db"].cpu().numpy(), db_ref, TOL_DGAMMA,
                scale=np.maximum(np.abs(db_ref), sb))
-    norm_dx = dx_ref
     if dsum is not None:
         ds64 = dsum.astype(np.float64) if w.dtype != "bf16" else \
             gen.bf16_to_f32(dsum).astype(np.float64)
         dx_ref = dx_ref + ds64
     dx = rows_to_host64(out["dx"], rows)
-    if w.dtype == "f32" and N == 1:
-        # one-element rows: the plain backward's term-scaled fp32 bound, on the sum,
-        # widened by the added gradient
-        terms = dx_term_scale(w, {**inp, "x": s_bits}, rows, norm_dx, orc)
-        _check("dx", dx, dx_ref, TOL_F32, scale=np.maximum(terms, np.abs(dx_ref)))
+    if w.dtype == "f32":
+        # the plain backward's fp32 bound, taken at the sum
+        _check("dx", dx, dx_ref, TOL_F32,
+               scale=fp32_dx_scale(w, {**inp, "x": s_bits}, rows, dx, dx_ref, orc))
     else:
         _check("dx", dx, dx_ref, out_tol(w.dtype))
-    _check("dgamma", out["dg"].cpu().numpy(), dg_ref, TOL_DGAMMA,
-           scale=np.maximum(np.abs(dg_ref), sg))
+    dg = out["dg"].cpu().numpy()
+    _check("dgamma", dg, dg_ref, TOL_DGAMMA,
+           scale=dgamma_scale(w, {**inp, "x": s_bits}, dg, dg_ref, sg, orc))
 
 
 @pytest.mark.parametrize("with_dsum", [False, True], ids=["no-dsum", "dsum"])

@@ -22,7 +22,7 @@ import plan_cases
 
 pytestmark = pytest.mark.gpu
 
-SMALL_N = (1, 7, 64, 100, 256, 384, 512, 768, 770, 1000, 1024, 2048, 4095, 4096, 8190, 8192,
+SMALL_N = (1, 2, 3, 7, 64, 100, 256, 384, 512, 768, 770, 1000, 1024, 2048, 4095, 4096, 8190, 8192,
            8195, 16384, 32768, 65536, 131072)
 
 

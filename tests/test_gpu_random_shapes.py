@@ -46,3 +46,19 @@ def test_random_shape(device, kind, dtype, pdtype, M, N):
 
 def _code(d):
     return {"bf16": rn.NORM_DTYPE_BF16, "f32": rn.NORM_DTYPE_F32, "f16": rn.NORM_DTYPE_F16}[d]
+
+
+# Cases a seeded random search over forced plans turned up, where the plain relative
+# bounds do not hold for fp32 arithmetic (LayerNorm rows of two elements; a column of a
+# single long row whose x sits at the row's mean): held to the bounds that account for
+# the cancellation and for the mean's rounding.
+FOUND = [("ln", "f32", None, 590, 2, None), ("ln", "bf16", "f32", 1, 74776, rn.NORM_PATH_GENERIC)]
+
+
+@pytest.mark.parametrize("kind,dtype,pdtype,M,N,path", FOUND,
+                         ids=[f"{k}-{d}{'+' + p if p else ''}-{m}x{n}" for k, d, p, m, n, _ in FOUND])
+def test_found_cases(device, kind, dtype, pdtype, M, N, path):
+    opt = rn.Options(path=path) if path else None
+    w = small_workload(kind, dtype, N, M=M, pdtype=pdtype)
+    full_check(w, device, rows=np.arange(M), fwd_options=opt, bwd_options=opt)
+
