@@ -62,3 +62,12 @@ def test_found_cases(device, kind, dtype, pdtype, M, N, path):
     w = small_workload(kind, dtype, N, M=M, pdtype=pdtype)
     full_check(w, device, rows=np.arange(M), fwd_options=opt, bwd_options=opt)
 
+
+@pytest.mark.parametrize("N", [64, 1024, 8192])
+@pytest.mark.parametrize("kind", ["rms", "ln"])
+def test_rows_with_a_large_mean(device, kind, N):
+    """fp32 rows whose mean is a hundred times their spread: x - mean loses bits before
+    rstd scales it up, so many LayerNorm dx elements are ill-conditioned and held to their
+    sensitivity; RMSNorm has no mean to subtract and stays on the literal rule."""
+    w = small_workload(kind, "f32", N, M=max(8, 400_000 // N), x_mean=5.0, x_std=0.05)
+    full_check(w, device, rows=np.arange(w.M))

@@ -8,6 +8,9 @@ definitions give them) and against planted mistakes:
   1e-5 * max(1, |ref|) there but meets 1e-5 of the element's sensitivity S to its terms
   and to the row's mean; well-conditioned elements stay on the literal rule, and a
   dropped term still fails.
+* fp32 LayerNorm y of rows whose mean is large next to their spread: y = (x - mean) *
+  rstd * gamma + beta carries the mean's rounding times rstd; held to 1e-5 of its
+  sensitivity there, the literal rule elsewhere.
 * LayerNorm dgamma of a column whose x sits at its row's mean: the term dy * xhat is
   near zero and carries the mean's rounding, so the 1e-4 relative rule fails for fp32
   arithmetic; the floor from the mean's own bound admits it, and a dgamma computed
@@ -20,7 +23,8 @@ import numpy as np
 
 import gen
 import oracle
-from parity import KAPPA, TOL_DGAMMA, TOL_F32, dgamma_scale, dx_terms, fp32_dx_scale
+from parity import (KAPPA, TOL_DGAMMA, TOL_F32, dgamma_scale, dx_terms, fp32_dx_scale,
+                    fp32_y_scale, y_terms)
 from test_gpu_parity import small_workload
 
 F = np.float32
@@ -143,3 +147,47 @@ def test_ln_dgamma_floor_admits_the_means_rounding_only():
     # RMSNorm's dgamma has no mean: its scale is the plain one
     wr = gen.Workload("rms_f32_1x4", "rms", "f32", 1, 4, 1e-5, config=9)
     assert np.array_equal(dgamma_scale(wr, inp, wrong, ref, sg, orc), np.maximum(np.abs(ref), sg))
+
+
+def _ln_fwd_fp32(x, gamma, beta, eps):
+    x, gamma, beta = x.astype(F), gamma.astype(F), beta.astype(F)
+    n = F(x.shape[1])
+    mu = (x.sum(axis=1, dtype=F) / n).astype(F)
+    d = x - mu[:, None]
+    var = ((d * d).sum(axis=1, dtype=F) / n).astype(F)
+    r = (F(1) / np.sqrt(var + F(eps))).astype(F)
+    return (d * r[:, None] * gamma[None, :] + beta[None, :]).astype(np.float64)
+
+
+def test_ln_forward_rows_with_a_large_mean():
+    w = gen.Workload("ln_f32_4096x64", "ln", "f32", 4096, 64, 1e-5, x_mean=5.0, x_std=0.05,
+                     config=9)
+    inp = gen.make_inputs(w)
+    orc = oracle.get()
+    rows = np.arange(w.M)
+    ref, _, _ = orc.ln_fwd(inp["x"], inp["gamma"], inp["beta"], w.eps)
+    y = _ln_fwd_fp32(inp["x"], inp["gamma"], inp["beta"], w.eps)
+    err = np.abs(y - ref)
+    literal = TOL_F32 * np.maximum(1.0, np.abs(ref))
+    miss = err > literal
+    assert np.count_nonzero(miss) > 100
+    scale = fp32_y_scale(w, inp, rows, y, ref, orc)
+    assert np.all(err <= TOL_F32 * scale)
+    sens = y_terms(w, inp, rows, orc)
+    ill = sens > KAPPA * np.maximum(1.0, np.abs(ref))
+    assert np.all(ill[miss])
+    # the unbiased variance (a plausible slip: rstd off by sqrt(64/63)) is caught, and so is
+    # a dropped beta
+    x64 = inp["x"].astype(np.float64)
+    xc = x64 - x64.mean(axis=1, keepdims=True)
+    r_unb = 1.0 / np.sqrt((xc * xc).sum(axis=1, keepdims=True) / (w.N - 1) + w.eps)
+    for bad in (xc * r_unb * inp["gamma"] + inp["beta"], y - inp["beta"][None, :]):
+        sb = fp32_y_scale(w, inp, rows, bad, ref, orc)
+        assert np.count_nonzero(np.abs(bad - ref) > TOL_F32 * sb) > bad.size // 2
+    # centred rows of the same spread are well-conditioned: the literal rule holds
+    w0 = gen.Workload("ln_f32_4096x64", "ln", "f32", 4096, 64, 1e-5, x_mean=0.0, x_std=0.05,
+                      config=9)
+    i0 = gen.make_inputs(w0)
+    r0, _, _ = orc.ln_fwd(i0["x"], i0["gamma"], i0["beta"], w0.eps)
+    y0 = _ln_fwd_fp32(i0["x"], i0["gamma"], i0["beta"], w0.eps)
+    assert np.all(np.abs(y0 - r0) <= 0.5 * TOL_F32 * np.maximum(1.0, np.abs(r0)))
