@@ -143,3 +143,34 @@ def test_fused_residual_beyond_a_cluster(device, kind, dtype, M, N):
     """The residual add and gradient on the sliced passes, at rows no cluster holds: the
     statistics pass writes the sum, the normalize pass reads it back."""
     _check_all(*_run(device, kind, dtype, None, M, N, True))
+
+
+def test_fused_random_forced_plans(device):
+    """The residual entry points under seeded random options (the draws of
+    test_gpu_random_options with another seed), with and without the gradient at the
+    sum; draws the planner or the entry point refuses are left out."""
+    from test_gpu_random_options import _CODE, _cases, _describe
+    rng = np.random.default_rng(7)
+    ran = 0
+    for i, kind, dtype, pdtype, M, N, fo, bo, _, _ in _cases(20261204, 400):
+        code = rn.dtype_mixed(_CODE[dtype], _CODE[pdtype]) if pdtype else _CODE[dtype]
+        try:
+            for bwd, o in ((False, fo), (True, bo)):
+                rn.norm_plan(bwd, kind == "ln", M, N, code, True, o)
+        except rn.NormError:
+            continue
+        with_dsum = bool(rng.integers(2))
+        name = (f"case {i}: {kind} {dtype}{'+' + pdtype if pdtype else ''} {M}x{N}, "
+                f"dsum {with_dsum}; forward [{_describe(fo)}], backward [{_describe(bo)}]")
+        print(name, flush=True)
+        try:
+            got = _run(device, kind, dtype, pdtype, M, N, with_dsum, fo, bo)
+        except rn.NormError as e:
+            print(f"  refused: {e}", flush=True)
+            continue
+        try:
+            _check_all(*got)
+        except AssertionError as e:
+            raise AssertionError(f"{name}: {e}") from None
+        ran += 1
+    assert ran >= 100, f"only {ran} drawn cases ran"
