@@ -1,7 +1,8 @@
 """Parity under options drawn at random (seeded): a forced path (register rows with a
 drawn mapping and kernel, sliced passes, element loads, cluster with a drawn size, rows
 per step and wait), a drawn grid, now and then an atomic dgamma, on drawn shapes, type
-pairs and data (means up to 5, spreads from 0.05 to 3).  Draws the planner refuses are
+pairs and data (means up to 5, spreads from 0.05 to 3), x and dy now and then at an
+element offset (not 16-byte aligned).  Draws the planner refuses are
 left out; every other one must match the oracle on every row, forward and backward.
 One test walks the cases in order and names the first that fails."""
 import numpy as np
@@ -68,20 +69,25 @@ def _cases(seed, n):
 
 def test_random_forced_plans(device):
     ran = 0
+    offsets = np.random.default_rng(5)
     for i, kind, dtype, pdtype, M, N, fo, bo, x_mean, x_std in _cases(20261203, 600):
         code = rn.dtype_mixed(_CODE[dtype], _CODE[pdtype]) if pdtype else _CODE[dtype]
+        # one case in five puts x and dy at an element offset: not 16-byte aligned
+        off = int(offsets.integers(1, 8)) if offsets.random() < 0.2 else 0
+        aligned = off * (4 if dtype == "f32" else 2) % 16 == 0
         try:
             for bwd, o in ((False, fo), (True, bo)):
-                rn.norm_plan(bwd, kind == "ln", M, N, code, True, o)
+                rn.norm_plan(bwd, kind == "ln", M, N, code, aligned, o)
         except rn.NormError:
             continue  # a draw the planner refuses (a mapping that does not cover N, ...)
         name = (f"case {i}: {kind} {dtype}{'+' + pdtype if pdtype else ''} {M}x{N}, "
-                f"x ~ N({x_mean}, {x_std}); forward [{_describe(fo)}], "
-                f"backward [{_describe(bo)}]")
+                f"x ~ N({x_mean}, {x_std}), x and dy offset by {off}; forward "
+                f"[{_describe(fo)}], backward [{_describe(bo)}]")
         print(name, flush=True)
         w = small_workload(kind, dtype, N, M=M, x_mean=x_mean, x_std=x_std, pdtype=pdtype)
         try:
-            full_check(w, device, rows=np.arange(M), fwd_options=fo, bwd_options=bo)
+            full_check(w, device, rows=np.arange(M), fwd_options=fo, bwd_options=bo,
+                       x_offset=off)
         except AssertionError as e:
             raise AssertionError(f"{name}: {e}") from None
         ran += 1
