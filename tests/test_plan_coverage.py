@@ -59,3 +59,43 @@ def test_sliced_plan_geometry(backward):
                         assert 1 <= p.partial_rows <= min(M, 65535)
                         need += 4 * p.partial_rows * N * (2 if ln else 1)
                     assert p.workspace_bytes >= need, (M, N, p.workspace_bytes, need)
+
+
+def test_forced_options_are_honoured():
+    """The seeded draws of forced options the GPU tests run (test_gpu_random_options):
+    every draw the planner accepts takes the path, mapping, cluster size and rows per
+    step it was given, and enough of them are accepted for those tests to mean something.
+    A forced cluster may still end on the sliced passes only when the cluster does not
+    fit the device, which the planner reports through norm_cluster_resident."""
+    from test_gpu_random_options import _CODE, _cases
+    accepted = 0
+    for i, kind, dtype, pdtype, M, N, fo, bo, _, _ in _cases(20261203, 600):
+        code = rn.dtype_mixed(_CODE[dtype], _CODE[pdtype]) if pdtype else _CODE[dtype]
+        plans = []
+        try:
+            for bwd, o in ((False, fo), (True, bo)):
+                plans.append((bwd, o, rn.norm_plan(bwd, kind == "ln", M, N, code, True, o)))
+        except rn.NormError as e:
+            assert e.status == rn.NORM_ERR_BAD_OPTION, (i, str(e))
+            continue
+        accepted += 1
+        for bwd, o, p in plans:
+            if o is None or o.path == rn.NORM_PATH_AUTO:
+                continue
+            where = (i, bwd, kind, dtype, M, N)
+            if o.path == rn.NORM_PATH_GENERIC and bwd:
+                # the backward's long rows of elements take the sliced passes over elements
+                assert p.path in (rn.NORM_PATH_GENERIC, rn.NORM_PATH_SPLIT), where
+            else:
+                assert p.path == o.path, (where, p.path)
+            if o.path == rn.NORM_PATH_ROWS:
+                if o.lanes_per_row:
+                    assert p.lanes_per_row == o.lanes_per_row, where
+                if o.vecs_per_lane:
+                    assert p.vecs_per_lane == o.vecs_per_lane, where
+            if o.path == rn.NORM_PATH_CLUSTER:
+                if o.cluster_size:
+                    assert p.cluster_size == o.cluster_size, where
+                if o.cluster_rows:
+                    assert p.cluster_rows == o.cluster_rows, where
+    assert accepted >= 150, accepted
