@@ -124,7 +124,11 @@ def lib() -> ctypes.CDLL:
         # library (which names the soname) came first: torch's device pointers and
         # streams would then be foreign to it.  Importing torch first makes this library
         # bind to torch's runtime.
-        _torch()
+        torch = _torch()
+        global _F32, _RAW_STREAM
+        _F32 = torch.float32
+        _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or \
+            (lambda d: torch.cuda.current_stream(d).cuda_stream)
         handle = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(handle, name)
@@ -160,41 +164,40 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bfloat16, float16 or float32)")
 
 
-def _pdtype(x, gamma):
-    return x.dtype if gamma is None else gamma.dtype
-
-
 _TYPES = {}
+_F32 = None
 
 
-def _types(x, gamma):
-    """The library's dtype code for activations like x and parameters like gamma."""
-    key = (x.dtype, None if gamma is None else gamma.dtype)
+def _types(xd, gd):
+    """The library's dtype code for activations of dtype xd and parameters of dtype gd."""
+    key = (xd, gd)
     code = _TYPES.get(key)
     if code is not None:
         return code
-    act = _dtype_code(x)
-    par = act if gamma is None else _dtype_code(gamma)
+    torch = _torch()
+    codes = {torch.bfloat16: NORM_DTYPE_BF16, torch.float32: NORM_DTYPE_F32,
+             torch.float16: NORM_DTYPE_F16}
+    for d in (xd, gd):
+        if d not in codes:
+            raise TypeError(f"unsupported dtype {d} (bfloat16, float16 or float32)")
+    act, par = codes[xd], codes[gd]
     if par == act:
         code = act
     elif par == NORM_DTYPE_F32 and act in (NORM_DTYPE_BF16, NORM_DTYPE_F16):
         code = dtype_mixed(act, par)
     else:
-        raise TypeError(f"gamma/beta of {gamma.dtype} with activations of {x.dtype}: use "
+        raise TypeError(f"gamma/beta of {gd} with activations of {xd}: use "
                         f"the activations' type or float32")
     _TYPES[key] = code
     return code
 
 
-def _ptr(t):
-    return None if t is None else t.data_ptr()
-
-
 def _need(t, name, numel, dtype, dev):
-    """t (unless None) is a contiguous tensor of numel elements of dtype on GPU dev (an
-    index).  One combined test on the common path: these checks run on every call."""
+    """The device address of t (None when t is None) after checking that it is a
+    contiguous tensor of numel elements of dtype on GPU dev (an index).  One combined
+    test on the common path: these checks run on every call."""
     if t is None:
-        return
+        return None
     if t.dtype is not dtype or t.numel() != numel or t.get_device() != dev or \
             not t.is_contiguous():
         if t.get_device() != dev:
@@ -204,17 +207,18 @@ def _need(t, name, numel, dtype, dev):
         if t.dtype != dtype:
             raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
         raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return t.data_ptr()
 
 
 def _shape(x):
     """(M, N, device index) of the activations x."""
-    if x.dim() != 2:
+    shape = x.shape
+    if len(shape) != 2:
         raise ValueError("x must be 2-D [M, N] (reshape leading dimensions into M)")
     dev = x.get_device()
-    if dev < 0 or not x.is_cuda:
+    if dev < 0:
         raise ValueError("x must be a GPU tensor")
-    M, N = x.shape
-    return M, N, dev
+    return shape[0], shape[1], dev
 
 
 _RAW_STREAM = None
@@ -222,12 +226,7 @@ _RAW_STREAM = None
 
 def _stream(dev, stream):
     """The raw HIP stream: the given one, else torch's current stream on GPU dev."""
-    global _RAW_STREAM
     if stream is None:
-        if _RAW_STREAM is None:
-            torch = _torch()
-            _RAW_STREAM = getattr(torch._C, "_cuda_getCurrentRawStream", None) or \
-                (lambda d: torch.cuda.current_stream(d).cuda_stream)
         return _RAW_STREAM(dev)
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
@@ -260,19 +259,12 @@ def norm_fwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
 _FWD_WS = {}
 
 
-def _aligned16(*tensors):
-    bits = 0
-    for t in tensors:
-        if t is not None:
-            bits |= t.data_ptr()
-    return bits & 15 == 0
-
-
 def _fwd_workspace(M, N, ln, dtype, dev, workspace, options, stream, aligned):
-    """The caller's workspace (the library checks its size), or a new one of the size the
-    call needs with its pointers' alignment (None when it needs none)."""
+    """(address, bytes, tensor) of the caller's workspace (the library checks its size),
+    or of a new one of the size the call needs with its pointers' alignment (None, 0,
+    None when it needs none)."""
     if workspace is not None:
-        return workspace, workspace.numel() * workspace.element_size()
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
     key = (M, N, ln, dtype, aligned)
     need = _FWD_WS.get(key) if options is None else None
     if need is None:
@@ -280,53 +272,70 @@ def _fwd_workspace(M, N, ln, dtype, dev, workspace, options, stream, aligned):
         if options is None:
             _FWD_WS[key] = need
     if need == 0:
-        return None, 0
-    ws = _torch().empty(need, dtype=_torch().uint8, device=dev)
+        return None, 0, None
+    torch = _torch()
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
     _keep_for_stream(ws, dev, stream)
-    return ws, need
+    return ws.data_ptr(), need, ws
+
+
+def _fail(status, where):
+    raise NormError(status, where)
 
 
 def norm_rms_fwd(x, gamma, y, rstd=None, eps: float = 1e-6, workspace=None, stream=None,
                  options=None):
     """y = x * rstd * gamma with rstd = 1/sqrt(mean(x^2) + eps) per row; rstd saved if given."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(x)
-    _need(x, "x", M * N, x.dtype, dev)
-    _need(y, "y", M * N, x.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
-    _need(rstd, "rstd", M, torch.float32, dev)
-    dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, dev, workspace, options, stream,
-                                  _aligned16(x, gamma, y))
-    args = (_ptr(x), _ptr(gamma), _ptr(y), _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
-            _stream(dev, stream))
+    xd = x.dtype
+    gd = xd if gamma is None else gamma.dtype
+    px = _need(x, "x", M * N, xd, dev)
+    py = _need(y, "y", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _fwd_workspace(M, N, False, dt, dev, workspace, options, stream,
+                                  ((px or 0) | (pg or 0) | (py or 0)) & 15 == 0)
+    st = _stream(dev, stream)
     if options is None:
-        _check(lib().norm_rms_fwd(*args), "norm_rms_fwd")
+        status = L.norm_rms_fwd(px, pg, py, pr, M, N, float(eps), dt, pw, nw, st)
+        if status:
+            _fail(status, "norm_rms_fwd")
     else:
-        _check(lib().norm_rms_fwd_ex(*args, _opt(options)), "norm_rms_fwd_ex")
+        status = L.norm_rms_fwd_ex(px, pg, py, pr, M, N, float(eps), dt, pw, nw, st,
+                                   _opt(options))
+        if status:
+            _fail(status, "norm_rms_fwd_ex")
     return y
 
 
 def norm_ln_fwd(x, gamma, beta, y, mean=None, rstd=None, eps: float = 1e-5, workspace=None,
                 stream=None, options=None):
     """y = (x - mean) * rstd * gamma + beta per row; mean and rstd saved if given."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(x)
-    _need(x, "x", M * N, x.dtype, dev)
-    _need(y, "y", M * N, x.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
-    _need(beta, "beta", N, _pdtype(x, gamma), dev)
-    _need(mean, "mean", M, torch.float32, dev)
-    _need(rstd, "rstd", M, torch.float32, dev)
-    dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, dev, workspace, options, stream,
-                                  _aligned16(x, gamma, beta, y))
-    args = (_ptr(x), _ptr(gamma), _ptr(beta), _ptr(y), _ptr(mean), _ptr(rstd), M, N, float(eps),
-            dt, _ptr(ws), ws_bytes, _stream(dev, stream))
+    xd = x.dtype
+    gd = xd if gamma is None else gamma.dtype
+    px = _need(x, "x", M * N, xd, dev)
+    py = _need(y, "y", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pb = _need(beta, "beta", N, gd, dev)
+    pm = _need(mean, "mean", M, _F32, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _fwd_workspace(M, N, True, dt, dev, workspace, options, stream,
+                                  ((px or 0) | (pg or 0) | (pb or 0) | (py or 0)) & 15 == 0)
+    st = _stream(dev, stream)
     if options is None:
-        _check(lib().norm_ln_fwd(*args), "norm_ln_fwd")
+        status = L.norm_ln_fwd(px, pg, pb, py, pm, pr, M, N, float(eps), dt, pw, nw, st)
+        if status:
+            _fail(status, "norm_ln_fwd")
     else:
-        _check(lib().norm_ln_fwd_ex(*args, _opt(options)), "norm_ln_fwd_ex")
+        status = L.norm_ln_fwd_ex(px, pg, pb, py, pm, pr, M, N, float(eps), dt, pw, nw, st,
+                                  _opt(options))
+        if status:
+            _fail(status, "norm_ln_fwd_ex")
     return y
 
 
@@ -337,74 +346,101 @@ def norm_bwd_workspace_size(M: int, N: int, is_layernorm: bool, dtype: int, opti
                                                 _opt(options)))
 
 
+_BWD_WS = {}
+
+
 def _workspace(M, N, ln, dtype, dev, workspace, options, stream):
-    """The caller's workspace (the library checks its size), or a new one of the size the
-    call needs."""
+    """(address, bytes, tensor) of the caller's workspace (the library checks its size),
+    or of a new one of the size the call needs."""
     if workspace is None:
+        key = (M, N, ln, dtype)
+        need = _BWD_WS.get(key) if options is None else None
+        if need is None:
+            need = norm_bwd_workspace_size(M, N, ln, dtype, options)
+            if options is None:
+                _BWD_WS[key] = need
         torch = _torch()
-        need = norm_bwd_workspace_size(M, N, ln, dtype, options)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         _keep_for_stream(workspace, dev, stream)
-    return workspace, workspace.numel() * workspace.element_size()
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size(), workspace
 
 
 def norm_rms_bwd(dy, x, gamma, rstd, dx, dgamma, workspace=None, stream=None, options=None):
     """dx and dgamma (overwritten) of RMSNorm from the forward's saved rstd."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(x)
-    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
-        _need(t, n, k, x.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
-    _need(rstd, "rstd", M, torch.float32, dev)
-    _need(dgamma, "dgamma", N, torch.float32, dev)
-    dt = _types(x, gamma)
-    ws, ws_bytes = _workspace(M, N, False, dt, dev, workspace, options, stream)
-    args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(rstd), _ptr(dx), _ptr(dgamma), M, N, dt,
-            _ptr(ws), ws_bytes, _stream(dev, stream))
+    xd = x.dtype
+    gd = xd if gamma is None else gamma.dtype
+    pdy = _need(dy, "dy", M * N, xd, dev)
+    px = _need(x, "x", M * N, xd, dev)
+    pdx = _need(dx, "dx", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    pdg = _need(dgamma, "dgamma", N, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _workspace(M, N, False, dt, dev, workspace, options, stream)
+    st = _stream(dev, stream)
     if options is None:
-        _check(lib().norm_rms_bwd(*args), "norm_rms_bwd")
+        status = L.norm_rms_bwd(pdy, px, pg, pr, pdx, pdg, M, N, dt, pw, nw, st)
+        if status:
+            _fail(status, "norm_rms_bwd")
     else:
-        _check(lib().norm_rms_bwd_ex(*args, _opt(options)), "norm_rms_bwd_ex")
+        status = L.norm_rms_bwd_ex(pdy, px, pg, pr, pdx, pdg, M, N, dt, pw, nw, st,
+                                   _opt(options))
+        if status:
+            _fail(status, "norm_rms_bwd_ex")
     return dx, dgamma
 
 
 def norm_ln_bwd(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, workspace=None, stream=None,
                 options=None):
     """dx, dgamma and dbeta (overwritten) of LayerNorm from the saved mean and rstd."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(x)
-    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
-        _need(t, n, k, x.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
-    for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
-                    (dbeta, "dbeta", N)):
-        _need(t, n, k, torch.float32, dev)
-    dt = _types(x, gamma)
-    ws, ws_bytes = _workspace(M, N, True, dt, dev, workspace, options, stream)
-    args = (_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd), _ptr(dx), _ptr(dgamma),
-            _ptr(dbeta), M, N, dt, _ptr(ws), ws_bytes, _stream(dev, stream))
+    xd = x.dtype
+    gd = xd if gamma is None else gamma.dtype
+    pdy = _need(dy, "dy", M * N, xd, dev)
+    px = _need(x, "x", M * N, xd, dev)
+    pdx = _need(dx, "dx", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pm = _need(mean, "mean", M, _F32, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    pdg = _need(dgamma, "dgamma", N, _F32, dev)
+    pdb = _need(dbeta, "dbeta", N, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _workspace(M, N, True, dt, dev, workspace, options, stream)
+    st = _stream(dev, stream)
     if options is None:
-        _check(lib().norm_ln_bwd(*args), "norm_ln_bwd")
+        status = L.norm_ln_bwd(pdy, px, pg, pm, pr, pdx, pdg, pdb, M, N, dt, pw, nw, st)
+        if status:
+            _fail(status, "norm_ln_bwd")
     else:
-        _check(lib().norm_ln_bwd_ex(*args, _opt(options)), "norm_ln_bwd_ex")
+        status = L.norm_ln_bwd_ex(pdy, px, pg, pm, pr, pdx, pdg, pdb, M, N, dt, pw, nw, st,
+                                  _opt(options))
+        if status:
+            _fail(status, "norm_ln_bwd_ex")
     return dx, dgamma, dbeta
 
 
 def norm_ln_bwd_noalloc(dy, x, gamma, mean, rstd, dx, dgamma, dbeta, stream=None):
     """norm_ln_bwd on the library's static scratch: no workspace, no allocation (the
     binding allocates nothing either).  Calls that overlap on one device race."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(x)
-    for t, n, k in ((dy, "dy", M * N), (x, "x", M * N), (dx, "dx", M * N)):
-        _need(t, n, k, x.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
-    for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
-                    (dbeta, "dbeta", N)):
-        _need(t, n, k, torch.float32, dev)
-    _check(lib().norm_ln_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(gamma), _ptr(mean), _ptr(rstd),
-                                     _ptr(dx), _ptr(dgamma), _ptr(dbeta), M, N,
-                                     _types(x, gamma), _stream(dev, stream)),
-           "norm_ln_bwd_noalloc")
+    xd = x.dtype
+    gd = xd if gamma is None else gamma.dtype
+    pdy = _need(dy, "dy", M * N, xd, dev)
+    px = _need(x, "x", M * N, xd, dev)
+    pdx = _need(dx, "dx", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pm = _need(mean, "mean", M, _F32, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    pdg = _need(dgamma, "dgamma", N, _F32, dev)
+    pdb = _need(dbeta, "dbeta", N, _F32, dev)
+    status = L.norm_ln_bwd_noalloc(pdy, px, pg, pm, pr, pdx, pdg, pdb, M, N, _types(xd, gd),
+                                   _stream(dev, stream))
+    if status:
+        _fail(status, "norm_ln_bwd_noalloc")
     return dx, dgamma, dbeta
 
 
@@ -427,39 +463,50 @@ def norm_cluster_resident(is_backward: bool, is_layernorm: bool, M: int, N: int,
 def norm_rms_fwd_add(x, residual, gamma, y, sum_out, rstd=None, eps: float = 1e-6,
                      workspace=None, stream=None, options=None):
     """sum_out = x + residual (rounded to x's type); y = RMSNorm(sum_out)."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(x)
-    for t, n in ((x, "x"), (residual, "residual"), (y, "y"), (sum_out, "sum_out")):
-        _need(t, n, M * N, x.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
-    _need(rstd, "rstd", M, torch.float32, dev)
-    dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, False, dt, dev, workspace, options, stream,
-                                  _aligned16(x, residual, gamma, y, sum_out))
-    _check(lib().norm_rms_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(y), _ptr(sum_out),
-                                  _ptr(rstd), M, N, float(eps), dt, _ptr(ws), ws_bytes,
-                                  _stream(dev, stream), _opt(options)), "norm_rms_fwd_add")
+    xd = x.dtype
+    gd = xd if gamma is None else gamma.dtype
+    px = _need(x, "x", M * N, xd, dev)
+    pres = _need(residual, "residual", M * N, xd, dev)
+    py = _need(y, "y", M * N, xd, dev)
+    ps = _need(sum_out, "sum_out", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _fwd_workspace(
+        M, N, False, dt, dev, workspace, options, stream,
+        ((px or 0) | (pres or 0) | (pg or 0) | (py or 0) | (ps or 0)) & 15 == 0)
+    status = L.norm_rms_fwd_add(px, pres, pg, py, ps, pr, M, N, float(eps), dt, pw, nw,
+                                _stream(dev, stream), _opt(options))
+    if status:
+        _fail(status, "norm_rms_fwd_add")
     return y, sum_out
 
 
 def norm_ln_fwd_add(x, residual, gamma, beta, y, sum_out, mean=None, rstd=None,
                     eps: float = 1e-5, workspace=None, stream=None, options=None):
     """sum_out = x + residual (rounded to x's type); y = LayerNorm(sum_out)."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(x)
-    for t, n in ((x, "x"), (residual, "residual"), (y, "y"), (sum_out, "sum_out")):
-        _need(t, n, M * N, x.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(x, gamma), dev)
-    _need(beta, "beta", N, _pdtype(x, gamma), dev)
-    _need(mean, "mean", M, torch.float32, dev)
-    _need(rstd, "rstd", M, torch.float32, dev)
-    dt = _types(x, gamma)
-    ws, ws_bytes = _fwd_workspace(M, N, True, dt, dev, workspace, options, stream,
-                                  _aligned16(x, residual, gamma, beta, y, sum_out))
-    _check(lib().norm_ln_fwd_add(_ptr(x), _ptr(residual), _ptr(gamma), _ptr(beta), _ptr(y),
-                                 _ptr(sum_out), _ptr(mean), _ptr(rstd), M, N, float(eps), dt,
-                                 _ptr(ws), ws_bytes, _stream(dev, stream), _opt(options)),
-           "norm_ln_fwd_add")
+    xd = x.dtype
+    gd = xd if gamma is None else gamma.dtype
+    px = _need(x, "x", M * N, xd, dev)
+    pres = _need(residual, "residual", M * N, xd, dev)
+    py = _need(y, "y", M * N, xd, dev)
+    ps = _need(sum_out, "sum_out", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pb = _need(beta, "beta", N, gd, dev)
+    pm = _need(mean, "mean", M, _F32, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _fwd_workspace(
+        M, N, True, dt, dev, workspace, options, stream,
+        ((px or 0) | (pres or 0) | (pg or 0) | (pb or 0) | (py or 0) | (ps or 0)) & 15 == 0)
+    status = L.norm_ln_fwd_add(px, pres, pg, pb, py, ps, pm, pr, M, N, float(eps), dt, pw, nw,
+                               _stream(dev, stream), _opt(options))
+    if status:
+        _fail(status, "norm_ln_fwd_add")
     return y, sum_out
 
 
@@ -467,39 +514,48 @@ def norm_rms_bwd_add(dy, sum_in, gamma, rstd, dsum, dx, dgamma, workspace=None, 
                      options=None):
     """dx = RMSNorm backward at sum_in (+ dsum, the gradient arriving at the sum, if given);
     dgamma overwritten."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(sum_in)
-    for t, n in ((dy, "dy"), (sum_in, "sum_in"), (dsum, "dsum"), (dx, "dx")):
-        _need(t, n, M * N, sum_in.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), dev)
-    _need(rstd, "rstd", M, torch.float32, dev)
-    _need(dgamma, "dgamma", N, torch.float32, dev)
-    dt = _types(sum_in, gamma)
-    ws, ws_bytes = _workspace(M, N, False, dt, dev, workspace, options, stream)
-    _check(lib().norm_rms_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(rstd), _ptr(dsum),
-                                  _ptr(dx), _ptr(dgamma), M, N, dt, _ptr(ws), ws_bytes,
-                                  _stream(dev, stream), _opt(options)),
-           "norm_rms_bwd_add")
+    xd = sum_in.dtype
+    gd = xd if gamma is None else gamma.dtype
+    pdy = _need(dy, "dy", M * N, xd, dev)
+    ps = _need(sum_in, "sum_in", M * N, xd, dev)
+    pds = _need(dsum, "dsum", M * N, xd, dev)
+    pdx = _need(dx, "dx", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    pdg = _need(dgamma, "dgamma", N, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _workspace(M, N, False, dt, dev, workspace, options, stream)
+    status = L.norm_rms_bwd_add(pdy, ps, pg, pr, pds, pdx, pdg, M, N, dt, pw, nw,
+                                _stream(dev, stream), _opt(options))
+    if status:
+        _fail(status, "norm_rms_bwd_add")
     return dx, dgamma
 
 
 def norm_ln_bwd_add(dy, sum_in, gamma, mean, rstd, dsum, dx, dgamma, dbeta, workspace=None,
                     stream=None, options=None):
     """dx = LayerNorm backward at sum_in (+ dsum if given); dgamma, dbeta overwritten."""
-    torch = _torch()
+    L = _lib or lib()
     M, N, dev = _shape(sum_in)
-    for t, n in ((dy, "dy"), (sum_in, "sum_in"), (dsum, "dsum"), (dx, "dx")):
-        _need(t, n, M * N, sum_in.dtype, dev)
-    _need(gamma, "gamma", N, _pdtype(sum_in, gamma), dev)
-    for t, n, k in ((mean, "mean", M), (rstd, "rstd", M), (dgamma, "dgamma", N),
-                    (dbeta, "dbeta", N)):
-        _need(t, n, k, torch.float32, dev)
-    dt = _types(sum_in, gamma)
-    ws, ws_bytes = _workspace(M, N, True, dt, dev, workspace, options, stream)
-    _check(lib().norm_ln_bwd_add(_ptr(dy), _ptr(sum_in), _ptr(gamma), _ptr(mean), _ptr(rstd),
-                                 _ptr(dsum), _ptr(dx), _ptr(dgamma), _ptr(dbeta), M, N, dt,
-                                 _ptr(ws), ws_bytes, _stream(dev, stream),
-                                 _opt(options)), "norm_ln_bwd_add")
+    xd = sum_in.dtype
+    gd = xd if gamma is None else gamma.dtype
+    pdy = _need(dy, "dy", M * N, xd, dev)
+    ps = _need(sum_in, "sum_in", M * N, xd, dev)
+    pds = _need(dsum, "dsum", M * N, xd, dev)
+    pdx = _need(dx, "dx", M * N, xd, dev)
+    pg = _need(gamma, "gamma", N, gd, dev)
+    pm = _need(mean, "mean", M, _F32, dev)
+    pr = _need(rstd, "rstd", M, _F32, dev)
+    pdg = _need(dgamma, "dgamma", N, _F32, dev)
+    pdb = _need(dbeta, "dbeta", N, _F32, dev)
+    dt = _types(xd, gd)
+    pw, nw, keep = _workspace(M, N, True, dt, dev, workspace, options, stream)
+    status = L.norm_ln_bwd_add(pdy, ps, pg, pm, pr, pds, pdx, pdg, pdb, M, N, dt, pw, nw,
+                               _stream(dev, stream), _opt(options))
+    if status:
+        _fail(status, "norm_ln_bwd_add")
     return dx, dgamma, dbeta
 
 
