@@ -327,6 +327,54 @@ def stream_reference_ms(nbytes, device, two_reads=False, reps=10):
     return ms
 
 
+def host_overhead(w, device, calls=2000):
+    """Host time per call, in microseconds, of the workload's forward, backward and step
+    through the binding and through bare ctypes calls with the arguments prepared, one
+    buffer set (so the GPU keeps up at small sizes): (host-only time, time to the GPU's
+    end) per entry.  The binding's share is the difference."""
+    import torch
+    import row_normalization_norm_amd as rn
+    b = Bench(w, device)
+    k = b.bufs[0]
+    L = rn.lib()
+    ln = w.kind == "ln"
+    code = lib_dtype(w)
+    st = torch.cuda.current_stream().cuda_stream
+    p = lambda t: None if t is None else t.data_ptr()
+    fws = (p(b.fws), 0 if b.fws is None else b.fws.numel())
+    bws = (b.ws.data_ptr(), b.ws.numel())
+    if ln:
+        fa = (p(k["x"]), p(b.gamma), p(b.beta), p(k["y"]), p(k["mean"]), p(k["rstd"]), w.M, w.N,
+              w.eps, code) + fws + (st,)
+        ba = (p(k["dy"]), p(k["x"]), p(b.gamma), p(k["mean"]), p(k["rstd"]), p(k["dx"]),
+              p(b.dgamma), p(b.dbeta), w.M, w.N, code) + bws + (st,)
+        cf, cb = (lambda: L.norm_ln_fwd(*fa)), (lambda: L.norm_ln_bwd(*ba))
+    else:
+        fa = (p(k["x"]), p(b.gamma), p(k["y"]), p(k["rstd"]), w.M, w.N, w.eps, code) + fws + (st,)
+        ba = (p(k["dy"]), p(k["x"]), p(b.gamma), p(k["rstd"]), p(k["dx"]), p(b.dgamma), w.M, w.N,
+              code) + bws + (st,)
+        cf, cb = (lambda: L.norm_rms_fwd(*fa)), (lambda: L.norm_rms_bwd(*ba))
+
+    def timed(fn):
+        for _ in range(50):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(calls):
+            fn()
+        t1 = time.perf_counter()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        return [round((t1 - t0) / calls * 1e6, 2), round((t2 - t0) / calls * 1e6, 2)]
+
+    return {"workload": w.name, "calls": calls,
+            "binding_fwd": timed(lambda: b.forward(0)),
+            "binding_bwd": timed(lambda: b.backward(0)),
+            "binding_step": timed(lambda: b.step(0)),
+            "ctypes_fwd": timed(cf), "ctypes_bwd": timed(cb),
+            "ctypes_step": timed(lambda: (cf(), cb()))}
+
+
 def copy_probe(nbytes, steps, device):
     """Time a plain device copy of nbytes (torch's copy kernel): the achievable
     read+write bandwidth next to the nominal peak, and the kernel whose rocprofv3
@@ -675,6 +723,9 @@ def main():
     ap.add_argument("--all", metavar="JSON", help="also time every workload, write a table")
     ap.add_argument("--copy-probe", type=int, metavar="BYTES",
                     help="only time a plain device copy of BYTES and print it")
+    ap.add_argument("--host-overhead", action="store_true",
+                    help="only time the host side of --workload's calls (binding and bare "
+                         "ctypes, microseconds per call) and print it")
     ap.add_argument("--stream-reference", type=int, metavar="BYTES",
                     help="only time the streaming reference kernel (copy, then two reads "
                          "and one write) over BYTES per stream, --steps launches per "
@@ -714,6 +765,9 @@ def main():
     device = torch.device("cuda:0")
     if args.copy_probe:
         print(json.dumps(copy_probe(args.copy_probe, args.steps, device)), flush=True)
+        return
+    if args.host_overhead:
+        print(json.dumps(host_overhead(workload_by_name(args.workload), device)), flush=True)
         return
 
     if args.stream_reference:
